@@ -1,0 +1,225 @@
+/*
+ * gdnq.h -- C ABI of libgdnq.so: quantized recurrent-state decode for
+ * Gated-DeltaNet (GDN) and Kimi-Delta-Attention (KDA) linear-attention
+ * layers on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources are web pages; the method is given
+ * there in prose, the formulas below are the readings this library takes):
+ *
+ *  - Recurrence ("LinQuant: Functional Invariances for Low-Precision Linear
+ *    Recurrences", appendix Table 3, Gated DeltaNet and KDA rows).  The
+ *    state of one (batch, head) is S in R^{dk x dv}, key channel i = row,
+ *    value channel j = column (the transpose of Table 3's dv x dk form):
+ *        S' = a S  (GDN, scalar gate)   or  diag(a) S  (KDA, a in R^dk)
+ *        u  = b (v - S'^T k),   S_t = S' + k u^T,   o = S_t^T q.
+ *
+ *  - Per-token state traffic ("LeapQuant: Efficient Linear Attention with
+ *    Accurate Recurrent State Quantization", project page, opening
+ *    paragraphs): each token loads the state from HBM, applies a light
+ *    update and writes it back; the state is kept in 8 bits here.
+ *
+ *  - State codec (LeapQuant, residual-smoothing paragraph; STEPQuant page,
+ *    key-row and value-column scales).  Layout 0, per head, every step one
+ *    IEEE fp32 operation rounded to nearest even, no fused multiply-add:
+ *        r_i = max_j |X_ij|,  s_i = sqrt(r_i),  rho_i = 1/s_i,
+ *        Y_ij = X_ij rho_i,   m_j = max_i |Y_ij|,
+ *        c_j = m_j/127,  iota_j = 127/m_j,  Q_ij = rint_even(Y_ij iota_j)
+ *    clamped to [-127, 127] (zero rows/columns: scale 0, code 0; a column
+ *    whose 127/m_j overflows fp32 is a zero column).  Dequantized value:
+ *        D(Q)_ij = (Q_ij c_j) s_i   (two rounded fp32 products).
+ *
+ *  - Per-window mode (LeapQuant, per-window quantization paragraph): the
+ *    INT8 state of the window start stays fixed for W tokens, each token's
+ *    rank-1 update (k_t, u_t) is buffered in fp32, outputs are computed
+ *    from the fixed state plus the buffer, and the state is rebuilt and
+ *    requantized only at the window end (gdn_quant_window_flush).
+ *
+ *  - Compensator Tokens (LeapQuant, Compensator Tokens paragraph): before
+ *    quantization, r rank-1 terms p_c w_c^T (fp32) are taken out of the
+ *    state by `power_iters` steps of power iteration each (start: the
+ *    all-equal unit vector; v <- R^T R v / |R^T R v|; p = R v, w = v;
+ *    sequential deflation R <- R - p w^T with the stored fp32 pair).  They
+ *    are part of the fixed state inside a window and decay with it.
+ *
+ *  - DAMP rows ("DAMP: Decay-Aware Mixed-Precision Recurrent-State
+ *    Quantization", abstract).  Layout 1: n_hp key rows per head, chosen
+ *    offline by calibrate_scales, are stored as IEEE fp16 (round to nearest
+ *    even, saturating at +-65504); the other rows are INT8 with
+ *    value-column scales over those rows only and no row smoothing.
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are caller-allocated, contiguous, 16-byte
+ *    aligned device buffers; the library allocates nothing, keeps no state
+ *    between calls except a thread-local error string, and is reentrant.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  The library never synchronizes.
+ *  - State arrays are updated in place.  q, k, v, a, b, o must not overlap
+ *    any state array; overlapping buffers are rejected.
+ *  - Return value: GDNQ_OK, or an error code with a message readable from
+ *    gdnq_last_error().  Argument errors are found on the host before any
+ *    launch, so a failed call has not touched device memory.
+ *  - Inputs that are NaN or infinite give undefined results.  Gates must
+ *    satisfy 0 < a <= 1 and the product of a window's gates must stay above
+ *    1e-30 per key channel (the KDA buffer stores k / (cumulative gate)).
+ *  - bf16 inputs are widened exactly; a bf16 output is rounded to nearest
+ *    even from fp32.
+ */
+#ifndef GDNQ_H
+#define GDNQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    GDNQ_OK = 0,
+    GDNQ_EINVAL = 1,      /* invalid argument (null, misaligned, overlap, range) */
+    GDNQ_EUNSUPPORTED = 2,/* shape or mode this build does not implement        */
+    GDNQ_ELAUNCH = 3      /* the HIP runtime reported an error at launch        */
+};
+
+enum { GDNQ_DECAY_SCALAR = 0, GDNQ_DECAY_CHANNEL = 1 };
+enum { GDNQ_IO_F32 = 0, GDNQ_IO_BF16 = 1 };
+enum { GDNQ_LAYOUT_ROWCOL = 0, GDNQ_LAYOUT_DAMP = 1 };
+
+/* flags */
+#define GDNQ_DEBUG_PREQUANT 1u  /* also store the fp32 tensor the codec consumed */
+
+/* Problem description shared by all calls. */
+typedef struct {
+    int32_t B, H;         /* batch and heads: B*H independent states           */
+    int32_t dk, dv;       /* key / value head dims, each 64 or 128             */
+    int32_t W;            /* window length, >= 1                               */
+    int32_t r;            /* Compensator Tokens per head, 0..8                 */
+    int32_t decay;        /* GDNQ_DECAY_SCALAR or GDNQ_DECAY_CHANNEL           */
+    int32_t io_dtype;     /* GDNQ_IO_F32 or GDNQ_IO_BF16 for q, k, v and o     */
+    int32_t layout;       /* GDNQ_LAYOUT_ROWCOL or GDNQ_LAYOUT_DAMP            */
+    int32_t n_hp;         /* DAMP fp16 rows per head (layout 1), 1..dk/2       */
+    int32_t power_iters;  /* power-iteration steps per compensator, 1..64      */
+    uint32_t flags;       /* GDNQ_DEBUG_PREQUANT or 0                          */
+} gdnq_desc;
+
+/*
+ * Quantized state of B*H heads (all device pointers; NULL where unused).
+ * Per-step mode is W == 1 && r == 0; everything else is window mode.
+ *   codes       int8   layout 0: [B,H,dk,dv]; layout 1: [B,H,dk-n_hp,dv]
+ *                      (the non-DAMP rows in ascending row order); row-major
+ *   row_scale   fp32   [B,H,dk]        layout 0 only (smoothing scales s)
+ *   col_scale   fp32   [B,H,dv]        value-column scales c
+ *   comp_k      fp32   [B,H,r,dk]      compensator key-side vectors p (r > 0)
+ *   comp_v      fp32   [B,H,r,dv]      compensator value-side unit vectors w
+ *   buf_k       fp32   [B,H,W,dk]      window buffer keys k_t / G_t, where
+ *                                      G_t is the gate product since the
+ *                                      window start (per key channel)
+ *   buf_u       fp32   [B,H,W,dv]      window buffer updates u_t
+ *   g_cur       fp32   [B,H] (scalar) or [B,H,dk] (channel): gate product
+ *                                      since the window start
+ *   hp_rows     uint16 [B,H,n_hp,dv]   layout 1: fp16 bit patterns
+ *   hp_idx      int32  [B,H,n_hp]      layout 1: row indices, strictly
+ *                                      ascending, in [0, dk)
+ *   prequant_out fp32  [B,H,dk,dv]     with GDNQ_DEBUG_PREQUANT: the fp32
+ *                                      tensor handed to the codec
+ * Buffers for window mode (buf_k, buf_u, g_cur) are needed when W > 1,
+ * r > 0 or layout == GDNQ_LAYOUT_DAMP.
+ */
+typedef struct {
+    int8_t *codes;
+    float *row_scale;
+    float *col_scale;
+    float *comp_k;
+    float *comp_v;
+    float *buf_k;
+    float *buf_u;
+    float *g_cur;
+    uint16_t *hp_rows;
+    int32_t *hp_idx;
+    float *prequant_out;
+} gdnq_state;
+
+/*
+ * One decode token for all B*H heads.
+ *   q, k   device, io_dtype, [B,H,dk];   v device, io_dtype, [B,H,dv]
+ *   a      device fp32 [B,H] (scalar decay) or [B,H,dk] (channel decay)
+ *   b      device fp32 [B,H]
+ *   o      device, io_dtype, [B,H,dv]    output o_t = S_t^T q_t
+ *   t_in_window: position of this token in the current window, 0..W-1
+ *               (all heads move in lockstep; must be 0 in per-step mode).
+ * Per-step mode: dequantize, update, emit o from the updated fp32 state,
+ * requantize and store codes and scales in place (one fused kernel).
+ * Window mode: read the fixed state, compensators and the t_in_window
+ * buffered tokens, emit o, append (k_t, u_t) to buffer slot t_in_window
+ * and update g_cur; the codes are not written.
+ * Per-step mode with layout 1 runs the window step and a one-token flush.
+ */
+int gdn_quant_decode_step(const gdnq_desc *desc, const gdnq_state *state, const void *q,
+                          const void *k, const void *v, const float *a, const float *b,
+                          void *o, int32_t t_in_window, void *stream);
+
+/*
+ * Window end: rebuild S_W = diag(G) (D(Q) + sum_c p_c w_c^T) +
+ * sum_{t<n} ((G/G_t) . k_t) u_t^T from the first n_tokens buffer slots
+ * (fp32 MFMA rank-(n+r) product), take r new Compensator Tokens out of it,
+ * requantize the residual, store codes, scales and compensators, and reset
+ * g_cur to 1.  n_tokens in 1..W; n_tokens < W gives a self-contained
+ * snapshot of a partial window.  In per-step mode this is a no-op.
+ */
+int gdn_quant_window_flush(const gdnq_desc *desc, const gdnq_state *state, int32_t n_tokens,
+                           void *stream);
+
+/*
+ * Encode fp32 states S [B,H,dk,dv] (device): r compensators, then the
+ * residual through the codec of desc->layout (layout 1 reads
+ * state->hp_idx).  Writes codes, scales, compensators; sets g_cur to 1
+ * when given.  This is the back half of the flush.
+ */
+int gdn_state_quantize(const gdnq_desc *desc, const float *S, const gdnq_state *state,
+                       void *stream);
+
+/*
+ * Decode the stored state: S_out [B,H,dk,dv] fp32 (device) =
+ * D(Q) + sum_c p_c w_c^T, i.e. the fixed state of the window start.
+ */
+int gdn_state_dequantize(const gdnq_desc *desc, const gdnq_state *state, float *S_out,
+                         void *stream);
+
+/*
+ * DAMP calibration (DAMP abstract: error energy and decay persistence
+ * pick the high-risk channels offline).  Runs n_steps of the fp32
+ * recurrence from S0 [B,H,dk,dv]; after each step quantizes every head
+ * with value-column scales over all rows and no smoothing and accumulates
+ * E_i = sum_t sum_j (S_ij - D_ij)^2; abar_i = mean gate of key channel i;
+ * score_i = E_i / max(1 - abar_i, 1e-6).  Writes the n_hp highest-scoring
+ * rows per head (lower index first on ties), ascending, to hp_idx_out
+ * [B,H,n_hp] int32, and the scores to row_score_out [B,H,dk] fp32 when
+ * not NULL.  k, v: io_dtype [n_steps,B,H,dk|dv]; a fp32 [n_steps,B,H] or
+ * [n_steps,B,H,dk]; b fp32 [n_steps,B,H].  All device pointers.
+ */
+int calibrate_scales(const gdnq_desc *desc, const float *S0, const void *k, const void *v,
+                     const float *a, const float *b, int32_t n_steps, int32_t *hp_idx_out,
+                     float *row_score_out, void *stream);
+
+/*
+ * Baseline: one decode token on fp32 states S [B,H,dk,dv] (device, in
+ * place), same inputs and output as gdn_quant_decode_step.
+ */
+int gdn_fp32_decode_step(const gdnq_desc *desc, float *S, const void *q, const void *k,
+                         const void *v, const float *a, const float *b, void *o, void *stream);
+
+/*
+ * Byte sizes of the 11 gdnq_state arrays for this descriptor, in field
+ * order (codes, row_scale, col_scale, comp_k, comp_v, buf_k, buf_u, g_cur,
+ * hp_rows, hp_idx, prequant_out); 0 where the array is unused.
+ */
+int gdnq_state_sizes(const gdnq_desc *desc, size_t bytes_out[11]);
+
+/* Message of the last error on this thread ("" if none). */
+const char *gdnq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDNQ_H */

@@ -1,0 +1,348 @@
+// codec.hpp -- device-side state codec and Compensator Token extraction on
+// the register tile (see tile.hpp for the layout).  Every kernel that writes
+// codes calls these functions, so the stand-alone codec and the codec fused
+// into the decode/flush kernels are the same code.
+//
+// Codec, layout 0 (LeapQuant project page, residual-smoothing paragraph:
+// rows are balanced before quantization; STEPQuant page: key-row and
+// value-column scales).  Per head, each step one IEEE fp32 operation with
+// round to nearest even and no fused multiply-add (the library is built with
+// -ffp-contract=off and correctly rounded divide and sqrt):
+//   r_i = max_j |X_ij|; s_i = sqrt(r_i); rho_i = 1/s_i (0 if s_i = 0)
+//   Y_ij = X_ij rho_i; m_j = max_i |Y_ij|
+//   c_j = m_j/127, iota_j = 127/m_j (both 0 if m_j = 0 or 127/m_j overflows)
+//   Q_ij = rint_even(Y_ij iota_j)
+// No clamp is applied: |Y_ij| <= m_j and iota_j <= (127/m_j)(1 + 2^-24), so
+// |Y_ij iota_j| <= 127 (1 + 2^-24)^2 < 127.5 and the code is in [-127, 127].
+//
+// Layout 1 (DAMP abstract: high-risk channels in higher precision, the rest
+// INT8): listed rows -> IEEE fp16 (round to nearest even, saturating at
+// +-65504); other rows -> the per-column steps above with s = 1 and m_j
+// taken over those rows only; their codes are stored compacted.
+//
+// Compensator Tokens (LeapQuant, Compensator Tokens paragraph): r rank-1
+// terms taken out by power iteration before the codec runs; see
+// power_deflate.
+#pragma once
+
+#include "launch.hpp"
+#include "tile.hpp"
+
+namespace gdnq {
+
+template <class G>
+struct CodecLds {
+    float rho[G::DK];
+    float red[2][G::NW][G::DV];
+    float iota[G::DV];
+    int misc;
+};
+
+// Which of a thread's 8 rows are DAMP (fp16) rows, their slot in hp_idx and,
+// for the other rows, their index among the compacted INT8 rows.
+struct RowMap {
+    int slot[8];   // -1: INT8 row
+    int crow[8];   // compacted INT8 row index (valid when slot < 0)
+};
+
+template <class G>
+__device__ __forceinline__ RowMap row_map(const Lane &c, const int *hp_lds, int n_hp)
+{
+    RowMap m;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const int i = row_of<G>(c, k);
+        int slot = -1, below = 0;
+        for (int t = 0; t < n_hp; t++) {
+            const int h = hp_lds[t];
+            slot = (h == i) ? t : slot;
+            below += (h < i) ? 1 : 0;
+        }
+        m.slot[k] = slot;
+        m.crow[k] = i - below;
+    }
+    return m;
+}
+
+__device__ __forceinline__ float select8(const float (&v)[8], int i)
+{
+    float r = v[0];
+#pragma unroll
+    for (int k = 1; k < 8; k++) r = (i == k) ? v[k] : r;
+    return r;
+}
+
+// Column scales from the per-wave column maxima in L.red[0]; thread t < DV
+// owns column t.  Writes c to global memory and iota to LDS.
+template <class G>
+__device__ __forceinline__ void column_scales(const Lane &c, CodecLds<G> &L, float *__restrict__ col_scale)
+{
+    if (c.t < G::DV) {
+        float m = L.red[0][0][c.t];
+#pragma unroll
+        for (int w = 1; w < G::NW; w++) m = fmaxf(m, L.red[0][w][c.t]);
+        float cj = 0.0f, io = 0.0f;
+        if (m > 0.0f) {
+            io = 127.0f / m;
+            if (__builtin_isinf(io)) io = 0.0f;
+            else cj = m / 127.0f;
+        }
+        col_scale[c.t] = cj;
+        L.iota[c.t] = io;
+    }
+}
+
+// Per-thread column maxima m[8] -> L.red[0][w][*] (wave partials).
+template <class G>
+__device__ __forceinline__ void column_max_to_lds(const Lane &c, CodecLds<G> &L, const float (&m)[8])
+{
+    float z[2];
+    col_reduce_scatter<G, OpMax, 8>(m, z);
+#pragma unroll
+    for (int p = 0; p < 2; p++) L.red[0][c.w][c.cb * 8 + scatter_index(c, p)] = z[p];
+}
+
+// Layout-0 codec of the register tile P (overwritten with Y).  Writes this
+// head's codes [DK][DV], row scales [DK] and column scales [DV].
+template <class G>
+__device__ void codec_rowcol(float (&P)[8][8], const Lane &c, CodecLds<G> &L, int8_t *__restrict__ codes,
+                             float *__restrict__ row_scale, float *__restrict__ col_scale)
+{
+    float r[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        float m = fabsf(P[k][0]);
+#pragma unroll
+        for (int j = 1; j < 8; j++) m = fmaxf(m, fabsf(P[k][j]));
+        r[k] = row_max<G>(m);
+    }
+    if (c.cb < 8) {  // lane cb owns row k = cb of its row group
+        const float rk = select8(r, c.cb);
+        const float s = (rk > 0.0f) ? sqrtf(rk) : 0.0f;
+        const float rho = (s > 0.0f) ? 1.0f / s : 0.0f;
+        const int i = row_of<G>(c, c.cb);
+        L.rho[i] = rho;
+        row_scale[i] = s;
+    }
+    wave_lds_sync();  // a row group lives in one wave
+    float rho[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) rho[k] = L.rho[row_of<G>(c, k)];
+    float m[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) m[j] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            P[k][j] = P[k][j] * rho[k];
+            m[j] = fmaxf(m[j], fabsf(P[k][j]));
+        }
+    column_max_to_lds<G>(c, L, m);
+    __syncthreads();
+    column_scales<G>(c, L, col_scale);
+    __syncthreads();
+    float io[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) io[j] = L.iota[c.cb * 8 + j];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        float y[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const float t = P[k][j] * io[j];
+            y[j] = t + RINT_MAGIC;
+        }
+        uint2 q;
+        q.x = pack_low_bytes(y[0], y[1], y[2], y[3]);
+        q.y = pack_low_bytes(y[4], y[5], y[6], y[7]);
+        *reinterpret_cast<uint2 *>(codes + (size_t)row_of<G>(c, k) * G::DV + c.cb * 8) = q;
+    }
+}
+
+// fp32 -> IEEE fp16 bits, round to nearest even, saturating at +-65504.
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float x)
+{
+    x = fminf(fmaxf(x, -65504.0f), 65504.0f);
+    _Float16 h = (_Float16)x;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// Layout-1 (DAMP) codec of P.  codes_c: this head's compacted INT8 rows
+// [DK-n_hp][DV]; hp_rows: [n_hp][DV] fp16 bits.
+template <class G>
+__device__ void codec_damp(float (&P)[8][8], const Lane &c, CodecLds<G> &L, const RowMap &rm,
+                           int8_t *__restrict__ codes_c, float *__restrict__ col_scale,
+                           uint16_t *__restrict__ hp_rows)
+{
+    float m[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) m[j] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const bool hp = rm.slot[k] >= 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) m[j] = hp ? m[j] : fmaxf(m[j], fabsf(P[k][j]));
+    }
+    column_max_to_lds<G>(c, L, m);
+    __syncthreads();
+    column_scales<G>(c, L, col_scale);
+    __syncthreads();
+    float io[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) io[j] = L.iota[c.cb * 8 + j];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        if (rm.slot[k] >= 0) {
+            uint32_t h[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                h[j] = (uint32_t)f32_to_f16_sat(P[k][2 * j]) | ((uint32_t)f32_to_f16_sat(P[k][2 * j + 1]) << 16);
+            *reinterpret_cast<uint4 *>(hp_rows + (size_t)rm.slot[k] * G::DV + c.cb * 8) =
+                make_uint4(h[0], h[1], h[2], h[3]);
+        } else {
+            float y[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const float t = P[k][j] * io[j];
+                y[j] = t + RINT_MAGIC;
+            }
+            uint2 q;
+            q.x = pack_low_bytes(y[0], y[1], y[2], y[3]);
+            q.y = pack_low_bytes(y[4], y[5], y[6], y[7]);
+            *reinterpret_cast<uint2 *>(codes_c + (size_t)rm.crow[k] * G::DV + c.cb * 8) = q;
+        }
+    }
+}
+
+// Column sums of per-thread partials y[8] over the whole tile, returned to
+// every thread for its own 8 columns.  Uses L.red[buf]; the caller
+// alternates buf between calls so one barrier per call suffices.
+template <class G>
+__device__ __forceinline__ void column_sum_all(const Lane &c, CodecLds<G> &L, int buf, const float (&yp)[8],
+                                               float (&y)[8])
+{
+    float z[2];
+    col_reduce_scatter<G, OpSum, 8>(yp, z);
+#pragma unroll
+    for (int p = 0; p < 2; p++) L.red[buf][c.w][c.cb * 8 + scatter_index(c, p)] = z[p];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        float s = L.red[buf][0][c.cb * 8 + j];
+#pragma unroll
+        for (int w = 1; w < G::NW; w++) s += L.red[buf][w][c.cb * 8 + j];
+        y[j] = s;
+    }
+}
+
+// Compensator Tokens by power iteration with sequential deflation, on the
+// register tile P (the rebuilt state; left holding the residual).
+// For each c < r: v = all-equal unit vector; `iters` times
+//   y = P^T (P v); if |y| = 0: on the first step restart from the unit
+//   vector of P's largest column (lowest index on ties) when P != 0,
+//   otherwise keep v; v = y/|y|.
+// p = P v, w = v (fp32), P -= p w^T.  P == 0 gives p = w = 0.
+// comp_k: this head's [r][DK]; comp_v: [r][DV].
+template <class G>
+__device__ void power_deflate(float (&P)[8][8], const Lane &c, CodecLds<G> &L, int r, int iters,
+                              float *__restrict__ comp_k, float *__restrict__ comp_v)
+{
+    int buf = 0;
+    for (int cc = 0; cc < r; cc++) {
+        bool nz = false;
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+#pragma unroll
+            for (int j = 0; j < 8; j++) nz |= (P[k][j] != 0.0f);
+        const int any = __syncthreads_or(nz);
+        float v[8], p[8];
+        if (!any) {
+#pragma unroll
+            for (int j = 0; j < 8; j++) { v[j] = 0.0f; p[j] = 0.0f; }
+        } else {
+            const float v0 = (G::DV == 128) ? 0.08838834764831845f : 0.125f;
+#pragma unroll
+            for (int j = 0; j < 8; j++) v[j] = v0;
+            bool restarted = false;
+            for (int it = 0; it < iters; it++) {
+                float x[8];
+#pragma unroll
+                for (int k = 0; k < 8; k++) {
+                    float s = P[k][0] * v[0];
+#pragma unroll
+                    for (int j = 1; j < 8; j++) s = fmaf(P[k][j], v[j], s);
+                    x[k] = row_sum<G>(s);
+                }
+                float yp[8], y[8];
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    float s = P[0][j] * x[0];
+#pragma unroll
+                    for (int k = 1; k < 8; k++) s = fmaf(P[k][j], x[k], s);
+                    yp[j] = s;
+                }
+                column_sum_all<G>(c, L, buf, yp, y);
+                buf ^= 1;
+                float n2 = y[0] * y[0];
+#pragma unroll
+                for (int j = 1; j < 8; j++) n2 = fmaf(y[j], y[j], n2);
+                n2 = row_sum<G>(n2);
+                if (n2 == 0.0f) {  // uniform: every lane holds the same n2
+                    if (it > 0 || restarted) break;
+                    float cn[8], cs[8];
+#pragma unroll
+                    for (int j = 0; j < 8; j++) {
+                        float s = P[0][j] * P[0][j];
+#pragma unroll
+                        for (int k = 1; k < 8; k++) s = fmaf(P[k][j], P[k][j], s);
+                        cn[j] = s;
+                    }
+                    column_sum_all<G>(c, L, buf, cn, cs);
+                    buf ^= 1;
+                    if (c.t == 0) {
+                        int best = 0;
+                        float bv = -1.0f;
+                        for (int j = 0; j < G::DV; j++) {
+                            float s = L.red[buf ^ 1][0][j];
+                            for (int w = 1; w < G::NW; w++) s += L.red[buf ^ 1][w][j];
+                            if (s > bv) { bv = s; best = j; }
+                        }
+                        L.misc = best;
+                    }
+                    __syncthreads();
+                    const int jb = L.misc;
+#pragma unroll
+                    for (int j = 0; j < 8; j++) v[j] = (c.cb * 8 + j == jb) ? 1.0f : 0.0f;
+                    restarted = true;
+                    it = -1;
+                    continue;
+                }
+                const float inv = 1.0f / sqrtf(n2);
+#pragma unroll
+                for (int j = 0; j < 8; j++) v[j] = y[j] * inv;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                float s = P[k][0] * v[0];
+#pragma unroll
+                for (int j = 1; j < 8; j++) s = fmaf(P[k][j], v[j], s);
+                p[k] = row_sum<G>(s);
+            }
+        }
+        if (c.cb == 0) {
+#pragma unroll
+            for (int k = 0; k < 8; k++) comp_k[(size_t)cc * G::DK + row_of<G>(c, k)] = p[k];
+        }
+        if (c.w == 0 && c.rgl == 0) store_f32x8(comp_v + (size_t)cc * G::DV + c.cb * 8, v);
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+#pragma unroll
+            for (int j = 0; j < 8; j++) P[k][j] = fmaf(-p[k], v[j], P[k][j]);
+    }
+    if (r > 0) __syncthreads();  // L.red is reused by the codec
+}
+
+}  // namespace gdnq

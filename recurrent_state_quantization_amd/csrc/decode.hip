@@ -1,0 +1,265 @@
+// decode.hip -- per-step decode kernels: the fused INT8 step (dequantize,
+// gated delta update, output, requantize, store) and the fp32-state
+// baseline step.  One workgroup per (batch, head) state.
+//
+// Recurrence: LinQuant (Functional Invariances for Low-Precision Linear
+// Recurrences), appendix Table 3, Gated DeltaNet / KDA rows, transposed to
+// S in R^{dk x dv}:  S' = diag(a) S;  u = b (v - S'^T k);  S_t = S' + k u^T;
+// o = S_t^T q  (scalar gate: a_i = a for every row).
+// Per-token load / update / write-back of the state: LeapQuant project
+// page, opening paragraphs.
+//
+// With X_ij = s_i c_j Q_ij (dequantized state) the two mat-vecs are read
+// straight off the codes:
+//   (S'^T k)_j = c_j sum_i (a_i s_i k_i) Q_ij
+//   o_j        = c_j sum_i (a_i s_i q_i) Q_ij + u_j (k . q)
+// which is S_t^T q of the updated fp32 state before requantization.  The
+// codec then runs on P_ij = fma(k_i, u_j, (Q_ij c_j)(a_i s_i)).
+#include "codec.hpp"
+#include "launch.hpp"
+
+namespace gdnq {
+
+struct StepArgs {
+    const void *q, *k, *v;
+    const float *a, *b;
+    void *o;
+    int8_t *codes;
+    float *row_scale, *col_scale;
+    float *prequant;  // nullable
+    float *S;         // fp32 state (baseline kernel)
+};
+
+// Column sums of R (retrieval) and O (output) partials plus k.q, reduced to
+// LDS; consumer threads (t < DV) then hold full sums.
+template <class G>
+struct StepLds {
+    float red[G::NW][2][G::DV];
+    float red_kq[G::NW];
+    float u[G::DV];
+};
+
+template <class G>
+__device__ __forceinline__ void reduce_ro(const Lane &c, StepLds<G> &S, const float (&R)[8], const float (&O)[8],
+                                          float kq_part)
+{
+    float x[16], z[4];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        x[j] = R[j];
+        x[8 + j] = O[j];
+    }
+    col_reduce_scatter<G, OpSum, 16>(x, z);
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const int idx = scatter_index(c, p);
+        S.red[c.w][idx >> 3][c.cb * 8 + (idx & 7)] = z[p];
+    }
+    kq_part = col_allreduce<G, OpSum>(kq_part);
+    if (c.lane == 0) S.red_kq[c.w] = kq_part;
+}
+
+template <class G, bool BF16, bool KDA>
+__global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
+{
+    __shared__ CodecLds<G> L;
+    __shared__ StepLds<G> SL;
+    const Lane c = lane_coords<G>();
+    const size_t h = blockIdx.x;
+    constexpr size_t E = (size_t)G::DK * G::DV;
+    int8_t *codes = A.codes + h * E;
+    float *rs = A.row_scale + h * G::DK;
+    float *cs = A.col_scale + h * G::DV;
+
+    uint2 qraw[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+        qraw[k] = *reinterpret_cast<const uint2 *>(codes + (size_t)row_of<G>(c, k) * G::DV + c.cb * 8);
+    float cc[8];
+    load_f32x8(cs + c.cb * 8, cc);
+    float s[8], kk[8], qq[8], av[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const int i = row_of<G>(c, k);
+        s[k] = rs[i];
+        kk[k] = load1<BF16>(A.k, h * G::DK + i);
+        qq[k] = load1<BF16>(A.q, h * G::DK + i);
+        av[k] = KDA ? A.a[h * G::DK + i] : 0.0f;
+    }
+    if constexpr (!KDA) {
+        const float ag = A.a[h];
+#pragma unroll
+        for (int k = 0; k < 8; k++) av[k] = ag;
+    }
+    const float bh = A.b[h];
+    float vj = 0.0f, cj = 0.0f;
+    if (c.t < G::DV) {
+        vj = load1<BF16>(A.v, h * G::DV + c.t);
+        cj = cs[c.t];
+    }
+
+    float as[8], ask[8], asq[8];
+    float kq = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        as[k] = av[k] * s[k];
+        ask[k] = as[k] * kk[k];
+        asq[k] = as[k] * qq[k];
+        kq = fmaf(kk[k], qq[k], kq);
+    }
+    float X[8][8], R[8], O[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) unpack8(qraw[k], X[k]);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        R[j] = X[0][j] * ask[0];
+        O[j] = X[0][j] * asq[0];
+    }
+#pragma unroll
+    for (int k = 1; k < 8; k++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            R[j] = fmaf(X[k][j], ask[k], R[j]);
+            O[j] = fmaf(X[k][j], asq[k], O[j]);
+        }
+    reduce_ro<G>(c, SL, R, O, kq);
+    __syncthreads();
+    if (c.t < G::DV) {
+        float Rj = SL.red[0][0][c.t], Oj = SL.red[0][1][c.t], kqs = SL.red_kq[0];
+#pragma unroll
+        for (int w = 1; w < G::NW; w++) {
+            Rj += SL.red[w][0][c.t];
+            Oj += SL.red[w][1][c.t];
+            kqs += SL.red_kq[w];
+        }
+        const float u = bh * (vj - cj * Rj);
+        store1<BF16>(A.o, h * G::DV + c.t, fmaf(u, kqs, cj * Oj));
+        SL.u[c.t] = u;
+    }
+    __syncthreads();
+    float u8[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) u8[j] = SL.u[c.cb * 8 + j];
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) X[k][j] = fmaf(kk[k], u8[j], (X[k][j] * cc[j]) * as[k]);
+    if (A.prequant) {
+        float *pq = A.prequant + h * E;
+#pragma unroll
+        for (int k = 0; k < 8; k++) store_f32x8(pq + (size_t)row_of<G>(c, k) * G::DV + c.cb * 8, X[k]);
+    }
+    codec_rowcol<G>(X, c, L, codes, rs, cs);
+}
+
+template <class G, bool BF16, bool KDA>
+__global__ __launch_bounds__(G::NT) void step_fp32_kernel(StepArgs A)
+{
+    __shared__ StepLds<G> SL;
+    const Lane c = lane_coords<G>();
+    const size_t h = blockIdx.x;
+    constexpr size_t E = (size_t)G::DK * G::DV;
+    float *S = A.S + h * E;
+
+    float X[8][8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) load_f32x8(S + (size_t)row_of<G>(c, k) * G::DV + c.cb * 8, X[k]);
+    float kk[8], qq[8], av[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const int i = row_of<G>(c, k);
+        kk[k] = load1<BF16>(A.k, h * G::DK + i);
+        qq[k] = load1<BF16>(A.q, h * G::DK + i);
+        av[k] = KDA ? A.a[h * G::DK + i] : 0.0f;
+    }
+    if constexpr (!KDA) {
+        const float ag = A.a[h];
+#pragma unroll
+        for (int k = 0; k < 8; k++) av[k] = ag;
+    }
+    const float bh = A.b[h];
+    float vj = 0.0f;
+    if (c.t < G::DV) vj = load1<BF16>(A.v, h * G::DV + c.t);
+
+    float ak[8], aq[8], kq = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        ak[k] = av[k] * kk[k];
+        aq[k] = av[k] * qq[k];
+        kq = fmaf(kk[k], qq[k], kq);
+    }
+    float R[8], O[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        R[j] = X[0][j] * ak[0];
+        O[j] = X[0][j] * aq[0];
+    }
+#pragma unroll
+    for (int k = 1; k < 8; k++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            R[j] = fmaf(X[k][j], ak[k], R[j]);
+            O[j] = fmaf(X[k][j], aq[k], O[j]);
+        }
+    reduce_ro<G>(c, SL, R, O, kq);
+    __syncthreads();
+    if (c.t < G::DV) {
+        float Rj = SL.red[0][0][c.t], Oj = SL.red[0][1][c.t], kqs = SL.red_kq[0];
+#pragma unroll
+        for (int w = 1; w < G::NW; w++) {
+            Rj += SL.red[w][0][c.t];
+            Oj += SL.red[w][1][c.t];
+            kqs += SL.red_kq[w];
+        }
+        const float u = bh * (vj - Rj);
+        store1<BF16>(A.o, h * G::DV + c.t, fmaf(u, kqs, Oj));
+        SL.u[c.t] = u;
+    }
+    __syncthreads();
+    float u8[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) u8[j] = SL.u[c.cb * 8 + j];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) X[k][j] = fmaf(kk[k], u8[j], X[k][j] * av[k]);
+        store_f32x8(S + (size_t)row_of<G>(c, k) * G::DV + c.cb * 8, X[k]);
+    }
+}
+
+hipError_t launch_step_fused(const gdnq_desc &d, const gdnq_state &s, const void *q, const void *k,
+                             const void *v, const float *a, const float *b, void *o, hipStream_t st)
+{
+    StepArgs A{q, k, v, a, b, o, s.codes, s.row_scale, s.col_scale,
+               (d.flags & GDNQ_DEBUG_PREQUANT) ? s.prequant_out : nullptr, nullptr};
+    const unsigned nh = (unsigned)d.B * (unsigned)d.H;
+    return with_dims(d.dk, d.dv, [&](auto DK, auto DV) {
+        using G = Geom<decltype(DK)::value, decltype(DV)::value>;
+        return with_bool(d.io_dtype == GDNQ_IO_BF16, [&](auto bf) {
+            return with_bool(d.decay == GDNQ_DECAY_CHANNEL, [&](auto kda) {
+                hipLaunchKernelGGL((step_fused_kernel<G, decltype(bf)::value, decltype(kda)::value>), dim3(nh),
+                                   dim3(G::NT), 0, st, A);
+                return hipGetLastError();
+            });
+        });
+    });
+}
+
+hipError_t launch_step_fp32(const gdnq_desc &d, float *S, const void *q, const void *k, const void *v,
+                            const float *a, const float *b, void *o, hipStream_t st)
+{
+    StepArgs A{q, k, v, a, b, o, nullptr, nullptr, nullptr, nullptr, S};
+    const unsigned nh = (unsigned)d.B * (unsigned)d.H;
+    return with_dims(d.dk, d.dv, [&](auto DK, auto DV) {
+        using G = Geom<decltype(DK)::value, decltype(DV)::value>;
+        return with_bool(d.io_dtype == GDNQ_IO_BF16, [&](auto bf) {
+            return with_bool(d.decay == GDNQ_DECAY_CHANNEL, [&](auto kda) {
+                hipLaunchKernelGGL((step_fp32_kernel<G, decltype(bf)::value, decltype(kda)::value>), dim3(nh),
+                                   dim3(G::NT), 0, st, A);
+                return hipGetLastError();
+            });
+        });
+    });
+}
+
+}  // namespace gdnq

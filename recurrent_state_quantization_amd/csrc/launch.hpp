@@ -1,0 +1,52 @@
+// launch.hpp -- host-side launchers of the gdnq kernels (internal; the
+// public boundary is include/gdnq.h).  Arguments are validated by api.cpp
+// before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <utility>
+
+#include "gdnq.h"
+
+namespace gdnq {
+
+// Limits of the kernels' LDS tables: window length, compensators per
+// head, DAMP rows per head.
+constexpr int MAX_W = 256;
+constexpr int MAX_R = 8;
+constexpr int MAX_HP = 64;
+
+hipError_t launch_step_fused(const gdnq_desc &d, const gdnq_state &s, const void *q, const void *k,
+                             const void *v, const float *a, const float *b, void *o, hipStream_t st);
+hipError_t launch_step_fp32(const gdnq_desc &d, float *S, const void *q, const void *k, const void *v,
+                            const float *a, const float *b, void *o, hipStream_t st);
+hipError_t launch_window_step(const gdnq_desc &d, const gdnq_state &s, const void *q, const void *k,
+                              const void *v, const float *a, const float *b, void *o, int t_in_window,
+                              hipStream_t st);
+hipError_t launch_flush(const gdnq_desc &d, const gdnq_state &s, int n_tokens, hipStream_t st);
+hipError_t launch_quantize(const gdnq_desc &d, const float *S, const gdnq_state &s, hipStream_t st);
+hipError_t launch_dequantize(const gdnq_desc &d, const gdnq_state &s, float *S_out, hipStream_t st);
+hipError_t launch_calibrate(const gdnq_desc &d, const float *S0, const void *k, const void *v,
+                            const float *a, const float *b, int n_steps, int32_t *hp_idx,
+                            float *score, hipStream_t st);
+
+// Call f(DK, DV) as compile-time constants for the supported head dims.
+template <class F>
+hipError_t with_dims(int dk, int dv, F &&f)
+{
+    if (dk == 128 && dv == 128) return f(std::integral_constant<int, 128>{}, std::integral_constant<int, 128>{});
+    if (dk == 64 && dv == 64) return f(std::integral_constant<int, 64>{}, std::integral_constant<int, 64>{});
+    if (dk == 128 && dv == 64) return f(std::integral_constant<int, 128>{}, std::integral_constant<int, 64>{});
+    if (dk == 64 && dv == 128) return f(std::integral_constant<int, 64>{}, std::integral_constant<int, 128>{});
+    return hipErrorInvalidValue;
+}
+
+template <class F>
+hipError_t with_bool(bool x, F &&f)
+{
+    if (x) return f(std::true_type{});
+    return f(std::false_type{});
+}
+
+}  // namespace gdnq

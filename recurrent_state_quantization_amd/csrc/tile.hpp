@@ -1,0 +1,275 @@
+// tile.hpp -- register-tile geometry and cross-lane primitives shared by the
+// gdnq kernels (gfx950 / CDNA4, wave64).
+//
+// One workgroup owns one (batch, head) state tile of DK x DV elements
+// (row i = key channel, column j = value channel).  Every thread holds an
+// 8 x 8 block: 8 rows and 8 *contiguous* columns, so one row of its block is
+// one 8-byte INT8 load or two 16-byte fp32 loads.
+//
+//   NCB = DV/8 column blocks; lane = rgl*NCB + cb  (cb = column block,
+//   rgl = row group within the wave); RGW = 64/NCB row groups per wave;
+//   the wave owns RGW*8 rows; NW = DK/(RGW*8) waves per tile.
+//   Row k (0..7) of a thread: w*RGW*8 + (k/4)*RGW*4 + 4*rgl + (k%4).
+//
+// With that row map one load instruction of a wave covers RGW whole rows,
+// and the layout equals the accumulator layout of the 16x16x4 fp32 MFMA
+// when the MFMA's logical column n is mapped to global column
+// 8*(n%16) + n/16 (used by the window flush; DV = 128 only).
+//
+// Reductions:
+//   * along a row (over the NCB lanes of a row group): DPP quad_perm,
+//     row_half_mirror, row_mirror -- all-reduce, every lane gets the result;
+//   * along a column inside a wave (over the RGW row-group lanes):
+//     v_permlane32_swap / v_permlane16_swap reduce-scatter (plus one DPP
+//     row_ror:8 all-reduce step when NCB = 8), then across waves in LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdnq {
+
+template <int DK_, int DV_>
+struct Geom {
+    static constexpr int DK = DK_;
+    static constexpr int DV = DV_;
+    static constexpr int CPT = 8;
+    static constexpr int RPT = 8;
+    static constexpr int NCB = DV / CPT;
+    static constexpr int RGW = 64 / NCB;
+    static constexpr int ROWS_W = RGW * RPT;
+    static constexpr int NW = DK / ROWS_W;
+    static constexpr int NT = NW * 64;
+    static_assert(NCB == 8 || NCB == 16, "DV must be 64 or 128");
+    static_assert(NW >= 1 && DK % ROWS_W == 0, "DK must be 64 or 128");
+};
+
+struct Lane {
+    int t, lane, w, cb, rgl;
+};
+
+template <class G>
+__device__ __forceinline__ Lane lane_coords()
+{
+    Lane c;
+    c.t = threadIdx.x;
+    c.lane = c.t & 63;
+    c.w = c.t >> 6;
+    c.cb = c.lane % G::NCB;
+    c.rgl = c.lane / G::NCB;
+    return c;
+}
+
+template <class G>
+__device__ __forceinline__ int row_of(const Lane &c, int k)
+{
+    return c.w * G::ROWS_W + (k >> 2) * (G::RGW * 4) + 4 * c.rgl + (k & 3);
+}
+
+// ---------------------------------------------------------------- DPP
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+constexpr int DPP_ROR8 = 0x128;
+
+// All-reduce over the NCB column-block lanes of a row group (lane bits
+// 0..log2(NCB)-1).  The mirror steps equal xor-4 / xor-8 once the smaller
+// groups already hold equal values.
+template <class G>
+__device__ __forceinline__ float row_sum(float x)
+{
+    x += dpp<DPP_XOR1>(x);
+    x += dpp<DPP_XOR2>(x);
+    x += dpp<DPP_HALF_MIRROR>(x);
+    if constexpr (G::NCB == 16) x += dpp<DPP_MIRROR>(x);
+    return x;
+}
+
+template <class G>
+__device__ __forceinline__ float row_max(float x)
+{
+    x = fmaxf(x, dpp<DPP_XOR1>(x));
+    x = fmaxf(x, dpp<DPP_XOR2>(x));
+    x = fmaxf(x, dpp<DPP_HALF_MIRROR>(x));
+    if constexpr (G::NCB == 16) x = fmaxf(x, dpp<DPP_MIRROR>(x));
+    return x;
+}
+
+// --------------------------------------------------------- permlane swaps
+// swap32(a, b): a <- [a_lo, b_lo], b <- [a_hi, b_hi] (lo = lanes 0..31).
+__device__ __forceinline__ void swap32(float &a, float &b)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(a), __float_as_int(b), false, false);
+    a = __int_as_float((int)r[0]);
+    b = __int_as_float((int)r[1]);
+}
+// swap16(a, b): odd 16-lane rows of a trade places with even rows of b.
+__device__ __forceinline__ void swap16(float &a, float &b)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(a), __float_as_int(b), false, false);
+    a = __int_as_float((int)r[0]);
+    b = __int_as_float((int)r[1]);
+}
+
+struct OpSum {
+    __device__ static float f(float a, float b) { return a + b; }
+};
+struct OpMax {
+    __device__ static float f(float a, float b) { return fmaxf(a, b); }
+};
+
+// Column reduce-scatter inside a wave: x[0..N-1] are per-lane partials over
+// this lane's rows; afterwards z[p] (p < N/4) holds the whole wave's
+// reduction of x[4p + e], e = 2*bit4(lane) + bit5(lane).
+template <class G, class Op, int N>
+__device__ __forceinline__ void col_reduce_scatter(const float (&x)[N], float (&z)[N / 4])
+{
+    static_assert(N % 4 == 0, "N must be a multiple of 4");
+    float y[N / 2];
+#pragma unroll
+    for (int p = 0; p < N / 2; p++) {
+        float a = x[2 * p], b = x[2 * p + 1];
+        if constexpr (G::NCB == 8) {  // lane bit 3 first: all-reduce with row_ror:8
+            a = Op::f(a, dpp<DPP_ROR8>(a));
+            b = Op::f(b, dpp<DPP_ROR8>(b));
+        }
+        swap32(a, b);
+        y[p] = Op::f(a, b);
+    }
+#pragma unroll
+    for (int p = 0; p < N / 4; p++) {
+        float a = y[2 * p], b = y[2 * p + 1];
+        swap16(a, b);
+        z[p] = Op::f(a, b);
+    }
+}
+
+// Index (within x[]) of the value z[p] holds after col_reduce_scatter.
+__device__ __forceinline__ int scatter_index(const Lane &c, int p)
+{
+    return 4 * p + 2 * ((c.lane >> 4) & 1) + ((c.lane >> 5) & 1);
+}
+
+// All-reduce of one value over the RGW row-group lanes (column direction).
+template <class G, class Op>
+__device__ __forceinline__ float col_allreduce(float x)
+{
+    if constexpr (G::NCB == 8) x = Op::f(x, dpp<DPP_ROR8>(x));
+    float a = x, b = x;
+    swap32(a, b);
+    x = Op::f(a, b);
+    a = x;
+    b = x;
+    swap16(a, b);
+    return Op::f(a, b);
+}
+
+// --------------------------------------------------------------- LDS sync
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t f32_to_bf16(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Load 8 consecutive io-dtype values starting at element `off`.
+template <bool BF16>
+__device__ __forceinline__ void load8(const void *base, size_t off, float (&out)[8])
+{
+    if constexpr (BF16) {
+        const uint4 raw = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + off);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            out[2 * i] = __uint_as_float(w[i] << 16);
+            out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + off);
+        float4 a = p[0], b = p[1];
+        out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+        out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void *base, size_t off)
+{
+    if constexpr (BF16) return bf16_to_f32(reinterpret_cast<const uint16_t *>(base)[off]);
+    else return reinterpret_cast<const float *>(base)[off];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store1(void *base, size_t off, float x)
+{
+    if constexpr (BF16) reinterpret_cast<uint16_t *>(base)[off] = f32_to_bf16(x);
+    else reinterpret_cast<float *>(base)[off] = x;
+}
+
+// The thread's 8 row values of a per-row vector (rows r0..r0+3 and
+// r0+RGW*4..+3 are contiguous runs of 4).
+template <class G, bool BF16>
+__device__ __forceinline__ void load_rows(const void *base, size_t head_off, const Lane &c, float (&out)[8])
+{
+#pragma unroll
+    for (int k = 0; k < 8; k++) out[k] = load1<BF16>(base, head_off + row_of<G>(c, k));
+}
+
+__device__ __forceinline__ void load_f32x8(const float *p, float (&out)[8])
+{
+    float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+__device__ __forceinline__ void store_f32x8(float *p, const float (&v)[8])
+{
+    reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// int8 x 8 (one row of the block) -> fp32
+__device__ __forceinline__ void unpack8(uint2 q, float (&out)[8])
+{
+    const int32_t lo = (int32_t)q.x, hi = (int32_t)q.y;
+    out[0] = (float)(int8_t)(lo & 0xff);
+    out[1] = (float)(int8_t)((lo >> 8) & 0xff);
+    out[2] = (float)(int8_t)((lo >> 16) & 0xff);
+    out[3] = (float)(lo >> 24);
+    out[4] = (float)(int8_t)(hi & 0xff);
+    out[5] = (float)(int8_t)((hi >> 8) & 0xff);
+    out[6] = (float)(int8_t)((hi >> 16) & 0xff);
+    out[7] = (float)(hi >> 24);
+}
+
+// Low bytes of four fp32 bit patterns -> one dword (byte i from value i).
+__device__ __forceinline__ uint32_t pack_low_bytes(float a, float b, float c, float d)
+{
+    uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0c0c0400u);
+    uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x04000c0cu);
+    return lo | hi;
+}
+
+// Round to nearest even integer for |t| < 2^22 by adding 1.5*2^23: the sum
+// is exact up to the one rounding at unit spacing, so its low mantissa byte
+// is rint(t) mod 256 (two's complement int8).
+constexpr float RINT_MAGIC = 12582912.0f;
+
+}  // namespace gdnq

@@ -1,0 +1,423 @@
+// window.hip -- per-window decode step and window flush.
+//
+// LeapQuant project page, per-window quantization paragraph: the low-bit
+// state of the window start stays fixed, each token's high-precision
+// update is buffered, outputs come from the fixed state plus the buffer,
+// and only at the window end is the full state rebuilt and requantized.
+// Compensator Tokens paragraph: the compensators are rank-1 terms of the
+// same form as token updates and ride on the same path (here: slots of the
+// fixed state that decay with it).
+//
+// Let G_t = a_1 ... a_t (per key channel; one value per head for the scalar
+// gate) be the gate product since the window start and X_0 the fixed state
+// (dequantized codes + DAMP fp16 rows + compensators).  Unrolling the
+// recurrence from X_0:
+//   S_t = diag(G_t) X_0 + sum_{l<=t} ((G_t/G_l) . k_l) u_l^T
+// so with the buffer holding k^_l = k_l / G_l (elementwise):
+//   S'^T k_t = X_0^T (G_t . k_t) + sum_{l<t} u_l (k^_l . (G_t . k_t))
+//   o_t      = X_0^T (G_t . q_t) + sum_{l<t} u_l (k^_l . (G_t . q_t)) + u_t (k_t . q_t)
+//   S_W      = diag(G_W) [ X_0 + sum_{l<=n} k^_l u_l^T ]
+// Every rank-1 piece of X_0 (compensator p w^T, DAMP row e_i h_i^T) is a
+// "slot" with key-side vector and value-side vector, like a buffered token.
+#include "codec.hpp"
+#include "launch.hpp"
+
+namespace gdnq {
+
+constexpr int MAX_SLOTS = MAX_R + MAX_HP + MAX_W;
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+struct WinArgs {
+    const void *q, *k, *v;
+    const float *a, *b;
+    void *o;
+    const int8_t *codes;
+    const float *row_scale, *col_scale;
+    const float *comp_k, *comp_v;
+    float *buf_k, *buf_u, *g_cur;
+    const uint16_t *hp_rows;
+    const int32_t *hp_idx;
+    int r, n_hp, W, t;
+};
+
+// sum over the 16 lanes of a DPP row
+__device__ __forceinline__ float sum16(float x)
+{
+    x += dpp<DPP_XOR1>(x);
+    x += dpp<DPP_XOR2>(x);
+    x += dpp<DPP_HALF_MIRROR>(x);
+    x += dpp<DPP_MIRROR>(x);
+    return x;
+}
+
+__device__ __forceinline__ void load_f16x8(const uint16_t *p, float (&out)[8])
+{
+    const uint4 raw = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        out[2 * i] = f16_to_f32((uint16_t)(w[i] & 0xFFFFu));
+        out[2 * i + 1] = f16_to_f32((uint16_t)(w[i] >> 16));
+    }
+}
+
+template <class G>
+struct WinLds {
+    float ks[G::DK], qs[G::DK], gs[G::DK], gk[G::DK], gq[G::DK];
+    float alpha[MAX_SLOTS + 1], beta[MAX_SLOTS + 1];
+    int hp[MAX_HP];
+    float red[G::NW][2][G::DV];
+};
+
+template <class G, bool BF16, bool KDA, bool DAMP>
+__global__ __launch_bounds__(G::NT) void window_step_kernel(WinArgs A)
+{
+    __shared__ WinLds<G> L;
+    const Lane c = lane_coords<G>();
+    const size_t h = blockIdx.x;
+    const int n_hp = DAMP ? A.n_hp : 0;
+    const int r = A.r;
+
+    // per-row vectors: gate product, gated k and q
+    if (c.t < G::DK) {
+        const float kv = load1<BF16>(A.k, h * G::DK + c.t);
+        const float qv = load1<BF16>(A.q, h * G::DK + c.t);
+        const float av = KDA ? A.a[h * G::DK + c.t] : A.a[h];
+        const float gprev = (A.t == 0) ? 1.0f : (KDA ? A.g_cur[h * G::DK + c.t] : A.g_cur[h]);
+        const float g = gprev * av;
+        L.ks[c.t] = kv;
+        L.qs[c.t] = qv;
+        L.gs[c.t] = g;
+        L.gk[c.t] = g * kv;
+        L.gq[c.t] = g * qv;
+    }
+    if (DAMP && c.t < n_hp) L.hp[c.t] = A.hp_idx[h * n_hp + c.t];
+    __syncthreads();
+
+    // fixed INT8 tile of this thread (DAMP rows carry no codes)
+    RowMap rm;
+    if constexpr (DAMP) rm = row_map<G>(c, L.hp, n_hp);
+    const size_t nrows_c = (size_t)(G::DK - n_hp);
+    const int8_t *codes = A.codes + h * nrows_c * G::DV;
+    uint2 qraw[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        if (!DAMP || rm.slot[k] < 0) {
+            const int row = DAMP ? rm.crow[k] : row_of<G>(c, k);
+            qraw[k] = *reinterpret_cast<const uint2 *>(codes + (size_t)row * G::DV + c.cb * 8);
+        } else {
+            qraw[k] = make_uint2(0u, 0u);
+        }
+    }
+    float cc[8];
+    load_f32x8(A.col_scale + h * G::DV + c.cb * 8, cc);
+
+    // slot dot products: alpha_l = kvec_l . (G.k), beta_l = kvec_l . (G.q);
+    // slot NS is k . q.  16 lanes per slot.
+    const int NS = r + n_hp + A.t;
+    {
+        constexpr int PER = G::DK / 16;
+        const int l16 = c.t & 15;
+        for (int base = 0; base <= NS; base += G::NT / 16) {
+            const int l = base + (c.t >> 4);
+            if (l > NS) break;  // whole 16-lane groups leave together
+            float al = 0.0f, be = 0.0f;
+            if (l == NS) {
+#pragma unroll
+                for (int e = 0; e < PER; e++) al = fmaf(L.ks[l16 * PER + e], L.qs[l16 * PER + e], al);
+            } else if (l >= r && l < r + n_hp) {
+                if (l16 == 0) {
+                    const int i = L.hp[l - r];
+                    al = L.gk[i];
+                    be = L.gq[i];
+                }
+            } else {
+                const float *vec = (l < r) ? A.comp_k + ((h * r + l) * G::DK)
+                                           : A.buf_k + ((h * A.W + (l - r - n_hp)) * G::DK);
+#pragma unroll
+                for (int e = 0; e < PER; e++) {
+                    const float x = vec[l16 * PER + e];
+                    al = fmaf(x, L.gk[l16 * PER + e], al);
+                    be = fmaf(x, L.gq[l16 * PER + e], be);
+                }
+            }
+            al = sum16(al);
+            be = sum16(be);
+            if (l16 == 0) {
+                L.alpha[l] = al;
+                L.beta[l] = be;
+            }
+        }
+    }
+
+    // fixed-state mat-vecs straight off the codes
+    float gsk[8], gsq[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const int i = row_of<G>(c, k);
+        const float s = DAMP ? 1.0f : A.row_scale[h * G::DK + i];
+        gsk[k] = s * L.gk[i];
+        gsq[k] = s * L.gq[i];
+    }
+    float R[8], O[8];
+    {
+        float X[8];
+        unpack8(qraw[0], X);
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            R[j] = X[j] * gsk[0];
+            O[j] = X[j] * gsq[0];
+        }
+#pragma unroll
+        for (int k = 1; k < 8; k++) {
+            unpack8(qraw[k], X);
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                R[j] = fmaf(X[j], gsk[k], R[j]);
+                O[j] = fmaf(X[j], gsq[k], O[j]);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        R[j] *= cc[j];
+        O[j] *= cc[j];
+    }
+    __syncthreads();  // alpha / beta ready
+
+    // slot value-side terms, slots spread over the row groups
+    constexpr int NRG = G::NW * G::RGW;
+    const int rg = c.w * G::RGW + c.rgl;
+    for (int l = rg; l < NS; l += NRG) {
+        const float al = L.alpha[l], be = L.beta[l];
+        float uv[8];
+        if (l < r) load_f32x8(A.comp_v + (h * r + l) * G::DV + c.cb * 8, uv);
+        else if (l < r + n_hp) load_f16x8(A.hp_rows + (h * n_hp + (l - r)) * G::DV + c.cb * 8, uv);
+        else load_f32x8(A.buf_u + (h * A.W + (l - r - n_hp)) * G::DV + c.cb * 8, uv);
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            R[j] = fmaf(al, uv[j], R[j]);
+            O[j] = fmaf(be, uv[j], O[j]);
+        }
+    }
+    {
+        float x[16], z[4];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            x[j] = R[j];
+            x[8 + j] = O[j];
+        }
+        col_reduce_scatter<G, OpSum, 16>(x, z);
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            const int idx = scatter_index(c, p);
+            L.red[c.w][idx >> 3][c.cb * 8 + (idx & 7)] = z[p];
+        }
+    }
+    __syncthreads();
+    if (c.t < G::DV) {
+        float ret = L.red[0][0][c.t], ot = L.red[0][1][c.t];
+#pragma unroll
+        for (int w = 1; w < G::NW; w++) {
+            ret += L.red[w][0][c.t];
+            ot += L.red[w][1][c.t];
+        }
+        const float u = A.b[h] * (load1<BF16>(A.v, h * G::DV + c.t) - ret);
+        store1<BF16>(A.o, h * G::DV + c.t, fmaf(u, L.alpha[NS], ot));
+        A.buf_u[(h * A.W + A.t) * G::DV + c.t] = u;
+    }
+    if (c.t < G::DK) {
+        const float g = L.gs[c.t];
+        A.buf_k[(h * A.W + A.t) * G::DK + c.t] = L.ks[c.t] / g;
+        if (KDA) A.g_cur[h * G::DK + c.t] = g;
+        else if (c.t == 0) A.g_cur[h] = g;
+    }
+}
+
+// -------------------------------------------------------------------------
+struct FlushArgs {
+    int8_t *codes;
+    float *row_scale, *col_scale, *comp_k, *comp_v;
+    const float *buf_k, *buf_u;
+    float *g_cur;
+    uint16_t *hp_rows;
+    const int32_t *hp_idx;
+    float *prequant;
+    int r, n_hp, W, n, iters;
+};
+
+template <class G>
+struct FlushLds {
+    float gs[G::DK];
+    int hp[MAX_HP];
+};
+
+// Key-side value of slot l at row i (already multiplied by G_W,i) and the
+// 8 value-side entries at columns col..col+7.  Slots: r compensators, n_hp
+// DAMP rows, n buffered tokens; l >= K is a zero pad.
+template <class G>
+__device__ __forceinline__ float slot_key(const FlushArgs &A, const FlushLds<G> &L, size_t h, int l, int i, int K)
+{
+    if (l >= K) return 0.0f;
+    if (l < A.r) return L.gs[i] * A.comp_k[(h * A.r + l) * G::DK + i];
+    if (l < A.r + A.n_hp) return (L.hp[l - A.r] == i) ? L.gs[i] : 0.0f;
+    return L.gs[i] * A.buf_k[(h * A.W + (l - A.r - A.n_hp)) * G::DK + i];
+}
+
+template <class G>
+__device__ __forceinline__ void slot_val(const FlushArgs &A, size_t h, int l, int col, int K, float (&out)[8])
+{
+    if (l >= K) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) out[j] = 0.0f;
+    } else if (l < A.r) {
+        load_f32x8(A.comp_v + (h * A.r + l) * G::DV + col, out);
+    } else if (l < A.r + A.n_hp) {
+        load_f16x8(A.hp_rows + (h * A.n_hp + (l - A.r)) * G::DV + col, out);
+    } else {
+        load_f32x8(A.buf_u + (h * A.W + (l - A.r - A.n_hp)) * G::DV + col, out);
+    }
+}
+
+template <class G, bool KDA, bool DAMP>
+__global__ __launch_bounds__(G::NT) void flush_kernel(FlushArgs A)
+{
+    __shared__ CodecLds<G> L;
+    __shared__ FlushLds<G> F;
+    const Lane c = lane_coords<G>();
+    const size_t h = blockIdx.x;
+    const int n_hp = DAMP ? A.n_hp : 0;
+    if (!DAMP) A.n_hp = 0;
+    if (c.t < G::DK) F.gs[c.t] = KDA ? A.g_cur[h * G::DK + c.t] : A.g_cur[h];
+    if (DAMP && c.t < n_hp) F.hp[c.t] = A.hp_idx[h * n_hp + c.t];
+    __syncthreads();
+
+    RowMap rm;
+    if constexpr (DAMP) rm = row_map<G>(c, F.hp, n_hp);
+    const size_t nrows_c = (size_t)(G::DK - n_hp);
+    int8_t *codes = A.codes + h * nrows_c * G::DV;
+    float cc[8];
+    load_f32x8(A.col_scale + h * G::DV + c.cb * 8, cc);
+    float P[8][8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const int i = row_of<G>(c, k);
+        if (!DAMP || rm.slot[k] < 0) {
+            const int row = DAMP ? rm.crow[k] : i;
+            const uint2 q = *reinterpret_cast<const uint2 *>(codes + (size_t)row * G::DV + c.cb * 8);
+            float X[8];
+            unpack8(q, X);
+            const float s = DAMP ? 1.0f : A.row_scale[h * G::DK + i];
+            const float g = F.gs[i];
+#pragma unroll
+            for (int j = 0; j < 8; j++) P[k][j] = DAMP ? (X[j] * cc[j]) * g : ((X[j] * cc[j]) * s) * g;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; j++) P[k][j] = 0.0f;
+        }
+    }
+
+    // rank-K update with the slots (compensators, DAMP rows, tokens)
+    const int K = A.r + n_hp + A.n;
+    if constexpr (G::DV == 128) {
+        // 16x16x4 fp32 MFMA.  MFMA row m of block hb of wave w is tile row
+        // w*32 + hb*16 + m; MFMA column n of block nb is tile column
+        // 8*n + nb, so the accumulator of (hb, nb) holds P[hb*4 + i][nb].
+        floatx4 acc[2][8];
+#pragma unroll
+        for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+            for (int nb = 0; nb < 8; nb++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc[hb][nb][i] = P[hb * 4 + i][nb];
+        const int lm = c.lane & 15, lk = c.lane >> 4;
+        for (int kk = 0; kk < K; kk += 4) {
+            const int l = kk + lk;
+            float av[2], bv[8];
+#pragma unroll
+            for (int hb = 0; hb < 2; hb++) av[hb] = slot_key<G>(A, F, h, l, c.w * 32 + hb * 16 + lm, K);
+            slot_val<G>(A, h, l, 8 * lm, K, bv);
+#pragma unroll
+            for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+                for (int nb = 0; nb < 8; nb++)
+                    acc[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[hb], bv[nb], acc[hb][nb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+            for (int nb = 0; nb < 8; nb++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) P[hb * 4 + i][nb] = acc[hb][nb][i];
+    } else {
+        for (int l = 0; l < K; l++) {
+            float kv[8], uv[8];
+#pragma unroll
+            for (int k = 0; k < 8; k++) kv[k] = slot_key<G>(A, F, h, l, row_of<G>(c, k), K);
+            slot_val<G>(A, h, l, c.cb * 8, K, uv);
+#pragma unroll
+            for (int k = 0; k < 8; k++)
+#pragma unroll
+                for (int j = 0; j < 8; j++) P[k][j] = fmaf(kv[k], uv[j], P[k][j]);
+        }
+    }
+
+    power_deflate<G>(P, c, L, A.r, A.iters, A.comp_k + h * A.r * G::DK, A.comp_v + h * A.r * G::DV);
+    if (A.prequant) {
+        float *pq = A.prequant + h * (size_t)G::DK * G::DV;
+#pragma unroll
+        for (int k = 0; k < 8; k++) store_f32x8(pq + (size_t)row_of<G>(c, k) * G::DV + c.cb * 8, P[k]);
+    }
+    __syncthreads();  // every read of codes / scales / DAMP rows is done
+    if constexpr (DAMP)
+        codec_damp<G>(P, c, L, rm, codes, A.col_scale + h * G::DV, A.hp_rows + h * n_hp * G::DV);
+    else
+        codec_rowcol<G>(P, c, L, codes, A.row_scale + h * G::DK, A.col_scale + h * G::DV);
+    if (c.t < G::DK) {
+        if (KDA) A.g_cur[h * G::DK + c.t] = 1.0f;
+        else if (c.t == 0) A.g_cur[h] = 1.0f;
+    }
+}
+
+hipError_t launch_window_step(const gdnq_desc &d, const gdnq_state &s, const void *q, const void *k,
+                              const void *v, const float *a, const float *b, void *o, int t_in_window,
+                              hipStream_t st)
+{
+    WinArgs A{q, k, v, a, b, o, s.codes, s.row_scale, s.col_scale, s.comp_k, s.comp_v,
+              s.buf_k, s.buf_u, s.g_cur, s.hp_rows, s.hp_idx, d.r, d.n_hp, d.W, t_in_window};
+    const unsigned nh = (unsigned)d.B * (unsigned)d.H;
+    return with_dims(d.dk, d.dv, [&](auto DK, auto DV) {
+        using G = Geom<decltype(DK)::value, decltype(DV)::value>;
+        return with_bool(d.io_dtype == GDNQ_IO_BF16, [&](auto bf) {
+            return with_bool(d.decay == GDNQ_DECAY_CHANNEL, [&](auto kda) {
+                return with_bool(d.layout == GDNQ_LAYOUT_DAMP, [&](auto damp) {
+                    hipLaunchKernelGGL((window_step_kernel<G, decltype(bf)::value, decltype(kda)::value,
+                                                           decltype(damp)::value>),
+                                       dim3(nh), dim3(G::NT), 0, st, A);
+                    return hipGetLastError();
+                });
+            });
+        });
+    });
+}
+
+hipError_t launch_flush(const gdnq_desc &d, const gdnq_state &s, int n_tokens, hipStream_t st)
+{
+    FlushArgs A{s.codes, s.row_scale, s.col_scale, s.comp_k, s.comp_v, s.buf_k, s.buf_u, s.g_cur,
+                s.hp_rows, s.hp_idx, (d.flags & GDNQ_DEBUG_PREQUANT) ? s.prequant_out : nullptr,
+                d.r, d.n_hp, d.W, n_tokens, d.power_iters};
+    const unsigned nh = (unsigned)d.B * (unsigned)d.H;
+    return with_dims(d.dk, d.dv, [&](auto DK, auto DV) {
+        using G = Geom<decltype(DK)::value, decltype(DV)::value>;
+        return with_bool(d.decay == GDNQ_DECAY_CHANNEL, [&](auto kda) {
+            return with_bool(d.layout == GDNQ_LAYOUT_DAMP, [&](auto damp) {
+                hipLaunchKernelGGL((flush_kernel<G, decltype(kda)::value, decltype(damp)::value>), dim3(nh),
+                                   dim3(G::NT), 0, st, A);
+                return hipGetLastError();
+            });
+        });
+    });
+}
+
+}  // namespace gdnq

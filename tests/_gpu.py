@@ -1,0 +1,140 @@
+"""Helpers for the GPU parity tests: moving seeded numpy inputs to the
+device, reading results back, and the error measures of the parity
+contract.  No method arithmetic lives here."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+
+
+def torch_cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def lib():
+    import recurrent_state_quantization_amd as g
+    return g
+
+
+def say(*a):
+    """Name the case before a GPU step (flushed), so a fault names it."""
+    print("[gpu-case]", *a, file=sys.stderr, flush=True)
+
+
+def dev(x, dtype=None):
+    torch = torch_cuda()
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def dev_io(inp: dict, name: str, bf16: bool):
+    """Upload q/k/v either as fp32 or as the bf16 bit patterns."""
+    torch = torch_cuda()
+    if bf16:
+        bits = np.ascontiguousarray(inp[name + "16"]).view(np.int16)
+        return torch.from_numpy(bits).cuda().view(torch.bfloat16)
+    return dev(inp[name].astype(np.float32))
+
+
+def host_io(t, bf16: bool) -> np.ndarray:
+    torch = torch_cuda()
+    if bf16:
+        bits = t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return synth.bf16_to_f32(bits)
+    return t.float().cpu().numpy()
+
+
+def host(t) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def rel_l2(got, ref, axis=None):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = np.sqrt(np.sum((got - ref) ** 2, axis=axis))
+    n = np.sqrt(np.sum(ref ** 2, axis=axis))
+    return d / np.maximum(n, 1e-300)
+
+
+def per_head_rel(got, ref):
+    """l2-relative error per head over all but the first axis."""
+    got = np.asarray(got, np.float64).reshape(got.shape[0], -1)
+    ref = np.asarray(ref, np.float64).reshape(ref.shape[0], -1)
+    return rel_l2(got, ref, axis=1)
+
+
+def near_tie_codes(X32: np.ndarray, s: np.ndarray | None, c: np.ndarray, margin: float):
+    """For the codec input X (fp32, [nh,dk,dv]) and its scales, mark the
+    elements whose pre-rounding value lies within `margin` of a half-integer
+    (computed in fp64 from the stored scales).  Used only to decide where a
+    +-1 code difference is allowed."""
+    X = X32.astype(np.float64)
+    if s is not None:
+        s64 = s.astype(np.float64)[:, :, None]
+        X = np.where(s64 > 0, X / np.where(s64 > 0, s64, 1), 0)
+    c64 = c.astype(np.float64)[:, None, :]
+    t = np.where(c64 > 0, X / np.where(c64 > 0, c64, 1), 0)
+    frac = np.abs(t - np.floor(t) - 0.5)
+    return frac < margin
+
+
+def desc_for(cfg: dict, **over):
+    g = lib()
+    d = g.Desc(B=cfg["B"], H=cfg["H"], dk=cfg["dk"], dv=cfg["dv"], W=cfg["W"], r=cfg["r"],
+               decay=g.DECAY_CHANNEL if cfg["decay"] == "channel" else g.DECAY_SCALAR,
+               io_dtype=g.IO_BF16 if cfg["io"] == "bf16" else g.IO_F32,
+               layout=g.LAYOUT_DAMP if cfg.get("n_hp") else g.LAYOUT_ROWCOL,
+               n_hp=cfg.get("n_hp", 0), power_iters=20)
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def sub_cfg(cfg: dict, B=None, H=None, **over):
+    c = dict(cfg)
+    if B is not None:
+        c["B"] = B
+    if H is not None:
+        c["H"] = H
+    c.update(over)
+    return c
+
+
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half the bf16 spacing at |x| (8 significant bits)."""
+    ax = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
+    return 2.0 ** (e - 8)
+
+
+def check_outputs(got, ref, bf16: bool, fp32_tol=1e-4):
+    """Output bar.  fp32 I/O: l2-relative <= 1e-4 per head.  bf16 output:
+    (1) every element is a correct bf16 rounding of a value within fp32
+    arithmetic error (1e-5 of the head's largest output) of the oracle;
+    (2) per head, |got - bf16(oracle)| / |oracle| <= 2e-3 (like for like:
+    the oracle's output rounded to bf16); (3) per head the raw l2-relative
+    gap to the fp64 oracle is within the bf16 rounding bound 2^-8."""
+    got = np.asarray(got, np.float64).reshape(len(ref), -1)
+    ref = np.asarray(ref, np.float64).reshape(len(ref), -1)
+    rel = per_head_rel(got, ref)
+    if not bf16:
+        assert rel.max() <= fp32_tol, rel.max()
+        return rel
+    slack = 1e-5 * np.abs(ref).max(axis=1, keepdims=True)
+    bound = bf16_half_ulp(np.maximum(np.abs(ref), np.abs(got))) + slack
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), f"{bad.sum()} outputs are not a rounding of the oracle's value"
+    ref16 = synth.bf16_to_f32(synth.bf16_bits(ref.astype(np.float32))).astype(np.float64)
+    like = np.sqrt(np.sum((got - ref16) ** 2, axis=1)) / np.maximum(np.sqrt(np.sum(ref ** 2, axis=1)), 1e-300)
+    assert like.max() <= 2e-3, like.max()
+    assert rel.max() <= 2.0 ** -8, rel.max()
+    return rel
