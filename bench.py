@@ -1,0 +1,333 @@
+"""Benchmark: INT8 per-step decode of many concurrent GDN states on one GPU.
+
+Workload (default, "prefix_cache"): B=1024 states x H=32 heads of 128x128,
+pre-filled N(0,1) with 4 outlier key rows and 4 outlier value columns per
+head scaled x50, bf16 q/k/v, scalar gate.  One step = one call of
+gdn_quant_decode_step over all 32768 states (dequantize, gated delta
+update, output, requantize, write back).  The fp32-state kernel
+(gdn_fp32_decode_step) is timed on the same states and inputs beside it.
+
+Printed: one JSON line (metric, value = token-head updates/s, roofline of
+the decode kernel against 8 TB/s HBM, and the plain fp64 CPU oracle timed
+on a bounded sample of the same workload).
+
+    python bench.py [--steps 100] [--warmup 10] [--gpus 1]
+                    [--workload prefix_cache|gdn_serving|kda|damp]
+                    [--no-cpu] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def src_hash() -> str:
+    """Hash of the kernel sources, to tell whether stored counters still
+    describe the current kernels."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "recurrent_state_quantization_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def step_bytes(cfg: dict, quant: bool) -> int:
+    """Algorithmic HBM bytes of one per-step decode of one state."""
+    dk, dv = cfg["dk"], cfg["dv"]
+    io = 2 if cfg["io"] == "bf16" else 4
+    na = dk if cfg["decay"] == "channel" else 1
+    inputs = (2 * dk + dv) * io + 4 * na + 4
+    out = dv * io
+    if quant:
+        state = dk * dv + 4 * (dk + dv)          # codes + row and column scales
+    else:
+        state = 4 * dk * dv
+    return 2 * state + inputs + out             # read + write the state
+
+
+def window_step_bytes(cfg: dict, t: int) -> int:
+    """Algorithmic bytes of one window decode step at position t."""
+    dk, dv, r = cfg["dk"], cfg["dv"], cfg["r"]
+    n_hp = cfg.get("n_hp", 0)
+    io = 2 if cfg["io"] == "bf16" else 4
+    na = dk if cfg["decay"] == "channel" else 1
+    rows = dk - n_hp
+    state = rows * dv + (0 if n_hp else 4 * dk) + 4 * dv + 2 * n_hp * dv + 4 * n_hp
+    comps = 4 * r * (dk + dv)
+    buf = t * 4 * (dk + dv)
+    g = 4 * na * (2 if t > 0 else 1)
+    inputs = (2 * dk + dv) * io + 4 * na + 4
+    return state + comps + buf + g + inputs + dv * io + 4 * (dk + dv)
+
+
+def flush_bytes(cfg: dict, n: int) -> int:
+    dk, dv, r = cfg["dk"], cfg["dv"], cfg["r"]
+    n_hp = cfg.get("n_hp", 0)
+    na = dk if cfg["decay"] == "channel" else 1
+    rows = dk - n_hp
+    state = rows * dv + (0 if n_hp else 4 * dk) + 4 * dv + 2 * n_hp * dv + 4 * n_hp
+    comps = 4 * r * (dk + dv)
+    return 2 * (state + comps) + n * 4 * (dk + dv) + 8 * na
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(workload, {}).get(kernel)
+    if not ent or ent.get("src_hash") != src_hash():
+        return None
+    return ent["bytes_per_launch"]
+
+
+def cpu_baseline(cfg: dict, S_first: np.ndarray, inputs: list, budget_s: float = 12.0):
+    """The fp64 CPU oracle's per-step INT8 decode on the first heads of the
+    workload, single-threaded, for about budget_s seconds."""
+    import oracle
+
+    nh = S_first.shape[0]
+    Q, s, c = oracle.quantize(S_first)
+    done = 0
+    t0 = time.perf_counter()
+    step = 0
+    while True:
+        inp = inputs[step % len(inputs)]
+        sub = {k: v[:nh] for k, v in inp.items()}
+        r = oracle.quant_step(Q, s, c, sub["q"], sub["k"], sub["v"], sub["a"], sub["b"])
+        Q, s, c = r["Q"], r["s"], r["c"]
+        done += nh
+        step += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "token-head updates/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {nh} of the {cfg['B'] * cfg['H']} states, {step} consecutive per-step "
+                      f"INT8 decode steps ({done} token-head updates) in {dt:.1f} s, one thread"}
+
+
+def time_launches(torch, fn, steps: int, warmup: int):
+    """Whole-loop time (barrier + synchronize on both sides) and the mean
+    duration of one launch from HIP events on the launch stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(warmup + steps + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+    return wall, float(np.mean(per))
+
+
+def bench_prefix_cache(args, torch, g):
+    cfg = synth.WORKLOADS["prefix_cache"]
+    nh, dk, dv = cfg["B"] * cfg["H"], cfg["dk"], cfg["dv"]
+    log(f"generating {nh} pre-filled states")
+    S = synth.prefill_states(cfg)
+    n_sets = 4
+    inputs = [synth.step_inputs(cfg, t) for t in range(n_sets)]
+
+    def up(inp):
+        bits = lambda n: torch.from_numpy(inp[n + "16"].view(np.int16)).cuda().view(torch.bfloat16)
+        return [bits("q"), bits("k"), bits("v"), torch.from_numpy(inp["a"]).cuda(),
+                torch.from_numpy(inp["b"]).cuda()]
+
+    dev_inputs = [up(i) for i in inputs]
+    d = g.Desc(B=cfg["B"], H=cfg["H"], dk=dk, dv=dv, io_dtype=g.IO_BF16)
+    st = g.alloc_state(d)
+    S_dev = torch.from_numpy(S).cuda()
+    g.gdn_state_quantize(d, S_dev, st)
+    o = torch.empty(nh * dv, dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    def int8_step(i):
+        g.gdn_quant_decode_step(d, st, *dev_inputs[i % n_sets], o, 0)
+
+    def fp32_step(i):
+        g.gdn_fp32_decode_step(d, S_dev, *dev_inputs[i % n_sets], o)
+
+    log("timing INT8 per-step decode")
+    wall, per = time_launches(torch, int8_step, args.steps, args.warmup)
+    log("timing fp32-state decode")
+    wall32, per32 = time_launches(torch, fp32_step, args.steps, args.warmup)
+    b8 = step_bytes(cfg, True) * nh
+    b32 = step_bytes(cfg, False) * nh
+    value = nh * args.steps / wall
+    res = {
+        "metric": "token-head state updates/s, INT8 GDN per-step decode (1 GPU)",
+        "value": value,
+        "unit": "token-head updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 state, fp32 math, bf16 q/k/v/o",
+        "data": "synthetic (seeded pre-filled states with outlier rows/columns; no weights)",
+        "config": {"workload": "prefix_cache: B=1024 states, H=32, dk=dv=128, one per-step INT8 "
+                               "decode of every state per step, bf16 I/O, scalar gate",
+                   "global_batch": cfg["B"], "heads": cfg["H"], "dk": dk, "dv": dv,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": b8 / per / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": b8 / per / 1e9 / HBM_PEAK_GBS,
+                     "traffic": stored_traffic("step_fused", "prefix_cache"),
+                     "kernel": "step_fused_kernel<128x128, bf16, scalar gate>",
+                     "algorithmic_bytes_per_launch": b8, "mean_launch_s": per},
+        "fp32_state": {"value": nh * args.steps / wall32, "ms_per_step": wall32 / args.steps * 1e3,
+                       "achieved_GBs": b32 / per32 / 1e9, "frac": b32 / per32 / 1e9 / HBM_PEAK_GBS,
+                       "algorithmic_bytes_per_launch": b32, "mean_launch_s": per32,
+                       "traffic": stored_traffic("step_fp32", "prefix_cache")},
+        "speedup_vs_fp32_state": wall32 / wall,
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(cfg, S[:2048], inputs)
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def bench_window(args, torch, g, name):
+    """Window-mode workloads: steps = decode tokens (flushes every W)."""
+    cfg = synth.WORKLOADS[name]
+    nh, dk, dv, W, r = cfg["B"] * cfg["H"], cfg["dk"], cfg["dv"], cfg["W"], cfg["r"]
+    n_hp = cfg.get("n_hp", 0)
+    d = g.Desc(B=cfg["B"], H=cfg["H"], dk=dk, dv=dv, W=W, r=r,
+               decay=g.DECAY_CHANNEL if cfg["decay"] == "channel" else g.DECAY_SCALAR, io_dtype=g.IO_BF16,
+               layout=g.LAYOUT_DAMP if n_hp else g.LAYOUT_ROWCOL, n_hp=n_hp, power_iters=20)
+    st = g.alloc_state(d)
+    if n_hp:
+        gr = synth.misc_rng(cfg["seed"], 5)
+        hp = np.stack([np.sort(gr.choice(dk, n_hp, replace=False)) for _ in range(nh)]).astype(np.int32)
+        st["hp_idx"].copy_(torch.from_numpy(hp.reshape(-1)))
+    S = synth.random_states(cfg["seed"], nh, dk, dv, scale=0.3)
+    g.gdn_state_quantize(d, torch.from_numpy(S).cuda(), st)
+    steps = max(W, (args.steps // W) * W)
+    log(f"generating {W} input steps for {nh} heads")
+    dev_in = []
+    for t in range(W):
+        inp = synth.step_inputs(cfg, t)
+        bits = lambda n: torch.from_numpy(inp[n + "16"].view(np.int16)).cuda().view(torch.bfloat16)
+        dev_in.append([bits("q"), bits("k"), bits("v"), torch.from_numpy(inp["a"]).cuda(),
+                       torch.from_numpy(inp["b"]).cuda()])
+    o = torch.empty(nh * dv, dtype=torch.bfloat16, device="cuda")
+
+    def token(i):
+        t = i % W
+        g.gdn_quant_decode_step(d, st, *dev_in[t], o, t)
+        if t == W - 1:
+            g.gdn_quant_window_flush(d, st, W)
+
+    wall, _ = time_launches(torch, token, steps, W * max(1, args.warmup // W))
+    # per-kernel means: window steps and flushes separately
+    stream = torch.cuda.current_stream()
+    ev_s = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(W)]
+    ev_f = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for t in range(W):
+        ev_s[t][0].record(stream)
+        g.gdn_quant_decode_step(d, st, *dev_in[t], o, t)
+        ev_s[t][1].record(stream)
+    ev_f[0].record(stream)
+    g.gdn_quant_window_flush(d, st, W)
+    ev_f[1].record(stream)
+    torch.cuda.synchronize()
+    t_steps = [a.elapsed_time(b) * 1e-3 for a, b in ev_s]
+    t_flush = ev_f[0].elapsed_time(ev_f[1]) * 1e-3
+    bsteps = [window_step_bytes(cfg, t) * nh for t in range(W)]
+    res = {
+        "metric": f"token-head state updates/s, INT8 window-mode decode ({name}, 1 GPU)",
+        "value": nh * steps / wall, "unit": "token-head updates/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": wall / steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8 state, fp32 math, bf16 q/k/v/o",
+        "data": "synthetic", "config": {"workload": name, "B": cfg["B"], "H": cfg["H"], "W": W, "r": r,
+                                         "n_hp": n_hp, "decay": cfg["decay"]},
+        "roofline": {"bound": "hbm", "achieved": sum(bsteps) / sum(t_steps) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": sum(bsteps) / sum(t_steps) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": stored_traffic("window_step", name),
+                     "kernel": "window_step_kernel (mean over window positions)"},
+        "window_step_us": [round(x * 1e6, 2) for x in t_steps],
+        "flush_us": t_flush * 1e6,
+        "flush_GBs": flush_bytes(cfg, W) * nh / t_flush / 1e9,
+        "cpu_baseline": None,
+    }
+    return res
+
+
+def copy_calibration(torch):
+    """A plain device copy of known size, for scaling the HBM counters."""
+    n = 1 << 28  # 1 GiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 5 copies of {4 * n} bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefix_cache",
+                    choices=["prefix_cache", "gdn_serving", "kda", "damp"])
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the decode path shards over independent "
+              f"(batch, head) states with no exchange, and this build measures one GPU's share "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import recurrent_state_quantization_amd as g
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    if args.workload == "prefix_cache":
+        res = bench_prefix_cache(args, torch, g)
+    else:
+        res = bench_window(args, torch, g, args.workload)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
