@@ -40,7 +40,9 @@
  *  - value-column scales are symmetric: c_j = m_j / 127, codes in
  *    [-127, 127], round half to even;
  *  - every codec step is one IEEE fp32 operation rounded to nearest even,
- *    in the order written below, with no fused multiply-add;
+ *    in the order written below, with no fused multiply-add, except the
+ *    last: the code is the integer nearest to the exact product
+ *    Y_ij * iota_j (ties to even), with no intermediate rounding;
  *  - zero rows/columns get scale 0, reciprocal 0 and code 0; a column whose
  *    reciprocal scale 127/m_j overflows fp32 is treated as a zero column;
  *  - the output of a per-step quantized decode is taken from the updated
@@ -114,8 +116,8 @@ static void quantize_tile(int dk, int dv, const float *X, int8_t *Q, float *s, f
         }
         c[j] = cj;
         for (int i = 0; i < dk; i++) {
-            float t = f32_mul(Y[i * dv + j], iota);       /* t_ij = Y_ij iota_j */
-            double qv = round_half_even((double)t);
+            /* exact product of two fp32 values (fits in fp64), rounded once */
+            double qv = round_half_even((double)Y[i * dv + j] * (double)iota);
             if (qv > 127.0) qv = 127.0;
             if (qv < -127.0) qv = -127.0;
             Q[i * dv + j] = (int8_t)qv;
@@ -212,8 +214,7 @@ static void quantize_tile_damp(int dk, int dv, int n_hp, const int32_t *hp_idx, 
         int row = 0;
         for (int i = 0; i < dk; i++) {
             if (is_hp_row(i, n_hp, hp_idx)) continue;
-            float t = f32_mul(X[i * dv + j], iota);
-            double qv = round_half_even((double)t);
+            double qv = round_half_even((double)X[i * dv + j] * (double)iota);
             if (qv > 127.0) qv = 127.0;
             if (qv < -127.0) qv = -127.0;
             Qc[row * dv + j] = (int8_t)qv;

@@ -40,6 +40,18 @@ def test_hand_worked_example(orc):
     assert c[0, 0] == np.float32(np.float32(2.0) / np.float32(127.0))
 
 
+def test_rounding_takes_the_exact_product(orc):
+    # Rows [4, x]: s = 2 and rho = 1/2 exactly, so Y = x/2.  Column 1 has
+    # m = 1.5, iota = fp32(127/1.5) = 84.66666412353516.  For these Y the
+    # exact product Y * iota lies just off a half-integer while its fp32
+    # rounding lands on it: 0.50000002 -> 1, 7.49999998 -> 7, 8.50000011 -> 9
+    # (rounding the fp32 product instead would give 0, 8, 8).
+    ys = [0.0059055122546851635, 0.08858267962932587, 0.10039370507001877]
+    X = np.array([[[4.0, 3.0]] + [[4.0, 2 * y] for y in ys]], np.float32)
+    Q, s, c = orc.quantize(X)
+    assert Q[0].tolist() == [[127, 127], [127, 1], [127, 7], [127, 9]]
+
+
 def test_code_range_and_full_scale(orc):
     X = _states(11)
     Q, s, c = orc.quantize(X)
@@ -130,8 +142,9 @@ def test_denormal_inputs_are_kept(orc):
 
 def test_rounding_is_exhaustive_nearest_even(orc):
     # For every element, the code is the member of {-127..127} nearest to
-    # t_ij = Y_ij * iota_j, ties to the even code, found by trying all 255.
-    # t is rebuilt from the stored scales with numpy's IEEE fp32 ops.
+    # the exact product t_ij = Y_ij * iota_j, ties to the even code, found by
+    # trying all 255.  Y and iota are rebuilt from the stored scales with
+    # numpy's IEEE fp32 ops; the product is taken exactly in fp64.
     X = _states(19, nh=3, dk=32, dv=32)
     Q, s, c = orc.quantize(X)
     s32 = s.astype(np.float32)
@@ -140,7 +153,7 @@ def test_rounding_is_exhaustive_nearest_even(orc):
     Y = (X * rho[:, :, None]).astype(np.float32)
     m = np.abs(Y).max(axis=1)
     iota = np.where(m > 0, np.float32(127) / m, np.float32(0)).astype(np.float32)
-    t = (Y * iota[:, None, :]).astype(np.float64)
+    t = Y.astype(np.float64) * iota[:, None, :].astype(np.float64)
     codes = np.arange(-127, 128, dtype=np.float64)
     d = np.abs(t[..., None] - codes)
     best = d.min(axis=-1, keepdims=True)
