@@ -297,6 +297,55 @@ def copy_calibration(torch):
     log(f"copy calibration: 5 copies of {4 * n} bytes")
 
 
+def summarize_pmc(fetch_db: str, write_db: str, copy_fetch_db: str, copy_write_db: str, workload: str,
+                  out_md: str | None):
+    """Per-kernel mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) from two
+    rocprofv3 --pmc databases, scaled by what the same counters read for
+    the 1 GiB device copy of --copy-calibration; records bytes per launch
+    of the decode kernels in profiles/traffic.json with the current kernel
+    source hash."""
+    import collections
+    import sqlite3
+
+    def means(db, counter):
+        con = sqlite3.connect(db)
+        rows = con.execute("select kernel_name, value from counters_collection where counter_name = ?",
+                           (counter,)).fetchall()
+        agg = collections.defaultdict(list)
+        for k, v in rows:
+            agg[k.split("(")[0]].append(v)
+        return {k: float(np.mean(v)) for k, v in agg.items()}
+
+    copy_bytes = 4 << 28
+    cf = [v for k, v in means(copy_fetch_db, "FETCH_SIZE").items() if "copyBuffer" in k][0]
+    cw = [v for k, v in means(copy_write_db, "WRITE_SIZE").items() if "copyBuffer" in k][0]
+    fscale, wscale = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    fetch, write = means(fetch_db, "FETCH_SIZE"), means(write_db, "WRITE_SIZE")
+    lines = [f"copy calibration: 1 GiB device copy reads FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB "
+             f"-> scale fetch x{fscale:.4f}, write x{wscale:.4f}", "",
+             "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | scaled HBM bytes/launch |",
+             "|---|---|---|---|"]
+    path = os.path.join(PROFILES, "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    for k in sorted(fetch):
+        if k not in write:
+            continue
+        b = fetch[k] * 1024 * fscale + write[k] * 1024 * wscale
+        lines.append(f"| {k} | {fetch[k]:.1f} | {write[k]:.1f} | {b:.4g} |")
+        for tag in ("step_fused", "step_fp32", "window_step", "flush"):
+            if f"gdnq::{tag}_kernel" in k:
+                data.setdefault(workload, {})[tag] = {
+                    "bytes_per_launch": b, "src_hash": src_hash(), "fetch_kib": fetch[k],
+                    "write_kib": write[k], "fetch_scale": fscale, "write_scale": wscale}
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+    text = "\n".join(lines)
+    print(text)
+    if out_md:
+        with open(out_md, "a") as f:
+            f.write(text + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,7 +355,13 @@ def main():
                     choices=["prefix_cache", "gdn_serving", "kda", "damp"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
+                    help="summarize rocprofv3 --pmc databases into profiles/traffic.json (no GPU needed)")
+    ap.add_argument("--md", default=None, help="append the --summarize-pmc table to this file")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.workload, args.md)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the decode path shards over independent "
               f"(batch, head) states with no exchange, and this build measures one GPU's share "

@@ -5,6 +5,9 @@ Each source is compiled to an object in parallel, then linked.  Flags:
     operations round one at a time; kernels ask for fmaf() explicitly;
   * -fhip-fp32-correctly-rounded-divide-sqrt: IEEE division and sqrt;
   * -fno-gpu-flush-denormals-to-zero: fp32 subnormals are kept;
+  * -mno-amdgpu-ieee -fno-honor-nans: NaN inputs are unsupported, so the
+    kernels run without IEEE NaN quieting and max() needs no
+    canonicalizing moves (max reductions fuse with DPP);
   * packed fp32 instructions are switched off for the device code.
 """
 from __future__ import annotations
@@ -26,6 +29,7 @@ HEADERS = ["tile.hpp", "codec.hpp", "launch.hpp"]
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
+    "-mno-amdgpu-ieee", "-fno-honor-nans",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(G::NT) void calibrate_kernel(CalArgs A)
 {
     __shared__ CalLds<G> L;
     const Lane c = lane_coords<G>();
-    const size_t h = blockIdx.x;
+    const size_t h = __builtin_amdgcn_workgroup_id_x();
     constexpr size_t E = (size_t)G::DK * G::DV;
     float P[8][8];
 #pragma unroll
@@ -118,8 +118,7 @@ __global__ __launch_bounds__(G::NT) void calibrate_kernel(CalArgs A)
         for (int k = 0; k < 8; k++)
 #pragma unroll
             for (int j = 0; j < 8; j++) {
-                const float tq = P[k][j] * io[j];
-                const float q = (tq + RINT_MAGIC) - RINT_MAGIC;  // rint, exact
+                const float q = fmaf(P[k][j], io[j], RINT_MAGIC) - RINT_MAGIC;  // rint of the exact product
                 const float d = P[k][j] - q * cj[j];
                 En[k] = fmaf(d, d, En[k]);
             }

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(G::NT) void quantize_kernel(QuantArgs A)
     __shared__ CodecLds<G> L;
     __shared__ int hp[MAX_HP];
     const Lane c = lane_coords<G>();
-    const size_t h = blockIdx.x;
+    const size_t h = __builtin_amdgcn_workgroup_id_x();
     constexpr size_t E = (size_t)G::DK * G::DV;
     const int n_hp = DAMP ? A.n_hp : 0;
     if (DAMP && c.t < n_hp) hp[c.t] = A.hp_idx[h * n_hp + c.t];
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(G::NT) void dequantize_kernel(QuantArgs A)
 {
     __shared__ int hp[MAX_HP];
     const Lane c = lane_coords<G>();
-    const size_t h = blockIdx.x;
+    const size_t h = __builtin_amdgcn_workgroup_id_x();
     constexpr size_t E = (size_t)G::DK * G::DV;
     const int n_hp = DAMP ? A.n_hp : 0;
     if (DAMP && c.t < n_hp) hp[c.t] = A.hp_idx[h * n_hp + c.t];

@@ -11,9 +11,9 @@
 //   r_i = max_j |X_ij|; s_i = sqrt(r_i); rho_i = 1/s_i (0 if s_i = 0)
 //   Y_ij = X_ij rho_i; m_j = max_i |Y_ij|
 //   c_j = m_j/127, iota_j = 127/m_j (both 0 if m_j = 0 or 127/m_j overflows)
-//   Q_ij = rint_even(Y_ij iota_j)
+//   Q_ij = rint_even(Y_ij iota_j), the exact product rounded once (one fma)
 // No clamp is applied: |Y_ij| <= m_j and iota_j <= (127/m_j)(1 + 2^-24), so
-// |Y_ij iota_j| <= 127 (1 + 2^-24)^2 < 127.5 and the code is in [-127, 127].
+// |Y_ij iota_j| <= 127 (1 + 2^-24) < 127.5 and the code is in [-127, 127].
 //
 // Layout 1 (DAMP abstract: high-risk channels in higher precision, the rest
 // INT8): listed rows -> IEEE fp16 (round to nearest even, saturating at
@@ -116,18 +116,18 @@ __device__ void codec_rowcol(float (&P)[8][8], const Lane &c, CodecLds<G> &L, in
         for (int j = 1; j < 8; j++) m = fmaxf(m, fabsf(P[k][j]));
         r[k] = row_max<G>(m);
     }
+    const int row0 = row0_of<G>(c);
     if (c.cb < 8) {  // lane cb owns row k = cb of its row group
         const float rk = select8(r, c.cb);
         const float s = (rk > 0.0f) ? sqrtf(rk) : 0.0f;
         const float rho = (s > 0.0f) ? 1.0f / s : 0.0f;
-        const int i = row_of<G>(c, c.cb);
+        const int i = row0 + (c.cb >> 2) * (G::RGW * 4) + (c.cb & 3);
         L.rho[i] = rho;
         row_scale[i] = s;
     }
     wave_lds_sync();  // a row group lives in one wave
     float rho[8];
-#pragma unroll
-    for (int k = 0; k < 8; k++) rho[k] = L.rho[row_of<G>(c, k)];
+    load_rows_f32<G>(L.rho + row0, rho);
     float m[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) m[j] = 0.0f;
@@ -145,18 +145,16 @@ __device__ void codec_rowcol(float (&P)[8][8], const Lane &c, CodecLds<G> &L, in
     float io[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) io[j] = L.iota[c.cb * 8 + j];
+    int8_t *cbase = codes + (size_t)row0 * G::DV + c.cb * 8;
 #pragma unroll
     for (int k = 0; k < 8; k++) {
         float y[8];
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const float t = P[k][j] * io[j];
-            y[j] = t + RINT_MAGIC;
-        }
+        for (int j = 0; j < 8; j++) y[j] = fmaf(P[k][j], io[j], RINT_MAGIC);
         uint2 q;
         q.x = pack_low_bytes(y[0], y[1], y[2], y[3]);
         q.y = pack_low_bytes(y[4], y[5], y[6], y[7]);
-        *reinterpret_cast<uint2 *>(codes + (size_t)row_of<G>(c, k) * G::DV + c.cb * 8) = q;
+        *reinterpret_cast<uint2 *>(cbase + koff<G>(k) * G::DV) = q;
     }
 }
 
@@ -205,10 +203,7 @@ __device__ void codec_damp(float (&P)[8][8], const Lane &c, CodecLds<G> &L, cons
         } else {
             float y[8];
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const float t = P[k][j] * io[j];
-                y[j] = t + RINT_MAGIC;
-            }
+            for (int j = 0; j < 8; j++) y[j] = fmaf(P[k][j], io[j], RINT_MAGIC);
             uint2 q;
             q.x = pack_low_bytes(y[0], y[1], y[2], y[3]);
             q.y = pack_low_bytes(y[4], y[5], y[6], y[7]);

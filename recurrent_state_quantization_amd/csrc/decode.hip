@@ -65,28 +65,26 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     __shared__ CodecLds<G> L;
     __shared__ StepLds<G> SL;
     const Lane c = lane_coords<G>();
-    const size_t h = blockIdx.x;
+    const size_t h = __builtin_amdgcn_workgroup_id_x();
     constexpr size_t E = (size_t)G::DK * G::DV;
     int8_t *codes = A.codes + h * E;
     float *rs = A.row_scale + h * G::DK;
     float *cs = A.col_scale + h * G::DV;
 
+    const int row0 = row0_of<G>(c);
+    const int8_t *cbase = codes + (size_t)row0 * G::DV + c.cb * 8;
     uint2 qraw[8];
 #pragma unroll
-    for (int k = 0; k < 8; k++)
-        qraw[k] = *reinterpret_cast<const uint2 *>(codes + (size_t)row_of<G>(c, k) * G::DV + c.cb * 8);
+    for (int k = 0; k < 8; k++) qraw[k] = *reinterpret_cast<const uint2 *>(cbase + koff<G>(k) * G::DV);
     float cc[8];
     load_f32x8(cs + c.cb * 8, cc);
     float s[8], kk[8], qq[8], av[8];
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-        const int i = row_of<G>(c, k);
-        s[k] = rs[i];
-        kk[k] = load1<BF16>(A.k, h * G::DK + i);
-        qq[k] = load1<BF16>(A.q, h * G::DK + i);
-        av[k] = KDA ? A.a[h * G::DK + i] : 0.0f;
-    }
-    if constexpr (!KDA) {
+    load_rows_f32<G>(rs + row0, s);
+    load_rows<G, BF16>(A.k, h * G::DK, row0, kk);
+    load_rows<G, BF16>(A.q, h * G::DK, row0, qq);
+    if constexpr (KDA) {
+        load_rows_f32<G>(A.a + h * G::DK + row0, av);
+    } else {
         const float ag = A.a[h];
 #pragma unroll
         for (int k = 0; k < 8; k++) av[k] = ag;
@@ -145,9 +143,9 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
 #pragma unroll
         for (int j = 0; j < 8; j++) X[k][j] = fmaf(kk[k], u8[j], (X[k][j] * cc[j]) * as[k]);
     if (A.prequant) {
-        float *pq = A.prequant + h * E;
+        float *pq = A.prequant + h * E + (size_t)row0 * G::DV + c.cb * 8;
 #pragma unroll
-        for (int k = 0; k < 8; k++) store_f32x8(pq + (size_t)row_of<G>(c, k) * G::DV + c.cb * 8, X[k]);
+        for (int k = 0; k < 8; k++) store_f32x8(pq + koff<G>(k) * G::DV, X[k]);
     }
     codec_rowcol<G>(X, c, L, codes, rs, cs);
 }
@@ -157,22 +155,21 @@ __global__ __launch_bounds__(G::NT) void step_fp32_kernel(StepArgs A)
 {
     __shared__ StepLds<G> SL;
     const Lane c = lane_coords<G>();
-    const size_t h = blockIdx.x;
+    const size_t h = __builtin_amdgcn_workgroup_id_x();
     constexpr size_t E = (size_t)G::DK * G::DV;
     float *S = A.S + h * E;
 
+    const int row0 = row0_of<G>(c);
+    float *Sb = S + (size_t)row0 * G::DV + c.cb * 8;
     float X[8][8];
 #pragma unroll
-    for (int k = 0; k < 8; k++) load_f32x8(S + (size_t)row_of<G>(c, k) * G::DV + c.cb * 8, X[k]);
+    for (int k = 0; k < 8; k++) load_f32x8(Sb + koff<G>(k) * G::DV, X[k]);
     float kk[8], qq[8], av[8];
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-        const int i = row_of<G>(c, k);
-        kk[k] = load1<BF16>(A.k, h * G::DK + i);
-        qq[k] = load1<BF16>(A.q, h * G::DK + i);
-        av[k] = KDA ? A.a[h * G::DK + i] : 0.0f;
-    }
-    if constexpr (!KDA) {
+    load_rows<G, BF16>(A.k, h * G::DK, row0, kk);
+    load_rows<G, BF16>(A.q, h * G::DK, row0, qq);
+    if constexpr (KDA) {
+        load_rows_f32<G>(A.a + h * G::DK + row0, av);
+    } else {
         const float ag = A.a[h];
 #pragma unroll
         for (int k = 0; k < 8; k++) av[k] = ag;
@@ -223,7 +220,7 @@ __global__ __launch_bounds__(G::NT) void step_fp32_kernel(StepArgs A)
     for (int k = 0; k < 8; k++) {
 #pragma unroll
         for (int j = 0; j < 8; j++) X[k][j] = fmaf(kk[k], u8[j], X[k][j] * av[k]);
-        store_f32x8(S + (size_t)row_of<G>(c, k) * G::DV + c.cb * 8, X[k]);
+        store_f32x8(Sb + koff<G>(k) * G::DV, X[k]);
     }
 }
 

@@ -52,7 +52,7 @@ template <class G>
 __device__ __forceinline__ Lane lane_coords()
 {
     Lane c;
-    c.t = threadIdx.x;
+    c.t = (int)__builtin_amdgcn_workitem_id_x();
     c.lane = c.t & 63;
     c.w = c.t >> 6;
     c.cb = c.lane % G::NCB;
@@ -60,10 +60,24 @@ __device__ __forceinline__ Lane lane_coords()
     return c;
 }
 
+// First row of the thread's block; row k is row0 + koff(k), a compile-time
+// offset once k is unrolled (so loads and stores use immediate offsets).
+template <class G>
+__device__ __forceinline__ int row0_of(const Lane &c)
+{
+    return c.w * G::ROWS_W + 4 * c.rgl;
+}
+
+template <class G>
+__host__ __device__ constexpr int koff(int k)
+{
+    return (k >> 2) * (G::RGW * 4) + (k & 3);
+}
+
 template <class G>
 __device__ __forceinline__ int row_of(const Lane &c, int k)
 {
-    return c.w * G::ROWS_W + (k >> 2) * (G::RGW * 4) + 4 * c.rgl + (k & 3);
+    return row0_of<G>(c) + koff<G>(k);
 }
 
 // ---------------------------------------------------------------- DPP
@@ -223,13 +237,35 @@ __device__ __forceinline__ void store1(void *base, size_t off, float x)
     else reinterpret_cast<float *>(base)[off] = x;
 }
 
-// The thread's 8 row values of a per-row vector (rows r0..r0+3 and
-// r0+RGW*4..+3 are contiguous runs of 4).
+// The thread's 8 row values of a per-row vector: rows row0..row0+3 and
+// row0+RGW*4..+3 are two aligned runs of 4, loaded as two vectors.
 template <class G, bool BF16>
-__device__ __forceinline__ void load_rows(const void *base, size_t head_off, const Lane &c, float (&out)[8])
+__device__ __forceinline__ void load_rows(const void *base, size_t head_off, int row0, float (&out)[8])
 {
-#pragma unroll
-    for (int k = 0; k < 8; k++) out[k] = load1<BF16>(base, head_off + row_of<G>(c, k));
+    if constexpr (BF16) {
+        const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + head_off + row0;
+        const uint2 a = *reinterpret_cast<const uint2 *>(p);
+        const uint2 b = *reinterpret_cast<const uint2 *>(p + G::RGW * 4);
+        out[0] = __uint_as_float(a.x << 16); out[1] = __uint_as_float(a.x & 0xFFFF0000u);
+        out[2] = __uint_as_float(a.y << 16); out[3] = __uint_as_float(a.y & 0xFFFF0000u);
+        out[4] = __uint_as_float(b.x << 16); out[5] = __uint_as_float(b.x & 0xFFFF0000u);
+        out[6] = __uint_as_float(b.y << 16); out[7] = __uint_as_float(b.y & 0xFFFF0000u);
+    } else {
+        const float *p = reinterpret_cast<const float *>(base) + head_off + row0;
+        const float4 a = *reinterpret_cast<const float4 *>(p);
+        const float4 b = *reinterpret_cast<const float4 *>(p + G::RGW * 4);
+        out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+        out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+    }
+}
+
+template <class G>
+__device__ __forceinline__ void load_rows_f32(const float *p, float (&out)[8])
+{
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + G::RGW * 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
 __device__ __forceinline__ void load_f32x8(const float *p, float (&out)[8])
@@ -267,9 +303,10 @@ __device__ __forceinline__ uint32_t pack_low_bytes(float a, float b, float c, fl
     return lo | hi;
 }
 
-// Round to nearest even integer for |t| < 2^22 by adding 1.5*2^23: the sum
-// is exact up to the one rounding at unit spacing, so its low mantissa byte
-// is rint(t) mod 256 (two's complement int8).
+// fma(y, iota, 1.5*2^23) rounds the exact value y*iota + 1.5*2^23 once, at
+// unit spacing (the sum lies in [2^23, 2^24) for |y*iota| < 2^22), so it
+// equals 1.5*2^23 + rint_even(y*iota) with the product taken exactly; the
+// low mantissa byte is that integer mod 256 (two's complement int8).
 constexpr float RINT_MAGIC = 12582912.0f;
 
 }  // namespace gdnq

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(G::NT) void window_step_kernel(WinArgs A)
 {
     __shared__ WinLds<G> L;
     const Lane c = lane_coords<G>();
-    const size_t h = blockIdx.x;
+    const size_t h = __builtin_amdgcn_workgroup_id_x();
     const int n_hp = DAMP ? A.n_hp : 0;
     const int r = A.r;
 
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(G::NT) void flush_kernel(FlushArgs A)
     __shared__ CodecLds<G> L;
     __shared__ FlushLds<G> F;
     const Lane c = lane_coords<G>();
-    const size_t h = blockIdx.x;
+    const size_t h = __builtin_amdgcn_workgroup_id_x();
     const int n_hp = DAMP ? A.n_hp : 0;
     if (!DAMP) A.n_hp = 0;
     if (c.t < G::DK) F.gs[c.t] = KDA ? A.g_cur[h * G::DK + c.t] : A.g_cur[h];

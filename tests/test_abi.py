@@ -1,0 +1,171 @@
+"""The C ABI without a GPU: libgdnq.so loads, exports every function that
+include/gdnq.h declares, reports state sizes, and rejects every invalid
+argument on the host -- before any HIP call -- with its error code and a
+message.  Device pointers here are fake aligned addresses: a rejected call
+never dereferences them."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdnq.h")
+
+
+@pytest.fixture(scope="module")
+def g():
+    import recurrent_state_quantization_amd as g
+    return g
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^(?:int|const char \*)\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(g):
+    names = declared_functions()
+    assert len(names) == 8, names
+    out = subprocess.run(["nm", "-D", "--defined-only", g.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(g.LIB_PATH)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_struct_layouts_match_header(g):
+    # field order and count of gdnq_desc / gdnq_state as declared
+    text = open(HEADER).read()
+    desc = re.search(r"typedef struct \{(.*?)\} gdnq_desc;", text, re.S).group(1)
+    desc = re.sub(r"/\*.*?\*/", "", desc, flags=re.S)
+    fields = re.findall(r"(\w+)(?=\s*[,;])", desc)
+    assert fields == [f[0] for f in g._Desc._fields_]
+    state = re.search(r"typedef struct \{(.*?)\} gdnq_state;", text, re.S).group(1)
+    sfields = re.findall(r"\*(\w+);", state)
+    assert tuple(sfields) == g.STATE_FIELDS
+    assert ctypes.sizeof(g._Desc) == 12 * 4
+
+
+FAKE = 1 << 40      # aligned, never dereferenced
+FAKE2 = 1 << 41
+
+
+def _fake_state(g, d, base=FAKE):
+    sizes = g.gdnq_state_sizes(d)
+    st, off = {}, base
+    for name, n in zip(g.STATE_FIELDS, sizes):
+        if n:
+            st[name] = off
+            off += (n + 255) // 256 * 256
+    return st
+
+
+def _err(fn):
+    import recurrent_state_quantization_amd as g
+    with pytest.raises(g.GdnqError) as e:
+        fn()
+    return e.value.code, str(e.value)
+
+
+def test_state_sizes(g):
+    d = g.Desc(B=2, H=3, dk=128, dv=64, W=4, r=2, decay=g.DECAY_CHANNEL)
+    nh = 6
+    assert g.gdnq_state_sizes(d) == [nh * 128 * 64, nh * 128 * 4, nh * 64 * 4, nh * 2 * 128 * 4,
+                                     nh * 2 * 64 * 4, nh * 4 * 128 * 4, nh * 4 * 64 * 4, nh * 128 * 4,
+                                     0, 0, 0]
+    d = g.Desc(B=1, H=2, W=16, r=2, layout=g.LAYOUT_DAMP, n_hp=8, flags=g.DEBUG_PREQUANT)
+    s = g.gdnq_state_sizes(d)
+    assert s[0] == 2 * 120 * 128 and s[1] == 0 and s[8] == 2 * 8 * 128 * 2 and s[9] == 2 * 8 * 4
+    assert s[10] == 2 * 128 * 128 * 4
+    d = g.Desc(B=4, H=1)       # per-step: no window buffers
+    assert g.gdnq_state_sizes(d)[5:8] == [0, 0, 0]
+
+
+@pytest.mark.parametrize("over,code,msg", [
+    (dict(dk=96), 2, "dk and dv"),
+    (dict(dv=256), 2, "dk and dv"),
+    (dict(B=0), 1, "B and H"),
+    (dict(W=0), 1, "W must"),
+    (dict(W=300), 1, "W must"),
+    (dict(r=9), 1, "r must"),
+    (dict(decay=5), 1, "decay"),
+    (dict(io_dtype=7), 1, "io_dtype"),
+    (dict(layout=3), 1, "layout"),
+    (dict(layout=1, n_hp=0), 1, "n_hp"),
+    (dict(layout=1, n_hp=65), 1, "n_hp"),
+    (dict(r=2, W=4, power_iters=0), 1, "power_iters"),
+    (dict(flags=8), 1, "flag"),
+])
+def test_descriptor_errors(g, over, code, msg):
+    kw = dict(B=2, H=2)
+    kw.update(over)
+    d = g.Desc(**kw)
+    c, m = _err(lambda: g.gdnq_state_sizes(d))
+    assert c == code and msg in m
+
+
+def test_decode_step_argument_errors(g):
+    d = g.Desc(B=2, H=2, W=8, r=2)
+    st = _fake_state(g, d)
+    io = [FAKE2 + i * (1 << 20) for i in range(6)]
+    call = lambda s=st, t=0, args=io: g.gdn_quant_decode_step(d, s, *args, t, stream=0)
+    assert _err(lambda: call(t=8))[0] == 1
+    assert _err(lambda: call(t=-1))[0] == 1
+    c, m = _err(lambda: call(s={k: v for k, v in st.items() if k != "buf_u"}))
+    assert c == 1 and "buf_u" in m
+    bad = dict(st, comp_k=st["comp_k"] + 4)
+    c, m = _err(lambda: call(s=bad))
+    assert c == 1 and "aligned" in m
+    over = dict(st, buf_k=st["codes"])
+    c, m = _err(lambda: call(s=over))
+    assert c == 1 and "overlaps" in m
+    # output inside a state array
+    args = list(io)
+    args[5] = st["codes"]
+    c, m = _err(lambda: call(args=args))
+    assert c == 1 and "o overlaps" in m
+    # input null
+    args = list(io)
+    args[1] = None
+    c, m = _err(lambda: call(args=args))
+    assert c == 1 and "k is NULL" in m
+    # q may alias k (both read-only)
+    args = list(io)
+    args[0] = args[1] = FAKE2 + (1 << 30)
+    # still rejected for other reasons? no: this one would launch, so only
+    # check that aliasing inputs is not itself an error by making o bad
+    args[5] = None
+    c, m = _err(lambda: call(args=args))
+    assert "o is NULL" in m
+
+
+def test_flush_quantize_dequantize_calibrate_errors(g):
+    d = g.Desc(B=1, H=2, W=4, r=1)
+    st = _fake_state(g, d)
+    assert _err(lambda: g.gdn_quant_window_flush(d, st, 0, stream=0))[0] == 1
+    assert _err(lambda: g.gdn_quant_window_flush(d, st, 5, stream=0))[0] == 1
+    c, m = _err(lambda: g.gdn_state_quantize(d, st["codes"], st, stream=0))
+    assert c == 1 and "S overlaps" in m
+    c, m = _err(lambda: g.gdn_state_dequantize(d, st, FAKE + 8, stream=0))
+    assert c == 1 and "aligned" in m
+    dd = g.Desc(B=1, H=2, layout=g.LAYOUT_DAMP, n_hp=4)
+    c, m = _err(lambda: g.calibrate_scales(dd, FAKE, FAKE2, FAKE2 + (1 << 24), FAKE2 + (2 << 24),
+                                           FAKE2 + (3 << 24), 0, FAKE2 + (4 << 24), None, stream=0))
+    assert c == 1 and "n_steps" in m
+    c, m = _err(lambda: g.calibrate_scales(dd, FAKE, FAKE2, FAKE2 + (1 << 24), FAKE2 + (2 << 24),
+                                           FAKE2 + (3 << 24), 4, FAKE, None, stream=0))
+    assert c == 1 and "overlaps" in m
+    c, m = _err(lambda: g.gdn_fp32_decode_step(g.Desc(B=1, H=1, dk=32), FAKE, *([FAKE2] * 6), stream=0))
+    assert c == 2
+
+
+def test_per_step_flush_is_noop(g):
+    d = g.Desc(B=1, H=2)
+    g.gdn_quant_window_flush(d, {}, 1, stream=0)      # no launch, no pointers needed
+    assert _err(lambda: g.gdn_quant_window_flush(d, {}, 2, stream=0))[0] == 1
