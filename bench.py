@@ -212,6 +212,7 @@ def bench_prefix_cache(args, torch, g):
                        "traffic": stored_traffic("step_fp32", "prefix_cache")},
         "speedup_vs_fp32_state": wall32 / wall,
     }
+    res["device_copy"] = device_copy(torch)
     if not args.no_cpu:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(cfg, S[:2048], inputs)
@@ -284,6 +285,27 @@ def bench_window(args, torch, g, name):
         "cpu_baseline": None,
     }
     return res
+
+
+def device_copy(torch, nbytes: int = 2 << 30, reps: int = 5):
+    """Context for the roofline: the best of `reps` device-to-device copies
+    of nbytes (torch copy_, one read and one write per byte) in the same
+    run, timed with events; reported as read+write GB/s."""
+    n = nbytes // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    best = 1e9
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    del a, b
+    return {"bytes": 2 * nbytes, "best_s": best, "GBs": 2 * nbytes / best / 1e9,
+            "frac_of_peak": 2 * nbytes / best / 1e9 / HBM_PEAK_GBS}
 
 
 def copy_calibration(torch):

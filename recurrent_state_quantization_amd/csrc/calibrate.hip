@@ -125,16 +125,21 @@ __global__ __launch_bounds__(G::NT) void calibrate_kernel(CalArgs A)
         // the next step's first barrier orders these LDS reads before the
         // next writes of L.red / L.u / L.iota
     }
-#pragma unroll
-    for (int k = 0; k < 8; k++) En[k] = row_sum<G>(En[k]);
-    if (c.cb < 8) {
-        const int i = row_of<G>(c, c.cb);
-        const float e = select8(En, c.cb);
-        const float abar = select8(asum, c.cb) / (float)A.n_steps;
+    {
+        const float e = row_reduce_scatter<G, OpSum>(En, c.cb);
+        const int k = row_scatter_k<G>(c.cb);
+        // every lane of the row group holds the same gate sums, so their
+        // reduce-scatter is exactly NCB times row k's sum (pairwise sums of
+        // equal values are exact)
+        const float as = row_reduce_scatter<G, OpSum>(asum, c.cb) * (1.0f / G::NCB);
+        if (G::NCB == 8 || (c.cb & 1) == 0) {
+        const int i = row0_of<G>(c) + (k >> 2) * (G::RGW * 4) + (k & 3);
+        const float abar = as / (float)A.n_steps;
         const float den = fmaxf(1.0f - abar, 1e-6f);
         const float s = e / den;
         L.sc[i] = s;
         if (A.score) A.score[h * G::DK + i] = s;
+        }
     }
     __syncthreads();
     if (c.t == 0) {

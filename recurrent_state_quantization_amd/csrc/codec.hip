@@ -25,7 +25,7 @@ struct QuantArgs {
 };
 
 template <class G, bool DAMP>
-__global__ __launch_bounds__(G::NT) void quantize_kernel(QuantArgs A)
+__global__ __launch_bounds__(G::NT, 2) void quantize_kernel(QuantArgs A)
 {
     __shared__ CodecLds<G> L;
     __shared__ int hp[MAX_HP];

@@ -64,13 +64,6 @@ __device__ __forceinline__ RowMap row_map(const Lane &c, const int *hp_lds, int 
     return m;
 }
 
-__device__ __forceinline__ float select8(const float (&v)[8], int i)
-{
-    float r = v[0];
-#pragma unroll
-    for (int k = 1; k < 8; k++) r = (i == k) ? v[k] : r;
-    return r;
-}
 
 // Column scales from the per-wave column maxima in L.red[0]; thread t < DV
 // owns column t.  Writes c to global memory and iota to LDS.
@@ -114,16 +107,20 @@ __device__ void codec_rowcol(float (&P)[8][8], const Lane &c, CodecLds<G> &L, in
         float m = fabsf(P[k][0]);
 #pragma unroll
         for (int j = 1; j < 8; j++) m = fmaxf(m, fabsf(P[k][j]));
-        r[k] = row_max<G>(m);
+        r[k] = m;
     }
     const int row0 = row0_of<G>(c);
-    if (c.cb < 8) {  // lane cb owns row k = cb of its row group
-        const float rk = select8(r, c.cb);
-        const float s = (rk > 0.0f) ? sqrtf(rk) : 0.0f;
-        const float rho = (s > 0.0f) ? 1.0f / s : 0.0f;
-        const int i = row0 + (c.cb >> 2) * (G::RGW * 4) + (c.cb & 3);
-        L.rho[i] = rho;
-        row_scale[i] = s;
+    {
+        // this lane ends up with the full max of row k = row_scatter_k(cb)
+        const float rk = row_reduce_scatter<G, OpMax>(r, c.cb);
+        const int k = row_scatter_k<G>(c.cb);
+        if (G::NCB == 8 || (c.cb & 1) == 0) {
+            const float s = (rk > 0.0f) ? sqrtf(rk) : 0.0f;
+            const float rho = (s > 0.0f) ? 1.0f / s : 0.0f;
+            const int i = row0 + (k >> 2) * (G::RGW * 4) + (k & 3);
+            L.rho[i] = rho;
+            row_scale[i] = s;
+        }
     }
     wave_lds_sync();  // a row group lives in one wave
     float rho[8];
@@ -216,21 +213,51 @@ __device__ void codec_damp(float (&P)[8][8], const Lane &c, CodecLds<G> &L, cons
 // every thread for its own 8 columns.  Uses L.red[buf]; the caller
 // alternates buf between calls so one barrier per call suffices.
 template <class G>
-__device__ __forceinline__ void column_sum_all(const Lane &c, CodecLds<G> &L, int buf, const float (&yp)[8],
+__device__ __forceinline__ void column_sum_all(const Lane &c, float (&red)[G::NW][G::DV], const float (&yp)[8],
                                                float (&y)[8])
 {
     float z[2];
     col_reduce_scatter<G, OpSum, 8>(yp, z);
 #pragma unroll
-    for (int p = 0; p < 2; p++) L.red[buf][c.w][c.cb * 8 + scatter_index(c, p)] = z[p];
+    for (int p = 0; p < 2; p++) red[c.w][c.cb * 8 + scatter_index(c, p)] = z[p];
     __syncthreads();
+    load_f32x8(&red[0][c.cb * 8], y);
+#pragma unroll
+    for (int w = 1; w < G::NW; w++) {
+        float t[8];
+        load_f32x8(&red[w][c.cb * 8], t);
+#pragma unroll
+        for (int j = 0; j < 8; j++) y[j] += t[j];
+    }
+}
+
+// One power-iteration step v <- P^T (P v) / |P^T (P v)| using LDS buffer
+// `red` for the column sums; returns |.|^2 (the same value in every lane).
+template <class G>
+__device__ __forceinline__ float power_step(const float (&P)[8][8], const Lane &c, float (&red)[G::NW][G::DV],
+                                            float (&v)[8], float (&y)[8])
+{
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        float s = P[k][0] * v[0];
+#pragma unroll
+        for (int j = 1; j < 8; j++) s = fmaf(P[k][j], v[j], s);
+        x[k] = row_sum<G>(s);
+    }
+    float yp[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        float s = L.red[buf][0][c.cb * 8 + j];
+        float s = P[0][j] * x[0];
 #pragma unroll
-        for (int w = 1; w < G::NW; w++) s += L.red[buf][w][c.cb * 8 + j];
-        y[j] = s;
+        for (int k = 1; k < 8; k++) s = fmaf(P[k][j], x[k], s);
+        yp[j] = s;
     }
+    column_sum_all<G>(c, red, yp, y);
+    float n2 = y[0] * y[0];
+#pragma unroll
+    for (int j = 1; j < 8; j++) n2 = fmaf(y[j], y[j], n2);
+    return row_sum<G>(n2);
 }
 
 // Compensator Tokens by power iteration with sequential deflation, on the
@@ -245,7 +272,6 @@ template <class G>
 __device__ void power_deflate(float (&P)[8][8], const Lane &c, CodecLds<G> &L, int r, int iters,
                               float *__restrict__ comp_k, float *__restrict__ comp_v)
 {
-    int buf = 0;
     for (int cc = 0; cc < r; cc++) {
         bool nz = false;
 #pragma unroll
@@ -261,63 +287,59 @@ __device__ void power_deflate(float (&P)[8][8], const Lane &c, CodecLds<G> &L, i
             const float v0 = (G::DV == 128) ? 0.08838834764831845f : 0.125f;
 #pragma unroll
             for (int j = 0; j < 8; j++) v[j] = v0;
-            bool restarted = false;
-            for (int it = 0; it < iters; it++) {
-                float x[8];
-#pragma unroll
-                for (int k = 0; k < 8; k++) {
-                    float s = P[k][0] * v[0];
-#pragma unroll
-                    for (int j = 1; j < 8; j++) s = fmaf(P[k][j], v[j], s);
-                    x[k] = row_sum<G>(s);
-                }
-                float yp[8], y[8];
+            // first step, with the restart rule; L.red[0] is free here (the
+            // barrier of __syncthreads_or follows every earlier read of it)
+            float y[8];
+            float n2 = power_step<G>(P, c, L.red[0], v, y);
+            if (n2 == 0.0f) {  // uniform: every lane holds the same n2
+                float cn[8], cs[8];
 #pragma unroll
                 for (int j = 0; j < 8; j++) {
-                    float s = P[0][j] * x[0];
+                    float s = P[0][j] * P[0][j];
 #pragma unroll
-                    for (int k = 1; k < 8; k++) s = fmaf(P[k][j], x[k], s);
-                    yp[j] = s;
+                    for (int k = 1; k < 8; k++) s = fmaf(P[k][j], P[k][j], s);
+                    cn[j] = s;
                 }
-                column_sum_all<G>(c, L, buf, yp, y);
-                buf ^= 1;
-                float n2 = y[0] * y[0];
-#pragma unroll
-                for (int j = 1; j < 8; j++) n2 = fmaf(y[j], y[j], n2);
-                n2 = row_sum<G>(n2);
-                if (n2 == 0.0f) {  // uniform: every lane holds the same n2
-                    if (it > 0 || restarted) break;
-                    float cn[8], cs[8];
-#pragma unroll
-                    for (int j = 0; j < 8; j++) {
-                        float s = P[0][j] * P[0][j];
-#pragma unroll
-                        for (int k = 1; k < 8; k++) s = fmaf(P[k][j], P[k][j], s);
-                        cn[j] = s;
+                column_sum_all<G>(c, L.red[1], cn, cs);
+                if (c.t == 0) {
+                    int best = 0;
+                    float bv = -1.0f;
+                    for (int j = 0; j < G::DV; j++) {
+                        float s = L.red[1][0][j];
+                        for (int w = 1; w < G::NW; w++) s += L.red[1][w][j];
+                        if (s > bv) { bv = s; best = j; }
                     }
-                    column_sum_all<G>(c, L, buf, cn, cs);
-                    buf ^= 1;
-                    if (c.t == 0) {
-                        int best = 0;
-                        float bv = -1.0f;
-                        for (int j = 0; j < G::DV; j++) {
-                            float s = L.red[buf ^ 1][0][j];
-                            for (int w = 1; w < G::NW; w++) s += L.red[buf ^ 1][w][j];
-                            if (s > bv) { bv = s; best = j; }
-                        }
-                        L.misc = best;
-                    }
-                    __syncthreads();
-                    const int jb = L.misc;
-#pragma unroll
-                    for (int j = 0; j < 8; j++) v[j] = (c.cb * 8 + j == jb) ? 1.0f : 0.0f;
-                    restarted = true;
-                    it = -1;
-                    continue;
+                    L.misc = best;
                 }
-                const float inv = 1.0f / sqrtf(n2);
+                __syncthreads();
+                const int jb = L.misc;
+#pragma unroll
+                for (int j = 0; j < 8; j++) v[j] = (c.cb * 8 + j == jb) ? 1.0f : 0.0f;
+                n2 = power_step<G>(P, c, L.red[0], v, y);
+            }
+            // the normalization only rescales the iterate: the hardware
+            // reciprocal square root (about 1 ulp) is accurate enough
+            int it = 1;
+            if (n2 != 0.0f) {
+                float inv = __builtin_amdgcn_rsqf(n2);
 #pragma unroll
                 for (int j = 0; j < 8; j++) v[j] = y[j] * inv;
+                // remaining steps two at a time so each LDS buffer is fixed;
+                // consecutive steps alternate buffers, so one barrier per
+                // step orders every read of a buffer before its next write
+                for (; it < iters; it += 2) {
+                    n2 = power_step<G>(P, c, L.red[1], v, y);
+                    if (n2 == 0.0f) break;
+                    inv = __builtin_amdgcn_rsqf(n2);
+#pragma unroll
+                    for (int j = 0; j < 8; j++) v[j] = y[j] * inv;
+                    if (it + 1 >= iters) break;
+                    n2 = power_step<G>(P, c, L.red[0], v, y);
+                    if (n2 == 0.0f) break;
+                    inv = __builtin_amdgcn_rsqf(n2);
+#pragma unroll
+                    for (int j = 0; j < 8; j++) v[j] = y[j] * inv;
+                }
             }
 #pragma unroll
             for (int k = 0; k < 8; k++) {

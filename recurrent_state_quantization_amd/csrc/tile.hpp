@@ -115,6 +115,74 @@ __device__ __forceinline__ float row_max(float x)
     return x;
 }
 
+// Row reduce-scatter over the NCB column-block lanes of a row group:
+// x[0..7] are this lane's partials for its 8 rows; the result is the whole
+// row group's reduction of x[k] with k = cb >> 1 (NCB = 16) or k = cb
+// (NCB = 8).  Each step pairs lanes that still hold the same index set
+// (mirror, half-mirror, then quad swaps), keeps half the values and sends
+// the other half; no dynamically indexed array is involved.
+template <class G, class Op>
+__device__ __forceinline__ float row_reduce_scatter(const float (&x)[8], int cb)
+{
+    float v4[4], v2[2];
+    if constexpr (G::NCB == 16) {
+        // row_mirror pairs cb with cb ^ 15: every lane still holds all 8
+        // values, so keep/send is decided by bit 3 alone
+        const bool b3 = (cb >> 3) & 1;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float keep = b3 ? x[j + 4] : x[j];
+            const float send = b3 ? x[j] : x[j + 4];
+            v4[j] = Op::f(keep, dpp<DPP_MIRROR>(send));
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; j++) v4[j] = 0.0f;
+    }
+    // row_half_mirror pairs cb with cb ^ 7 (same bit 3): decided by bit 2
+    const bool b2 = (cb >> 2) & 1;
+    if constexpr (G::NCB == 16) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const float keep = b2 ? v4[j + 2] : v4[j];
+            const float send = b2 ? v4[j] : v4[j + 2];
+            v2[j] = Op::f(keep, dpp<DPP_HALF_MIRROR>(send));
+        }
+    } else {
+        float w4[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float keep = b2 ? x[j + 4] : x[j];
+            const float send = b2 ? x[j] : x[j + 4];
+            w4[j] = Op::f(keep, dpp<DPP_HALF_MIRROR>(send));
+        }
+        const bool b1 = (cb >> 1) & 1;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const float keep = b1 ? w4[j + 2] : w4[j];
+            const float send = b1 ? w4[j] : w4[j + 2];
+            v2[j] = Op::f(keep, dpp<DPP_XOR2>(send));
+        }
+        const bool b0 = cb & 1;
+        const float keep = b0 ? v2[1] : v2[0];
+        const float send = b0 ? v2[0] : v2[1];
+        return Op::f(keep, dpp<DPP_XOR1>(send));  // row k = cb
+    }
+    const bool b1 = (cb >> 1) & 1;
+    const float keep = b1 ? v2[1] : v2[0];
+    const float send = b1 ? v2[0] : v2[1];
+    const float v1 = Op::f(keep, dpp<DPP_XOR2>(send));
+    return Op::f(v1, dpp<DPP_XOR1>(v1));           // row k = cb >> 1, both lanes of the pair
+}
+
+// Row index (0..7 within the thread's block) row_reduce_scatter leaves in
+// this lane.
+template <class G>
+__device__ __forceinline__ int row_scatter_k(int cb)
+{
+    return (G::NCB == 16) ? (cb >> 1) : cb;
+}
+
 // --------------------------------------------------------- permlane swaps
 // swap32(a, b): a <- [a_lo, b_lo], b <- [a_hi, b_hi] (lo = lanes 0..31).
 __device__ __forceinline__ void swap32(float &a, float &b)

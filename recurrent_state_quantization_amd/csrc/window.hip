@@ -281,7 +281,7 @@ __device__ __forceinline__ void slot_val(const FlushArgs &A, size_t h, int l, in
 }
 
 template <class G, bool KDA, bool DAMP>
-__global__ __launch_bounds__(G::NT) void flush_kernel(FlushArgs A)
+__global__ __launch_bounds__(G::NT, 2) void flush_kernel(FlushArgs A)
 {
     __shared__ CodecLds<G> L;
     __shared__ FlushLds<G> F;

@@ -243,3 +243,21 @@ def test_scalar_decay_ranking_is_energy_ranking(orc):
     E, _ = _energy(orc, S0, k, v, a, b)
     for h in range(nh):
         assert np.array_equal(np.argsort(-score[h], kind="stable"), np.argsort(-E[h], kind="stable"))
+
+
+def test_power_iteration_restart_with_exact_pairs(orc):
+    # Column pairs (c, -c) make every row sum to zero exactly, so the first
+    # step vanishes for both compensators; the result still matches the SVD.
+    g = synth.misc_rng(31, 1)
+    dk, dv = 16, 12
+    A = 10.0 * np.outer(g.standard_normal(dk), g.standard_normal(dv // 2))
+    A += 0.1 * g.standard_normal((dk, dv // 2))
+    X = np.zeros((1, dk, dv))
+    X[0, :, 0::2] = A
+    X[0, :, 1::2] = -A
+    out = orc.compress(X, 2)
+    S, U, Vt = _svd_top(X[0])
+    for ci in range(2):
+        ref = S[ci] * np.outer(U[:, ci], Vt[ci])
+        got = np.outer(out["p"][0, ci], out["w"][0, ci]).astype(np.float64)
+        assert np.max(np.abs(got - ref)) <= 1e-5 * S[0]
