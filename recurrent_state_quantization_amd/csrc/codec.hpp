@@ -96,8 +96,9 @@ __device__ __forceinline__ void column_max_to_lds(const Lane &c, CodecLds<G> &L,
 }
 
 // Layout-0 codec of the register tile P (overwritten with Y).  Writes this
-// head's codes [DK][DV], row scales [DK] and column scales [DV].
-template <class G>
+// head's codes [DK][DV], row scales [DK] and column scales [DV]; STREAM
+// marks the code stores non-temporal.
+template <class G, bool STREAM = false>
 __device__ void codec_rowcol(float (&P)[8][8], const Lane &c, CodecLds<G> &L, int8_t *__restrict__ codes,
                              float *__restrict__ row_scale, float *__restrict__ col_scale)
 {
@@ -151,7 +152,8 @@ __device__ void codec_rowcol(float (&P)[8][8], const Lane &c, CodecLds<G> &L, in
         uint2 q;
         q.x = pack_low_bytes(y[0], y[1], y[2], y[3]);
         q.y = pack_low_bytes(y[4], y[5], y[6], y[7]);
-        *reinterpret_cast<uint2 *>(cbase + koff<G>(k) * G::DV) = q;
+        if constexpr (STREAM) store_nt8(cbase + koff<G>(k) * G::DV, q);
+        else *reinterpret_cast<uint2 *>(cbase + koff<G>(k) * G::DV) = q;
     }
 }
 

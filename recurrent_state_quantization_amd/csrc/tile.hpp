@@ -349,6 +349,23 @@ __device__ __forceinline__ void store_f32x8(float *p, const float (&v)[8])
     reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// 8-byte loads / stores with the non-temporal hint: the per-step decode
+// streams every head's codes once per call (read, then overwritten in
+// place), so they should not displace other lines in the caches.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint2 load_nt8(const int8_t *p)
+{
+    const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    return make_uint2(t.x, t.y);
+}
+
+__device__ __forceinline__ void store_nt8(int8_t *p, uint2 v)
+{
+    const u32x2 t = {v.x, v.y};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x2 *>(p));
+}
+
 // int8 x 8 (one row of the block) -> fp32
 __device__ __forceinline__ void unpack8(uint2 q, float (&out)[8])
 {

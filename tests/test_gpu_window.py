@@ -245,3 +245,36 @@ def test_checkpoint_restore_and_determinism():
     for k in st_a:
         if st_a[k] is not None:
             assert torch.equal(st_a[k], st_b[k]), k
+
+
+@pytest.mark.parametrize("case", [
+    # the library's limits: window 256, 8 compensators, 64 DAMP rows
+    dict(name="kda", over=dict(B=1, H=2, W=256, r=8), n=256, warm=48),
+    dict(name="damp", over=dict(B=1, H=2, W=8, r=8, n_hp=64), n=8, warm=48),
+    # the serving workload's own window start: 512 fp32 warm-up steps
+    dict(name="gdn_serving", over=dict(B=1, H=3), n=16, warm=512),
+], ids=["W256-r8", "r8-nhp64", "warmup512"])
+def test_window_limits_and_warmup(case):
+    torch = torch_cuda()
+    g = lib()
+    cfg = sub_cfg(synth.WORKLOADS[case["name"]], **case["over"])
+    nh, dk, dv, W, r = cfg["B"] * cfg["H"], cfg["dk"], cfg["dv"], cfg["W"], cfg["r"]
+    n = case["n"]
+    hp = _hp_rows(cfg, nh) if cfg.get("n_hp") else None
+    d = desc_for(cfg, flags=g.DEBUG_PREQUANT)
+    enc = oracle.compress(_warm_state(cfg, nh, steps=case["warm"]).astype(np.float64), r, 20, hp_idx=hp)
+    st = g.alloc_state(d)
+    _upload(torch, st, enc, hp)
+    inp = synth.steps_inputs(cfg, 0, n)
+    say("limits", case)
+    outs = _run_gpu_window(torch, g, d, st, inp, n, True, torch.bfloat16)
+    g.gdn_quant_window_flush(d, st, n)
+    torch.cuda.synchronize()
+    o_ref, _, SW = oracle.window(_base(enc, hp), inp["q"], inp["k"], inp["v"], inp["a"], inp["b"])
+    for t in range(0, n, max(1, n // 16)):
+        check_outputs(host_io(outs[t], True), o_ref[t], True)
+    check_outputs(host_io(outs[n - 1], True), o_ref[n - 1], True)
+    ref = oracle.compress(SW, r, 20, hp_idx=hp)
+    scale = np.sqrt(np.sum(SW ** 2, axis=(1, 2)))
+    R = host(st["prequant_out"]).reshape(nh, dk, dv).astype(np.float64)
+    assert (np.sqrt(np.sum((R - ref["R"]) ** 2, axis=(1, 2))) / scale).max() <= 1e-4
