@@ -11,7 +11,7 @@ Printed: one JSON line (metric, value = token-head updates/s, roofline of
 the decode kernel against 8 TB/s HBM, and the plain fp64 CPU oracle timed
 on a bounded sample of the same workload).
 
-    python bench.py [--steps 100] [--warmup 10] [--gpus 1]
+    python bench.py [--steps 100] [--warmup 200] [--gpus 1]
                     [--workload prefix_cache|gdn_serving|kda|damp]
                     [--no-cpu] [--copy-calibration]
 """
@@ -129,23 +129,23 @@ def cpu_baseline(cfg: dict, S_first: np.ndarray, inputs: list, budget_s: float =
 
 
 def time_launches(torch, fn, steps: int, warmup: int):
-    """Whole-loop time (barrier + synchronize on both sides) and the mean
-    duration of one launch from HIP events on the launch stream."""
+    """Run `warmup` untimed calls, then time exactly `steps` calls: the wall
+    time from a synchronize before to a synchronize after, and each call's
+    duration from HIP events recorded around it on the launch stream (the
+    library launches on torch's current stream).  Returns (wall seconds,
+    mean per-call seconds) of the same `steps` calls."""
     for i in range(warmup):
         fn(i)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        fn(warmup + i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
         ev[i][0].record(stream)
-        fn(warmup + steps + i)
+        fn(warmup + i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     per = [a.elapsed_time(b) * 1e-3 for a, b in ev]
     return wall, float(np.mean(per))
 
@@ -368,11 +368,32 @@ def summarize_pmc(fetch_db: str, write_db: str, copy_fetch_db: str, copy_write_d
             f.write(text + "\n")
 
 
+def summarize_trace(db: str, last: int):
+    """Per-kernel dispatch count and mean duration from a rocprofv3
+    --kernel-trace database, over all dispatches and over the last `last`
+    dispatches of each kernel (the bench's timed calls follow its warm-up)."""
+    import collections
+    import sqlite3
+
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, duration from kernels order by start").fetchall()
+    agg = collections.defaultdict(list)
+    for name, dur in rows:
+        agg[name.split("(")[0]].append(dur)
+    print("| kernel | dispatches | mean ns (all) | mean ns (last %d) | min ns | max ns |" % last)
+    print("|---|---|---|---|---|---|")
+    for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        tail = v[-last:]
+        print(f"| {k} | {len(v)} | {np.mean(v):.0f} | {np.mean(tail):.0f} | {min(v)} | {max(v)} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    # ~200 calls (~50 ms of sustained load) bring the GPU to its steady
+    # clocks; the first calls after start-up run up to ~40% slower
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="prefix_cache",
                     choices=["prefix_cache", "gdn_serving", "kda", "damp"])
     ap.add_argument("--no-cpu", action="store_true")
@@ -380,7 +401,12 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
                     help="summarize rocprofv3 --pmc databases into profiles/traffic.json (no GPU needed)")
     ap.add_argument("--md", default=None, help="append the --summarize-pmc table to this file")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DB",
+                    help="per-kernel mean durations from a rocprofv3 --kernel-trace database (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.steps)
+        return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.workload, args.md)
         return

@@ -60,7 +60,8 @@
  *    launch, so a failed call has not touched device memory.
  *  - Inputs that are NaN or infinite give undefined results.  Gates must
  *    satisfy 0 < a <= 1 and the product of a window's gates must stay above
- *    1e-30 per key channel (the KDA buffer stores k / (cumulative gate)).
+ *    1e-30 (per key channel for KDA): the window buffer stores each key
+ *    divided by the cumulative gate up to its token.
  *  - bf16 inputs are widened exactly; a bf16 output is rounded to nearest
  *    even from fp32.
  */
