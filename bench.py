@@ -12,8 +12,8 @@ the decode kernel against 8 TB/s HBM, and the plain fp64 CPU oracle timed
 on a bounded sample of the same workload).
 
     python bench.py [--steps 100] [--warmup 200] [--gpus 1]
-                    [--workload prefix_cache|gdn_serving|kda|damp]
-                    [--no-cpu] [--copy-calibration]
+                    [--workload prefix_cache|gdn_serving|kda|damp|tiny]
+                    [--no-cpu] [--no-graph] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -103,29 +103,85 @@ def stored_traffic(kernel: str, workload: str):
     return ent["bytes_per_launch"]
 
 
-def cpu_baseline(cfg: dict, S_first: np.ndarray, inputs: list, budget_s: float = 12.0):
-    """The fp64 CPU oracle's per-step INT8 decode on the first heads of the
-    workload, single-threaded, for about budget_s seconds."""
+def _oracle_int8_run(S: np.ndarray, inputs: list, budget_s: float):
+    """Consecutive per-step INT8 decodes of the states S by the fp64 CPU
+    oracle (one thread) until budget_s has passed: (updates, steps, s)."""
     import oracle
 
-    nh = S_first.shape[0]
-    Q, s, c = oracle.quantize(S_first)
-    done = 0
+    nh = S.shape[0]
+    Q, s, c = oracle.quantize(S)
+    done, step = 0, 0
     t0 = time.perf_counter()
-    step = 0
     while True:
         inp = inputs[step % len(inputs)]
-        sub = {k: v[:nh] for k, v in inp.items()}
-        r = oracle.quant_step(Q, s, c, sub["q"], sub["k"], sub["v"], sub["a"], sub["b"])
+        r = oracle.quant_step(Q, s, c, inp["q"], inp["k"], inp["v"], inp["a"], inp["b"])
         Q, s, c = r["Q"], r["s"], r["c"]
         done += nh
         step += 1
         if time.perf_counter() - t0 >= budget_s:
             break
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "token-head updates/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {nh} of the {cfg['B'] * cfg['H']} states, {step} consecutive per-step "
-                      f"INT8 decode steps ({done} token-head updates) in {dt:.1f} s, one thread"}
+    return done, step, time.perf_counter() - t0
+
+
+def _slice_inputs(inputs: list, lo: int, hi: int) -> list:
+    return [{k: v[lo:hi] for k, v in inp.items()} for inp in inputs]
+
+
+# (states, inputs, heads per worker, budget) shared with forked workers
+_CPU_JOB = None
+
+
+def _cpu_worker(i: int):
+    S, inputs, per, budget = _CPU_JOB
+    return _oracle_int8_run(S[i * per:(i + 1) * per], _slice_inputs(inputs, i * per, (i + 1) * per), budget)
+
+
+def cpu_baselines(cfg: dict, S: np.ndarray, inputs: list) -> dict:
+    """The fp64 CPU oracle timed on bounded samples of the workload: the
+    per-step INT8 decode on one thread (the reported baseline) and on every
+    host core as independent processes over disjoint heads, and the
+    unquantized (fp32-state mode) recurrence on one thread.  Runs before
+    anything touches the GPU, so the workers are plain forks."""
+    import multiprocessing
+
+    import oracle
+
+    global _CPU_JOB
+    total = cfg["B"] * cfg["H"]
+    nh1 = 2048
+    done, step, dt = _oracle_int8_run(S[:nh1], _slice_inputs(inputs, 0, nh1), 12.0)
+    one = {"value": done / dt, "unit": "token-head updates/s", "cores": 1, "kind": "oracle",
+           "sample": f"first {nh1} of the {total} states, {step} consecutive per-step INT8 decode "
+                     f"steps ({done} token-head updates) in {dt:.1f} s, one thread"}
+
+    ncores = max(1, min(16, len(os.sched_getaffinity(0))))
+    per = 512
+    _CPU_JOB = (S, inputs, per, 8.0)
+    with multiprocessing.get_context("fork").Pool(ncores) as pool:
+        res = pool.map(_cpu_worker, range(ncores))
+    _CPU_JOB = None
+    done_all = sum(r[0] for r in res)
+    dt_all = max(r[2] for r in res)
+    allc = {"value": done_all / dt_all, "unit": "token-head updates/s", "cores": ncores, "kind": "oracle",
+            "sample": f"{ncores} processes, each on its own {per} states (the first {ncores * per} of "
+                      f"{total}), consecutive per-step INT8 decode steps for ~8 s: {done_all} "
+                      f"token-head updates in {dt_all:.1f} s"}
+
+    nh32 = 512
+    S64 = S[:nh32]
+    done32, step32 = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 5.0:
+        inp = inputs[step32 % len(inputs)]
+        S64, _ = oracle.recur(S64, inp["q"][None, :nh32], inp["k"][None, :nh32], inp["v"][None, :nh32],
+                              inp["a"][None, :nh32], inp["b"][None, :nh32])
+        done32 += nh32
+        step32 += 1
+    dt32 = time.perf_counter() - t0
+    f32 = {"value": done32 / dt32, "unit": "token-head updates/s", "cores": 1, "kind": "oracle",
+           "sample": f"first {nh32} states, {step32} consecutive steps of the unquantized recurrence "
+                     f"in fp64 ({done32} token-head updates) in {dt32:.1f} s, one thread"}
+    return {"cpu_baseline": one, "cpu_baseline_all_cores": allc, "cpu_baseline_fp32_state": f32}
 
 
 def time_launches(torch, fn, steps: int, warmup: int):
@@ -150,13 +206,19 @@ def time_launches(torch, fn, steps: int, warmup: int):
     return wall, float(np.mean(per))
 
 
-def bench_prefix_cache(args, torch, g):
+def prefix_cache_data():
+    """Host data of the prefix_cache workload: the pre-filled fp32 states
+    and 4 input sets (calls cycle through them)."""
     cfg = synth.WORKLOADS["prefix_cache"]
-    nh, dk, dv = cfg["B"] * cfg["H"], cfg["dk"], cfg["dv"]
-    log(f"generating {nh} pre-filled states")
+    log(f"generating {cfg['B'] * cfg['H']} pre-filled states")
     S = synth.prefill_states(cfg)
-    n_sets = 4
-    inputs = [synth.step_inputs(cfg, t) for t in range(n_sets)]
+    inputs = [synth.step_inputs(cfg, t) for t in range(4)]
+    return cfg, S, inputs
+
+
+def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
+    nh, dk, dv = cfg["B"] * cfg["H"], cfg["dk"], cfg["dv"]
+    n_sets = len(inputs)
 
     def up(inp):
         bits = lambda n: torch.from_numpy(inp[n + "16"].view(np.int16)).cuda().view(torch.bfloat16)
@@ -171,11 +233,16 @@ def bench_prefix_cache(args, torch, g):
     o = torch.empty(nh * dv, dtype=torch.bfloat16, device="cuda")
     torch.cuda.synchronize()
 
+    # marshalled once: the loop passes the C structs, raw pointers and the stream
+    dc, sc, sh = d.c(), g.state_struct(st), torch.cuda.current_stream().cuda_stream
+    ptrs = [[t.data_ptr() for t in inp] for inp in dev_inputs]
+    o_p, S_p = o.data_ptr(), S_dev.data_ptr()
+
     def int8_step(i):
-        g.gdn_quant_decode_step(d, st, *dev_inputs[i % n_sets], o, 0)
+        g.gdn_quant_decode_step(dc, sc, *ptrs[i % n_sets], o_p, 0, sh)
 
     def fp32_step(i):
-        g.gdn_fp32_decode_step(d, S_dev, *dev_inputs[i % n_sets], o)
+        g.gdn_fp32_decode_step(dc, S_p, *ptrs[i % n_sets], o_p, sh)
 
     log("timing INT8 per-step decode")
     wall, per = time_launches(torch, int8_step, args.steps, args.warmup)
@@ -212,12 +279,10 @@ def bench_prefix_cache(args, torch, g):
                        "traffic": stored_traffic("step_fp32", "prefix_cache")},
         "speedup_vs_fp32_state": wall32 / wall,
     }
+    res["outliers"] = host_outliers(S[:256])
     res["device_copy"] = device_copy(torch)
-    if not args.no_cpu:
-        log("timing the CPU oracle")
-        res["cpu_baseline"] = cpu_baseline(cfg, S[:2048], inputs)
-    else:
-        res["cpu_baseline"] = None
+    res["roofline"]["frac_of_device_copy"] = res["roofline"]["achieved"] / res["device_copy"]["GBs"]
+    res.update(cpu or {"cpu_baseline": None})
     return res
 
 
@@ -246,13 +311,23 @@ def bench_window(args, torch, g, name):
                        torch.from_numpy(inp["b"]).cuda()])
     o = torch.empty(nh * dv, dtype=torch.bfloat16, device="cuda")
 
+    dc, sc, sh = d.c(), g.state_struct(st), torch.cuda.current_stream().cuda_stream
+    ptrs = [[x.data_ptr() for x in inp] for inp in dev_in]
+    o_p = o.data_ptr()
+
     def token(i):
         t = i % W
-        g.gdn_quant_decode_step(d, st, *dev_in[t], o, t)
+        g.gdn_quant_decode_step(dc, sc, *ptrs[t], o_p, t, sh)
         if t == W - 1:
-            g.gdn_quant_window_flush(d, st, W)
+            g.gdn_quant_window_flush(dc, sc, W, sh)
 
-    wall, _ = time_launches(torch, token, steps, W * max(1, args.warmup // W))
+    wall_eager, _ = time_launches(torch, token, steps, W * max(1, args.warmup // W))
+    if args.no_graph:
+        wall, per_window = wall_eager, None
+    else:
+        # the same windows replayed from a HIP graph of one window's launches
+        graph = capture_window(torch, g, d, st, dev_in, o, W)
+        wall, per_window = time_launches(torch, lambda i: graph.replay(), steps // W, max(1, args.warmup // W))
     # per-kernel means: window steps and flushes separately
     stream = torch.cuda.current_stream()
     ev_s = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(W)]
@@ -279,12 +354,116 @@ def bench_window(args, torch, g, name):
                      "unit": "GB/s", "frac": sum(bsteps) / sum(t_steps) / 1e9 / HBM_PEAK_GBS,
                      "traffic": stored_traffic("window_step", name),
                      "kernel": "window_step_kernel (mean over window positions)"},
+        "launch": "eager calls" if args.no_graph else "one HIP graph per window (W decode steps + flush), replayed",
+        "window_us": None if per_window is None else per_window * 1e6,
+        "eager": {"value": nh * steps / wall_eager, "ms_per_step": wall_eager / steps * 1e3},
         "window_step_us": [round(x * 1e6, 2) for x in t_steps],
         "flush_us": t_flush * 1e6,
         "flush_GBs": flush_bytes(cfg, W) * nh / t_flush / 1e9,
         "cpu_baseline": None,
     }
+    res["outliers"] = window_outliers(torch, g, d, st, dev_in, o, nh, dk, dv, W, n_hp)
     return res
+
+
+def capture_window(torch, g, d, st, dev_in, o, W):
+    """One window (W decode steps and the flush) captured as a HIP graph.
+    The library launches on torch's current stream, which is the capturing
+    stream inside torch.cuda.graph; it sets or copies no memory, so the
+    graph holds kernel nodes only.  One eager window on a side stream
+    precedes the capture (it advances the state like any other window)."""
+    def window():
+        for t in range(W):
+            g.gdn_quant_decode_step(d, st, *dev_in[t], o, t)
+        g.gdn_quant_window_flush(d, st, W)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        window()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        window()
+    torch.cuda.synchronize()
+    return graph
+
+
+def _max_over_median(x):
+    """Per head max|x| / median|x| (x: [nh, E]); the median over heads."""
+    a = x.abs()
+    return float((a.amax(dim=1) / a.median(dim=1).values.clamp_min(1e-30)).median())
+
+
+def host_outliers(X: np.ndarray) -> dict:
+    """Diagnostic: median over heads of max|x|/median|x| of the fp32 states
+    and of the same states after key-row smoothing (row i divided by the
+    square root of its largest magnitude)."""
+    A = np.abs(X.reshape(X.shape[0], -1)).astype(np.float64)
+    r = lambda a: float(np.median(a.max(axis=1) / np.maximum(np.median(a, axis=1), 1e-30)))
+    Y = np.abs(X).astype(np.float64) / np.sqrt(np.maximum(np.abs(X).max(axis=2, keepdims=True), 1e-30))
+    return {"state": r(A), "after_smoothing": r(Y.reshape(X.shape[0], -1))}
+
+
+def window_outliers(torch, g, d, st, dev_in, o, nh, dk, dv, W, n_hp):
+    """Diagnostic after one more window: the outlier ratio max/median of
+    the rebuilt state, of the residual left after the compensators (the
+    codec's input), and of that residual after key-row smoothing."""
+    import dataclasses
+
+    dbg = dataclasses.replace(d, flags=g.DEBUG_PREQUANT)
+    st = dict(st)
+    st["prequant_out"] = torch.empty(nh * dk * dv, dtype=torch.float32, device="cuda")
+    for t in range(W):
+        g.gdn_quant_decode_step(dbg, st, *dev_in[t], o, t)
+    g.gdn_quant_window_flush(dbg, st, W)
+    S_out = torch.empty(nh * dk * dv, dtype=torch.float32, device="cuda")
+    g.gdn_state_dequantize(d, st, S_out)
+    torch.cuda.synchronize()
+    R = st["prequant_out"].view(nh, dk * dv)
+    out = {"rebuilt_state": _max_over_median(S_out.view(nh, dk * dv)),
+           "after_compensators": _max_over_median(R)}
+    if not n_hp:
+        Y = R.view(nh, dk, dv) / st["row_scale"].view(nh, dk, 1)
+        out["after_smoothing"] = _max_over_median(Y.reshape(nh, dk * dv))
+    return out
+
+
+def bench_tiny(args, torch, g):
+    """Latency of one per-step INT8 decode call on the tiny workload (4
+    heads of 64x64, fp32 I/O, zero initial state): launch-bound, so the
+    wall time per call from the host is reported beside the kernel's own
+    duration from HIP events."""
+    cfg = synth.WORKLOADS["tiny"]
+    nh, dk, dv, T = cfg["B"] * cfg["H"], cfg["dk"], cfg["dv"], cfg["T"]
+    d = g.Desc(B=cfg["B"], H=cfg["H"], dk=dk, dv=dv, io_dtype=g.IO_F32)
+    st = g.alloc_state(d)
+    g.gdn_state_quantize(d, torch.zeros(nh * dk * dv, dtype=torch.float32, device="cuda"), st)
+    dev_in = []
+    for t in range(T):
+        inp = synth.step_inputs(cfg, t)
+        dev_in.append([torch.from_numpy(inp[n]).cuda() for n in ("q", "k", "v", "a", "b")])
+    o = torch.empty(nh * dv, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    dc, sc, sh = d.c(), g.state_struct(st), torch.cuda.current_stream().cuda_stream
+    ptrs = [[x.data_ptr() for x in inp] for inp in dev_in]
+    o_p = o.data_ptr()
+
+    def step(i):
+        g.gdn_quant_decode_step(dc, sc, *ptrs[i % T], o_p, 0, sh)
+
+    wall, per = time_launches(torch, step, args.steps, args.warmup)
+    return {
+        "metric": "per-step INT8 decode latency, tiny workload (1 GPU)",
+        "value": wall / args.steps * 1e6, "unit": "us per call (host wall clock)", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8 state, fp32 math, fp32 q/k/v/o", "data": "synthetic",
+        "config": {"workload": "tiny: B=1, H=4, dk=dv=64, fp32 I/O, scalar gate, zero initial state"},
+        "kernel_us": per * 1e6, "roofline": None, "cpu_baseline": None,
+    }
 
 
 def device_copy(torch, nbytes: int = 2 << 30, reps: int = 5):
@@ -395,8 +574,10 @@ def main():
     # clocks; the first calls after start-up run up to ~40% slower
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="prefix_cache",
-                    choices=["prefix_cache", "gdn_serving", "kda", "damp"])
+                    choices=["prefix_cache", "gdn_serving", "kda", "damp", "tiny"])
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="window workloads: time eager calls only (for counter passes)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
                     help="summarize rocprofv3 --pmc databases into profiles/traffic.json (no GPU needed)")
@@ -415,6 +596,12 @@ def main():
               f"(batch, head) states with no exchange, and this build measures one GPU's share "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
+    data = cpu = None
+    if args.workload == "prefix_cache" and not args.copy_calibration:
+        data = prefix_cache_data()
+        if not args.no_cpu:
+            log("timing the CPU oracle")
+            cpu = cpu_baselines(*data)
     import torch
 
     import recurrent_state_quantization_amd as g
@@ -426,7 +613,9 @@ def main():
         copy_calibration(torch)
         return
     if args.workload == "prefix_cache":
-        res = bench_prefix_cache(args, torch, g)
+        res = bench_prefix_cache(args, torch, g, *data, cpu)
+    elif args.workload == "tiny":
+        res = bench_tiny(args, torch, g)
     else:
         res = bench_window(args, torch, g, args.workload)
     print(json.dumps(res), flush=True)

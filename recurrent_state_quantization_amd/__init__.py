@@ -123,45 +123,57 @@ def _stream(stream):
 
 
 def state_struct(state: dict) -> _State:
+    """The gdnq_state of a dict of device tensors (missing or None: 0).
+    Every call below also takes the struct itself, which spares a caller
+    that repeats calls on the same state the per-call marshalling."""
     return _State(*(_ptr(state.get(n)) for n in STATE_FIELDS))
+
+
+def _state(state) -> _State:
+    return state if isinstance(state, _State) else state_struct(state)
+
+
+def _desc(desc) -> _Desc:
+    """Desc or an already marshalled gdnq_desc (Desc.c())."""
+    return desc if isinstance(desc, _Desc) else desc.c()
 
 
 # ------------------------------------------------------------------ C ABI
 def gdnq_state_sizes(desc: Desc) -> list[int]:
     out = (ctypes.c_size_t * 11)()
-    _check(lib.gdnq_state_sizes(ctypes.byref(desc.c()), ctypes.byref(out)))
+    _check(lib.gdnq_state_sizes(ctypes.byref(_desc(desc)), ctypes.byref(out)))
     return list(out)
 
 
 def gdn_quant_decode_step(desc, state, q, k, v, a, b, o, t_in_window=0, stream=None):
-    st = state_struct(state)
-    _check(lib.gdn_quant_decode_step(ctypes.byref(desc.c()), ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v),
+    st = _state(state)
+    _check(lib.gdn_quant_decode_step(ctypes.byref(_desc(desc)), ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v),
                                      _ptr(a), _ptr(b), _ptr(o), int(t_in_window), _stream(stream)))
 
 
 def gdn_quant_window_flush(desc, state, n_tokens, stream=None):
-    st = state_struct(state)
-    _check(lib.gdn_quant_window_flush(ctypes.byref(desc.c()), ctypes.byref(st), int(n_tokens),
+    st = _state(state)
+    _check(lib.gdn_quant_window_flush(ctypes.byref(_desc(desc)), ctypes.byref(st), int(n_tokens),
                                       _stream(stream)))
 
 
 def gdn_state_quantize(desc, S, state, stream=None):
-    st = state_struct(state)
-    _check(lib.gdn_state_quantize(ctypes.byref(desc.c()), _ptr(S), ctypes.byref(st), _stream(stream)))
+    st = _state(state)
+    _check(lib.gdn_state_quantize(ctypes.byref(_desc(desc)), _ptr(S), ctypes.byref(st), _stream(stream)))
 
 
 def gdn_state_dequantize(desc, state, S_out, stream=None):
-    st = state_struct(state)
-    _check(lib.gdn_state_dequantize(ctypes.byref(desc.c()), ctypes.byref(st), _ptr(S_out), _stream(stream)))
+    st = _state(state)
+    _check(lib.gdn_state_dequantize(ctypes.byref(_desc(desc)), ctypes.byref(st), _ptr(S_out), _stream(stream)))
 
 
 def calibrate_scales(desc, S0, k, v, a, b, n_steps, hp_idx_out, row_score_out=None, stream=None):
-    _check(lib.calibrate_scales(ctypes.byref(desc.c()), _ptr(S0), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+    _check(lib.calibrate_scales(ctypes.byref(_desc(desc)), _ptr(S0), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
                                 int(n_steps), _ptr(hp_idx_out), _ptr(row_score_out), _stream(stream)))
 
 
 def gdn_fp32_decode_step(desc, S, q, k, v, a, b, o, stream=None):
-    _check(lib.gdn_fp32_decode_step(ctypes.byref(desc.c()), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+    _check(lib.gdn_fp32_decode_step(ctypes.byref(_desc(desc)), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
                                     _ptr(b), _ptr(o), _stream(stream)))
 
 

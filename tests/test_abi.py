@@ -169,3 +169,20 @@ def test_per_step_flush_is_noop(g):
     d = g.Desc(B=1, H=2)
     g.gdn_quant_window_flush(d, {}, 1, stream=0)      # no launch, no pointers needed
     assert _err(lambda: g.gdn_quant_window_flush(d, {}, 2, stream=0))[0] == 1
+
+
+def test_prebuilt_structs_marshal_like_dicts(g):
+    """Every call also takes the marshalled gdnq_desc / gdnq_state; the
+    library then sees the same arguments and rejects them the same way."""
+    d = g.Desc(B=2, H=2, W=8, r=2)
+    st = _fake_state(g, d)
+    io = [FAKE2 + i * (1 << 20) for i in range(6)]
+    for desc, state in ((d, st), (d.c(), g.state_struct(st))):
+        c, m = _err(lambda: g.gdn_quant_decode_step(desc, state, *io, 8, stream=0))
+        assert c == 1 and "t_in_window" in m
+        c, m = _err(lambda: g.gdn_quant_window_flush(desc, state, 9, stream=0))
+        assert c == 1
+    bad = dict(st, buf_k=st["codes"])
+    for state in (bad, g.state_struct(bad)):
+        c, m = _err(lambda: g.gdn_quant_decode_step(d.c(), state, *io, 0, stream=0))
+        assert c == 1 and "overlaps" in m
