@@ -233,11 +233,37 @@ __device__ __forceinline__ void column_sum_all(const Lane &c, float (&red)[G::NW
     }
 }
 
-// One power-iteration step v <- P^T (P v) / |P^T (P v)| using LDS buffer
-// `red` for the column sums; returns |.|^2 (the same value in every lane).
+// Column sums of per-thread partials yp[8] over the whole tile, finished
+// only for the two columns this lane holds after the in-wave reduce-scatter:
+// z[p] = column cb*8 + scatter_index(c, p), the wave partials added in wave
+// order.  Uses `red`; the caller alternates buffers between calls so one
+// barrier per call suffices.
+template <class G>
+__device__ __forceinline__ void column_sum_scattered(const Lane &c, float (&red)[G::NW][G::DV],
+                                                     const float (&yp)[8], float (&z)[2])
+{
+    float zp[2];
+    col_reduce_scatter<G, OpSum, 8>(yp, zp);
+#pragma unroll
+    for (int p = 0; p < 2; p++) red[c.w][c.cb * 8 + scatter_index(c, p)] = zp[p];
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 2; p++) {
+        const int col = c.cb * 8 + scatter_index(c, p);
+        float s = red[0][col];
+#pragma unroll
+        for (int w = 1; w < G::NW; w++) s += red[w][col];
+        z[p] = s;
+    }
+}
+
+// One power-iteration step y = P^T (P v); when |y|^2 != 0, v <- y / |y|
+// (v is kept otherwise).  Returns |y|^2, the same value in every lane.
+// The norm and the scaling run on the two columns a lane holds after the
+// reduce-scatter; the scaled values are then gathered back to all lanes.
 template <class G>
 __device__ __forceinline__ float power_step(const float (&P)[8][8], const Lane &c, float (&red)[G::NW][G::DV],
-                                            float (&v)[8], float (&y)[8])
+                                            float (&v)[8])
 {
     float x[8];
 #pragma unroll
@@ -255,11 +281,22 @@ __device__ __forceinline__ float power_step(const float (&P)[8][8], const Lane &
         for (int k = 1; k < 8; k++) s = fmaf(P[k][j], x[k], s);
         yp[j] = s;
     }
-    column_sum_all<G>(c, red, yp, y);
-    float n2 = y[0] * y[0];
-#pragma unroll
-    for (int j = 1; j < 8; j++) n2 = fmaf(y[j], y[j], n2);
-    return row_sum<G>(n2);
+    float z[2];
+    column_sum_scattered<G>(c, red, yp, z);
+    // each column is held by one lane of the wave (by two lanes that differ
+    // in lane bit 3 when NCB = 8: the all-reduce then counts it twice)
+    float n2 = fmaf(z[1], z[1], z[0] * z[0]);
+    n2 = col_allreduce<G, OpSum>(row_sum<G>(n2));
+    if constexpr (G::NCB == 8) n2 *= 0.5f;
+    if (n2 != 0.0f) {
+        // the normalization only rescales the iterate: the hardware
+        // reciprocal square root (about 1 ulp) is accurate enough
+        const float inv = __builtin_amdgcn_rsqf(n2);
+        z[0] *= inv;
+        z[1] *= inv;
+        col_allgather(z, v);
+    }
+    return n2;
 }
 
 // Compensator Tokens by power iteration with sequential deflation, on the
@@ -291,8 +328,7 @@ __device__ void power_deflate(float (&P)[8][8], const Lane &c, CodecLds<G> &L, i
             for (int j = 0; j < 8; j++) v[j] = v0;
             // first step, with the restart rule; L.red[0] is free here (the
             // barrier of __syncthreads_or follows every earlier read of it)
-            float y[8];
-            float n2 = power_step<G>(P, c, L.red[0], v, y);
+            float n2 = power_step<G>(P, c, L.red[0], v);
             if (n2 == 0.0f) {  // uniform: every lane holds the same n2
                 float cn[8], cs[8];
 #pragma unroll
@@ -317,30 +353,16 @@ __device__ void power_deflate(float (&P)[8][8], const Lane &c, CodecLds<G> &L, i
                 const int jb = L.misc;
 #pragma unroll
                 for (int j = 0; j < 8; j++) v[j] = (c.cb * 8 + j == jb) ? 1.0f : 0.0f;
-                n2 = power_step<G>(P, c, L.red[0], v, y);
+                n2 = power_step<G>(P, c, L.red[0], v);
             }
-            // the normalization only rescales the iterate: the hardware
-            // reciprocal square root (about 1 ulp) is accurate enough
-            int it = 1;
             if (n2 != 0.0f) {
-                float inv = __builtin_amdgcn_rsqf(n2);
-#pragma unroll
-                for (int j = 0; j < 8; j++) v[j] = y[j] * inv;
                 // remaining steps two at a time so each LDS buffer is fixed;
                 // consecutive steps alternate buffers, so one barrier per
                 // step orders every read of a buffer before its next write
-                for (; it < iters; it += 2) {
-                    n2 = power_step<G>(P, c, L.red[1], v, y);
-                    if (n2 == 0.0f) break;
-                    inv = __builtin_amdgcn_rsqf(n2);
-#pragma unroll
-                    for (int j = 0; j < 8; j++) v[j] = y[j] * inv;
+                for (int it = 1; it < iters; it += 2) {
+                    if (power_step<G>(P, c, L.red[1], v) == 0.0f) break;
                     if (it + 1 >= iters) break;
-                    n2 = power_step<G>(P, c, L.red[0], v, y);
-                    if (n2 == 0.0f) break;
-                    inv = __builtin_amdgcn_rsqf(n2);
-#pragma unroll
-                    for (int j = 0; j < 8; j++) v[j] = y[j] * inv;
+                    if (power_step<G>(P, c, L.red[0], v) == 0.0f) break;
                 }
             }
 #pragma unroll

@@ -238,6 +238,27 @@ __device__ __forceinline__ int scatter_index(const Lane &c, int p)
     return 4 * p + 2 * ((c.lane >> 4) & 1) + ((c.lane >> 5) & 1);
 }
 
+// Inverse distribution of col_reduce_scatter<G, Op, 8>: z[p] holds the
+// value of index 4p + e (e = 2*bit4(lane) + bit5(lane)); afterwards every
+// lane holds all eight, y[i] = the value of index i.  swap16 with both
+// operands equal hands each lane the bit4 = 0 lane's value in the first and
+// the bit4 = 1 lane's in the second; swap32 does the same for bit5.
+__device__ __forceinline__ void col_allgather(const float (&z)[2], float (&y)[8])
+{
+#pragma unroll
+    for (int p = 0; p < 2; p++) {
+        float a = z[p], b = z[p];
+        swap16(a, b);                 // a: index 4p + bit5, b: 4p + 2 + bit5
+        float a0 = a, a1 = a, b0 = b, b1 = b;
+        swap32(a0, a1);               // a0: 4p,     a1: 4p + 1
+        swap32(b0, b1);               // b0: 4p + 2, b1: 4p + 3
+        y[4 * p + 0] = a0;
+        y[4 * p + 1] = a1;
+        y[4 * p + 2] = b0;
+        y[4 * p + 3] = b1;
+    }
+}
+
 // All-reduce of one value over the RGW row-group lanes (column direction).
 template <class G, class Op>
 __device__ __forceinline__ float col_allreduce(float x)

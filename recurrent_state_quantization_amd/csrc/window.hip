@@ -70,8 +70,11 @@ struct WinLds {
     float red[G::NW][2][G::DV];
 };
 
+// 8 workgroups per CU (64 VGPRs, no spills): a serving batch of 2048
+// heads then runs as one round over the 256 CUs instead of 7 per CU and a
+// tail round of 256.
 template <class G, bool BF16, bool KDA, bool DAMP>
-__global__ __launch_bounds__(G::NT) void window_step_kernel(WinArgs A)
+__global__ __launch_bounds__(G::NT, 8) void window_step_kernel(WinArgs A)
 {
     __shared__ WinLds<G> L;
     const Lane c = lane_coords<G>();
@@ -280,8 +283,16 @@ __device__ __forceinline__ void slot_val(const FlushArgs &A, size_t h, int l, in
     }
 }
 
+// Occupancy: the 128x128 rowcol flush fits 128 VGPRs without spilling, so
+// it asks for 4 workgroups per CU (4 waves per SIMD: the power iteration
+// is VALU-bound and its per-step barrier is hidden by the other
+// workgroups); the DAMP and 64-row or 64-column variants would spill at that bound
+// and ask for 2 (3 waves per SIMD at their register counts).
+template <class G, bool DAMP>
+constexpr int flush_min_blocks() { return (G::DK == 128 && G::DV == 128 && !DAMP) ? 4 : 2; }
+
 template <class G, bool KDA, bool DAMP>
-__global__ __launch_bounds__(G::NT, 2) void flush_kernel(FlushArgs A)
+__global__ __launch_bounds__(G::NT, (flush_min_blocks<G, DAMP>())) void flush_kernel(FlushArgs A)
 {
     __shared__ CodecLds<G> L;
     __shared__ FlushLds<G> F;
