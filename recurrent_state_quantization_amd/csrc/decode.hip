@@ -39,6 +39,7 @@ struct StepArgs {
 // LDS; consumer threads (t < DV) then hold full sums.
 template <class G>
 struct StepLds {
+    alignas(16) float rv[4][G::DK];  // per key row: a s, a s k, a s q, k (read as float4)
     float red[G::NW][2][G::DV];
     float red_kq[G::NW];
     float u[G::DV];
@@ -76,6 +77,22 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     float *rs = A.row_scale + h * G::DK;
     float *cs = A.col_scale + h * G::DV;
 
+    // The per-row factors are formed once per row (thread t < DK owns row
+    // t; NT >= DK) and shared through LDS instead of by each of the row's
+    // NCB lanes.  Their loads are issued first and unconditionally (rows
+    // wrap for t >= DK) so that waiting for them does not wait for the
+    // codes, which load meanwhile.
+    const int tr = c.t % G::DK;
+    const float ki = load1<BF16>(A.k, h * G::DK + tr);
+    const float qi = load1<BF16>(A.q, h * G::DK + tr);
+    const float ai = KDA ? A.a[h * G::DK + tr] : A.a[h];
+    const float si = rs[tr];
+    // likewise v_j and c_j of the consumer lanes (t < DV; columns wrap)
+    const int tc = c.t % G::DV;
+    const float vj = load1<BF16>(A.v, h * G::DV + tc);
+    const float cj = cs[tc];
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the codes'
+
     const int row0 = row0_of<G>(c);
     const int8_t *cbase = codes + (size_t)row0 * G::DV + c.cb * 8;
     uint2 qraw[8];
@@ -83,33 +100,23 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     for (int k = 0; k < 8; k++) qraw[k] = load_nt8(cbase + koff<G>(k) * G::DV);
     float cc[8];
     load_f32x8(cs + c.cb * 8, cc);
-    float s[8], kk[8], qq[8], av[8];
-    load_rows_f32<G>(rs + row0, s);
-    load_rows<G, BF16>(A.k, h * G::DK, row0, kk);
-    load_rows<G, BF16>(A.q, h * G::DK, row0, qq);
-    if constexpr (KDA) {
-        load_rows_f32<G>(A.a + h * G::DK + row0, av);
-    } else {
-        const float ag = A.a[h];
-#pragma unroll
-        for (int k = 0; k < 8; k++) av[k] = ag;
-    }
     const float bh = A.b[h];
-    float vj = 0.0f, cj = 0.0f;
-    if (c.t < G::DV) {
-        vj = load1<BF16>(A.v, h * G::DV + c.t);
-        cj = cs[c.t];
+    float kq_row = 0.0f;
+    if (c.t < G::DK) {
+        const float asi = ai * si;
+        SL.rv[0][c.t] = asi;
+        SL.rv[1][c.t] = asi * ki;
+        SL.rv[2][c.t] = asi * qi;
+        SL.rv[3][c.t] = ki;
+        kq_row = ki * qi;
     }
-
-    float as[8], ask[8], asq[8];
-    float kq = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-        as[k] = av[k] * s[k];
-        ask[k] = as[k] * kk[k];
-        asq[k] = as[k] * qq[k];
-        kq = fmaf(kk[k], qq[k], kq);
-    }
+    __syncthreads();
+    float as[8], ask[8], asq[8], kk[8];
+    load_rows_f32<G>(&SL.rv[0][row0], as);
+    load_rows_f32<G>(&SL.rv[1][row0], ask);
+    load_rows_f32<G>(&SL.rv[2][row0], asq);
+    load_rows_f32<G>(&SL.rv[3][row0], kk);
+    const float kq = row_sum<G>(kq_row);  // this lane's row group's share: reduce_ro adds the rest
     float X[8][8], R[8], O[8];
 #pragma unroll
     for (int k = 0; k < 8; k++) unpack8(qraw[k], X[k]);
