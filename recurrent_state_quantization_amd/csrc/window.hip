@@ -64,46 +64,75 @@ __device__ __forceinline__ void load_f16x8(const uint16_t *p, float (&out)[8])
 
 template <class G>
 struct WinLds {
+    alignas(16) float sgk[G::DK];  // s_i G_i k_i and s_i G_i q_i (s = 1 for DAMP), read as float4
+    alignas(16) float sgq[G::DK];
+    alignas(16) float cs[G::DV];   // column scales
     float ks[G::DK], qs[G::DK], gs[G::DK], gk[G::DK], gq[G::DK];
     float alpha[MAX_SLOTS + 1], beta[MAX_SLOTS + 1];
     int hp[MAX_HP];
     float red[G::NW][2][G::DV];
 };
 
-// 8 workgroups per CU (64 VGPRs, no spills): a serving batch of 2048
-// heads then runs as one round over the 256 CUs instead of 7 per CU and a
-// tail round of 256.
-template <class G, bool BF16, bool KDA, bool DAMP>
-__global__ __launch_bounds__(G::NT, 8) void window_step_kernel(WinArgs A)
+// Key-side vector of slot l (a compensator or a buffered token), entries
+// l16*PER .. l16*PER+PER-1; false (nothing read) for a DAMP-row slot, the
+// k.q slot and l >= NS.
+template <class G>
+__device__ __forceinline__ bool slot_kvec(const WinArgs &A, size_t h, int l, int NS, int n_hp, int l16,
+                                          float (&x)[G::DK / 16])
 {
-    __shared__ WinLds<G> L;
-    const Lane c = lane_coords<G>();
-    const size_t h = __builtin_amdgcn_workgroup_id_x();
-    const int n_hp = DAMP ? A.n_hp : 0;
+    constexpr int PER = G::DK / 16;
     const int r = A.r;
-
-    // per-row vectors: gate product, gated k and q
-    if (c.t < G::DK) {
-        const float kv = load1<BF16>(A.k, h * G::DK + c.t);
-        const float qv = load1<BF16>(A.q, h * G::DK + c.t);
-        const float av = KDA ? A.a[h * G::DK + c.t] : A.a[h];
-        const float gprev = (A.t == 0) ? 1.0f : (KDA ? A.g_cur[h * G::DK + c.t] : A.g_cur[h]);
-        const float g = gprev * av;
-        L.ks[c.t] = kv;
-        L.qs[c.t] = qv;
-        L.gs[c.t] = g;
-        L.gk[c.t] = g * kv;
-        L.gq[c.t] = g * qv;
+    if (l >= NS || (l >= r && l < r + n_hp)) return false;
+    const float *vec = (l < r) ? A.comp_k + ((h * r + l) * G::DK)
+                               : A.buf_k + ((h * A.W + (l - r - n_hp)) * G::DK);
+#pragma unroll
+    for (int e = 0; e < PER; e += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(vec + l16 * PER + e);
+        x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
     }
-    if (DAMP && c.t < n_hp) L.hp[c.t] = A.hp_idx[h * n_hp + c.t];
-    __syncthreads();
+    return true;
+}
 
-    // fixed INT8 tile of this thread (DAMP rows carry no codes)
-    RowMap rm;
-    if constexpr (DAMP) rm = row_map<G>(c, L.hp, n_hp);
-    const size_t nrows_c = (size_t)(G::DK - n_hp);
-    const int8_t *codes = A.codes + h * nrows_c * G::DV;
-    uint2 qraw[8];
+// Value-side entries col..col+7 of slot l (l < NS), loaded as raw bits so
+// that nothing waits for them until slot_vvec_use: eight fp32 words, or
+// (returns true) eight fp16 halves in raw[0..3] for a DAMP-row slot.
+template <class G>
+__device__ __forceinline__ bool slot_vvec_load(const WinArgs &A, size_t h, int l, int n_hp, int col,
+                                               uint4 (&raw)[2])
+{
+    const int r = A.r;
+    const bool f16 = l >= r && l < r + n_hp;
+    // one load path (a second load into the same registers on another
+    // path would make the first one be waited for)
+    const uint4 *p = f16 ? reinterpret_cast<const uint4 *>(A.hp_rows + (h * n_hp + (l - r)) * G::DV + col)
+                   : reinterpret_cast<const uint4 *>((l < r) ? A.comp_v + (h * r + l) * G::DV + col
+                                                             : A.buf_u + (h * A.W + (l - r - n_hp)) * G::DV + col);
+    raw[0] = p[0];
+    if (!f16) raw[1] = p[1];
+    return f16;
+}
+
+__device__ __forceinline__ void slot_vvec_use(const uint4 (&raw)[2], bool f16, float (&uv)[8])
+{
+    if (f16) {
+        const uint32_t w[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            uv[2 * i] = f16_to_f32((uint16_t)(w[i] & 0xFFFFu));
+            uv[2 * i + 1] = f16_to_f32((uint16_t)(w[i] >> 16));
+        }
+    } else {
+        const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+#pragma unroll
+        for (int j = 0; j < 8; j++) uv[j] = __uint_as_float(w[j]);
+    }
+}
+
+// This thread's 8 code rows of the fixed tile (DAMP rows carry no codes).
+template <class G, bool DAMP>
+__device__ __forceinline__ void load_tile_codes(const int8_t *codes, const Lane &c, const RowMap &rm,
+                                                uint2 (&qraw)[8])
+{
 #pragma unroll
     for (int k = 0; k < 8; k++) {
         if (!DAMP || rm.slot[k] < 0) {
@@ -113,56 +142,114 @@ __global__ __launch_bounds__(G::NT, 8) void window_step_kernel(WinArgs A)
             qraw[k] = make_uint2(0u, 0u);
         }
     }
-    float cc[8];
-    load_f32x8(A.col_scale + h * G::DV + c.cb * 8, cc);
+}
+
+// 8 workgroups per CU (64 VGPRs, no spills; the column scales wait in LDS
+// so the prefetched slot vectors fit beside the codes): 2048 heads run as
+// one round over the 256 CUs, 8192 as four.
+template <class G, bool BF16, bool KDA, bool DAMP>
+__global__ __launch_bounds__(G::NT, 8) void window_step_kernel(WinArgs A)
+{
+    __shared__ WinLds<G> L;
+    const Lane c = lane_coords<G>();
+    const size_t h = __builtin_amdgcn_workgroup_id_x();
+    const int n_hp = DAMP ? A.n_hp : 0;
+    const int r = A.r;
+
+    // Every load that does not depend on LDS is issued before the first
+    // barrier, the small ones first so that the barrier waits for them
+    // only: the per-row inputs (thread t < DK owns row t; rows wrap for
+    // t >= DK), the scales, the DAMP row indices, then the first slot
+    // vectors and the codes.
+    const int tr = c.t % G::DK;
+    const float kv = load1<BF16>(A.k, h * G::DK + tr);
+    const float qv = load1<BF16>(A.q, h * G::DK + tr);
+    const float av = KDA ? A.a[h * G::DK + tr] : A.a[h];
+    const float gprev = (A.t == 0) ? 1.0f : (KDA ? A.g_cur[h * G::DK + tr] : A.g_cur[h]);
+    const float srow = DAMP ? 1.0f : A.row_scale[h * G::DK + tr];
+    // column scales go through LDS (thread t < DV owns column t) so they
+    // hold no registers during the mat-vecs
+    const float cj = A.col_scale[h * G::DV + (c.t % G::DV)];
+    int hpi = 0;
+    if (DAMP && c.t < n_hp) hpi = A.hp_idx[h * n_hp + c.t];
+    __builtin_amdgcn_sched_barrier(0);
+    // the first slot each 16-lane group dots (key side) and each row group
+    // adds (value side); later ones, if any, load in their loops
+    const int NS = r + n_hp + A.t;
+    constexpr int PER = G::DK / 16;
+    const int l16 = c.t & 15;
+    float xk[PER];
+    const bool xk0 = slot_kvec<G>(A, h, c.t >> 4, NS, n_hp, l16, xk);
+    constexpr int NRG = G::NW * G::RGW;
+    const int rg = c.w * G::RGW + c.rgl;
+    uint4 uvraw[2];
+    bool uv16 = false;
+    if (rg < NS) uv16 = slot_vvec_load<G>(A, h, rg, n_hp, c.cb * 8, uvraw);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // fixed INT8 tile: the DAMP row map needs the row indices in LDS, so
+    // DAMP loads its codes after the barrier
+    const size_t nrows_c = (size_t)(G::DK - n_hp);
+    const int8_t *codes = A.codes + h * nrows_c * G::DV;
+    uint2 qraw[8];
+    RowMap rm;
+    if constexpr (!DAMP) load_tile_codes<G, false>(codes, c, rm, qraw);
+
+    // per-row vectors: gate product, gated k and q (and times the row scale)
+    if (c.t < G::DK) {
+        const float g = gprev * av;
+        const float gk = g * kv, gq = g * qv;
+        L.ks[c.t] = kv;
+        L.qs[c.t] = qv;
+        L.gs[c.t] = g;
+        L.gk[c.t] = gk;
+        L.gq[c.t] = gq;
+        L.sgk[c.t] = srow * gk;
+        L.sgq[c.t] = srow * gq;
+    }
+    if (c.t < G::DV) L.cs[c.t] = cj;
+    if (DAMP && c.t < n_hp) L.hp[c.t] = hpi;
+    __syncthreads();
+    if constexpr (DAMP) {
+        rm = row_map<G>(c, L.hp, n_hp);
+        load_tile_codes<G, true>(codes, c, rm, qraw);
+    }
 
     // slot dot products: alpha_l = kvec_l . (G.k), beta_l = kvec_l . (G.q);
     // slot NS is k . q.  16 lanes per slot.
-    const int NS = r + n_hp + A.t;
-    {
-        constexpr int PER = G::DK / 16;
-        const int l16 = c.t & 15;
-        for (int base = 0; base <= NS; base += G::NT / 16) {
-            const int l = base + (c.t >> 4);
-            if (l > NS) break;  // whole 16-lane groups leave together
-            float al = 0.0f, be = 0.0f;
-            if (l == NS) {
+    for (int base = 0; base <= NS; base += G::NT / 16) {
+        const int l = base + (c.t >> 4);
+        if (l > NS) break;  // whole 16-lane groups leave together
+        const bool has = base == 0 ? xk0 : slot_kvec<G>(A, h, l, NS, n_hp, l16, xk);
+        float al = 0.0f, be = 0.0f;
+        if (l == NS) {
 #pragma unroll
-                for (int e = 0; e < PER; e++) al = fmaf(L.ks[l16 * PER + e], L.qs[l16 * PER + e], al);
-            } else if (l >= r && l < r + n_hp) {
-                if (l16 == 0) {
-                    const int i = L.hp[l - r];
-                    al = L.gk[i];
-                    be = L.gq[i];
-                }
-            } else {
-                const float *vec = (l < r) ? A.comp_k + ((h * r + l) * G::DK)
-                                           : A.buf_k + ((h * A.W + (l - r - n_hp)) * G::DK);
-#pragma unroll
-                for (int e = 0; e < PER; e++) {
-                    const float x = vec[l16 * PER + e];
-                    al = fmaf(x, L.gk[l16 * PER + e], al);
-                    be = fmaf(x, L.gq[l16 * PER + e], be);
-                }
-            }
-            al = sum16(al);
-            be = sum16(be);
+            for (int e = 0; e < PER; e++) al = fmaf(L.ks[l16 * PER + e], L.qs[l16 * PER + e], al);
+        } else if (!has) {  // DAMP row slot: e_i . (G.k) = G_i k_i
             if (l16 == 0) {
-                L.alpha[l] = al;
-                L.beta[l] = be;
+                const int i = L.hp[l - r];
+                al = L.gk[i];
+                be = L.gq[i];
             }
+        } else {
+#pragma unroll
+            for (int e = 0; e < PER; e++) {
+                al = fmaf(xk[e], L.gk[l16 * PER + e], al);
+                be = fmaf(xk[e], L.gq[l16 * PER + e], be);
+            }
+        }
+        al = sum16(al);
+        be = sum16(be);
+        if (l16 == 0) {
+            L.alpha[l] = al;
+            L.beta[l] = be;
         }
     }
 
     // fixed-state mat-vecs straight off the codes
     float gsk[8], gsq[8];
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-        const int i = row_of<G>(c, k);
-        const float s = DAMP ? 1.0f : A.row_scale[h * G::DK + i];
-        gsk[k] = s * L.gk[i];
-        gsq[k] = s * L.gq[i];
-    }
+    load_rows_f32<G>(&L.sgk[row0_of<G>(c)], gsk);
+    load_rows_f32<G>(&L.sgq[row0_of<G>(c)], gsq);
     float R[8], O[8];
     {
         float X[8];
@@ -182,22 +269,23 @@ __global__ __launch_bounds__(G::NT, 8) void window_step_kernel(WinArgs A)
             }
         }
     }
+    {
+        float cc[8];
+        load_f32x8(&L.cs[c.cb * 8], cc);
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        R[j] *= cc[j];
-        O[j] *= cc[j];
+        for (int j = 0; j < 8; j++) {
+            R[j] *= cc[j];
+            O[j] *= cc[j];
+        }
     }
     __syncthreads();  // alpha / beta ready
 
     // slot value-side terms, slots spread over the row groups
-    constexpr int NRG = G::NW * G::RGW;
-    const int rg = c.w * G::RGW + c.rgl;
     for (int l = rg; l < NS; l += NRG) {
         const float al = L.alpha[l], be = L.beta[l];
+        if (l != rg) uv16 = slot_vvec_load<G>(A, h, l, n_hp, c.cb * 8, uvraw);
         float uv[8];
-        if (l < r) load_f32x8(A.comp_v + (h * r + l) * G::DV + c.cb * 8, uv);
-        else if (l < r + n_hp) load_f16x8(A.hp_rows + (h * n_hp + (l - r)) * G::DV + c.cb * 8, uv);
-        else load_f32x8(A.buf_u + (h * A.W + (l - r - n_hp)) * G::DV + c.cb * 8, uv);
+        slot_vvec_use(uvraw, uv16, uv);
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             R[j] = fmaf(al, uv[j], R[j]);
