@@ -13,7 +13,7 @@ on a bounded sample of the same workload).
 
     python bench.py [--steps 100] [--warmup 200] [--gpus 1]
                     [--workload prefix_cache|gdn_serving|kda|damp|tiny]
-                    [--no-cpu] [--no-graph] [--copy-calibration]
+                    [--no-cpu] [--no-graph] [--no-diag] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -362,7 +362,8 @@ def bench_window(args, torch, g, name):
         "flush_GBs": flush_bytes(cfg, W) * nh / t_flush / 1e9,
         "cpu_baseline": None,
     }
-    res["outliers"] = window_outliers(torch, g, d, st, dev_in, o, nh, dk, dv, W, n_hp)
+    if not args.no_diag:
+        res["outliers"] = window_outliers(torch, g, d, st, dev_in, o, nh, dk, dv, W, n_hp)
     return res
 
 
@@ -566,6 +567,35 @@ def summarize_trace(db: str, last: int):
         print(f"| {k} | {len(v)} | {np.mean(v):.0f} | {np.mean(tail):.0f} | {min(v)} | {max(v)} |")
 
 
+def summarize_counters(db: str):
+    """Per-kernel mean of every counter in a rocprofv3 --pmc database, and
+    where the counters are there: VALU instructions per wave and VALU busy,
+    the share of CU cycles issuing VALU work: SQ_ACTIVE_INST_VALU (quad
+    cycles summed over a CU's four SIMDs) / (256 CUs x GRBM_GUI_ACTIVE per
+    XCD, the database holding the sum over the 8 XCDs)."""
+    import collections
+    import sqlite3
+
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, counter_name, value from counters_collection").fetchall()
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for k, cn, v in rows:
+        agg[k.split("(")[0]][cn].append(v)
+    names = sorted({cn for d in agg.values() for cn in d})
+    print("| kernel | dispatches | " + " | ".join(names) + " | VALU/wave | VALU busy |")
+    print("|---|---|" + "---|" * (len(names) + 2))
+    for k, d in sorted(agg.items()):
+        m = {cn: float(np.mean(v)) for cn, v in d.items()}
+        per_wave = m["SQ_INSTS_VALU"] / m["SQ_WAVES"] if "SQ_INSTS_VALU" in m and m.get("SQ_WAVES") else None
+        busy = (m["SQ_ACTIVE_INST_VALU"] / 256 / (m["GRBM_GUI_ACTIVE"] / 8)
+                if "SQ_ACTIVE_INST_VALU" in m and m.get("GRBM_GUI_ACTIVE") else None)
+        n = len(next(iter(d.values())))
+        cells = " | ".join(f"{m[cn]:.4g}" if cn in m else "" for cn in names)
+        pw = f"{per_wave:.1f}" if per_wave is not None else ""
+        bz = f"{100 * busy:.1f}%" if busy is not None else ""
+        print(f"| {k} | {n} | {cells} | {pw} | {bz} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -578,15 +608,23 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="window workloads: time eager calls only (for counter passes)")
+    ap.add_argument("--no-diag", action="store_true",
+                    help="window workloads: skip the outlier diagnostic (its extra window writes the "
+                         "fp32 codec input and would count in kernel traces and counters)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
                     help="summarize rocprofv3 --pmc databases into profiles/traffic.json (no GPU needed)")
     ap.add_argument("--md", default=None, help="append the --summarize-pmc table to this file")
     ap.add_argument("--summarize-trace", metavar="TRACE_DB",
                     help="per-kernel mean durations from a rocprofv3 --kernel-trace database (no GPU needed)")
+    ap.add_argument("--summarize-counters", metavar="PMC_DB",
+                    help="per-kernel counter means and VALU busy from a rocprofv3 --pmc database (no GPU needed)")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.steps)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.workload, args.md)
