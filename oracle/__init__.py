@@ -71,15 +71,37 @@ def _a_width(a, dk):
 
 
 # ---------------------------------------------------------------- codec (c2)
-def quantize(X):
-    """Layout-0 codec of each [dk, dv] tile (orc_quantize): returns Q, s, c."""
+def quantize(X, bits=8):
+    """Layout-0 codec of each [dk, dv] tile with b-bit codes (orc_quantize):
+    returns Q (unpacked, one int8 per code, in [-(2^(b-1)-1), 2^(b-1)-1]), s, c."""
     X = _f32(X)
     nh, dk, dv = X.shape
     Q = np.empty((nh, dk, dv), np.int8)
     s = np.empty((nh, dk), np.float32)
     c = np.empty((nh, dv), np.float32)
-    lib().orc_quantize(nh, dk, dv, _p(X), _p(Q), _p(s), _p(c))
+    lib().orc_quantize(nh, dk, dv, int(bits), _p(X), _p(Q), _p(s), _p(c))
     return Q, s, c
+
+
+def pack_codes(Q, bits):
+    """Unpacked codes [..., dv] -> the packed byte layout [..., dv*bits/8] (orc_pack_codes)."""
+    Q = np.ascontiguousarray(Q, np.int8)
+    dv = Q.shape[-1]
+    rows = Q.size // dv
+    P = np.empty(Q.shape[:-1] + (dv * bits // 8,), np.uint8)
+    lib().orc_pack_codes(rows, dv, int(bits), _p(Q), _p(P))
+    return P
+
+
+def unpack_codes(P, dv, bits):
+    """Packed bytes [..., dv*bits/8] -> unpacked codes [..., dv] (orc_unpack_codes)."""
+    P = np.ascontiguousarray(P, np.uint8)
+    nb = dv * bits // 8
+    assert P.shape[-1] == nb
+    rows = P.size // nb
+    Q = np.empty(P.shape[:-1] + (dv,), np.int8)
+    lib().orc_unpack_codes(rows, dv, int(bits), _p(P), _p(Q))
+    return Q
 
 
 def dequantize(Q, s, c):
@@ -152,8 +174,9 @@ def recur(S, q, k, v, a, b, want_u=False):
 
 
 # ------------------------------------------------- per-step quantized (c3)
-def quant_step(Q, s, c, q, k, v, a, b):
-    """One per-step quantized decode (orc_quant_step) on copies of Q, s, c.
+def quant_step(Q, s, c, q, k, v, a, b, bits=8):
+    """One per-step quantized decode (orc_quant_step) on copies of Q, s, c,
+    requantizing to b-bit codes (Q unpacked).
 
     q,k: [nh,dk], v: [nh,dv], a: [nh,1|dk], b: [nh].
     Returns dict(Q, s, c, o (fp64), S_pre (fp64 state before rounding),
@@ -167,8 +190,8 @@ def quant_step(Q, s, c, q, k, v, a, b):
     o = np.empty((nh, dv), np.float64)
     S_pre = np.empty((nh, dk, dv), np.float64)
     S_f32 = np.empty((nh, dk, dv), np.float32)
-    lib().orc_quant_step(nh, dk, dv, kda, _p(Q), _p(s), _p(c), _p(q), _p(k), _p(v), _p(a), _p(b),
-                         _p(o), _p(S_pre), _p(S_f32))
+    lib().orc_quant_step(nh, dk, dv, kda, int(bits), _p(Q), _p(s), _p(c), _p(q), _p(k), _p(v), _p(a),
+                         _p(b), _p(o), _p(S_pre), _p(S_f32))
     return dict(Q=Q, s=s, c=c, o=o, S_pre=S_pre, S_f32=S_f32)
 
 
@@ -216,8 +239,9 @@ def window(X0, q, k, v, a, b, rebuild=True):
     return o, u, SW
 
 
-def compress(SW, r, iters=20, hp_idx=None):
-    """Compensators + residual + codec of each rebuilt state (orc_compress).
+def compress(SW, r, iters=20, hp_idx=None, bits=8):
+    """Compensators + residual + codec of each rebuilt state (orc_compress);
+    layout 0 codes have b bits (unpacked), DAMP rows' codes 8.
 
     Returns dict(Q, s (layout 0) | hp_rows (DAMP), c, p [nh,r,dk],
     w [nh,r,dv], R (fp32 residual handed to the codec)).
@@ -235,8 +259,8 @@ def compress(SW, r, iters=20, hp_idx=None):
     p = np.zeros((nh, max(r, 0), dk), np.float32)
     w = np.zeros((nh, max(r, 0), dv), np.float32)
     R = np.empty((nh, dk, dv), np.float32)
-    lib().orc_compress(nh, dk, dv, r, iters, layout, n_hp, _p(hp_idx), _p(SW), _p(Q), _p(s),
-                       _p(c), _p(hp), _p(p), _p(w), _p(R))
+    lib().orc_compress(nh, dk, dv, r, iters, layout, n_hp, int(bits if layout == 0 else 8), _p(hp_idx),
+                       _p(SW), _p(Q), _p(s), _p(c), _p(hp), _p(p), _p(w), _p(R))
     return dict(Q=Q, s=s, c=c, hp_rows=hp, p=p, w=w, R=R)
 
 

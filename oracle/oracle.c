@@ -37,14 +37,21 @@
  * Readings taken where the pages are silent (each is repeated where used):
  *  - smoothing scale of key row i: s_i = sqrt(max_j |X_ij|); rows are
  *    divided by s_i before the value-column scales are taken;
- *  - value-column scales are symmetric: c_j = m_j / 127, codes in
- *    [-127, 127], round half to even;
+ *  - value-column scales are symmetric: c_j = m_j / Qb, codes in
+ *    [-Qb, Qb] with Qb = 2^(b-1) - 1 for a code width of b bits (127 for
+ *    the INT8 state; 31 and 7 for the 6- and 4-bit states the LeapQuant
+ *    accuracy table reports), round half to even;
+ *  - codes of b < 8 bits are stored packed (orc_pack_codes): 4 bits as two
+ *    two's-complement nibbles per byte, even column in the low nibble; 6
+ *    bits as that nibble plane of the low 4 bits followed by a plane of
+ *    the top 2 bits, four columns per byte, lowest column in the lowest
+ *    bits;
  *  - every codec step is one IEEE fp32 operation rounded to nearest even,
  *    in the order written below, with no fused multiply-add, except the
  *    last: the code is the integer nearest to the exact product
  *    Y_ij * iota_j (ties to even), with no intermediate rounding;
  *  - zero rows/columns get scale 0, reciprocal 0 and code 0; a column whose
- *    reciprocal scale 127/m_j overflows fp32 is treated as a zero column;
+ *    reciprocal scale Qb/m_j overflows fp32 is treated as a zero column;
  *  - the output of a per-step quantized decode is taken from the updated
  *    state before it is requantized;
  *  - Compensator Tokens: sequential deflation, each term found by
@@ -87,8 +94,9 @@ static double round_half_even(double t) { return nearbyint(t); }
  * X is one dk x dv fp32 tile.  Outputs: codes Q (int8, dk x dv), row
  * smoothing scales s (dk), column scales c (dv).
  * ==================================================================== */
-static void quantize_tile(int dk, int dv, const float *X, int8_t *Q, float *s, float *c)
+static void quantize_tile(int dk, int dv, int qmax, const float *X, int8_t *Q, float *s, float *c)
 {
+    const float qm = (float)qmax;
     float *Y = (float *)malloc(sizeof(float) * (size_t)dk * dv);
     for (int i = 0; i < dk; i++) {
         float r = 0.0f;                                   /* r_i = max_j |X_ij| */
@@ -110,16 +118,16 @@ static void quantize_tile(int dk, int dv, const float *X, int8_t *Q, float *s, f
         }
         float cj = 0.0f, iota = 0.0f;
         if (m > 0.0f) {
-            iota = f32_div(127.0f, m);                    /* iota_j = 127/m_j  */
+            iota = f32_div(qm, m);                        /* iota_j = Qb/m_j   */
             if (isinf(iota)) iota = 0.0f;                 /* overflow: zero column */
-            else cj = f32_div(m, 127.0f);                 /* c_j = m_j/127     */
+            else cj = f32_div(m, qm);                     /* c_j = m_j/Qb      */
         }
         c[j] = cj;
         for (int i = 0; i < dk; i++) {
             /* exact product of two fp32 values (fits in fp64), rounded once */
             double qv = round_half_even((double)Y[i * dv + j] * (double)iota);
-            if (qv > 127.0) qv = 127.0;
-            if (qv < -127.0) qv = -127.0;
+            if (qv > qmax) qv = qmax;
+            if (qv < -qmax) qv = -qmax;
             Q[i * dv + j] = (int8_t)qv;
         }
     }
@@ -132,6 +140,48 @@ static void dequantize_tile(int dk, int dv, const int8_t *Q, const float *s, con
     for (int i = 0; i < dk; i++)
         for (int j = 0; j < dv; j++)
             X[i * dv + j] = f32_mul(f32_mul((float)Q[i * dv + j], c[j]), s[i]);
+}
+
+/* largest code of a b-bit state: 2^(b-1) - 1 (b = 8, 6 or 4) */
+static int code_qmax(int bits) { return (1 << (bits - 1)) - 1; }
+
+/* ======================================================================
+ * Packed code layout of one row of dv codes (b = 8, 6, 4 bits), as stored
+ * in memory; rows follow each other, dv*b/8 bytes apart.
+ *   b = 8: one byte per code.
+ *   b = 4: code j in byte j/2, bits 4*(j%2)..+3 (two's complement nibble).
+ *   b = 6: bytes [0, dv/2): the low 4 bits of code j as for b = 4;
+ *          bytes [dv/2, 3dv/4): the top 2 bits of the code's 6-bit two's
+ *          complement form, code j in byte dv/2 + j/4, bits 2*(j%4)..+1.
+ * ==================================================================== */
+static void pack_row(int dv, int bits, const int8_t *Q, uint8_t *P)
+{
+    int nb = dv * bits / 8;
+    memset(P, 0, (size_t)nb);
+    for (int j = 0; j < dv; j++) {
+        unsigned u = (unsigned)(uint8_t)Q[j];            /* two's complement byte */
+        if (bits == 8) {
+            P[j] = (uint8_t)u;
+        } else {
+            P[j / 2] |= (uint8_t)((u & 0xFu) << (4 * (j % 2)));
+            if (bits == 6) P[dv / 2 + j / 4] |= (uint8_t)(((u >> 4) & 0x3u) << (2 * (j % 4)));
+        }
+    }
+}
+
+static void unpack_row(int dv, int bits, const uint8_t *P, int8_t *Q)
+{
+    for (int j = 0; j < dv; j++) {
+        int v;
+        if (bits == 8) {
+            v = (int8_t)P[j];
+        } else {
+            v = (P[j / 2] >> (4 * (j % 2))) & 0xF;
+            if (bits == 6) v |= ((P[dv / 2 + j / 4] >> (2 * (j % 4))) & 0x3) << 4;
+            if (v >= (1 << (bits - 1))) v -= 1 << bits;  /* sign of the b-bit field */
+        }
+        Q[j] = (int8_t)v;
+    }
 }
 
 /* ======================================================================
@@ -278,12 +328,26 @@ static void recur_step(int dk, int dv, int kda, double *S, const float *q, const
  * [step][head][...] .  a has 1 (GDN) or dk (KDA) entries per head-step.
  * ==================================================================== */
 
-/* c2 / layout 0 over nh heads */
-void orc_quantize(int nh, int dk, int dv, const float *X, int8_t *Q, float *s, float *c)
+/* c2 / layout 0 over nh heads, b-bit codes (unpacked, one int8 each) */
+void orc_quantize(int nh, int dk, int dv, int bits, const float *X, int8_t *Q, float *s, float *c)
 {
     size_t E = (size_t)dk * dv;
     for (int h = 0; h < nh; h++)
-        quantize_tile(dk, dv, X + h * E, Q + h * E, s + (size_t)h * dk, c + (size_t)h * dv);
+        quantize_tile(dk, dv, code_qmax(bits), X + h * E, Q + h * E, s + (size_t)h * dk,
+                      c + (size_t)h * dv);
+}
+
+/* n_rows rows of dv codes: unpacked int8 <-> the packed layout above */
+void orc_pack_codes(int n_rows, int dv, int bits, const int8_t *Q, uint8_t *P)
+{
+    size_t nb = (size_t)dv * bits / 8;
+    for (int r = 0; r < n_rows; r++) pack_row(dv, bits, Q + (size_t)r * dv, P + r * nb);
+}
+
+void orc_unpack_codes(int n_rows, int dv, int bits, const uint8_t *P, int8_t *Q)
+{
+    size_t nb = (size_t)dv * bits / 8;
+    for (int r = 0; r < n_rows; r++) unpack_row(dv, bits, P + r * nb, Q + (size_t)r * dv);
 }
 
 void orc_dequantize(int nh, int dk, int dv, const int8_t *Q, const float *s, const float *c, float *X)
@@ -347,9 +411,9 @@ void orc_recur(int nh, int dk, int dv, int kda, int n, double *S, const float *q
  * S_pre (nullable) receives the fp64 updated state, S_f32 (nullable) the
  * fp32 tensor handed to the codec.
  * ==================================================================== */
-void orc_quant_step(int nh, int dk, int dv, int kda, int8_t *Q, float *s, float *c, const float *q,
-                    const float *k, const float *v, const float *a, const float *b, double *o,
-                    double *S_pre, float *S_f32)
+void orc_quant_step(int nh, int dk, int dv, int kda, int bits, int8_t *Q, float *s, float *c,
+                    const float *q, const float *k, const float *v, const float *a, const float *b,
+                    double *o, double *S_pre, float *S_f32)
 {
     size_t E = (size_t)dk * dv;
     int na = kda ? dk : 1;
@@ -365,7 +429,7 @@ void orc_quant_step(int nh, int dk, int dv, int kda, int8_t *Q, float *s, float 
         if (S_pre) memcpy(S_pre + h * E, S, sizeof(double) * E);
         for (size_t e = 0; e < E; e++) X[e] = (float)S[e];
         if (S_f32) memcpy(S_f32 + h * E, X, sizeof(float) * E);
-        quantize_tile(dk, dv, X, Qh, sh, ch);
+        quantize_tile(dk, dv, code_qmax(bits), X, Qh, sh, ch);
     }
     free(X);
     free(S);
@@ -515,7 +579,7 @@ void orc_window(int nh, int dk, int dv, int kda, int n, const double *X0, const 
  * then coded by layout 0 (Q, s, c) or the DAMP split (Q, c, hp_rows).
  * p: [nh][r][dk], w: [nh][r][dv], R_out (nullable): fp32 [nh][dk][dv].
  * ==================================================================== */
-void orc_compress(int nh, int dk, int dv, int r, int iters, int layout, int n_hp,
+void orc_compress(int nh, int dk, int dv, int r, int iters, int layout, int n_hp, int bits,
                   const int32_t *hp_idx, const double *SW, int8_t *Q, float *s, float *c,
                   uint16_t *hp_rows, float *p, float *w, float *R_out)
 {
@@ -582,7 +646,8 @@ void orc_compress(int nh, int dk, int dv, int r, int iters, int layout, int n_hp
         for (size_t e = 0; e < E; e++) Rf[e] = (float)R[e];
         if (R_out) memcpy(R_out + h * E, Rf, sizeof(float) * E);
         if (layout == 0)
-            quantize_tile(dk, dv, Rf, Q + h * E, s + (size_t)h * dk, c + (size_t)h * dv);
+            quantize_tile(dk, dv, code_qmax(bits), Rf, Q + h * E, s + (size_t)h * dk,
+                          c + (size_t)h * dv);
         else
             quantize_tile_damp(dk, dv, n_hp, hp_idx + (size_t)h * n_hp, Rf,
                                Q + h * (size_t)(dk - n_hp) * dv, c + (size_t)h * dv,
