@@ -13,7 +13,7 @@ on a bounded sample of the same workload).
 
     python bench.py [--steps 100] [--warmup 200] [--gpus 1]
                     [--workload prefix_cache|gdn_serving|kda|damp|tiny]
-                    [--no-cpu] [--no-graph] [--no-diag] [--copy-calibration]
+                    [--no-cpu] [--no-graph] [--no-diag] [--bits 8|6|4] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -58,7 +58,7 @@ def step_bytes(cfg: dict, quant: bool) -> int:
     inputs = (2 * dk + dv) * io + 4 * na + 4
     out = dv * io
     if quant:
-        state = dk * dv + 4 * (dk + dv)          # codes + row and column scales
+        state = dk * dv * cfg.get("bits", 8) // 8 + 4 * (dk + dv)   # codes + row and column scales
     else:
         state = 4 * dk * dv
     return 2 * state + inputs + out             # read + write the state
@@ -71,7 +71,7 @@ def window_step_bytes(cfg: dict, t: int) -> int:
     io = 2 if cfg["io"] == "bf16" else 4
     na = dk if cfg["decay"] == "channel" else 1
     rows = dk - n_hp
-    state = rows * dv + (0 if n_hp else 4 * dk) + 4 * dv + 2 * n_hp * dv + 4 * n_hp
+    state = rows * dv * cfg.get("bits", 8) // 8 + (0 if n_hp else 4 * dk) + 4 * dv + 2 * n_hp * dv + 4 * n_hp
     comps = 4 * r * (dk + dv)
     buf = t * 4 * (dk + dv)
     g = 4 * na * (2 if t > 0 else 1)
@@ -84,7 +84,7 @@ def flush_bytes(cfg: dict, n: int) -> int:
     n_hp = cfg.get("n_hp", 0)
     na = dk if cfg["decay"] == "channel" else 1
     rows = dk - n_hp
-    state = rows * dv + (0 if n_hp else 4 * dk) + 4 * dv + 2 * n_hp * dv + 4 * n_hp
+    state = rows * dv * cfg.get("bits", 8) // 8 + (0 if n_hp else 4 * dk) + 4 * dv + 2 * n_hp * dv + 4 * n_hp
     comps = 4 * r * (dk + dv)
     return 2 * (state + comps) + n * 4 * (dk + dv) + 8 * na
 
@@ -103,18 +103,19 @@ def stored_traffic(kernel: str, workload: str):
     return ent["bytes_per_launch"]
 
 
-def _oracle_int8_run(S: np.ndarray, inputs: list, budget_s: float):
-    """Consecutive per-step INT8 decodes of the states S by the fp64 CPU
-    oracle (one thread) until budget_s has passed: (updates, steps, s)."""
+def _oracle_int8_run(S: np.ndarray, inputs: list, budget_s: float, bits: int = 8):
+    """Consecutive per-step quantized decodes (b-bit codes) of the states S
+    by the fp64 CPU oracle (one thread) until budget_s has passed:
+    (updates, steps, s)."""
     import oracle
 
     nh = S.shape[0]
-    Q, s, c = oracle.quantize(S)
+    Q, s, c = oracle.quantize(S, bits=bits)
     done, step = 0, 0
     t0 = time.perf_counter()
     while True:
         inp = inputs[step % len(inputs)]
-        r = oracle.quant_step(Q, s, c, inp["q"], inp["k"], inp["v"], inp["a"], inp["b"])
+        r = oracle.quant_step(Q, s, c, inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], bits=bits)
         Q, s, c = r["Q"], r["s"], r["c"]
         done += nh
         step += 1
@@ -132,8 +133,9 @@ _CPU_JOB = None
 
 
 def _cpu_worker(i: int):
-    S, inputs, per, budget = _CPU_JOB
-    return _oracle_int8_run(S[i * per:(i + 1) * per], _slice_inputs(inputs, i * per, (i + 1) * per), budget)
+    S, inputs, per, budget, bits = _CPU_JOB
+    return _oracle_int8_run(S[i * per:(i + 1) * per], _slice_inputs(inputs, i * per, (i + 1) * per), budget,
+                            bits)
 
 
 def cpu_baselines(cfg: dict, S: np.ndarray, inputs: list) -> dict:
@@ -149,14 +151,15 @@ def cpu_baselines(cfg: dict, S: np.ndarray, inputs: list) -> dict:
     global _CPU_JOB
     total = cfg["B"] * cfg["H"]
     nh1 = 2048
-    done, step, dt = _oracle_int8_run(S[:nh1], _slice_inputs(inputs, 0, nh1), 12.0)
+    bits = cfg.get("bits", 8)
+    done, step, dt = _oracle_int8_run(S[:nh1], _slice_inputs(inputs, 0, nh1), 12.0, bits)
     one = {"value": done / dt, "unit": "token-head updates/s", "cores": 1, "kind": "oracle",
-           "sample": f"first {nh1} of the {total} states, {step} consecutive per-step INT8 decode "
+           "sample": f"first {nh1} of the {total} states, {step} consecutive per-step {bits}-bit decode "
                      f"steps ({done} token-head updates) in {dt:.1f} s, one thread"}
 
     ncores = max(1, min(16, len(os.sched_getaffinity(0))))
     per = 512
-    _CPU_JOB = (S, inputs, per, 8.0)
+    _CPU_JOB = (S, inputs, per, 8.0, bits)
     with multiprocessing.get_context("fork").Pool(ncores) as pool:
         res = pool.map(_cpu_worker, range(ncores))
     _CPU_JOB = None
@@ -226,7 +229,8 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
                 torch.from_numpy(inp["b"]).cuda()]
 
     dev_inputs = [up(i) for i in inputs]
-    d = g.Desc(B=cfg["B"], H=cfg["H"], dk=dk, dv=dv, io_dtype=g.IO_BF16)
+    bits = cfg.get("bits", 8)
+    d = g.Desc(B=cfg["B"], H=cfg["H"], dk=dk, dv=dv, io_dtype=g.IO_BF16, bits=bits)
     st = g.alloc_state(d)
     S_dev = torch.from_numpy(S).cuda()
     g.gdn_state_quantize(d, S_dev, st)
@@ -244,7 +248,7 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
     def fp32_step(i):
         g.gdn_fp32_decode_step(dc, S_p, *ptrs[i % n_sets], o_p, sh)
 
-    log("timing INT8 per-step decode")
+    log(f"timing {bits}-bit per-step decode")
     wall, per = time_launches(torch, int8_step, args.steps, args.warmup)
     log("timing fp32-state decode")
     wall32, per32 = time_launches(torch, fp32_step, args.steps, args.warmup)
@@ -252,7 +256,8 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
     b32 = step_bytes(cfg, False) * nh
     value = nh * args.steps / wall
     res = {
-        "metric": "token-head state updates/s, INT8 GDN per-step decode (1 GPU)",
+        "metric": ("token-head state updates/s, INT8 GDN per-step decode (1 GPU)" if bits == 8 else
+                   f"token-head state updates/s, {bits}-bit GDN per-step decode (1 GPU)"),
         "value": value,
         "unit": "token-head updates/s",
         "n_gpus": 1,
@@ -262,16 +267,17 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 state, fp32 math, bf16 q/k/v/o",
+        "dtype": f"int{bits} state, fp32 math, bf16 q/k/v/o",
         "data": "synthetic (seeded pre-filled states with outlier rows/columns; no weights)",
-        "config": {"workload": "prefix_cache: B=1024 states, H=32, dk=dv=128, one per-step INT8 "
-                               "decode of every state per step, bf16 I/O, scalar gate",
-                   "global_batch": cfg["B"], "heads": cfg["H"], "dk": dk, "dv": dv,
+        "config": {"workload": "prefix_cache: B=1024 states, H=32, dk=dv=128, one per-step "
+                               f"{'INT8' if bits == 8 else f'{bits}-bit'} decode of every state per step, "
+                               "bf16 I/O, scalar gate",
+                   "global_batch": cfg["B"], "heads": cfg["H"], "dk": dk, "dv": dv, "bits": bits,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": b8 / per / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": b8 / per / 1e9 / HBM_PEAK_GBS,
-                     "traffic": stored_traffic("step_fused", "prefix_cache"),
-                     "kernel": "step_fused_kernel<128x128, bf16, scalar gate>",
+                     "traffic": stored_traffic("step_fused" + ("" if bits == 8 else f"_b{bits}"), "prefix_cache"),
+                     "kernel": f"step_fused_kernel<128x128, bf16, scalar gate, {bits}-bit codes>",
                      "algorithmic_bytes_per_launch": b8, "mean_launch_s": per},
         "fp32_state": {"value": nh * args.steps / wall32, "ms_per_step": wall32 / args.steps * 1e3,
                        "achieved_GBs": b32 / per32 / 1e9, "frac": b32 / per32 / 1e9 / HBM_PEAK_GBS,
@@ -288,10 +294,13 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
 
 def bench_window(args, torch, g, name):
     """Window-mode workloads: steps = decode tokens (flushes every W)."""
-    cfg = synth.WORKLOADS[name]
+    cfg = dict(synth.WORKLOADS[name], bits=args.bits)
     nh, dk, dv, W, r = cfg["B"] * cfg["H"], cfg["dk"], cfg["dv"], cfg["W"], cfg["r"]
     n_hp = cfg.get("n_hp", 0)
-    d = g.Desc(B=cfg["B"], H=cfg["H"], dk=dk, dv=dv, W=W, r=r,
+    if n_hp and args.bits != 8:
+        print("the DAMP layout keeps 8-bit codes: --bits applies to the other workloads", file=sys.stderr)
+        sys.exit(2)
+    d = g.Desc(B=cfg["B"], H=cfg["H"], dk=dk, dv=dv, W=W, r=r, bits=args.bits,
                decay=g.DECAY_CHANNEL if cfg["decay"] == "channel" else g.DECAY_SCALAR, io_dtype=g.IO_BF16,
                layout=g.LAYOUT_DAMP if n_hp else g.LAYOUT_ROWCOL, n_hp=n_hp, power_iters=20)
     st = g.alloc_state(d)
@@ -344,15 +353,16 @@ def bench_window(args, torch, g, name):
     t_flush = ev_f[0].elapsed_time(ev_f[1]) * 1e-3
     bsteps = [window_step_bytes(cfg, t) * nh for t in range(W)]
     res = {
-        "metric": f"token-head state updates/s, INT8 window-mode decode ({name}, 1 GPU)",
+        "metric": f"token-head state updates/s, {'INT8' if args.bits == 8 else f'{args.bits}-bit'} "
+                  f"window-mode decode ({name}, 1 GPU)",
         "value": nh * steps / wall, "unit": "token-head updates/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": wall / steps * 1e3, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "int8 state, fp32 math, bf16 q/k/v/o",
-        "data": "synthetic", "config": {"workload": name, "B": cfg["B"], "H": cfg["H"], "W": W, "r": r,
+        "scaling": "weak", "vs_baseline": None, "dtype": f"int{args.bits} state, fp32 math, bf16 q/k/v/o",
+        "data": "synthetic", "config": {"workload": name, "B": cfg["B"], "H": cfg["H"], "W": W, "r": r, "bits": args.bits,
                                          "n_hp": n_hp, "decay": cfg["decay"]},
         "roofline": {"bound": "hbm", "achieved": sum(bsteps) / sum(t_steps) / 1e9, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": sum(bsteps) / sum(t_steps) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": stored_traffic("window_step", name),
+                     "traffic": stored_traffic("window_step" + ("" if args.bits == 8 else f"_b{args.bits}"), name),
                      "kernel": "window_step_kernel (mean over window positions)"},
         "launch": "eager calls" if args.no_graph else "one HIP graph per window (W decode steps + flush), replayed",
         "window_us": None if per_window is None else per_window * 1e6,
@@ -438,7 +448,7 @@ def bench_tiny(args, torch, g):
     duration from HIP events."""
     cfg = synth.WORKLOADS["tiny"]
     nh, dk, dv, T = cfg["B"] * cfg["H"], cfg["dk"], cfg["dv"], cfg["T"]
-    d = g.Desc(B=cfg["B"], H=cfg["H"], dk=dk, dv=dv, io_dtype=g.IO_F32)
+    d = g.Desc(B=cfg["B"], H=cfg["H"], dk=dk, dv=dv, io_dtype=g.IO_F32, bits=args.bits)
     st = g.alloc_state(d)
     g.gdn_state_quantize(d, torch.zeros(nh * dk * dv, dtype=torch.float32, device="cuda"), st)
     dev_in = []
@@ -536,6 +546,10 @@ def summarize_pmc(fetch_db: str, write_db: str, copy_fetch_db: str, copy_write_d
         lines.append(f"| {k} | {fetch[k]:.1f} | {write[k]:.1f} | {b:.4g} |")
         for tag in ("step_fused", "step_fp32", "window_step", "flush"):
             if f"gdnq::{tag}_kernel" in k:
+                # the code width is the last template argument of the b-bit kernels
+                last = k.rstrip(">").split(",")[-1].strip()
+                if tag != "step_fp32" and last in ("6", "4"):
+                    tag += "_b" + last
                 data.setdefault(workload, {})[tag] = {
                     "bytes_per_launch": b, "src_hash": src_hash(), "fetch_kib": fetch[k],
                     "write_kib": write[k], "fetch_scale": fscale, "write_scale": wscale}
@@ -606,6 +620,8 @@ def main():
     ap.add_argument("--workload", default="prefix_cache",
                     choices=["prefix_cache", "gdn_serving", "kda", "damp", "tiny"])
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--bits", type=int, default=8, choices=[8, 6, 4],
+                    help="code width of the quantized state (default 8)")
     ap.add_argument("--no-graph", action="store_true",
                     help="window workloads: time eager calls only (for counter passes)")
     ap.add_argument("--no-diag", action="store_true",
@@ -637,6 +653,7 @@ def main():
     data = cpu = None
     if args.workload == "prefix_cache" and not args.copy_calibration:
         data = prefix_cache_data()
+        data = (dict(data[0], bits=args.bits),) + data[1:]
         if not args.no_cpu:
             log("timing the CPU oracle")
             cpu = cpu_baselines(*data)

@@ -101,13 +101,24 @@ typedef struct {
     int32_t n_hp;         /* DAMP fp16 rows per head (layout 1), 1..dk/2       */
     int32_t power_iters;  /* power-iteration steps per compensator, 1..64      */
     uint32_t flags;       /* GDNQ_DEBUG_PREQUANT or 0                          */
+    int32_t bits;         /* code width b: 8 (0 also means 8), 6 or 4; layout 1
+                             keeps 8-bit codes (DAMP: the rest in INT8)        */
 } gdnq_desc;
 
 /*
  * Quantized state of B*H heads (all device pointers; NULL where unused).
  * Per-step mode is W == 1 && r == 0; everything else is window mode.
  *   codes       int8   layout 0: [B,H,dk,dv]; layout 1: [B,H,dk-n_hp,dv]
- *                      (the non-DAMP rows in ascending row order); row-major
+ *                      (the non-DAMP rows in ascending row order); row-major.
+ *                      With b = 6 or 4 bits (layout 0) each row of dv
+ *                      codes takes dv*b/8 bytes: b = 4: code j in byte
+ *                      j/2, bits 4(j%2)..+3, two's complement; b = 6: the
+ *                      low 4 bits of every code packed as for b = 4 in
+ *                      bytes [0, dv/2), then the top 2 bits of the 6-bit
+ *                      two's complement form, code j in byte dv/2 + j/4,
+ *                      bits 2(j%4)..+1.  Codes lie in [-(2^(b-1)-1),
+ *                      2^(b-1)-1] (LeapQuant accuracy table: 8, 6 and 4
+ *                      bit states), column scales c = m / (2^(b-1)-1).
  *   row_scale   fp32   [B,H,dk]        layout 0 only (smoothing scales s)
  *   col_scale   fp32   [B,H,dv]        value-column scales c
  *   comp_k      fp32   [B,H,r,dk]      compensator key-side vectors p (r > 0)

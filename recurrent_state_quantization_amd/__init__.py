@@ -35,7 +35,7 @@ class GdnqError(RuntimeError):
 class _Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "H", "dk", "dv", "W", "r", "decay", "io_dtype", "layout", "n_hp", "power_iters")]
-    _fields_ += [("flags", ctypes.c_uint32)]
+    _fields_ += [("flags", ctypes.c_uint32), ("bits", ctypes.c_int32)]
 
 
 class _State(ctypes.Structure):
@@ -57,6 +57,7 @@ class Desc:
     n_hp: int = 0
     power_iters: int = 20
     flags: int = 0
+    bits: int = 8
 
     @property
     def nh(self) -> int:

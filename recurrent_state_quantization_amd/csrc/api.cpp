@@ -49,6 +49,7 @@ bool overlap(const Span &a, const Span &b)
 size_t io_size(const gdnq_desc &d) { return d.io_dtype == GDNQ_IO_BF16 ? 2 : 4; }
 size_t nheads(const gdnq_desc &d) { return (size_t)d.B * (size_t)d.H; }
 bool per_step(const gdnq_desc &d) { return d.W == 1 && d.r == 0; }
+int code_bits(const gdnq_desc &d) { return d.bits == 0 ? 8 : d.bits; }
 
 int check_desc(const gdnq_desc *d)
 {
@@ -73,6 +74,10 @@ int check_desc(const gdnq_desc *d)
     if (d->r > 0 && (d->power_iters < 1 || d->power_iters > 64))
         return fail(GDNQ_EINVAL, "power_iters must be in [1, 64] when r > 0 (got %d)", d->power_iters);
     if (d->flags & ~GDNQ_DEBUG_PREQUANT) return fail(GDNQ_EINVAL, "unknown flag bits 0x%x", d->flags);
+    if (d->bits != 0 && d->bits != 8 && d->bits != 6 && d->bits != 4)
+        return fail(GDNQ_EINVAL, "bits must be 8, 6 or 4 (0 means 8; got %d)", d->bits);
+    if (d->layout == GDNQ_LAYOUT_DAMP && code_bits(*d) != 8)
+        return fail(GDNQ_EUNSUPPORTED, "the DAMP layout keeps 8-bit codes (got bits=%d)", d->bits);
     return GDNQ_OK;
 }
 
@@ -83,7 +88,7 @@ void state_sizes(const gdnq_desc &d, size_t out[11])
     const bool damp = d.layout == GDNQ_LAYOUT_DAMP;
     const bool window = !per_step(d) || damp;
     const size_t rows = damp ? (size_t)(d.dk - d.n_hp) : (size_t)d.dk;
-    out[0] = nh * rows * d.dv;                                             // codes
+    out[0] = nh * rows * d.dv * code_bits(d) / 8;                          // codes
     out[1] = damp ? 0 : nh * d.dk * 4;                                     // row_scale
     out[2] = nh * d.dv * 4;                                                // col_scale
     out[3] = nh * (size_t)d.r * d.dk * 4;                                  // comp_k

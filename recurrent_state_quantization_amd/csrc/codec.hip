@@ -24,9 +24,10 @@ struct QuantArgs {
     int r, n_hp, iters, kda;
 };
 
-template <class G, bool DAMP>
+template <class G, bool DAMP, int BITS>
 __global__ __launch_bounds__(G::NT, 2) void quantize_kernel(QuantArgs A)
 {
+    static_assert(!DAMP || BITS == 8, "the DAMP layout keeps 8-bit codes");
     __shared__ CodecLds<G> L;
     __shared__ int hp[MAX_HP];
     const Lane c = lane_coords<G>();
@@ -48,7 +49,8 @@ __global__ __launch_bounds__(G::NT, 2) void quantize_kernel(QuantArgs A)
         codec_damp<G>(P, c, L, rm, A.codes + h * (size_t)(G::DK - n_hp) * G::DV, A.col_scale + h * G::DV,
                       A.hp_rows + h * n_hp * G::DV);
     } else {
-        codec_rowcol<G>(P, c, L, A.codes + h * E, A.row_scale + h * G::DK, A.col_scale + h * G::DV);
+        codec_rowcol<G, false, BITS>(P, c, L, A.codes + h * (size_t)G::DK * code_row_bytes<G, BITS>(),
+                                     A.row_scale + h * G::DK, A.col_scale + h * G::DV);
     }
     if (A.g_cur && c.t < G::DK) {
         if (A.kda) A.g_cur[h * G::DK + c.t] = 1.0f;
@@ -56,9 +58,11 @@ __global__ __launch_bounds__(G::NT, 2) void quantize_kernel(QuantArgs A)
     }
 }
 
-template <class G, bool DAMP>
+template <class G, bool DAMP, int BITS>
 __global__ __launch_bounds__(G::NT) void dequantize_kernel(QuantArgs A)
 {
+    static_assert(!DAMP || BITS == 8, "the DAMP layout keeps 8-bit codes");
+    constexpr int RB = code_row_bytes<G, BITS>();
     __shared__ int hp[MAX_HP];
     const Lane c = lane_coords<G>();
     const size_t h = __builtin_amdgcn_workgroup_id_x();
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(G::NT) void dequantize_kernel(QuantArgs A)
     __syncthreads();
     RowMap rm;
     if constexpr (DAMP) rm = row_map<G>(c, hp, n_hp);
-    const int8_t *codes = A.codes + h * (size_t)(G::DK - n_hp) * G::DV;
+    const int8_t *codes = A.codes + h * (size_t)(G::DK - n_hp) * RB;
     float cc[8];
     load_f32x8(A.col_scale + h * G::DV + c.cb * 8, cc);
     float P[8][8];
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(G::NT) void dequantize_kernel(QuantArgs A)
         } else {
             const int row = DAMP ? rm.crow[k] : i;
             float X[8];
-            unpack8(*reinterpret_cast<const uint2 *>(codes + (size_t)row * G::DV + c.cb * 8), X);
+            unpack_code8<BITS>(load_code8<G, BITS>(codes + (size_t)row * RB, c.cb), X);
             const float s = DAMP ? 1.0f : A.row_scale[h * G::DK + i];
 #pragma unroll
             for (int j = 0; j < 8; j++) P[k][j] = DAMP ? X[j] * cc[j] : (X[j] * cc[j]) * s;
@@ -115,8 +119,16 @@ hipError_t launch_quantize(const gdnq_desc &d, const float *S, const gdnq_state 
     return with_dims(d.dk, d.dv, [&](auto DK, auto DV) {
         using G = Geom<decltype(DK)::value, decltype(DV)::value>;
         return with_bool(d.layout == GDNQ_LAYOUT_DAMP, [&](auto damp) {
-            hipLaunchKernelGGL((quantize_kernel<G, decltype(damp)::value>), dim3(nh), dim3(G::NT), 0, st, A);
-            return hipGetLastError();
+            return with_bits(d.bits, [&](auto bits) {
+                constexpr bool DAMP = decltype(damp)::value;
+                constexpr int BITS = decltype(bits)::value;
+                if constexpr (DAMP && BITS != 8) {
+                    return hipErrorInvalidValue;
+                } else {
+                    hipLaunchKernelGGL((quantize_kernel<G, DAMP, BITS>), dim3(nh), dim3(G::NT), 0, st, A);
+                    return hipGetLastError();
+                }
+            });
         });
     });
 }
@@ -129,8 +141,16 @@ hipError_t launch_dequantize(const gdnq_desc &d, const gdnq_state &s, float *S_o
     return with_dims(d.dk, d.dv, [&](auto DK, auto DV) {
         using G = Geom<decltype(DK)::value, decltype(DV)::value>;
         return with_bool(d.layout == GDNQ_LAYOUT_DAMP, [&](auto damp) {
-            hipLaunchKernelGGL((dequantize_kernel<G, decltype(damp)::value>), dim3(nh), dim3(G::NT), 0, st, A);
-            return hipGetLastError();
+            return with_bits(d.bits, [&](auto bits) {
+                constexpr bool DAMP = decltype(damp)::value;
+                constexpr int BITS = decltype(bits)::value;
+                if constexpr (DAMP && BITS != 8) {
+                    return hipErrorInvalidValue;
+                } else {
+                    hipLaunchKernelGGL((dequantize_kernel<G, DAMP, BITS>), dim3(nh), dim3(G::NT), 0, st, A);
+                    return hipGetLastError();
+                }
+            });
         });
     });
 }

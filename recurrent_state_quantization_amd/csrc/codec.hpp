@@ -66,19 +66,21 @@ __device__ __forceinline__ RowMap row_map(const Lane &c, const int *hp_lds, int 
 
 
 // Column scales from the per-wave column maxima in L.red[0]; thread t < DV
-// owns column t.  Writes c to global memory and iota to LDS.
-template <class G>
+// owns column t.  Writes c to global memory and iota to LDS.  Codes of
+// BITS bits span [-Qb, Qb]: c = m/Qb, iota = Qb/m.
+template <class G, int BITS = 8>
 __device__ __forceinline__ void column_scales(const Lane &c, CodecLds<G> &L, float *__restrict__ col_scale)
 {
+    constexpr float QB = (float)code_qmax<BITS>();
     if (c.t < G::DV) {
         float m = L.red[0][0][c.t];
 #pragma unroll
         for (int w = 1; w < G::NW; w++) m = fmaxf(m, L.red[0][w][c.t]);
         float cj = 0.0f, io = 0.0f;
         if (m > 0.0f) {
-            io = 127.0f / m;
+            io = QB / m;
             if (__builtin_isinf(io)) io = 0.0f;
-            else cj = m / 127.0f;
+            else cj = m / QB;
         }
         col_scale[c.t] = cj;
         L.iota[c.t] = io;
@@ -96,9 +98,9 @@ __device__ __forceinline__ void column_max_to_lds(const Lane &c, CodecLds<G> &L,
 }
 
 // Layout-0 codec of the register tile P (overwritten with Y).  Writes this
-// head's codes [DK][DV], row scales [DK] and column scales [DV]; STREAM
-// marks the code stores non-temporal.
-template <class G, bool STREAM = false>
+// head's BITS-bit codes (DK rows of code_row_bytes), row scales [DK] and
+// column scales [DV]; STREAM marks the code stores non-temporal.
+template <class G, bool STREAM = false, int BITS = 8>
 __device__ void codec_rowcol(float (&P)[8][8], const Lane &c, CodecLds<G> &L, int8_t *__restrict__ codes,
                              float *__restrict__ row_scale, float *__restrict__ col_scale)
 {
@@ -138,22 +140,19 @@ __device__ void codec_rowcol(float (&P)[8][8], const Lane &c, CodecLds<G> &L, in
         }
     column_max_to_lds<G>(c, L, m);
     __syncthreads();
-    column_scales<G>(c, L, col_scale);
+    column_scales<G, BITS>(c, L, col_scale);
     __syncthreads();
     float io[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) io[j] = L.iota[c.cb * 8 + j];
-    int8_t *cbase = codes + (size_t)row0 * G::DV + c.cb * 8;
+    constexpr int RB = code_row_bytes<G, BITS>();
+    int8_t *rbase = codes + (size_t)row0 * RB;
 #pragma unroll
     for (int k = 0; k < 8; k++) {
         float y[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) y[j] = fmaf(P[k][j], io[j], RINT_MAGIC);
-        uint2 q;
-        q.x = pack_low_bytes(y[0], y[1], y[2], y[3]);
-        q.y = pack_low_bytes(y[4], y[5], y[6], y[7]);
-        if constexpr (STREAM) store_nt8(cbase + koff<G>(k) * G::DV, q);
-        else *reinterpret_cast<uint2 *>(cbase + koff<G>(k) * G::DV) = q;
+        store_code8<G, BITS, STREAM>(rbase + koff<G>(k) * RB, c.cb, pack_code8<BITS>(y));
     }
 }
 

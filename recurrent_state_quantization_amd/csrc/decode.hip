@@ -65,7 +65,7 @@ __device__ __forceinline__ void reduce_ro(const Lane &c, StepLds<G> &S, const fl
     if (c.lane == 0) S.red_kq[c.w] = kq_part;
 }
 
-template <class G, bool BF16, bool KDA>
+template <class G, bool BF16, bool KDA, int BITS>
 __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
 {
     __shared__ CodecLds<G> L;
@@ -73,7 +73,8 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     const Lane c = lane_coords<G>();
     const size_t h = __builtin_amdgcn_workgroup_id_x();
     constexpr size_t E = (size_t)G::DK * G::DV;
-    int8_t *codes = A.codes + h * E;
+    constexpr int RB = code_row_bytes<G, BITS>();
+    int8_t *codes = A.codes + h * (size_t)G::DK * RB;
     float *rs = A.row_scale + h * G::DK;
     float *cs = A.col_scale + h * G::DV;
 
@@ -94,10 +95,10 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the codes'
 
     const int row0 = row0_of<G>(c);
-    const int8_t *cbase = codes + (size_t)row0 * G::DV + c.cb * 8;
-    uint2 qraw[8];
+    const int8_t *rbase = codes + (size_t)row0 * RB;
+    CodeWord qraw[8];
 #pragma unroll
-    for (int k = 0; k < 8; k++) qraw[k] = load_nt8(cbase + koff<G>(k) * G::DV);
+    for (int k = 0; k < 8; k++) qraw[k] = load_code8<G, BITS, true>(rbase + koff<G>(k) * RB, c.cb);
     float cc[8];
     load_f32x8(cs + c.cb * 8, cc);
     const float bh = A.b[h];
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     const float kq = row_sum<G>(kq_row);  // this lane's row group's share: reduce_ro adds the rest
     float X[8][8], R[8], O[8];
 #pragma unroll
-    for (int k = 0; k < 8; k++) unpack8(qraw[k], X[k]);
+    for (int k = 0; k < 8; k++) unpack_code8<BITS>(qraw[k], X[k]);
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         R[j] = X[0][j] * ask[0];
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
 #pragma unroll
         for (int k = 0; k < 8; k++) store_f32x8(pq + koff<G>(k) * G::DV, X[k]);
     }
-    codec_rowcol<G, true>(X, c, L, codes, rs, cs);
+    codec_rowcol<G, true, BITS>(X, c, L, codes, rs, cs);
 }
 
 template <class G, bool BF16, bool KDA>
@@ -246,9 +247,12 @@ hipError_t launch_step_fused(const gdnq_desc &d, const gdnq_state &s, const void
         using G = Geom<decltype(DK)::value, decltype(DV)::value>;
         return with_bool(d.io_dtype == GDNQ_IO_BF16, [&](auto bf) {
             return with_bool(d.decay == GDNQ_DECAY_CHANNEL, [&](auto kda) {
-                hipLaunchKernelGGL((step_fused_kernel<G, decltype(bf)::value, decltype(kda)::value>), dim3(nh),
-                                   dim3(G::NT), 0, st, A);
-                return hipGetLastError();
+                return with_bits(d.bits, [&](auto bits) {
+                    hipLaunchKernelGGL((step_fused_kernel<G, decltype(bf)::value, decltype(kda)::value,
+                                                          decltype(bits)::value>),
+                                       dim3(nh), dim3(G::NT), 0, st, A);
+                    return hipGetLastError();
+                });
             });
         });
     });

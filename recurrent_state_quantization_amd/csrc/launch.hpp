@@ -49,4 +49,14 @@ hipError_t with_bool(bool x, F &&f)
     return f(std::false_type{});
 }
 
+// Call f(BITS) with the code width as a compile-time constant (0 means 8).
+template <class F>
+hipError_t with_bits(int bits, F &&f)
+{
+    if (bits == 0 || bits == 8) return f(std::integral_constant<int, 8>{});
+    if (bits == 6) return f(std::integral_constant<int, 6>{});
+    if (bits == 4) return f(std::integral_constant<int, 4>{});
+    return hipErrorInvalidValue;
+}
+
 }  // namespace gdnq

@@ -409,6 +409,120 @@ __device__ __forceinline__ uint32_t pack_low_bytes(float a, float b, float c, fl
     return lo | hi;
 }
 
+// Low bytes of four words -> one dword (byte i from word i).
+__device__ __forceinline__ uint32_t pack_low_bytes_u(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+    uint32_t hi = __builtin_amdgcn_perm(d, c, 0x04000c0cu);
+    return lo | hi;
+}
+
+// ------------------------------------------------------------ packed codes
+// BITS-bit two's complement codes in [-Qb, Qb], Qb = 2^(BITS-1) - 1.  One
+// row of DV codes takes DV*BITS/8 bytes:
+//   8: one byte per code;
+//   4: code j in byte j/2, bits 4(j%2)..+3;
+//   6: bytes [0, DV/2) hold the low 4 bits of every code as for 4 bits,
+//      bytes [DV/2, 3DV/4) the top 2 bits: code j in byte DV/2 + j/4,
+//      bits 2(j%4)..+1.
+// A lane's 8 columns 8cb..8cb+7 are one 8-byte word (8 bits), one 4-byte
+// word (4 bits), or a 4-byte and a 2-byte word (6 bits): CodeWord a, b.
+template <int BITS>
+constexpr int code_qmax() { return (1 << (BITS - 1)) - 1; }
+
+template <class G, int BITS>
+constexpr int code_row_bytes() { return G::DV * BITS / 8; }
+
+struct CodeWord {
+    uint32_t a, b;
+};
+
+template <class G, int BITS, bool NT = false>
+__device__ __forceinline__ CodeWord load_code8(const int8_t *row, int cb)
+{
+    CodeWord w;
+    if constexpr (BITS == 8) {
+        uint2 v;
+        if constexpr (NT) v = load_nt8(row + cb * 8);
+        else v = *reinterpret_cast<const uint2 *>(row + cb * 8);
+        w.a = v.x;
+        w.b = v.y;
+    } else {
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(row + cb * 4);
+        if constexpr (NT) w.a = __builtin_nontemporal_load(p);
+        else w.a = *p;
+        w.b = 0;
+        if constexpr (BITS == 6) {
+            const uint16_t *q = reinterpret_cast<const uint16_t *>(row + G::DV / 2 + cb * 2);
+            if constexpr (NT) w.b = __builtin_nontemporal_load(q);
+            else w.b = *q;
+        }
+    }
+    return w;
+}
+
+template <class G, int BITS, bool NT = false>
+__device__ __forceinline__ void store_code8(int8_t *row, int cb, const CodeWord &w)
+{
+    if constexpr (BITS == 8) {
+        if constexpr (NT) store_nt8(row + cb * 8, make_uint2(w.a, w.b));
+        else *reinterpret_cast<uint2 *>(row + cb * 8) = make_uint2(w.a, w.b);
+    } else {
+        uint32_t *p = reinterpret_cast<uint32_t *>(row + cb * 4);
+        if constexpr (NT) __builtin_nontemporal_store(w.a, p);
+        else *p = w.a;
+        if constexpr (BITS == 6) {
+            uint16_t *q = reinterpret_cast<uint16_t *>(row + G::DV / 2 + cb * 2);
+            if constexpr (NT) __builtin_nontemporal_store((uint16_t)w.b, q);
+            else *q = (uint16_t)w.b;
+        }
+    }
+}
+
+// The 8 codes of a CodeWord as fp32 (exact).
+template <int BITS>
+__device__ __forceinline__ void unpack_code8(const CodeWord &w, float (&out)[8])
+{
+    if constexpr (BITS == 8) {
+        unpack8(make_uint2(w.a, w.b), out);
+    } else if constexpr (BITS == 4) {
+#pragma unroll
+        for (int e = 0; e < 8; e++) out[e] = (float)((int32_t)(w.a << (28 - 4 * e)) >> 28);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const int32_t hi = (int32_t)(w.b << (30 - 2 * e)) >> 30;   // top 2 bits, signed
+            out[e] = (float)((hi << 4) | (int32_t)((w.a >> (4 * e)) & 0xFu));
+        }
+    }
+}
+
+// Pack 8 rounded codes: y[e] are fma(Y, iota, RINT_MAGIC) results, whose
+// low byte is the code in two's complement.
+template <int BITS>
+__device__ __forceinline__ CodeWord pack_code8(const float (&y)[8])
+{
+    CodeWord w;
+    uint32_t u[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) u[e] = __float_as_uint(y[e]);
+    if constexpr (BITS == 8) {
+        w.a = pack_low_bytes_u(u[0], u[1], u[2], u[3]);
+        w.b = pack_low_bytes_u(u[4], u[5], u[6], u[7]);
+    } else {
+        uint32_t n[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) n[i] = (u[2 * i] & 0xFu) | (u[2 * i + 1] << 4);   // low byte: the pair
+        w.a = pack_low_bytes_u(n[0], n[1], n[2], n[3]);
+        w.b = 0;
+        if constexpr (BITS == 6) {
+#pragma unroll
+            for (int e = 0; e < 8; e++) w.b |= ((u[e] >> 4) & 0x3u) << (2 * e);
+        }
+    }
+    return w;
+}
+
 // fma(y, iota, 1.5*2^23) rounds the exact value y*iota + 1.5*2^23 once, at
 // unit spacing (the sum lies in [2^23, 2^24) for |y*iota| < 2^22), so it
 // equals 1.5*2^23 + rint_even(y*iota) with the product taken exactly; the

@@ -129,27 +129,33 @@ __device__ __forceinline__ void slot_vvec_use(const uint4 (&raw)[2], bool f16, f
 }
 
 // This thread's 8 code rows of the fixed tile (DAMP rows carry no codes).
-template <class G, bool DAMP>
+template <class G, bool DAMP, int BITS>
 __device__ __forceinline__ void load_tile_codes(const int8_t *codes, const Lane &c, const RowMap &rm,
-                                                uint2 (&qraw)[8])
+                                                CodeWord (&qraw)[8])
 {
+    constexpr int RB = code_row_bytes<G, BITS>();
 #pragma unroll
     for (int k = 0; k < 8; k++) {
         if (!DAMP || rm.slot[k] < 0) {
             const int row = DAMP ? rm.crow[k] : row_of<G>(c, k);
-            qraw[k] = *reinterpret_cast<const uint2 *>(codes + (size_t)row * G::DV + c.cb * 8);
+            qraw[k] = load_code8<G, BITS>(codes + (size_t)row * RB, c.cb);
         } else {
-            qraw[k] = make_uint2(0u, 0u);
+            qraw[k] = CodeWord{0u, 0u};
         }
     }
 }
 
 // 8 workgroups per CU (64 VGPRs, no spills; the column scales wait in LDS
 // so the prefetched slot vectors fit beside the codes): 2048 heads run as
-// one round over the 256 CUs, 8192 as four.
-template <class G, bool BF16, bool KDA, bool DAMP>
-__global__ __launch_bounds__(G::NT, 8) void window_step_kernel(WinArgs A)
+// one round over the 256 CUs, 8192 as four.  The 6-bit unpack needs more
+// temporaries: 7 per CU (72 VGPRs) keeps it from spilling.
+template <int BITS>
+constexpr int step_min_blocks() { return BITS == 6 ? 7 : 8; }
+
+template <class G, bool BF16, bool KDA, bool DAMP, int BITS>
+__global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_kernel(WinArgs A)
 {
+    static_assert(!DAMP || BITS == 8, "the DAMP layout keeps 8-bit codes");
     __shared__ WinLds<G> L;
     const Lane c = lane_coords<G>();
     const size_t h = __builtin_amdgcn_workgroup_id_x();
@@ -190,10 +196,10 @@ __global__ __launch_bounds__(G::NT, 8) void window_step_kernel(WinArgs A)
     // fixed INT8 tile: the DAMP row map needs the row indices in LDS, so
     // DAMP loads its codes after the barrier
     const size_t nrows_c = (size_t)(G::DK - n_hp);
-    const int8_t *codes = A.codes + h * nrows_c * G::DV;
-    uint2 qraw[8];
+    const int8_t *codes = A.codes + h * nrows_c * code_row_bytes<G, BITS>();
+    CodeWord qraw[8];
     RowMap rm;
-    if constexpr (!DAMP) load_tile_codes<G, false>(codes, c, rm, qraw);
+    if constexpr (!DAMP) load_tile_codes<G, false, BITS>(codes, c, rm, qraw);
 
     // per-row vectors: gate product, gated k and q (and times the row scale)
     if (c.t < G::DK) {
@@ -212,7 +218,7 @@ __global__ __launch_bounds__(G::NT, 8) void window_step_kernel(WinArgs A)
     __syncthreads();
     if constexpr (DAMP) {
         rm = row_map<G>(c, L.hp, n_hp);
-        load_tile_codes<G, true>(codes, c, rm, qraw);
+        load_tile_codes<G, true, BITS>(codes, c, rm, qraw);
     }
 
     // slot dot products: alpha_l = kvec_l . (G.k), beta_l = kvec_l . (G.q);
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(G::NT, 8) void window_step_kernel(WinArgs A)
     float R[8], O[8];
     {
         float X[8];
-        unpack8(qraw[0], X);
+        unpack_code8<BITS>(qraw[0], X);
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             R[j] = X[j] * gsk[0];
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(G::NT, 8) void window_step_kernel(WinArgs A)
         }
 #pragma unroll
         for (int k = 1; k < 8; k++) {
-            unpack8(qraw[k], X);
+            unpack_code8<BITS>(qraw[k], X);
 #pragma unroll
             for (int j = 0; j < 8; j++) {
                 R[j] = fmaf(X[j], gsk[k], R[j]);
@@ -379,9 +385,11 @@ __device__ __forceinline__ void slot_val(const FlushArgs &A, size_t h, int l, in
 template <class G, bool DAMP>
 constexpr int flush_min_blocks() { return (G::DK == 128 && G::DV == 128 && !DAMP) ? 4 : 2; }
 
-template <class G, bool KDA, bool DAMP>
+template <class G, bool KDA, bool DAMP, int BITS>
 __global__ __launch_bounds__(G::NT, (flush_min_blocks<G, DAMP>())) void flush_kernel(FlushArgs A)
 {
+    static_assert(!DAMP || BITS == 8, "the DAMP layout keeps 8-bit codes");
+    constexpr int RB = code_row_bytes<G, BITS>();
     __shared__ CodecLds<G> L;
     __shared__ FlushLds<G> F;
     const Lane c = lane_coords<G>();
@@ -395,7 +403,7 @@ __global__ __launch_bounds__(G::NT, (flush_min_blocks<G, DAMP>())) void flush_ke
     RowMap rm;
     if constexpr (DAMP) rm = row_map<G>(c, F.hp, n_hp);
     const size_t nrows_c = (size_t)(G::DK - n_hp);
-    int8_t *codes = A.codes + h * nrows_c * G::DV;
+    int8_t *codes = A.codes + h * nrows_c * RB;
     float cc[8];
     load_f32x8(A.col_scale + h * G::DV + c.cb * 8, cc);
     float P[8][8];
@@ -404,9 +412,8 @@ __global__ __launch_bounds__(G::NT, (flush_min_blocks<G, DAMP>())) void flush_ke
         const int i = row_of<G>(c, k);
         if (!DAMP || rm.slot[k] < 0) {
             const int row = DAMP ? rm.crow[k] : i;
-            const uint2 q = *reinterpret_cast<const uint2 *>(codes + (size_t)row * G::DV + c.cb * 8);
             float X[8];
-            unpack8(q, X);
+            unpack_code8<BITS>(load_code8<G, BITS>(codes + (size_t)row * RB, c.cb), X);
             const float s = DAMP ? 1.0f : A.row_scale[h * G::DK + i];
             const float g = F.gs[i];
 #pragma unroll
@@ -472,7 +479,7 @@ __global__ __launch_bounds__(G::NT, (flush_min_blocks<G, DAMP>())) void flush_ke
     if constexpr (DAMP)
         codec_damp<G>(P, c, L, rm, codes, A.col_scale + h * G::DV, A.hp_rows + h * n_hp * G::DV);
     else
-        codec_rowcol<G>(P, c, L, codes, A.row_scale + h * G::DK, A.col_scale + h * G::DV);
+        codec_rowcol<G, false, BITS>(P, c, L, codes, A.row_scale + h * G::DK, A.col_scale + h * G::DV);
     if (c.t < G::DK) {
         if (KDA) A.g_cur[h * G::DK + c.t] = 1.0f;
         else if (c.t == 0) A.g_cur[h] = 1.0f;
@@ -491,10 +498,18 @@ hipError_t launch_window_step(const gdnq_desc &d, const gdnq_state &s, const voi
         return with_bool(d.io_dtype == GDNQ_IO_BF16, [&](auto bf) {
             return with_bool(d.decay == GDNQ_DECAY_CHANNEL, [&](auto kda) {
                 return with_bool(d.layout == GDNQ_LAYOUT_DAMP, [&](auto damp) {
-                    hipLaunchKernelGGL((window_step_kernel<G, decltype(bf)::value, decltype(kda)::value,
-                                                           decltype(damp)::value>),
-                                       dim3(nh), dim3(G::NT), 0, st, A);
-                    return hipGetLastError();
+                    return with_bits(d.bits, [&](auto bits) {
+                        constexpr bool DAMP = decltype(damp)::value;
+                        constexpr int BITS = decltype(bits)::value;
+                        if constexpr (DAMP && BITS != 8) {
+                            return hipErrorInvalidValue;
+                        } else {
+                            hipLaunchKernelGGL((window_step_kernel<G, decltype(bf)::value, decltype(kda)::value,
+                                                                   DAMP, BITS>),
+                                               dim3(nh), dim3(G::NT), 0, st, A);
+                            return hipGetLastError();
+                        }
+                    });
                 });
             });
         });
@@ -511,9 +526,17 @@ hipError_t launch_flush(const gdnq_desc &d, const gdnq_state &s, int n_tokens, h
         using G = Geom<decltype(DK)::value, decltype(DV)::value>;
         return with_bool(d.decay == GDNQ_DECAY_CHANNEL, [&](auto kda) {
             return with_bool(d.layout == GDNQ_LAYOUT_DAMP, [&](auto damp) {
-                hipLaunchKernelGGL((flush_kernel<G, decltype(kda)::value, decltype(damp)::value>), dim3(nh),
-                                   dim3(G::NT), 0, st, A);
-                return hipGetLastError();
+                return with_bits(d.bits, [&](auto bits) {
+                    constexpr bool DAMP = decltype(damp)::value;
+                    constexpr int BITS = decltype(bits)::value;
+                    if constexpr (DAMP && BITS != 8) {
+                        return hipErrorInvalidValue;
+                    } else {
+                        hipLaunchKernelGGL((flush_kernel<G, decltype(kda)::value, DAMP, BITS>), dim3(nh),
+                                           dim3(G::NT), 0, st, A);
+                        return hipGetLastError();
+                    }
+                });
             });
         });
     });

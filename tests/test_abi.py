@@ -49,7 +49,7 @@ def test_struct_layouts_match_header(g):
     state = re.search(r"typedef struct \{(.*?)\} gdnq_state;", text, re.S).group(1)
     sfields = re.findall(r"\*(\w+);", state)
     assert tuple(sfields) == g.STATE_FIELDS
-    assert ctypes.sizeof(g._Desc) == 12 * 4
+    assert ctypes.sizeof(g._Desc) == 13 * 4
 
 
 FAKE = 1 << 40      # aligned, never dereferenced
@@ -85,6 +85,10 @@ def test_state_sizes(g):
     assert s[10] == 2 * 128 * 128 * 4
     d = g.Desc(B=4, H=1)       # per-step: no window buffers
     assert g.gdnq_state_sizes(d)[5:8] == [0, 0, 0]
+    for bits, row in ((8, 128), (6, 96), (4, 64), (0, 128)):   # packed rows of 128 codes
+        d = g.Desc(B=2, H=3, W=16, r=2, bits=bits)
+        assert g.gdnq_state_sizes(d)[0] == 6 * 128 * row
+    assert g.gdnq_state_sizes(g.Desc(B=1, H=1, dv=64, bits=6))[0] == 128 * 48
 
 
 @pytest.mark.parametrize("over,code,msg", [
@@ -101,6 +105,9 @@ def test_state_sizes(g):
     (dict(layout=1, n_hp=65), 1, "n_hp"),
     (dict(r=2, W=4, power_iters=0), 1, "power_iters"),
     (dict(flags=8), 1, "flag"),
+    (dict(bits=5), 1, "bits must"),
+    (dict(bits=2), 1, "bits must"),
+    (dict(layout=1, n_hp=8, bits=4), 2, "DAMP layout keeps 8-bit"),
 ])
 def test_descriptor_errors(g, over, code, msg):
     kw = dict(B=2, H=2)
