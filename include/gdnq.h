@@ -113,10 +113,10 @@ typedef struct {
  *                      With b = 6 or 4 bits (layout 0) each row of dv
  *                      codes takes dv*b/8 bytes: b = 4: code j in byte
  *                      j/2, bits 4(j%2)..+3, two's complement; b = 6: the
- *                      low 4 bits of every code packed as for b = 4 in
- *                      bytes [0, dv/2), then the top 2 bits of the 6-bit
- *                      two's complement form, code j in byte dv/2 + j/4,
- *                      bits 2(j%4)..+1.  Codes lie in [-(2^(b-1)-1),
+ *                      codes of columns 8k..8k+7 form a 48-bit record
+ *                      (column 8k+e in bits 6e..6e+5, two's complement),
+ *                      its bits 0..31 in bytes 4k..4k+3 and its bits
+ *                      32..47 in bytes dv/2+2k, +1.  Codes lie in [-(2^(b-1)-1),
  *                      2^(b-1)-1] (LeapQuant accuracy table: 8, 6 and 4
  *                      bit states), column scales c = m / (2^(b-1)-1).
  *   row_scale   fp32   [B,H,dk]        layout 0 only (smoothing scales s)

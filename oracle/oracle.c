@@ -43,9 +43,9 @@
  *    accuracy table reports), round half to even;
  *  - codes of b < 8 bits are stored packed (orc_pack_codes): 4 bits as two
  *    two's-complement nibbles per byte, even column in the low nibble; 6
- *    bits as that nibble plane of the low 4 bits followed by a plane of
- *    the top 2 bits, four columns per byte, lowest column in the lowest
- *    bits;
+ *    bits as one 48-bit record per block of 8 columns (column 8k+e in bits
+ *    6e..6e+5), the records' low 32 bits in a first plane and their high
+ *    16 bits in a second;
  *  - every codec step is one IEEE fp32 operation rounded to nearest even,
  *    in the order written below, with no fused multiply-add, except the
  *    last: the code is the integer nearest to the exact product
@@ -150,9 +150,10 @@ static int code_qmax(int bits) { return (1 << (bits - 1)) - 1; }
  * in memory; rows follow each other, dv*b/8 bytes apart.
  *   b = 8: one byte per code.
  *   b = 4: code j in byte j/2, bits 4*(j%2)..+3 (two's complement nibble).
- *   b = 6: bytes [0, dv/2): the low 4 bits of code j as for b = 4;
- *          bytes [dv/2, 3dv/4): the top 2 bits of the code's 6-bit two's
- *          complement form, code j in byte dv/2 + j/4, bits 2*(j%4)..+1.
+ *   b = 6: block k = columns 8k..8k+7 forms a 48-bit little-endian record,
+ *          code 8k+e (6-bit two's complement) in record bits 6e..6e+5;
+ *          record bits 0..31 go to bytes 4k..4k+3, bits 32..47 to bytes
+ *          dv/2 + 2k .. dv/2 + 2k + 1.
  * ==================================================================== */
 static void pack_row(int dv, int bits, const int8_t *Q, uint8_t *P)
 {
@@ -162,9 +163,15 @@ static void pack_row(int dv, int bits, const int8_t *Q, uint8_t *P)
         unsigned u = (unsigned)(uint8_t)Q[j];            /* two's complement byte */
         if (bits == 8) {
             P[j] = (uint8_t)u;
-        } else {
+        } else if (bits == 4) {
             P[j / 2] |= (uint8_t)((u & 0xFu) << (4 * (j % 2)));
-            if (bits == 6) P[dv / 2 + j / 4] |= (uint8_t)(((u >> 4) & 0x3u) << (2 * (j % 4)));
+        } else {
+            int k = j / 8, pos = 6 * (j % 8);             /* record bit of the field */
+            for (int t = 0; t < 6; t++) {
+                int rb = pos + t;                         /* record bit */
+                int byte = rb < 32 ? 4 * k + rb / 8 : dv / 2 + 2 * k + (rb - 32) / 8;
+                P[byte] |= (uint8_t)(((u >> t) & 1u) << (rb % 8));
+            }
         }
     }
 }
@@ -172,12 +179,20 @@ static void pack_row(int dv, int bits, const int8_t *Q, uint8_t *P)
 static void unpack_row(int dv, int bits, const uint8_t *P, int8_t *Q)
 {
     for (int j = 0; j < dv; j++) {
-        int v;
+        int v = 0;
         if (bits == 8) {
             v = (int8_t)P[j];
         } else {
-            v = (P[j / 2] >> (4 * (j % 2))) & 0xF;
-            if (bits == 6) v |= ((P[dv / 2 + j / 4] >> (2 * (j % 4))) & 0x3) << 4;
+            if (bits == 4) {
+                v = (P[j / 2] >> (4 * (j % 2))) & 0xF;
+            } else {
+                int k = j / 8, pos = 6 * (j % 8);
+                for (int t = 0; t < 6; t++) {
+                    int rb = pos + t;
+                    int byte = rb < 32 ? 4 * k + rb / 8 : dv / 2 + 2 * k + (rb - 32) / 8;
+                    v |= ((P[byte] >> (rb % 8)) & 1) << t;
+                }
+            }
             if (v >= (1 << (bits - 1))) v -= 1 << bits;  /* sign of the b-bit field */
         }
         Q[j] = (int8_t)v;

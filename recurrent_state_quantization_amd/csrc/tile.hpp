@@ -422,9 +422,10 @@ __device__ __forceinline__ uint32_t pack_low_bytes_u(uint32_t a, uint32_t b, uin
 // row of DV codes takes DV*BITS/8 bytes:
 //   8: one byte per code;
 //   4: code j in byte j/2, bits 4(j%2)..+3;
-//   6: bytes [0, DV/2) hold the low 4 bits of every code as for 4 bits,
-//      bytes [DV/2, 3DV/4) the top 2 bits: code j in byte DV/2 + j/4,
-//      bits 2(j%4)..+1.
+//   6: the 8 codes of columns 8k..8k+7 form a 48-bit record (column 8k+e in
+//      bits 6e..6e+5) whose low 32 bits are bytes 4k..4k+3 and whose high
+//      16 bits are bytes DV/2 + 2k, +1: any code is one signed bit-field
+//      extract (the one straddling the two words, one funnel shift more).
 // A lane's 8 columns 8cb..8cb+7 are one 8-byte word (8 bits), one 4-byte
 // word (4 bits), or a 4-byte and a 2-byte word (6 bits): CodeWord a, b.
 template <int BITS>
@@ -490,10 +491,11 @@ __device__ __forceinline__ void unpack_code8(const CodeWord &w, float (&out)[8])
         for (int e = 0; e < 8; e++) out[e] = (float)((int32_t)(w.a << (28 - 4 * e)) >> 28);
     } else {
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const int32_t hi = (int32_t)(w.b << (30 - 2 * e)) >> 30;   // top 2 bits, signed
-            out[e] = (float)((hi << 4) | (int32_t)((w.a >> (4 * e)) & 0xFu));
-        }
+        for (int e = 0; e < 5; e++) out[e] = (float)((int32_t)(w.a << (26 - 6 * e)) >> 26);
+        const uint32_t mid = __builtin_amdgcn_alignbit(w.b, w.a, 30);   // record bits 30..61
+        out[5] = (float)((int32_t)(mid << 26) >> 26);
+        out[6] = (float)((int32_t)(w.b << 22) >> 26);
+        out[7] = (float)((int32_t)(w.b << 16) >> 26);
     }
 }
 
@@ -509,16 +511,18 @@ __device__ __forceinline__ CodeWord pack_code8(const float (&y)[8])
     if constexpr (BITS == 8) {
         w.a = pack_low_bytes_u(u[0], u[1], u[2], u[3]);
         w.b = pack_low_bytes_u(u[4], u[5], u[6], u[7]);
-    } else {
+    } else if constexpr (BITS == 4) {
         uint32_t n[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) n[i] = (u[2 * i] & 0xFu) | (u[2 * i + 1] << 4);   // low byte: the pair
         w.a = pack_low_bytes_u(n[0], n[1], n[2], n[3]);
         w.b = 0;
-        if constexpr (BITS == 6) {
+    } else {
+        uint32_t f[8];
 #pragma unroll
-            for (int e = 0; e < 8; e++) w.b |= ((u[e] >> 4) & 0x3u) << (2 * e);
-        }
+        for (int e = 0; e < 8; e++) f[e] = u[e] & 0x3Fu;
+        w.a = f[0] | (f[1] << 6) | (f[2] << 12) | (f[3] << 18) | (f[4] << 24) | (f[5] << 30);
+        w.b = (f[5] >> 2) | (f[6] << 4) | (f[7] << 10);
     }
     return w;
 }

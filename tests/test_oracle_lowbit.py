@@ -1,7 +1,8 @@
 """Pins of the oracle's 6- and 4-bit states: the layout-0 codec with code
 width b (codes in [-Qb, Qb], Qb = 2^(b-1) - 1; column scale m/Qb) and the
 packed byte layouts (4 bits: two's complement nibbles, even column low; 6
-bits: a nibble plane of the low 4 bits, then a plane of the top 2 bits).
+bits: a 48-bit record per block of 8 columns, its low 32 bits in a first
+plane, its high 16 bits in a second).
 
 Source: LeapQuant project page, accuracy table (LeapQuant at 8, 6 and 4
 bits).  The code range, the scale and the packing are readings: the pages
@@ -94,8 +95,9 @@ def test_pack_bytes_written_by_hand(orc):
     q4 = np.array([[1, -1, 7, -7, 0, 3, -4, 2]], np.int8)
     assert orc.pack_codes(q4, 4).tolist() == [[0xF1, 0x97, 0x30, 0x2C]]
     q6 = np.array([[1, -1, 31, -31, 16, -16, 0, 5]], np.int8)
-    # low nibbles 1,F,F,1,0,0,0,5; top bits of the 6-bit forms 0,3,1,2,1,3,0,0
-    assert orc.pack_codes(q6, 6).tolist() == [[0xF1, 0x1F, 0x00, 0x50, 0x9C, 0x0D]]
+    # 6-bit fields 01 3F 1F 21 10 30 00 05 at record bits 0, 6, ..., 42:
+    # record 0x140C_1085FFC1 -> plane 1: C1 FF 85 10, plane 2: 0C 14
+    assert orc.pack_codes(q6, 6).tolist() == [[0xC1, 0xFF, 0x85, 0x10, 0x0C, 0x14]]
     assert orc.pack_codes(q4, 8).view(np.int8).tolist() == q4.tolist()
 
 
@@ -114,7 +116,8 @@ def test_pack_round_trip_every_code(orc, bits):
     Q2 = Q.copy()
     Q2[1, 2, 37] = -1       # 0 -> -1 flips every bit of its field, in both planes
     diff = np.argwhere(orc.pack_codes(Q2, bits) != P)
-    expect = {8: [37], 4: [18], 6: [18, 64 + 9]}[bits]
+    # column 37 = block 4, field 5: record bits 30..35 (plane 1 byte 19, plane 2 byte 64 + 8)
+    expect = {8: [37], 4: [18], 6: [19, 64 + 8]}[bits]
     assert sorted(diff[:, 2].tolist()) == expect and np.all(diff[:, :2] == [1, 2])
 
 
