@@ -18,40 +18,49 @@ def _sample(nh, k=12, seed=0):
     return np.unique(np.concatenate([[0, nh - 1], g.choice(nh, k, replace=False)]))
 
 
-def test_prefix_cache_full_size():
-    """32768 pre-filled 128x128 states: quantize all, one fused INT8 step and
-    one fp32-state step over all of them."""
+def _codes(st, nh, rows, dv, bits):
+    """The GPU's packed codes of every head, unpacked by the oracle's layout."""
+    P = host(st["codes"]).view(np.uint8).reshape(nh, rows, dv * bits // 8)
+    return oracle.unpack_codes(P, dv, bits)
+
+
+@pytest.mark.parametrize("bits", [8, 6, 4])
+def test_prefix_cache_full_size(bits):
+    """32768 pre-filled 128x128 states: quantize all, one fused per-step
+    decode (b-bit codes) and one fp32-state step over all of them."""
     torch = torch_cuda()
     g = lib()
     cfg = synth.WORKLOADS["prefix_cache"]
     nh, dk, dv = cfg["B"] * cfg["H"], cfg["dk"], cfg["dv"]
     heads = _sample(nh)
     S = synth.prefill_states(cfg)
-    d = desc_for(cfg)
+    d = desc_for(cfg, bits=bits)
     st = g.alloc_state(d)
     Sd = dev(S)
-    say("prefix_cache full: quantize")
+    say("prefix_cache full: quantize", bits)
     g.gdn_state_quantize(d, Sd, st)
     torch.cuda.synchronize()
-    Q, s, c = oracle.quantize(S[heads])
-    assert np.array_equal(host(st["codes"]).reshape(nh, dk, dv)[heads], Q)
+    Q, s, c = oracle.quantize(S[heads], bits=bits)
+    assert np.array_equal(_codes(st, nh, dk, dv, bits)[heads], Q)
     assert np.array_equal(host(st["row_scale"]).reshape(nh, dk)[heads], s)
     assert np.array_equal(host(st["col_scale"]).reshape(nh, dv)[heads], c)
     inp = synth.step_inputs(cfg, 0)
     args = [dev_io(inp, "q", True), dev_io(inp, "k", True), dev_io(inp, "v", True), dev(inp["a"]),
             dev(inp["b"])]
     o = torch.empty(nh * dv, dtype=torch.bfloat16, device="cuda")
-    say("prefix_cache full: fused step")
+    say("prefix_cache full: fused step", bits)
     g.gdn_quant_decode_step(d, st, *args, o, 0)
     torch.cuda.synchronize()
     sub = {k: v[heads] for k, v in inp.items()}
-    ref = oracle.quant_step(Q, s, c, sub["q"], sub["k"], sub["v"], sub["a"], sub["b"])
+    ref = oracle.quant_step(Q, s, c, sub["q"], sub["k"], sub["v"], sub["a"], sub["b"], bits=bits)
     check_outputs(host_io(o, True).reshape(nh, dv)[heads], ref["o"], True)
-    gQ = host(st["codes"]).reshape(nh, dk, dv)[heads].astype(np.int32)
+    gQ = _codes(st, nh, dk, dv, bits)[heads].astype(np.int32)
     diff = gQ - ref["Q"].astype(np.int32)
     assert np.abs(diff).max() <= 1
     assert not np.any((diff != 0) & ~near_tie_codes(ref["S_f32"], ref["s"], ref["c"], 1e-3))
     np.testing.assert_allclose(host(st["row_scale"]).reshape(nh, dk)[heads], ref["s"], rtol=1e-5)
+    if bits != 8:
+        return
     # fp32-state baseline over all heads
     of = torch.empty(nh * dv, dtype=torch.bfloat16, device="cuda")
     say("prefix_cache full: fp32 step")
@@ -63,8 +72,9 @@ def test_prefix_cache_full_size():
     assert per_head_rel(host(Sd).reshape(nh, dk, dv)[heads], S_ref).max() <= 1e-5
 
 
-@pytest.mark.parametrize("name", ["gdn_serving", "kda", "damp"])
-def test_window_full_size(name):
+@pytest.mark.parametrize("name,bits", [("gdn_serving", 8), ("kda", 8), ("damp", 8), ("gdn_serving", 6),
+                                       ("kda", 4)])
+def test_window_full_size(name, bits):
     """All B*H heads of the window workloads: one full window and its flush.
     Every head starts from a seeded random state encoded by the GPU; the
     sampled heads are overwritten with the oracle's encoding of the same
@@ -77,18 +87,20 @@ def test_window_full_size(name):
     heads = _sample(nh, 8)
     S = synth.random_states(cfg["seed"], nh, dk, dv, scale=0.3)
     hp = None
-    d = desc_for(cfg, flags=g.DEBUG_PREQUANT)
+    d = desc_for(cfg, flags=g.DEBUG_PREQUANT, bits=bits)
     st = g.alloc_state(d)
     if n_hp:
         gr = synth.misc_rng(cfg["seed"], 5)
         hp = np.stack([np.sort(gr.choice(dk, n_hp, replace=False)) for _ in range(nh)]).astype(np.int32)
         st["hp_idx"].copy_(torch.from_numpy(hp.reshape(-1)))
-    say(name, "full: quantize")
+    say(name, "full: quantize", bits)
     g.gdn_state_quantize(d, dev(S), st)
-    enc = oracle.compress(S[heads].astype(np.float64), r, 20, hp_idx=None if hp is None else hp[heads])
+    enc = oracle.compress(S[heads].astype(np.float64), r, 20, hp_idx=None if hp is None else hp[heads],
+                          bits=bits)
     rows = dk - n_hp
-    codes = st["codes"].view(nh, rows * dv)
-    codes[torch.from_numpy(heads).cuda()] = torch.from_numpy(enc["Q"].reshape(len(heads), -1)).cuda()
+    codes = st["codes"].view(nh, rows * dv * bits // 8)
+    codes[torch.from_numpy(heads).cuda()] = torch.from_numpy(
+        oracle.pack_codes(enc["Q"], bits).view(np.int8).reshape(len(heads), -1)).cuda()
     hidx = torch.from_numpy(heads).cuda()
     st["col_scale"].view(nh, dv)[hidx] = torch.from_numpy(enc["c"]).cuda()
     if hp is None:
@@ -100,7 +112,7 @@ def test_window_full_size(name):
     st["comp_v"].view(nh, r * dv)[hidx] = torch.from_numpy(enc["w"].reshape(len(heads), -1)).cuda()
     inp = synth.steps_inputs(cfg, 0, W)
     outs = []
-    say(name, "full: window")
+    say(name, "full: window", bits)
     for t in range(W):
         one = {k: v[t] for k, v in inp.items()}
         o = torch.empty(nh * dv, dtype=torch.bfloat16, device="cuda")
@@ -118,7 +130,7 @@ def test_window_full_size(name):
     o_ref, _, SW = oracle.window(X0, sub["q"], sub["k"], sub["v"], sub["a"], sub["b"])
     for t in range(W):
         check_outputs(host_io(outs[t], True).reshape(nh, dv)[heads], o_ref[t], True)
-    ref = oracle.compress(SW, r, 20, hp_idx=None if hp is None else hp[heads])
+    ref = oracle.compress(SW, r, 20, hp_idx=None if hp is None else hp[heads], bits=bits)
     scale = np.sqrt(np.sum(SW ** 2, axis=(1, 2)))
     R = host(st["prequant_out"]).reshape(nh, dk, dv)[heads].astype(np.float64)
     assert (np.sqrt(np.sum((R - ref["R"]) ** 2, axis=(1, 2))) / scale).max() <= 1e-4
