@@ -103,6 +103,9 @@ typedef struct {
     uint32_t flags;       /* GDNQ_DEBUG_PREQUANT or 0                          */
     int32_t bits;         /* code width b: 8 (0 also means 8), 6 or 4; layout 1
                              keeps 8-bit codes (DAMP: the rest in INT8)        */
+    int32_t hk;           /* key/query heads, dividing H (0 means H): value
+                             head hh reads key head hh / (H / hk) of its batch
+                             entry; q and k are [B,hk,dk]                      */
 } gdnq_desc;
 
 /*
@@ -153,7 +156,7 @@ typedef struct {
 
 /*
  * One decode token for all B*H heads.
- *   q, k   device, io_dtype, [B,H,dk];   v device, io_dtype, [B,H,dv]
+ *   q, k   device, io_dtype, [B,hk,dk] (hk = H unless set); v device, io_dtype, [B,H,dv]
  *   a      device fp32 [B,H] (scalar decay) or [B,H,dk] (channel decay)
  *   b      device fp32 [B,H]
  *   o      device, io_dtype, [B,H,dv]    output o_t = S_t^T q_t
@@ -182,6 +185,32 @@ int gdn_quant_window_flush(const gdnq_desc *desc, const gdnq_state *state, int32
                            void *stream);
 
 /*
+ * Serving pool form of the decode step and the flush, for engines that keep
+ * the states of many requests or cached prefixes in one pool (LeapQuant
+ * project page, opening paragraphs: one recurrent state per cached prefix).
+ * The state arrays hold n_slots*H heads, sized as for a descriptor with
+ * B = n_slots; the call serves desc->B batch entries.  Entry b (0 <= b < B)
+ * uses pool slot slots[b] (device int32 [B]): state head slots[b]*H + hh,
+ * while q, k, v, a, b and o keep the [B,...] layout of the plain call.
+ *   t_pos     device int32 [B]: window position of each entry, 0..W-1
+ *             (window mode; entries may sit at different positions; NULL
+ *             in per-step mode).
+ *   n_tokens  device int32 [B]: tokens to flush for each entry, 1..W; 0
+ *             leaves the entry untouched (so one call can flush the
+ *             entries that reached their window end).
+ * An entry whose slot is outside [0, n_slots), or whose position or token
+ * count is outside its range, is skipped on the device (nothing read or
+ * written for it).  Slots of one call must be distinct: two entries on one
+ * slot race.  The plain calls are the case slots[b] = b, t_pos[b] = t.
+ */
+int gdn_quant_decode_step_pool(const gdnq_desc *desc, const gdnq_state *state, int32_t n_slots,
+                               const int32_t *slots, const int32_t *t_pos, const void *q,
+                               const void *k, const void *v, const float *a, const float *b,
+                               void *o, void *stream);
+int gdn_quant_window_flush_pool(const gdnq_desc *desc, const gdnq_state *state, int32_t n_slots,
+                                const int32_t *slots, const int32_t *n_tokens, void *stream);
+
+/*
  * Encode fp32 states S [B,H,dk,dv] (device): r compensators, then the
  * residual through the codec of desc->layout (layout 1 reads
  * state->hp_idx).  Writes codes, scales, compensators; sets g_cur to 1
@@ -206,7 +235,7 @@ int gdn_state_dequantize(const gdnq_desc *desc, const gdnq_state *state, float *
  * score_i = E_i / max(1 - abar_i, 1e-6).  Writes the n_hp highest-scoring
  * rows per head (lower index first on ties), ascending, to hp_idx_out
  * [B,H,n_hp] int32, and the scores to row_score_out [B,H,dk] fp32 when
- * not NULL.  k, v: io_dtype [n_steps,B,H,dk|dv]; a fp32 [n_steps,B,H] or
+ * not NULL.  k: io_dtype [n_steps,B,hk,dk], v: io_dtype [n_steps,B,H,dv]; a fp32 [n_steps,B,H] or
  * [n_steps,B,H,dk]; b fp32 [n_steps,B,H].  All device pointers.
  */
 int calibrate_scales(const gdnq_desc *desc, const float *S0, const void *k, const void *v,

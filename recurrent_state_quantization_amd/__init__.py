@@ -35,7 +35,7 @@ class GdnqError(RuntimeError):
 class _Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "H", "dk", "dv", "W", "r", "decay", "io_dtype", "layout", "n_hp", "power_iters")]
-    _fields_ += [("flags", ctypes.c_uint32), ("bits", ctypes.c_int32)]
+    _fields_ += [("flags", ctypes.c_uint32), ("bits", ctypes.c_int32), ("hk", ctypes.c_int32)]
 
 
 class _State(ctypes.Structure):
@@ -58,6 +58,7 @@ class Desc:
     power_iters: int = 20
     flags: int = 0
     bits: int = 8
+    hk: int = 0
 
     @property
     def nh(self) -> int:
@@ -83,6 +84,8 @@ def _load():
     sig = {
         "gdn_quant_decode_step": [D, S, P, P, P, P, P, P, i32, P],
         "gdn_quant_window_flush": [D, S, i32, P],
+        "gdn_quant_decode_step_pool": [D, S, i32, P, P, P, P, P, P, P, P, P],
+        "gdn_quant_window_flush_pool": [D, S, i32, P, P, P],
         "gdn_state_quantize": [D, P, S, P],
         "gdn_state_dequantize": [D, S, P, P],
         "calibrate_scales": [D, P, P, P, P, P, i32, P, P, P],
@@ -156,6 +159,19 @@ def gdn_quant_window_flush(desc, state, n_tokens, stream=None):
     st = _state(state)
     _check(lib.gdn_quant_window_flush(ctypes.byref(_desc(desc)), ctypes.byref(st), int(n_tokens),
                                       _stream(stream)))
+
+
+def gdn_quant_decode_step_pool(desc, state, n_slots, slots, t_pos, q, k, v, a, b, o, stream=None):
+    st = _state(state)
+    _check(lib.gdn_quant_decode_step_pool(ctypes.byref(_desc(desc)), ctypes.byref(st), int(n_slots), _ptr(slots),
+                                          _ptr(t_pos), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(o),
+                                          _stream(stream)))
+
+
+def gdn_quant_window_flush_pool(desc, state, n_slots, slots, n_tokens, stream=None):
+    st = _state(state)
+    _check(lib.gdn_quant_window_flush_pool(ctypes.byref(_desc(desc)), ctypes.byref(st), int(n_slots), _ptr(slots),
+                                           _ptr(n_tokens), _stream(stream)))
 
 
 def gdn_state_quantize(desc, S, state, stream=None):

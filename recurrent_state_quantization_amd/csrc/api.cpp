@@ -50,6 +50,7 @@ size_t io_size(const gdnq_desc &d) { return d.io_dtype == GDNQ_IO_BF16 ? 2 : 4; 
 size_t nheads(const gdnq_desc &d) { return (size_t)d.B * (size_t)d.H; }
 bool per_step(const gdnq_desc &d) { return d.W == 1 && d.r == 0; }
 int code_bits(const gdnq_desc &d) { return d.bits == 0 ? 8 : d.bits; }
+size_t nkheads(const gdnq_desc &d) { return (size_t)d.B * (size_t)(d.hk ? d.hk : d.H); }
 
 int check_desc(const gdnq_desc *d)
 {
@@ -78,6 +79,8 @@ int check_desc(const gdnq_desc *d)
         return fail(GDNQ_EINVAL, "bits must be 8, 6 or 4 (0 means 8; got %d)", d->bits);
     if (d->layout == GDNQ_LAYOUT_DAMP && code_bits(*d) != 8)
         return fail(GDNQ_EUNSUPPORTED, "the DAMP layout keeps 8-bit codes (got bits=%d)", d->bits);
+    if (d->hk < 0 || (d->hk > 0 && d->H % d->hk != 0))
+        return fail(GDNQ_EINVAL, "hk must divide H (0 means H; got hk=%d, H=%d)", d->hk, d->H);
     return GDNQ_OK;
 }
 
@@ -170,7 +173,7 @@ int check_step_io(const gdnq_desc &d, const void *q, const void *k, const void *
         const void *p;
         size_t n;
         const char *name;
-    } ins[5] = {{q, nh * d.dk * es, "q"}, {k, nh * d.dk * es, "k"}, {v, nh * d.dv * es, "v"},
+    } ins[5] = {{q, nkheads(d) * d.dk * es, "q"}, {k, nkheads(d) * d.dk * es, "k"}, {v, nh * d.dv * es, "v"},
                 {a, nh * na * 4, "a"}, {b, nh * 4, "b"}};
     for (const In &in : ins) {
         std::vector<Span> tmp = written;
@@ -219,9 +222,9 @@ int gdn_quant_decode_step(const gdnq_desc *desc, const gdnq_state *state, const 
     if ((rc = check_state(d, state, need, spans))) return rc;
     if ((rc = check_step_io(d, q, k, v, a, b, o, spans))) return rc;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (fused) return launched(gdnq::launch_step_fused(d, *state, q, k, v, a, b, o, st));
-    hipError_t e = gdnq::launch_window_step(d, *state, q, k, v, a, b, o, t_in_window, st);
-    if (e == hipSuccess && per_step(d)) e = gdnq::launch_flush(d, *state, 1, st);
+    if (fused) return launched(gdnq::launch_step_fused(d, gdnq::plain_map(d), *state, q, k, v, a, b, o, st));
+    hipError_t e = gdnq::launch_window_step(d, gdnq::plain_map(d), *state, q, k, v, a, b, o, t_in_window, st);
+    if (e == hipSuccess && per_step(d)) e = gdnq::launch_flush(d, gdnq::plain_map(d), *state, 1, st);
     return launched(e);
 }
 
@@ -242,7 +245,67 @@ int gdn_quant_window_flush(const gdnq_desc *desc, const gdnq_state *state, int32
                      (d.flags & GDNQ_DEBUG_PREQUANT) != 0};
     std::vector<Span> spans;
     if ((rc = check_state(d, state, need, spans))) return rc;
-    return launched(gdnq::launch_flush(d, *state, n_tokens, reinterpret_cast<hipStream_t>(stream)));
+    return launched(gdnq::launch_flush(d, gdnq::plain_map(d), *state, n_tokens, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gdn_quant_decode_step_pool(const gdnq_desc *desc, const gdnq_state *state, int32_t n_slots,
+                               const int32_t *slots, const int32_t *t_pos, const void *q, const void *k,
+                               const void *v, const float *a, const float *b, void *o, void *stream)
+{
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (n_slots < 1) return fail(GDNQ_EINVAL, "n_slots must be >= 1 (got %d)", n_slots);
+    if ((long long)n_slots * desc->H > 0x7fffffffLL) return fail(GDNQ_EINVAL, "n_slots*H too large");
+    gdnq_desc pool = *desc;   // the state arrays are sized for n_slots entries
+    pool.B = n_slots;
+    const gdnq_desc &d = *desc;
+    const bool damp = d.layout == GDNQ_LAYOUT_DAMP;
+    const bool fused = per_step(d) && !damp;
+    bool need[11] = {true, !damp, true, d.r > 0, d.r > 0, !fused, !fused, !fused, damp, damp,
+                     fused && (d.flags & GDNQ_DEBUG_PREQUANT)};
+    if (per_step(d) && damp) need[10] = (d.flags & GDNQ_DEBUG_PREQUANT) != 0;
+    std::vector<Span> spans;
+    if ((rc = check_state(pool, state, need, spans))) return rc;
+    if ((rc = check_step_io(d, q, k, v, a, b, o, spans))) return rc;
+    if ((rc = check_buf(slots, (size_t)d.B * 4, "slots", spans))) return rc;
+    if (!per_step(d) && (rc = check_buf(t_pos, (size_t)d.B * 4, "t_pos", spans))) return rc;
+    gdnq::HeadMap m = gdnq::plain_map(d);
+    m.slots = slots;
+    m.n_slots = n_slots;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (fused) return launched(gdnq::launch_step_fused(d, m, *state, q, k, v, a, b, o, st));
+    if (per_step(d)) {   // DAMP per-step: window step at position 0, then a one-token flush
+        hipError_t e = gdnq::launch_window_step(d, m, *state, q, k, v, a, b, o, 0, st);
+        if (e == hipSuccess) e = gdnq::launch_flush(d, m, *state, 1, st);
+        return launched(e);
+    }
+    m.pos = t_pos;
+    return launched(gdnq::launch_window_step(d, m, *state, q, k, v, a, b, o, 0, st));
+}
+
+int gdn_quant_window_flush_pool(const gdnq_desc *desc, const gdnq_state *state, int32_t n_slots,
+                                const int32_t *slots, const int32_t *n_tokens, void *stream)
+{
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (n_slots < 1) return fail(GDNQ_EINVAL, "n_slots must be >= 1 (got %d)", n_slots);
+    if ((long long)n_slots * desc->H > 0x7fffffffLL) return fail(GDNQ_EINVAL, "n_slots*H too large");
+    const gdnq_desc &d = *desc;
+    const bool damp = d.layout == GDNQ_LAYOUT_DAMP;
+    if (per_step(d)) return ok();   // per-step mode has no window to flush
+    gdnq_desc pool = d;
+    pool.B = n_slots;
+    bool need[11] = {true, !damp, true, d.r > 0, d.r > 0, true, true, true, damp, damp,
+                     (d.flags & GDNQ_DEBUG_PREQUANT) != 0};
+    std::vector<Span> spans;
+    if ((rc = check_state(pool, state, need, spans))) return rc;
+    if ((rc = check_buf(slots, (size_t)d.B * 4, "slots", spans))) return rc;
+    if ((rc = check_buf(n_tokens, (size_t)d.B * 4, "n_tokens", spans))) return rc;
+    gdnq::HeadMap m = gdnq::plain_map(d);
+    m.slots = slots;
+    m.pos = n_tokens;
+    m.n_slots = n_slots;
+    return launched(gdnq::launch_flush(d, m, *state, 1, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int gdn_state_quantize(const gdnq_desc *desc, const float *S, const gdnq_state *state, void *stream)
@@ -298,7 +361,7 @@ int calibrate_scales(const gdnq_desc *desc, const float *S0, const void *k, cons
         const void *p;
         size_t n;
         const char *name;
-    } ins[5] = {{S0, nh * d.dk * d.dv * 4, "S0"}, {k, ns * nh * d.dk * es, "k"}, {v, ns * nh * d.dv * es, "v"},
+    } ins[5] = {{S0, nh * d.dk * d.dv * 4, "S0"}, {k, ns * nkheads(d) * d.dk * es, "k"}, {v, ns * nh * d.dv * es, "v"},
                 {a, ns * nh * na * 4, "a"}, {b, ns * nh * 4, "b"}};
     for (const In &in : ins) {
         std::vector<Span> tmp = spans;

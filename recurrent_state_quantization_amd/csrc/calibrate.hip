@@ -21,6 +21,7 @@ struct CalArgs {
     float *score;
     int n_steps, n_hp;
     size_t nh;
+    HeadMap map;   // key heads of k (no pool form)
 };
 
 template <class G>
@@ -36,7 +37,10 @@ __global__ __launch_bounds__(G::NT) void calibrate_kernel(CalArgs A)
 {
     __shared__ CalLds<G> L;
     const Lane c = lane_coords<G>();
-    const size_t h = __builtin_amdgcn_workgroup_id_x();
+    HeadIdx x;
+    map_head(A.map, 0, 0, 0, x);
+    const size_t h = x.in;
+    const size_t nk = A.nh / A.map.H * A.map.HK;   // key heads per step
     constexpr size_t E = (size_t)G::DK * G::DV;
     float P[8][8];
 #pragma unroll
@@ -51,7 +55,7 @@ __global__ __launch_bounds__(G::NT) void calibrate_kernel(CalArgs A)
 #pragma unroll
         for (int k = 0; k < 8; k++) {
             const int i = row_of<G>(c, k);
-            kk[k] = load1<BF16>(A.k, hs * G::DK + i);
+            kk[k] = load1<BF16>(A.k, ((size_t)t * nk + x.key) * G::DK + i);
             av[k] = KDA ? A.a[hs * G::DK + i] : A.a[hs];
         }
         float R[8];
@@ -165,7 +169,7 @@ hipError_t launch_calibrate(const gdnq_desc &d, const float *S0, const void *k, 
                             float *score, hipStream_t st)
 {
     const size_t nh = (size_t)d.B * (size_t)d.H;
-    CalArgs A{S0, k, v, a, b, hp_idx, score, n_steps, d.n_hp, nh};
+    CalArgs A{S0, k, v, a, b, hp_idx, score, n_steps, d.n_hp, nh, plain_map(d)};
     return with_dims(d.dk, d.dv, [&](auto DK, auto DV) {
         using G = Geom<decltype(DK)::value, decltype(DV)::value>;
         return with_bool(d.io_dtype == GDNQ_IO_BF16, [&](auto bf) {

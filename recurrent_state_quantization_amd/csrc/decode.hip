@@ -33,6 +33,7 @@ struct StepArgs {
     float *row_scale, *col_scale;
     float *prequant;  // nullable
     float *S;         // fp32 state (baseline kernel)
+    HeadMap map;
 };
 
 // Column sums of R (retrieval) and O (output) partials plus k.q, reduced to
@@ -71,7 +72,9 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     __shared__ CodecLds<G> L;
     __shared__ StepLds<G> SL;
     const Lane c = lane_coords<G>();
-    const size_t h = __builtin_amdgcn_workgroup_id_x();
+    HeadIdx x;
+    if (!map_head(A.map, 0, 0, 0, x)) return;  // uniform per workgroup, before any barrier
+    const size_t h = x.state, hi = x.in, hk = x.key;
     constexpr size_t E = (size_t)G::DK * G::DV;
     constexpr int RB = code_row_bytes<G, BITS>();
     int8_t *codes = A.codes + h * (size_t)G::DK * RB;
@@ -84,13 +87,13 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     // wrap for t >= DK) so that waiting for them does not wait for the
     // codes, which load meanwhile.
     const int tr = c.t % G::DK;
-    const float ki = load1<BF16>(A.k, h * G::DK + tr);
-    const float qi = load1<BF16>(A.q, h * G::DK + tr);
-    const float ai = KDA ? A.a[h * G::DK + tr] : A.a[h];
+    const float ki = load1<BF16>(A.k, hk * G::DK + tr);
+    const float qi = load1<BF16>(A.q, hk * G::DK + tr);
+    const float ai = KDA ? A.a[hi * G::DK + tr] : A.a[hi];
     const float si = rs[tr];
     // likewise v_j and c_j of the consumer lanes (t < DV; columns wrap)
     const int tc = c.t % G::DV;
-    const float vj = load1<BF16>(A.v, h * G::DV + tc);
+    const float vj = load1<BF16>(A.v, hi * G::DV + tc);
     const float cj = cs[tc];
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the codes'
 
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     for (int k = 0; k < 8; k++) qraw[k] = load_code8<G, BITS, true>(rbase + koff<G>(k) * RB, c.cb);
     float cc[8];
     load_f32x8(cs + c.cb * 8, cc);
-    const float bh = A.b[h];
+    const float bh = A.b[hi];
     float kq_row = 0.0f;
     if (c.t < G::DK) {
         const float asi = ai * si;
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
             kqs += SL.red_kq[w];
         }
         const float u = bh * (vj - cj * Rj);
-        store1<BF16>(A.o, h * G::DV + c.t, fmaf(u, kqs, cj * Oj));
+        store1<BF16>(A.o, hi * G::DV + c.t, fmaf(u, kqs, cj * Oj));
         SL.u[c.t] = u;
     }
     __syncthreads();
@@ -168,7 +171,9 @@ __global__ __launch_bounds__(G::NT) void step_fp32_kernel(StepArgs A)
 {
     __shared__ StepLds<G> SL;
     const Lane c = lane_coords<G>();
-    const size_t h = __builtin_amdgcn_workgroup_id_x();
+    HeadIdx x;
+    map_head(A.map, 0, 0, 0, x);  // no pool form: every entry maps
+    const size_t h = x.in, hk = x.key;
     constexpr size_t E = (size_t)G::DK * G::DV;
     float *S = A.S + h * E;
 
@@ -178,8 +183,8 @@ __global__ __launch_bounds__(G::NT) void step_fp32_kernel(StepArgs A)
 #pragma unroll
     for (int k = 0; k < 8; k++) load_f32x8(Sb + koff<G>(k) * G::DV, X[k]);
     float kk[8], qq[8], av[8];
-    load_rows<G, BF16>(A.k, h * G::DK, row0, kk);
-    load_rows<G, BF16>(A.q, h * G::DK, row0, qq);
+    load_rows<G, BF16>(A.k, hk * G::DK, row0, kk);
+    load_rows<G, BF16>(A.q, hk * G::DK, row0, qq);
     if constexpr (KDA) {
         load_rows_f32<G>(A.a + h * G::DK + row0, av);
     } else {
@@ -237,11 +242,12 @@ __global__ __launch_bounds__(G::NT) void step_fp32_kernel(StepArgs A)
     }
 }
 
-hipError_t launch_step_fused(const gdnq_desc &d, const gdnq_state &s, const void *q, const void *k,
-                             const void *v, const float *a, const float *b, void *o, hipStream_t st)
+hipError_t launch_step_fused(const gdnq_desc &d, const HeadMap &m, const gdnq_state &s, const void *q,
+                             const void *k, const void *v, const float *a, const float *b, void *o,
+                             hipStream_t st)
 {
     StepArgs A{q, k, v, a, b, o, s.codes, s.row_scale, s.col_scale,
-               (d.flags & GDNQ_DEBUG_PREQUANT) ? s.prequant_out : nullptr, nullptr};
+               (d.flags & GDNQ_DEBUG_PREQUANT) ? s.prequant_out : nullptr, nullptr, m};
     const unsigned nh = (unsigned)d.B * (unsigned)d.H;
     return with_dims(d.dk, d.dv, [&](auto DK, auto DV) {
         using G = Geom<decltype(DK)::value, decltype(DV)::value>;
@@ -261,7 +267,7 @@ hipError_t launch_step_fused(const gdnq_desc &d, const gdnq_state &s, const void
 hipError_t launch_step_fp32(const gdnq_desc &d, float *S, const void *q, const void *k, const void *v,
                             const float *a, const float *b, void *o, hipStream_t st)
 {
-    StepArgs A{q, k, v, a, b, o, nullptr, nullptr, nullptr, nullptr, S};
+    StepArgs A{q, k, v, a, b, o, nullptr, nullptr, nullptr, nullptr, S, plain_map(d)};
     const unsigned nh = (unsigned)d.B * (unsigned)d.H;
     return with_dims(d.dk, d.dv, [&](auto DK, auto DV) {
         using G = Geom<decltype(DK)::value, decltype(DV)::value>;

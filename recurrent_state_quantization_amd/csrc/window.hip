@@ -39,6 +39,7 @@ struct WinArgs {
     const uint16_t *hp_rows;
     const int32_t *hp_idx;
     int r, n_hp, W, t;
+    HeadMap map;
 };
 
 // sum over the 16 lanes of a DPP row
@@ -158,7 +159,10 @@ __global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_ke
     static_assert(!DAMP || BITS == 8, "the DAMP layout keeps 8-bit codes");
     __shared__ WinLds<G> L;
     const Lane c = lane_coords<G>();
-    const size_t h = __builtin_amdgcn_workgroup_id_x();
+    HeadIdx x;
+    if (!map_head(A.map, A.t, 0, A.W - 1, x)) return;  // uniform per workgroup, before any barrier
+    const size_t h = x.state, hi = x.in, hk = x.key;  // state, input and key head
+    const int t = x.pos;
     const int n_hp = DAMP ? A.n_hp : 0;
     const int r = A.r;
 
@@ -168,10 +172,10 @@ __global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_ke
     // t >= DK), the scales, the DAMP row indices, then the first slot
     // vectors and the codes.
     const int tr = c.t % G::DK;
-    const float kv = load1<BF16>(A.k, h * G::DK + tr);
-    const float qv = load1<BF16>(A.q, h * G::DK + tr);
-    const float av = KDA ? A.a[h * G::DK + tr] : A.a[h];
-    const float gprev = (A.t == 0) ? 1.0f : (KDA ? A.g_cur[h * G::DK + tr] : A.g_cur[h]);
+    const float kv = load1<BF16>(A.k, hk * G::DK + tr);
+    const float qv = load1<BF16>(A.q, hk * G::DK + tr);
+    const float av = KDA ? A.a[hi * G::DK + tr] : A.a[hi];
+    const float gprev = (t == 0) ? 1.0f : (KDA ? A.g_cur[h * G::DK + tr] : A.g_cur[h]);
     const float srow = DAMP ? 1.0f : A.row_scale[h * G::DK + tr];
     // column scales go through LDS (thread t < DV owns column t) so they
     // hold no registers during the mat-vecs
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_ke
     __builtin_amdgcn_sched_barrier(0);
     // the first slot each 16-lane group dots (key side) and each row group
     // adds (value side); later ones, if any, load in their loops
-    const int NS = r + n_hp + A.t;
+    const int NS = r + n_hp + t;
     constexpr int PER = G::DK / 16;
     const int l16 = c.t & 15;
     float xk[PER];
@@ -320,13 +324,13 @@ __global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_ke
             ret += L.red[w][0][c.t];
             ot += L.red[w][1][c.t];
         }
-        const float u = A.b[h] * (load1<BF16>(A.v, h * G::DV + c.t) - ret);
-        store1<BF16>(A.o, h * G::DV + c.t, fmaf(u, L.alpha[NS], ot));
-        A.buf_u[(h * A.W + A.t) * G::DV + c.t] = u;
+        const float u = A.b[hi] * (load1<BF16>(A.v, hi * G::DV + c.t) - ret);
+        store1<BF16>(A.o, hi * G::DV + c.t, fmaf(u, L.alpha[NS], ot));
+        A.buf_u[(h * A.W + t) * G::DV + c.t] = u;
     }
     if (c.t < G::DK) {
         const float g = L.gs[c.t];
-        A.buf_k[(h * A.W + A.t) * G::DK + c.t] = L.ks[c.t] / g;
+        A.buf_k[(h * A.W + t) * G::DK + c.t] = L.ks[c.t] / g;
         if (KDA) A.g_cur[h * G::DK + c.t] = g;
         else if (c.t == 0) A.g_cur[h] = g;
     }
@@ -342,6 +346,7 @@ struct FlushArgs {
     const int32_t *hp_idx;
     float *prequant;
     int r, n_hp, W, n, iters;
+    HeadMap map;
 };
 
 template <class G>
@@ -393,7 +398,10 @@ __global__ __launch_bounds__(G::NT, (flush_min_blocks<G, DAMP>())) void flush_ke
     __shared__ CodecLds<G> L;
     __shared__ FlushLds<G> F;
     const Lane c = lane_coords<G>();
-    const size_t h = __builtin_amdgcn_workgroup_id_x();
+    HeadIdx x;
+    if (!map_head(A.map, A.n, 1, A.W, x)) return;  // uniform per workgroup, before any barrier
+    const size_t h = x.state;
+    const int n = x.pos;
     const int n_hp = DAMP ? A.n_hp : 0;
     if (!DAMP) A.n_hp = 0;
     if (c.t < G::DK) F.gs[c.t] = KDA ? A.g_cur[h * G::DK + c.t] : A.g_cur[h];
@@ -425,7 +433,7 @@ __global__ __launch_bounds__(G::NT, (flush_min_blocks<G, DAMP>())) void flush_ke
     }
 
     // rank-K update with the slots (compensators, DAMP rows, tokens)
-    const int K = A.r + n_hp + A.n;
+    const int K = A.r + n_hp + n;
     if constexpr (G::DV == 128) {
         // 16x16x4 fp32 MFMA.  MFMA row m of block hb of wave w is tile row
         // w*32 + hb*16 + m; MFMA column n of block nb is tile column
@@ -486,12 +494,12 @@ __global__ __launch_bounds__(G::NT, (flush_min_blocks<G, DAMP>())) void flush_ke
     }
 }
 
-hipError_t launch_window_step(const gdnq_desc &d, const gdnq_state &s, const void *q, const void *k,
-                              const void *v, const float *a, const float *b, void *o, int t_in_window,
-                              hipStream_t st)
+hipError_t launch_window_step(const gdnq_desc &d, const HeadMap &m, const gdnq_state &s, const void *q,
+                              const void *k, const void *v, const float *a, const float *b, void *o,
+                              int t_in_window, hipStream_t st)
 {
     WinArgs A{q, k, v, a, b, o, s.codes, s.row_scale, s.col_scale, s.comp_k, s.comp_v,
-              s.buf_k, s.buf_u, s.g_cur, s.hp_rows, s.hp_idx, d.r, d.n_hp, d.W, t_in_window};
+              s.buf_k, s.buf_u, s.g_cur, s.hp_rows, s.hp_idx, d.r, d.n_hp, d.W, t_in_window, m};
     const unsigned nh = (unsigned)d.B * (unsigned)d.H;
     return with_dims(d.dk, d.dv, [&](auto DK, auto DV) {
         using G = Geom<decltype(DK)::value, decltype(DV)::value>;
@@ -516,11 +524,11 @@ hipError_t launch_window_step(const gdnq_desc &d, const gdnq_state &s, const voi
     });
 }
 
-hipError_t launch_flush(const gdnq_desc &d, const gdnq_state &s, int n_tokens, hipStream_t st)
+hipError_t launch_flush(const gdnq_desc &d, const HeadMap &m, const gdnq_state &s, int n_tokens, hipStream_t st)
 {
     FlushArgs A{s.codes, s.row_scale, s.col_scale, s.comp_k, s.comp_v, s.buf_k, s.buf_u, s.g_cur,
                 s.hp_rows, s.hp_idx, (d.flags & GDNQ_DEBUG_PREQUANT) ? s.prequant_out : nullptr,
-                d.r, d.n_hp, d.W, n_tokens, d.power_iters};
+                d.r, d.n_hp, d.W, n_tokens, d.power_iters, m};
     const unsigned nh = (unsigned)d.B * (unsigned)d.H;
     return with_dims(d.dk, d.dv, [&](auto DK, auto DV) {
         using G = Geom<decltype(DK)::value, decltype(DV)::value>;

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(g):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     out = subprocess.run(["nm", "-D", "--defined-only", g.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -49,7 +49,7 @@ def test_struct_layouts_match_header(g):
     state = re.search(r"typedef struct \{(.*?)\} gdnq_state;", text, re.S).group(1)
     sfields = re.findall(r"\*(\w+);", state)
     assert tuple(sfields) == g.STATE_FIELDS
-    assert ctypes.sizeof(g._Desc) == 13 * 4
+    assert ctypes.sizeof(g._Desc) == 14 * 4
 
 
 FAKE = 1 << 40      # aligned, never dereferenced
@@ -108,6 +108,8 @@ def test_state_sizes(g):
     (dict(bits=5), 1, "bits must"),
     (dict(bits=2), 1, "bits must"),
     (dict(layout=1, n_hp=8, bits=4), 2, "DAMP layout keeps 8-bit"),
+    (dict(H=4, hk=3), 1, "hk must divide H"),
+    (dict(hk=-1), 1, "hk must divide H"),
 ])
 def test_descriptor_errors(g, over, code, msg):
     kw = dict(B=2, H=2)
@@ -193,3 +195,32 @@ def test_prebuilt_structs_marshal_like_dicts(g):
     for state in (bad, g.state_struct(bad)):
         c, m = _err(lambda: g.gdn_quant_decode_step(d.c(), state, *io, 0, stream=0))
         assert c == 1 and "overlaps" in m
+
+
+def test_pool_argument_errors(g):
+    """The pool entry points check the pool-sized state, the per-entry
+    arrays and the shared key heads on the host."""
+    d = g.Desc(B=2, H=4, W=8, r=2, hk=2)
+    pool = g.Desc(B=5, H=4, W=8, r=2, hk=2)            # state sized for 5 slots
+    st = _fake_state(g, pool)
+    io = [FAKE2 + i * (1 << 20) for i in range(6)]
+    slots, tpos = FAKE2 + (64 << 20), FAKE2 + (65 << 20)
+    call = lambda n=5, s=st, sl=slots, tp=tpos: g.gdn_quant_decode_step_pool(d, s, n, sl, tp, *io, stream=0)
+    assert _err(lambda: call(n=0))[0] == 1
+    c, m = _err(lambda: call(sl=None))
+    assert c == 1 and "slots is NULL" in m
+    c, m = _err(lambda: call(tp=None))
+    assert c == 1 and "t_pos is NULL" in m
+    c, m = _err(lambda: call(sl=st["codes"]))
+    assert c == 1 and "overlaps" in m
+    # a state too small for the pool: its arrays overlap one another
+    small = _fake_state(g, d)
+    c, m = _err(lambda: call(s=small))
+    assert c == 1 and "overlaps" in m
+    f = lambda n=5, nt=tpos: g.gdn_quant_window_flush_pool(d, st, n, slots, nt, stream=0)
+    c, m = _err(lambda: f(nt=None))
+    assert c == 1 and "n_tokens is NULL" in m
+    assert _err(lambda: f(n=-3))[0] == 1
+    # per-step mode: no t_pos needed, flush is a no-op
+    dp = g.Desc(B=2, H=4)
+    g.gdn_quant_window_flush_pool(dp, {}, 5, slots, None, stream=0)

@@ -1,0 +1,235 @@
+"""Serving shape through the C ABI: the pool entry points (state slots,
+per-entry window positions and flush lengths, skipped entries) and shared
+key heads (desc.hk < H).
+
+Pool form: every pool call is compared bit for bit with the plain calls on
+twin states (one plain state per entry, holding a copy of that entry's
+slot): the same kernels run either way, so outputs, codes, scales,
+compensators, buffers and gates must be identical; slots no entry uses, and
+entries with an out-of-range slot, position or token count, stay untouched.
+The plain calls are pinned to the oracle by the other GPU tests.
+
+Shared key heads: value head hh reads key head hh / (H / hk); the oracle is
+run with q and k repeated over their value heads (plain data movement in the
+test), with the parity bars of the per-step and window tests.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests._gpu import (check_outputs, desc_for, dev, dev_io, host, host_io, lib, per_head_rel, say,
+                        sub_cfg, torch_cuda)
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("codes", "row_scale", "col_scale", "comp_k", "comp_v", "buf_k", "buf_u", "g_cur", "hp_rows")
+
+
+def _slot_view(st, name, slot, n_slots):
+    t = st[name]
+    per = t.numel() // n_slots
+    return t[slot * per:(slot + 1) * per]
+
+
+def _twin(torch, g, d1, pool_st, slot, n_slots):
+    """A plain one-entry state holding a copy of one pool slot."""
+    st = g.alloc_state(d1)
+    for k in KEYS + ("hp_idx",):
+        if pool_st.get(k) is not None and st.get(k) is not None:
+            st[k].copy_(_slot_view(pool_st, k, slot, n_slots))
+    return st
+
+
+def _bytes_equal(a, b):
+    torch = torch_cuda()
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+def _inputs(torch, cfg, nb, t, bf):
+    inp = synth.step_inputs(dict(cfg, B=nb), t)
+    return inp, [dev_io(inp, "q", bf), dev_io(inp, "k", bf), dev_io(inp, "v", bf), dev(inp["a"]), dev(inp["b"])]
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_pool_per_step(bits):
+    torch = torch_cuda()
+    g = lib()
+    cfg = sub_cfg(synth.WORKLOADS["prefix_cache"], B=1, H=4)
+    H, dk, dv = cfg["H"], cfg["dk"], cfg["dv"]
+    n_slots = 7
+    slots = [5, 0, 3, -1, 9]            # the last two are skipped
+    nb = len(slots)
+    d = desc_for(cfg, B=nb, W=1, r=0, bits=bits)
+    dpool = desc_for(cfg, B=n_slots, W=1, r=0, bits=bits)
+    d1 = desc_for(cfg, B=1, W=1, r=0, bits=bits)
+    S = synth.prefill_states(dict(cfg, B=n_slots), heads=range(n_slots * H))
+    pool = g.alloc_state(dpool)
+    g.gdn_state_quantize(dpool, dev(S), pool)
+    before = {k: pool[k].clone() for k in KEYS if pool.get(k) is not None}
+    twins = {e: _twin(torch, g, d1, pool, s, n_slots) for e, s in enumerate(slots) if 0 <= s < n_slots}
+    inp, args = _inputs(torch, cfg, nb, 0, True)
+    o = torch.full((nb * H * dv,), 7.0, dtype=torch.bfloat16, device="cuda")
+    sl = torch.tensor(slots, dtype=torch.int32, device="cuda")
+    say("pool per-step", bits)
+    g.gdn_quant_decode_step_pool(d, pool, n_slots, sl, None, *args, o)
+    for e, st1 in twins.items():
+        o1 = torch.empty(H * dv, dtype=torch.bfloat16, device="cuda")
+        one = {k: v.reshape(nb, H, -1)[e] for k, v in inp.items()}
+        g.gdn_quant_decode_step(d1, st1, dev_io(one, "q", True), dev_io(one, "k", True), dev_io(one, "v", True),
+                                dev(one["a"]), dev(one["b"]), o1, 0)
+        torch.cuda.synchronize()
+        assert _bytes_equal(o.view(nb, H * dv)[e], o1), e
+        for k in KEYS:
+            if pool.get(k) is not None:
+                assert _bytes_equal(_slot_view(pool, k, slots[e], n_slots), st1[k]), (e, k)
+    torch.cuda.synchronize()
+    used = {s for s in slots if 0 <= s < n_slots}
+    for s in range(n_slots):
+        if s not in used:
+            for k in before:
+                assert _bytes_equal(_slot_view(pool, k, s, n_slots), _slot_view(before, k, s, n_slots)), (s, k)
+    for e, s in enumerate(slots):
+        if not 0 <= s < n_slots:
+            assert torch.all(o.view(nb, H * dv)[e] == 7.0)
+
+
+def test_pool_window_positions_and_flush():
+    """Three entries at different window positions in one call, then one
+    flush call that ends two of the windows (n_tokens = position + 1) and
+    leaves the third untouched (n_tokens = 0)."""
+    torch = torch_cuda()
+    g = lib()
+    cfg = sub_cfg(synth.WORKLOADS["gdn_serving"], B=1, H=3)
+    H, dk, dv, W, r = cfg["H"], cfg["dk"], cfg["dv"], cfg["W"], cfg["r"]
+    n_slots = 6
+    slots = [4, 1, 2]
+    pos = [0, 5, 11]
+    nb = len(slots)
+    d = desc_for(cfg, B=nb)
+    dpool = desc_for(cfg, B=n_slots)
+    d1 = desc_for(cfg, B=1)
+    S = synth.random_states(cfg["seed"], n_slots * H, dk, dv, scale=0.3)
+    pool = g.alloc_state(dpool)
+    g.gdn_state_quantize(dpool, dev(S), pool)
+    twins = {e: _twin(torch, g, d1, pool, s, n_slots) for e, s in enumerate(slots)}
+    say("pool window: history")
+    # each entry's own history: pos[e] tokens through the pool API (one
+    # entry per call) and through the plain API on its twin
+    for e, s in enumerate(slots):
+        for t in range(pos[e]):
+            inp, args = _inputs(torch, cfg, 1, 100 * e + t, True)
+            o = torch.empty(H * dv, dtype=torch.bfloat16, device="cuda")
+            g.gdn_quant_decode_step_pool(desc_for(cfg, B=1), pool, n_slots,
+                                         torch.tensor([s], dtype=torch.int32, device="cuda"),
+                                         torch.tensor([t], dtype=torch.int32, device="cuda"), *args, o)
+            g.gdn_quant_decode_step(d1, twins[e], *args, o, t)
+    torch.cuda.synchronize()
+    say("pool window: mixed positions")
+    inp, args = _inputs(torch, cfg, nb, 999, True)
+    o = torch.empty(nb * H * dv, dtype=torch.bfloat16, device="cuda")
+    g.gdn_quant_decode_step_pool(d, pool, n_slots, torch.tensor(slots, dtype=torch.int32, device="cuda"),
+                                 torch.tensor(pos, dtype=torch.int32, device="cuda"), *args, o)
+    for e in range(nb):
+        one = {k: v.reshape(nb, H, -1)[e] for k, v in inp.items()}
+        o1 = torch.empty(H * dv, dtype=torch.bfloat16, device="cuda")
+        g.gdn_quant_decode_step(d1, twins[e], dev_io(one, "q", True), dev_io(one, "k", True),
+                                dev_io(one, "v", True), dev(one["a"]), dev(one["b"]), o1, pos[e])
+        torch.cuda.synchronize()
+        assert _bytes_equal(o.view(nb, H * dv)[e], o1), e
+        for k in KEYS:
+            if pool.get(k) is not None:
+                assert _bytes_equal(_slot_view(pool, k, slots[e], n_slots), twins[e][k]), (e, k)
+    say("pool window: flush")
+    ntok = [pos[0] + 1, 0, pos[2] + 1]
+    keep = {k: _slot_view(pool, k, slots[1], n_slots).clone() for k in KEYS if pool.get(k) is not None}
+    g.gdn_quant_window_flush_pool(d, pool, n_slots, torch.tensor(slots, dtype=torch.int32, device="cuda"),
+                                  torch.tensor(ntok, dtype=torch.int32, device="cuda"))
+    for e in (0, 2):
+        g.gdn_quant_window_flush(d1, twins[e], ntok[e])
+    torch.cuda.synchronize()
+    for e in (0, 2):
+        for k in KEYS:
+            if pool.get(k) is not None:
+                assert _bytes_equal(_slot_view(pool, k, slots[e], n_slots), twins[e][k]), (e, k)
+    for k, v in keep.items():
+        assert _bytes_equal(_slot_view(pool, k, slots[1], n_slots), v), k
+
+
+def _expand(x, H, hk):
+    """[n, B*hk, d] key-head arrays -> [n, B*H, d]: value head hh reads key head hh // (H/hk)."""
+    n, nk, dd = x.shape
+    B = nk // hk
+    idx = np.array([b * hk + hh // (H // hk) for b in range(B) for hh in range(H)])
+    return x[:, idx]
+
+
+@pytest.mark.parametrize("case", [("prefix_cache", dict(B=2, H=8), 2), ("tiny", dict(H=4), 1)],
+                         ids=["prefix-hk2", "tiny-hk1"])
+def test_shared_key_heads_per_step(case):
+    torch = torch_cuda()
+    g = lib()
+    cfg = sub_cfg(synth.WORKLOADS[case[0]], **case[1])
+    hk = case[2]
+    B, H, dk, dv = cfg["B"], cfg["H"], cfg["dk"], cfg["dv"]
+    nh = B * H
+    bf = cfg["io"] == "bf16"
+    d = desc_for(cfg, W=1, r=0, hk=hk, flags=g.DEBUG_PREQUANT)
+    S = (synth.prefill_states(cfg, heads=range(nh)) if cfg.get("outlier_rows")
+         else synth.random_states(12, nh, dk, dv) * np.float32(0.3))
+    Q, s, c = oracle.quantize(S)
+    st = g.alloc_state(d)
+    st["codes"].copy_(torch.from_numpy(Q.reshape(-1)))
+    st["row_scale"].copy_(torch.from_numpy(s.reshape(-1)))
+    st["col_scale"].copy_(torch.from_numpy(c.reshape(-1)))
+    inp = synth.step_inputs(dict(cfg, H=hk), 5)         # q, k: [B*hk, dk]
+    vab = synth.step_inputs(cfg, 6)                     # v, a, b: per value head
+    o = torch.empty(nh * dv, dtype=torch.bfloat16 if bf else torch.float32, device="cuda")
+    say("shared key heads per-step", case)
+    g.gdn_quant_decode_step(d, st, dev_io(inp, "q", bf), dev_io(inp, "k", bf), dev_io(vab, "v", bf),
+                            dev(vab["a"]), dev(vab["b"]), o, 0)
+    torch.cuda.synchronize()
+    qx, kx = _expand(inp["q"][None], H, hk)[0], _expand(inp["k"][None], H, hk)[0]
+    ref = oracle.quant_step(Q, s, c, qx, kx, vab["v"], vab["a"], vab["b"])
+    check_outputs(host_io(o, bf), ref["o"], bf)
+    assert per_head_rel(host(st["prequant_out"]).reshape(nh, dk, dv), ref["S_pre"]).max() <= 1e-4
+    # the fp32-state kernel reads shared keys the same way
+    Sd = dev(S)
+    of = torch.empty_like(o)
+    g.gdn_fp32_decode_step(d, Sd, dev_io(inp, "q", bf), dev_io(inp, "k", bf), dev_io(vab, "v", bf),
+                           dev(vab["a"]), dev(vab["b"]), of)
+    torch.cuda.synchronize()
+    S_ref, o_ref = oracle.recur(S, qx[None], kx[None], vab["v"][None], vab["a"][None], vab["b"][None])
+    check_outputs(host_io(of, bf), o_ref[0], bf)
+    assert per_head_rel(host(Sd).reshape(nh, dk, dv), S_ref).max() <= 1e-5
+
+
+def test_shared_key_heads_window():
+    torch = torch_cuda()
+    g = lib()
+    cfg = sub_cfg(synth.WORKLOADS["kda"], B=2, H=4)
+    hk = 2
+    B, H, dk, dv, W, r = cfg["B"], cfg["H"], cfg["dk"], cfg["dv"], cfg["W"], cfg["r"]
+    nh = B * H
+    n = 6
+    d = desc_for(cfg, hk=hk)
+    S0 = synth.random_states(cfg["seed"], nh, dk, dv, scale=0.3).astype(np.float64)
+    enc = oracle.compress(S0, r, 20)
+    st = g.alloc_state(d)
+    for k, v in (("codes", enc["Q"]), ("row_scale", enc["s"]), ("col_scale", enc["c"]),
+                 ("comp_k", enc["p"]), ("comp_v", enc["w"])):
+        st[k].copy_(torch.from_numpy(np.ascontiguousarray(v).reshape(-1)))
+    kq = synth.steps_inputs(dict(cfg, H=hk), 0, n)
+    vab = synth.steps_inputs(cfg, 50, n)
+    outs = []
+    say("shared key heads window")
+    for t in range(n):
+        o = torch.empty(nh * dv, dtype=torch.bfloat16, device="cuda")
+        g.gdn_quant_decode_step(d, st, dev_io({"q16": kq["q16"][t]}, "q", True), dev_io({"k16": kq["k16"][t]}, "k", True),
+                                dev_io({"v16": vab["v16"][t]}, "v", True), dev(vab["a"][t]), dev(vab["b"][t]), o, t)
+        outs.append(o)
+    torch.cuda.synchronize()
+    X0 = oracle.state_base(enc["Q"], enc["s"], enc["c"], enc["p"], enc["w"])
+    o_ref, _, _ = oracle.window(X0, _expand(kq["q"], H, hk), _expand(kq["k"], H, hk), vab["v"], vab["a"], vab["b"])
+    for t in range(n):
+        check_outputs(host_io(outs[t], True), o_ref[t], True)
