@@ -235,6 +235,18 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
     S_dev = torch.from_numpy(S).cuda()
     g.gdn_state_quantize(d, S_dev, st)
     o = torch.empty(nh * dv, dtype=torch.bfloat16, device="cuda")
+    slots = None
+    if args.pool:
+        # a pool of args.pool slots; the B entries sit on a seeded random subset
+        if args.pool < cfg["B"]:
+            raise SystemExit("--pool must be at least the batch size")
+        perm = synth.misc_rng(cfg["seed"], 11).permutation(args.pool)[:cfg["B"]]
+        slots = torch.from_numpy(perm.astype(np.int32)).cuda()
+        pst = g.alloc_state(g.Desc(B=args.pool, H=cfg["H"], dk=dk, dv=dv, io_dtype=g.IO_BF16, bits=bits))
+        for name, t in st.items():
+            if t is not None:
+                pst[name].view(args.pool, -1)[slots.long()] = t.view(cfg["B"], -1)
+        st = pst
     torch.cuda.synchronize()
 
     # marshalled once: the loop passes the C structs, raw pointers and the stream
@@ -242,8 +254,14 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
     ptrs = [[t.data_ptr() for t in inp] for inp in dev_inputs]
     o_p, S_p = o.data_ptr(), S_dev.data_ptr()
 
-    def int8_step(i):
-        g.gdn_quant_decode_step(dc, sc, *ptrs[i % n_sets], o_p, 0, sh)
+    if slots is None:
+        def int8_step(i):
+            g.gdn_quant_decode_step(dc, sc, *ptrs[i % n_sets], o_p, 0, sh)
+    else:
+        sl_p = slots.data_ptr()
+
+        def int8_step(i):
+            g.gdn_quant_decode_step_pool(dc, sc, args.pool, sl_p, None, *ptrs[i % n_sets], o_p, sh)
 
     def fp32_step(i):
         g.gdn_fp32_decode_step(dc, S_p, *ptrs[i % n_sets], o_p, sh)
@@ -273,6 +291,7 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
                                f"{'INT8' if bits == 8 else f'{bits}-bit'} decode of every state per step, "
                                "bf16 I/O, scalar gate",
                    "global_batch": cfg["B"], "heads": cfg["H"], "dk": dk, "dv": dv, "bits": bits,
+                   "pool_slots": args.pool or None,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": b8 / per / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": b8 / per / 1e9 / HBM_PEAK_GBS,
@@ -375,6 +394,70 @@ def bench_window(args, torch, g, name):
     if not args.no_diag:
         res["outliers"] = window_outliers(torch, g, d, st, dev_in, o, nh, dk, dv, W, n_hp)
     return res
+
+
+def bench_window_stagger(args, torch, g, name):
+    """Continuous batching on a window workload: entry b sits at window
+    position (b + i) mod W at step i, so 1/W of the entries end their window
+    at every step.  Each step is one pool decode call over all entries (each
+    at its own position) and one pool flush call that flushes the entries at
+    position W-1 (n_tokens = W) and skips the rest (n_tokens = 0).  W steps
+    are captured as one HIP graph and replayed."""
+    cfg = dict(synth.WORKLOADS[name], bits=args.bits)
+    B, H, dk, dv, W, r = cfg["B"], cfg["H"], cfg["dk"], cfg["dv"], cfg["W"], cfg["r"]
+    nh = B * H
+    if cfg.get("n_hp"):
+        raise SystemExit("--stagger: use a workload without DAMP rows")
+    d = g.Desc(B=B, H=H, dk=dk, dv=dv, W=W, r=r, bits=args.bits,
+               decay=g.DECAY_CHANNEL if cfg["decay"] == "channel" else g.DECAY_SCALAR, io_dtype=g.IO_BF16,
+               power_iters=20)
+    st = g.alloc_state(d)
+    S = synth.random_states(cfg["seed"], nh, dk, dv, scale=0.3)
+    g.gdn_state_quantize(d, torch.from_numpy(S).cuda(), st)
+    steps = max(W, (args.steps // W) * W)
+    dev_in = []
+    for t in range(W):
+        inp = synth.step_inputs(cfg, t)
+        bits = lambda n: torch.from_numpy(inp[n + "16"].view(np.int16)).cuda().view(torch.bfloat16)
+        dev_in.append([bits("q"), bits("k"), bits("v"), torch.from_numpy(inp["a"]).cuda(),
+                       torch.from_numpy(inp["b"]).cuda()])
+    o = torch.empty(nh * dv, dtype=torch.bfloat16, device="cuda")
+    slots = torch.arange(B, dtype=torch.int32, device="cuda")
+    tpos = [(torch.arange(B, dtype=torch.int32, device="cuda") + i) % W for i in range(W)]
+    ntok = [torch.where(tp == W - 1, W, 0).to(torch.int32) for tp in tpos]
+
+    def step(i):
+        t = i % W
+        g.gdn_quant_decode_step_pool(d, st, B, slots, tpos[t], *dev_in[t], o)
+        g.gdn_quant_window_flush_pool(d, st, B, slots, ntok[t])
+
+    wall_eager, _ = time_launches(torch, step, steps, W * max(1, args.warmup // W))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(W):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(W):
+            step(i)
+    torch.cuda.synchronize()
+    wall, per = time_launches(torch, lambda i: graph.replay(), steps // W, max(1, args.warmup // W))
+    return {
+        "metric": f"token-head state updates/s, {'INT8' if args.bits == 8 else f'{args.bits}-bit'} "
+                  f"window-mode decode, staggered windows ({name}, 1 GPU)",
+        "value": nh * steps / wall, "unit": "token-head updates/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": wall / steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": f"int{args.bits} state, fp32 math, bf16 q/k/v/o",
+        "data": "synthetic",
+        "config": {"workload": name, "B": B, "H": H, "W": W, "r": r, "bits": args.bits, "decay": cfg["decay"],
+                   "windows": "staggered: entry b at position (b + step) mod W"},
+        "launch": "pool decode + pool flush per step; W steps per HIP graph, replayed",
+        "eager": {"value": nh * steps / wall_eager, "ms_per_step": wall_eager / steps * 1e3},
+        "roofline": None, "cpu_baseline": None,
+    }
 
 
 def capture_window(torch, g, d, st, dev_in, o, W):
@@ -622,6 +705,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--bits", type=int, default=8, choices=[8, 6, 4],
                     help="code width of the quantized state (default 8)")
+    ap.add_argument("--pool", type=int, default=0,
+                    help="prefix_cache: keep the states in a pool of this many slots, the batch on a "
+                         "seeded random subset (pool entry point)")
+    ap.add_argument("--stagger", action="store_true",
+                    help="window workloads: entries at staggered window positions, each step followed "
+                         "by a pool flush of the entries whose window ends (pool entry points)")
     ap.add_argument("--no-graph", action="store_true",
                     help="window workloads: time eager calls only (for counter passes)")
     ap.add_argument("--no-diag", action="store_true",
@@ -671,6 +760,8 @@ def main():
         res = bench_prefix_cache(args, torch, g, *data, cpu)
     elif args.workload == "tiny":
         res = bench_tiny(args, torch, g)
+    elif args.stagger:
+        res = bench_window_stagger(args, torch, g, args.workload)
     else:
         res = bench_window(args, torch, g, args.workload)
     print(json.dumps(res), flush=True)
