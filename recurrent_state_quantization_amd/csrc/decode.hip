@@ -72,29 +72,31 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     __shared__ CodecLds<G> L;
     __shared__ StepLds<G> SL;
     const Lane c = lane_coords<G>();
-    HeadIdx x;
-    if (!map_head(A.map, 0, 0, 0, x)) return;  // uniform per workgroup, before any barrier
-    const size_t h = x.state, hi = x.in, hk = x.key;
     constexpr size_t E = (size_t)G::DK * G::DV;
     constexpr int RB = code_row_bytes<G, BITS>();
-    int8_t *codes = A.codes + h * (size_t)G::DK * RB;
-    float *rs = A.row_scale + h * G::DK;
-    float *cs = A.col_scale + h * G::DV;
 
     // The per-row factors are formed once per row (thread t < DK owns row
     // t; NT >= DK) and shared through LDS instead of by each of the row's
     // NCB lanes.  Their loads are issued first and unconditionally (rows
     // wrap for t >= DK) so that waiting for them does not wait for the
-    // codes, which load meanwhile.
+    // codes, which load meanwhile; the input-side ones go out even before
+    // a pool call's slot is read.
+    HeadIdx x;
+    map_inputs(A.map, x);
+    const size_t hi = x.in, hk = x.key;
     const int tr = c.t % G::DK;
+    const int tc = c.t % G::DV;
     const float ki = load1<BF16>(A.k, hk * G::DK + tr);
     const float qi = load1<BF16>(A.q, hk * G::DK + tr);
     const float ai = KDA ? A.a[hi * G::DK + tr] : A.a[hi];
-    const float si = rs[tr];
-    // likewise v_j and c_j of the consumer lanes (t < DV; columns wrap)
-    const int tc = c.t % G::DV;
     const float vj = load1<BF16>(A.v, hi * G::DV + tc);
-    const float cj = cs[tc];
+    if (!map_state(A.map, 0, 0, 0, x)) return;  // uniform per workgroup, before any barrier
+    const size_t h = x.state;
+    int8_t *codes = A.codes + h * (size_t)G::DK * RB;
+    float *rs = A.row_scale + h * G::DK;
+    float *cs = A.col_scale + h * G::DV;
+    const float si = rs[tr];
+    const float cj = cs[tc];   // v_j and c_j serve the consumer lanes (t < DV; columns wrap)
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the codes'
 
     const int row0 = row0_of<G>(c);

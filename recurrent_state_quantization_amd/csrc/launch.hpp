@@ -17,6 +17,30 @@ constexpr int MAX_W = 256;
 constexpr int MAX_R = 8;
 constexpr int MAX_HP = 64;
 
+// Division of a workgroup index w < 2^31 by a divisor d fixed for the call,
+// without a divide: q = mulhi(w, m) >> (l - 1) with l = ceil(log2 d) and
+// m = ceil(2^(31+l) / d) is exact for every w < 2^31 (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994,
+// Theorem 4.2, with N = 31 dividend bits).  d = 1 is the identity.
+struct Divisor {
+    unsigned d, m, l;
+};
+
+inline Divisor make_divisor(unsigned d)
+{
+    Divisor v{d, 0u, 0u};
+    if (d > 1) {
+        v.l = 32u - (unsigned)__builtin_clz(d - 1u);
+        v.m = (unsigned)(((1ull << (31u + v.l)) + d - 1u) / d);
+    }
+    return v;
+}
+
+__device__ __forceinline__ unsigned div_by(unsigned w, const Divisor &v)
+{
+    return v.d <= 1u ? w : (__umulhi(w, v.m) >> (v.l - 1u));
+}
+
 // Batch entry -> heads of one call.  Input head hi = b*H + hh (the
 // workgroup) reads key head b*HK + hh/(H/HK) and state head slots[b]*H + hh
 // (hi itself when slots is null); pos[b], when given, replaces the call's
@@ -24,39 +48,62 @@ constexpr int MAX_HP = 64;
 struct HeadMap {
     const int32_t *slots, *pos;
     int H, HK, n_slots;
+    Divisor byH, byG;   // H, and the value heads per key head H/HK
 };
 
 struct HeadIdx {
     size_t in, state, key;
+    unsigned b, hh;
     int pos;
 };
 
-// The heads of this workgroup; false: the entry is skipped (slot outside
-// [0, n_slots) or pos outside [lo, hi]).  Uniform per workgroup.
-__device__ __forceinline__ bool map_head(const HeadMap &m, int pos, int lo, int hi, HeadIdx &x)
+// First half: the input and key heads of this workgroup (no memory read),
+// so the input loads can be issued before the slot is known.
+__device__ __forceinline__ void map_inputs(const HeadMap &m, HeadIdx &x)
 {
     const unsigned w = __builtin_amdgcn_workgroup_id_x();
-    if (!m.slots && !m.pos && m.HK == m.H) {   // the plain call: no divisions
-        x.in = x.state = x.key = w;
-        x.pos = pos;
-        return true;
-    }
-    const unsigned b = w / (unsigned)m.H, hh = w % (unsigned)m.H;
     x.in = w;
-    x.key = (size_t)b * m.HK + hh / (unsigned)(m.H / m.HK);
-    long long s = b;
-    if (m.slots) {
-        s = m.slots[b];
-        if (s < 0 || s >= m.n_slots) return false;
+    if (!m.slots && !m.pos && m.HK == m.H) {   // the plain call
+        x.b = 0;
+        x.hh = 0;
+        x.key = w;
+        return;
     }
-    x.state = (size_t)s * m.H + hh;
-    x.pos = m.pos ? m.pos[b] : pos;
+    // uniform values: readfirstlane lets the slot and position reads below
+    // be scalar loads, which do not wait behind the vector loads in flight
+    x.b = __builtin_amdgcn_readfirstlane(div_by(w, m.byH));
+    x.hh = __builtin_amdgcn_readfirstlane(w - x.b * (unsigned)m.H);
+    x.key = (size_t)x.b * m.HK + div_by(x.hh, m.byG);
+}
+
+// Second half: the state head and the entry's position; false: the entry is
+// skipped (slot outside [0, n_slots) or pos outside [lo, hi]).  Uniform per
+// workgroup.
+__device__ __forceinline__ bool map_state(const HeadMap &m, int pos, int lo, int hi, HeadIdx &x)
+{
+    x.state = x.in;
+    x.pos = pos;
+    if (!m.slots && !m.pos) return pos >= lo && pos <= hi;
+    if (m.slots) {
+        const long long s = m.slots[x.b];
+        if (s < 0 || s >= m.n_slots) return false;
+        x.state = (size_t)s * m.H + x.hh;
+    }
+    if (m.pos) x.pos = m.pos[x.b];
     return x.pos >= lo && x.pos <= hi;
+}
+
+__device__ __forceinline__ bool map_head(const HeadMap &m, int pos, int lo, int hi, HeadIdx &x)
+{
+    map_inputs(m, x);
+    return map_state(m, pos, lo, hi, x);
 }
 
 inline HeadMap plain_map(const gdnq_desc &d)
 {
-    return HeadMap{nullptr, nullptr, d.H, d.hk ? d.hk : d.H, d.B};
+    const int hk = d.hk ? d.hk : d.H;
+    return HeadMap{nullptr, nullptr, d.H, hk, d.B, make_divisor((unsigned)d.H),
+                   make_divisor((unsigned)(d.H / hk))};
 }
 
 hipError_t launch_step_fused(const gdnq_desc &d, const HeadMap &m, const gdnq_state &s, const void *q,
