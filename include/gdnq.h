@@ -250,6 +250,31 @@ int gdn_fp32_decode_step(const gdnq_desc *desc, float *S, const void *q, const v
                          const void *v, const float *a, const float *b, void *o, void *stream);
 
 /*
+ * Prefill ("LinQuant: Functional Invariances for Low-Precision Linear
+ * Recurrences", abstract: chunkwise-parallel prefill casts most of the
+ * recurrence as dense matrix products; appendix Table 3, Gated DeltaNet
+ * row).  Runs T tokens of the recurrence for all B*H heads at once, in
+ * chunks of 64 tokens on the matrix cores, and writes every token's output:
+ *   S      device fp32 [B,H,dk,dv], in place: the state before token 0 on
+ *          entry (zeros for a new sequence, gdn_state_dequantize's output to
+ *          continue a cached prefix), the state after token T-1 on return.
+ *   q, k   device bf16 [B,T,hk,dk] (hk = H unless set); v device bf16 [B,T,H,dv]
+ *   a      device fp32 [B,T,H], the scalar gate, 0 < a <= 1 (no bound on
+ *          the product of gates: the chunk form works with log-gates)
+ *   b      device fp32 [B,T,H]
+ *   o      device bf16 [B,T,H,dv], o_t = S_t^T q_t
+ * Supported: io_dtype GDNQ_IO_BF16, decay GDNQ_DECAY_SCALAR, dk == dv (64
+ * or 128); other descriptors return GDNQ_EUNSUPPORTED.  W, r, layout,
+ * n_hp, bits and the state struct play no part.  Products run in bf16 with
+ * fp32 accumulation, fp32 operands split into two bf16 parts, so results
+ * stay near fp32 accuracy.  T == 0 is a no-op (the buffers may be NULL).
+ * Follow with gdn_state_quantize(desc, S, state) to store the prefilled
+ * state in the quantized form for decoding.
+ */
+int gdn_prefill(const gdnq_desc *desc, float *S, const void *q, const void *k, const void *v,
+                const float *a, const float *b, void *o, int32_t T, void *stream);
+
+/*
  * Byte sizes of the 11 gdnq_state arrays for this descriptor, in field
  * order (codes, row_scale, col_scale, comp_k, comp_v, buf_k, buf_u, g_cur,
  * hp_rows, hp_idx, prequant_out); 0 where the array is unused.

@@ -90,9 +90,13 @@ def _load():
         "gdn_state_dequantize": [D, S, P, P],
         "calibrate_scales": [D, P, P, P, P, P, i32, P, P, P],
         "gdn_fp32_decode_step": [D, P, P, P, P, P, P, P, P],
+        "gdn_prefill": [D, P, P, P, P, P, P, P, i32, P],
         "gdnq_state_sizes": [D, ctypes.POINTER(ctypes.c_size_t * 11)],
     }
     for name, args in sig.items():
+        if not hasattr(lib, name):
+            raise ImportError(f"{LIB_PATH} does not export {name}: it predates its sources; rebuild it "
+                              "with __graft_entry__.build()")
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = ctypes.c_int
@@ -192,6 +196,11 @@ def calibrate_scales(desc, S0, k, v, a, b, n_steps, hp_idx_out, row_score_out=No
 def gdn_fp32_decode_step(desc, S, q, k, v, a, b, o, stream=None):
     _check(lib.gdn_fp32_decode_step(ctypes.byref(_desc(desc)), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
                                     _ptr(b), _ptr(o), _stream(stream)))
+
+
+def gdn_prefill(desc, S, q, k, v, a, b, o, T, stream=None):
+    _check(lib.gdn_prefill(ctypes.byref(_desc(desc)), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                           _ptr(o), int(T), _stream(stream)))
 
 
 # --------------------------------------------------------------- plumbing

@@ -383,4 +383,33 @@ int gdn_fp32_decode_step(const gdnq_desc *desc, float *S, const void *q, const v
     return launched(gdnq::launch_step_fp32(d, S, q, k, v, a, b, o, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int gdn_prefill(const gdnq_desc *desc, float *S, const void *q, const void *k, const void *v, const float *a,
+                const float *b, void *o, int32_t T, void *stream)
+{
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    const gdnq_desc &d = *desc;
+    if (d.io_dtype != GDNQ_IO_BF16) return fail(GDNQ_EUNSUPPORTED, "gdn_prefill takes bf16 q, k, v and o");
+    if (d.decay != GDNQ_DECAY_SCALAR) return fail(GDNQ_EUNSUPPORTED, "gdn_prefill implements the scalar gate");
+    if (d.dk != d.dv) return fail(GDNQ_EUNSUPPORTED, "gdn_prefill needs dk == dv (got %d, %d)", d.dk, d.dv);
+    if (T < 0) return fail(GDNQ_EINVAL, "T must be >= 0 (got %d)", T);
+    const size_t nh = nheads(d), nt = (size_t)T;
+    if (nt * nh > 0x7fffffffULL) return fail(GDNQ_EINVAL, "B*T*H too large");
+    std::vector<Span> spans;
+    if ((rc = check_buf(S, nh * d.dk * d.dv * 4, "S", spans))) return rc;
+    if ((rc = check_buf(o, nt * nh * d.dv * 2, "o", spans, T == 0))) return rc;
+    struct In {
+        const void *p;
+        size_t n;
+        const char *name;
+    } ins[5] = {{q, nt * nkheads(d) * d.dk * 2, "q"}, {k, nt * nkheads(d) * d.dk * 2, "k"},
+                {v, nt * nh * d.dv * 2, "v"}, {a, nt * nh * 4, "a"}, {b, nt * nh * 4, "b"}};
+    for (const In &in : ins) {
+        std::vector<Span> tmp = spans;
+        if ((rc = check_buf(in.p, in.n, in.name, tmp, T == 0))) return rc;
+    }
+    if (T == 0) return ok();
+    return launched(gdnq::launch_prefill(d, S, q, k, v, a, b, o, T, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(g):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     out = subprocess.run(["nm", "-D", "--defined-only", g.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -224,3 +224,30 @@ def test_pool_argument_errors(g):
     # per-step mode: no t_pos needed, flush is a no-op
     dp = g.Desc(B=2, H=4)
     g.gdn_quant_window_flush_pool(dp, {}, 5, slots, None, stream=0)
+
+
+def test_prefill_argument_errors(g):
+    """gdn_prefill: unsupported descriptors, T < 0, NULL and overlapping
+    buffers are refused on the host; T = 0 returns without a launch."""
+    d = g.Desc(B=2, H=4, io_dtype=g.IO_BF16, hk=2)
+    S = FAKE
+    io = [FAKE2 + i * (64 << 20) for i in range(6)]     # q, k, v, a, b, o
+    call = lambda desc=d, s=S, args=io, T=16: g.gdn_prefill(desc, s, *args, T, stream=0)
+    for over, msg in ((dict(io_dtype=g.IO_F32), "bf16"), (dict(decay=g.DECAY_CHANNEL), "scalar gate"),
+                      (dict(dv=64), "dk == dv")):
+        dd = g.Desc(B=2, H=4, io_dtype=g.IO_BF16, hk=2)
+        for k, v in over.items():
+            setattr(dd, k, v)
+        c, m = _err(lambda: call(desc=dd))
+        assert c == 2 and msg in m, m
+    c, m = _err(lambda: call(T=-1))
+    assert c == 1 and "T must be" in m
+    args = list(io)
+    args[1] = None
+    c, m = _err(lambda: call(args=args))
+    assert c == 1 and "k is NULL" in m
+    args = list(io)
+    args[5] = S + 4096
+    c, m = _err(lambda: call(args=args))
+    assert c == 1 and "o overlaps S" in m
+    g.gdn_prefill(d, S, None, None, None, None, None, None, 0, stream=0)   # T = 0: no launch
