@@ -12,7 +12,7 @@ the decode kernel against 8 TB/s HBM, and the plain fp64 CPU oracle timed
 on a bounded sample of the same workload).
 
     python bench.py [--steps 100] [--warmup 200] [--gpus 1]
-                    [--workload prefix_cache|gdn_serving|kda|damp|tiny]
+                    [--workload prefix_cache|gdn_serving|kda|damp|tiny|prefill]
                     [--no-cpu] [--no-graph] [--no-diag] [--bits 8|6|4] [--copy-calibration]
 """
 from __future__ import annotations
@@ -39,12 +39,29 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def src_hash() -> str:
-    """Hash of the kernel sources, to tell whether stored counters still
-    describe the current kernels."""
+# the sources each kernel family is compiled from (the launcher prototypes in
+# launchers.hpp and the host checks in api.cpp do not change device code)
+KERNEL_SOURCES = {
+    "step": ("decode.hip", "tile.hpp", "codec.hpp", "launch.hpp"),
+    "window": ("window.hip", "tile.hpp", "codec.hpp", "launch.hpp"),
+    "prefill": ("prefill.hip", "launch.hpp"),
+}
+
+
+def kernel_family(tag: str) -> str:
+    if tag.startswith("step_"):
+        return "step"
+    if tag.startswith(("window_step", "flush")):
+        return "window"
+    return "prefill"
+
+
+def src_hash(family: str) -> str:
+    """Hash of one kernel family's sources, to tell whether stored counters
+    still describe the current kernels."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "recurrent_state_quantization_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES[family]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -89,6 +106,32 @@ def flush_bytes(cfg: dict, n: int) -> int:
     return 2 * (state + comps) + n * 4 * (dk + dv) + 8 * na
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+
+
+def prefill_chunk_flops(D: int, C: int = 64) -> int:
+    """Algorithmic flops of one C-token chunk of one head in the chunk form
+    (each product of the form counted once; the second bf16 parts that keep
+    fp32 accuracy are not counted): K K^T and Q K^T on the 10 lower 16x16
+    tiles, the triangular inverse (forward substitution on four 16x16
+    blocks, then 4 + 12 block products), W and U (C x C x D each),
+    U - W S and Q S (C x D x D each), the causal P U' (6 of 8 32-token
+    blocks) and the state update (D x C x D)."""
+    gram = 2 * 10 * 16 * 16 * D * 2
+    inv = 2 * (4 * 16 * 120 + 16 * 16 * 16 * 16)
+    return gram + inv + 2 * (2 * C * C * D) + 2 * (2 * C * D * D) + (6 * C * C * D * 2) // 8 + 2 * D * C * D
+
+
+def prefill_bytes(cfg: dict, T: int) -> int:
+    """Algorithmic HBM bytes of one prefill call: q, k, v read and o written
+    once (bf16), a and b read once, each head's fp32 state read and written
+    once."""
+    B, H, D = cfg["B"], cfg["H"], cfg["dk"]
+    hk = cfg.get("hk", H)
+    per_token = B * (hk * 2 * D * 2 + H * (2 * D * 2 + 8))
+    return T * per_token + B * H * 2 * D * D * 4
+
+
 def stored_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel sources."""
@@ -98,7 +141,7 @@ def stored_traffic(kernel: str, workload: str):
     with open(path) as f:
         data = json.load(f)
     ent = data.get(workload, {}).get(kernel)
-    if not ent or ent.get("src_hash") != src_hash():
+    if not ent or ent.get("src_hash") != src_hash(kernel_family(kernel)):
         return None
     return ent["bytes_per_launch"]
 
@@ -308,6 +351,73 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
     res["device_copy"] = device_copy(torch)
     res["roofline"]["frac_of_device_copy"] = res["roofline"]["achieved"] / res["device_copy"]["GBs"]
     res.update(cpu or {"cpu_baseline": None})
+    return res
+
+
+def prefill_data():
+    cfg = synth.WORKLOADS["prefill"]
+    log(f"generating {cfg['T']} tokens x {cfg['B'] * cfg['H']} heads of prefill input")
+    return cfg, synth.token_major_inputs(cfg, cfg["T"])
+
+
+def cpu_prefill_baseline(cfg: dict, x: dict, budget_s: float = 10.0) -> dict:
+    """The oracle's sequential recurrence (fp64, one thread) on the first 8
+    heads of sequence 0, 128 tokens at a time until the time budget is
+    spent."""
+    import oracle
+
+    D, nh, step = cfg["dk"], 8, 128
+    S = np.zeros((nh, D, D), np.float32)
+    done, t, t0 = 0, 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and t < cfg["T"]:
+        n = min(step, cfg["T"] - t)
+        f = lambda name: np.ascontiguousarray(synth.bf16_to_f32(x[name][0, t:t + n, :nh]))
+        S, _ = oracle.recur(S, f("q16"), f("k16"), f("v16"), x["a"][0, t:t + n, :nh, None], x["b"][0, t:t + n, :nh])
+        t += n
+        done += n * nh
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "token-head updates/s", "cores": 1, "kind": "oracle",
+            "sample": f"heads 0-7 of sequence 0, tokens 0-{t - 1} of the sequential recurrence in fp64 "
+                      f"({done} token-head updates) in {dt:.1f} s, one thread"}
+
+
+def bench_prefill(args, torch, g, cfg, x, cpu):
+    B, H, D, T = cfg["B"], cfg["H"], cfg["dk"], cfg["T"]
+    nh = B * H
+    bits = lambda n: torch.from_numpy(x[n].view(np.int16)).cuda().view(torch.bfloat16)
+    q, k, v = bits("q16"), bits("k16"), bits("v16")
+    a, b = torch.from_numpy(x["a"]).cuda(), torch.from_numpy(x["b"]).cuda()
+    S = torch.zeros((nh, D, D), dtype=torch.float32, device="cuda")
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    d = g.Desc(B=B, H=H, dk=D, dv=D, io_dtype=g.IO_BF16)
+    dc, sh = d.c(), torch.cuda.current_stream().cuda_stream
+    p = [t.data_ptr() for t in (S, q, k, v, a, b, o)]
+
+    def call(i):
+        g.gdn_prefill(dc, *p, T, sh)
+
+    log("timing the prefill")
+    wall, per = time_launches(torch, call, args.steps, args.warmup)
+    flops = prefill_chunk_flops(D) * nh * ((T + 63) // 64)
+    nbytes = prefill_bytes(cfg, T)
+    res = {
+        "metric": "token-head state updates/s, chunkwise GDN prefill (1 GPU)",
+        "value": nh * T * args.steps / wall, "unit": "token-head updates/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 q/k/v/o, bf16 MFMA with split fp32 operands, fp32 state",
+        "data": "synthetic (seeded; no weights)",
+        "config": {"workload": f"prefill: B={B} sequences x H={H} heads x T={T} tokens, dk=dv={D}, "
+                               "bf16 I/O, scalar gate, zero initial state", "B": B, "H": H, "T": T, "dk": D},
+        "roofline": {"bound": "mfma", "achieved": flops / per / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flops / per / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": stored_traffic("prefill", "prefill"),
+                     "kernel": f"prefill_kernel<{D}>", "algorithmic_flops_per_launch": flops,
+                     "mean_launch_s": per},
+        "hbm": {"algorithmic_bytes_per_launch": nbytes, "achieved_GBs": nbytes / per / 1e9,
+                "frac": nbytes / per / 1e9 / HBM_PEAK_GBS},
+    }
+    res.update({"cpu_baseline": cpu})
     return res
 
 
@@ -627,14 +737,14 @@ def summarize_pmc(fetch_db: str, write_db: str, copy_fetch_db: str, copy_write_d
             continue
         b = fetch[k] * 1024 * fscale + write[k] * 1024 * wscale
         lines.append(f"| {k} | {fetch[k]:.1f} | {write[k]:.1f} | {b:.4g} |")
-        for tag in ("step_fused", "step_fp32", "window_step", "flush"):
+        for tag in ("step_fused", "step_fp32", "window_step", "flush", "prefill"):
             if f"gdnq::{tag}_kernel" in k:
                 # the code width is the last template argument of the b-bit kernels
                 last = k.rstrip(">").split(",")[-1].strip()
-                if tag != "step_fp32" and last in ("6", "4"):
+                if tag not in ("step_fp32", "prefill") and last in ("6", "4"):
                     tag += "_b" + last
                 data.setdefault(workload, {})[tag] = {
-                    "bytes_per_launch": b, "src_hash": src_hash(), "fetch_kib": fetch[k],
+                    "bytes_per_launch": b, "src_hash": src_hash(kernel_family(tag)), "fetch_kib": fetch[k],
                     "write_kib": write[k], "fetch_scale": fscale, "write_scale": wscale}
     with open(path, "w") as f:
         json.dump(data, f, indent=1)
@@ -701,7 +811,7 @@ def main():
     # clocks; the first calls after start-up run up to ~40% slower
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="prefix_cache",
-                    choices=["prefix_cache", "gdn_serving", "kda", "damp", "tiny"])
+                    choices=["prefix_cache", "gdn_serving", "kda", "damp", "tiny", "prefill"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--bits", type=int, default=8, choices=[8, 6, 4],
                     help="code width of the quantized state (default 8)")
@@ -746,6 +856,12 @@ def main():
         if not args.no_cpu:
             log("timing the CPU oracle")
             cpu = cpu_baselines(*data)
+    if args.workload == "prefill" and not args.copy_calibration:
+        data = prefill_data()
+        cpu = None
+        if not args.no_cpu:
+            log("timing the CPU oracle")
+            cpu = cpu_prefill_baseline(*data)
     import torch
 
     import recurrent_state_quantization_amd as g
@@ -758,6 +874,8 @@ def main():
         return
     if args.workload == "prefix_cache":
         res = bench_prefix_cache(args, torch, g, *data, cpu)
+    elif args.workload == "prefill":
+        res = bench_prefill(args, torch, g, *data, cpu)
     elif args.workload == "tiny":
         res = bench_tiny(args, torch, g)
     elif args.stagger:

@@ -24,7 +24,7 @@ LIB = os.path.join(HERE, "libgdnq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "decode.hip", "window.hip", "codec.hip", "calibrate.hip", "prefill.hip"]
-HEADERS = ["tile.hpp", "codec.hpp", "launch.hpp"]
+HEADERS = ["tile.hpp", "codec.hpp", "launch.hpp", "launchers.hpp"]
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -11,6 +11,7 @@
 
 #include "gdnq.h"
 #include "launch.hpp"
+#include "launchers.hpp"
 
 namespace {
 

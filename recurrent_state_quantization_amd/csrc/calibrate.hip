@@ -10,6 +10,7 @@
 // keep the n_hp highest scores (lower index first on ties), ascending.
 #include "codec.hpp"
 #include "launch.hpp"
+#include "launchers.hpp"
 
 namespace gdnq {
 

@@ -10,6 +10,7 @@
 // the fixed state of a window start.
 #include "codec.hpp"
 #include "launch.hpp"
+#include "launchers.hpp"
 
 namespace gdnq {
 

@@ -22,6 +22,7 @@
 // fp32-state kernel keeps ordinary accesses: the hint slows it by ~30%.
 #include "codec.hpp"
 #include "launch.hpp"
+#include "launchers.hpp"
 
 namespace gdnq {
 

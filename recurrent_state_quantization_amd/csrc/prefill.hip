@@ -12,7 +12,8 @@
 // its gated variant, Yang, Kautz and Hatamizadeh, "Gated Delta Networks",
 // 2024), restated for this state orientation.  For a chunk of C tokens with
 // g_i = sum_{t<=i} log a_t counted from the chunk start, Gam_ij = e^{g_i-g_j}
-// (i >= j), beta = b and S the state at the chunk start:
+// (i >= j), beta = b and S the state at the chunk start (the kernel keeps
+// the gates as base-2 logarithms and uses the hardware log2/exp2):
 //     A  = strictly lower part of diag(beta) (K K^T . Gam)
 //     T  = (I + A)^{-1}
 //     W  = T diag(beta e^g) K,        U = T diag(beta) V
@@ -44,6 +45,7 @@
 #include <hip/hip_runtime.h>
 
 #include "launch.hpp"
+#include "launchers.hpp"
 
 namespace gdnq {
 namespace {
@@ -54,6 +56,69 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 64;  // tokens per chunk
+
+__device__ __forceinline__ floatx4 mma(bf16x8 a, bf16x8 b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mma4(float a, float b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within rows of 16
+// lanes, then the last lane of rows 0 and 2 into rows 1 and 3, then lane 31
+// into rows 2 and 3 (DPP row_shr, row_bcast:15, row_bcast:31).
+__device__ __forceinline__ float scan64(float x)
+{
+#define GDNQ_DPP(x, ctrl, rmask) \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, rmask, 0xf, true))
+    x += GDNQ_DPP(x, 0x111, 0xf);  // row_shr:1
+    x += GDNQ_DPP(x, 0x112, 0xf);  // row_shr:2
+    x += GDNQ_DPP(x, 0x114, 0xf);  // row_shr:4
+    x += GDNQ_DPP(x, 0x118, 0xf);  // row_shr:8
+    x += GDNQ_DPP(x, 0x142, 0xa);  // row_bcast:15 into rows 1, 3
+    x += GDNQ_DPP(x, 0x143, 0xc);  // row_bcast:31 into rows 2, 3
+#undef GDNQ_DPP
+    return x;
+}
+
+// element e of h and l <- the two bf16 parts of x
+template <class V>
+__device__ __forceinline__ void split(float x, V &h, V &l, int e)
+{
+    const __bf16 hi = (__bf16)x;
+    h[e] = hi;
+    l[e] = (__bf16)(x - (float)hi);
+}
+
+// Operand in the permuted slot order: 4 values at p, then 4 at p + 16.
+__device__ __forceinline__ bf16x8 ld_pair(const __bf16 *p)
+{
+    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+    const bf16x4 y = *reinterpret_cast<const bf16x4 *>(p + 16);
+    return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+
+__device__ __forceinline__ bf16x8 ld8(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+__device__ __forceinline__ u32x4 keep(u32x4 x, bool ok) { return ok ? x : u32x4{0u, 0u, 0u, 0u}; }
+
+// one thread's share of a chunk's inputs, held in registers while the
+// previous chunk is computed
+struct ChunkRegs {
+    u32x4 k[4], q[4], v[4];
+    float a, b;
+};
+
+// Lower 16x16 tiles (I >= J) of a 64x64 chunk matrix, job n -> (I, J) from
+// nibble n of two constants (a table in memory would be a vector load, and
+// its wait would also wait for the next chunk's prefetch issued before it).
+__device__ __forceinline__ int tile_i(int n) { return (int)((0x3333222110ull >> (4 * n)) & 15u); }
+__device__ __forceinline__ int tile_j(int n) { return (int)((0x3210210100ull >> (4 * n)) & 15u); }
+
+}  // namespace
 
 template <int D>
 struct PrefillLds {
@@ -89,52 +154,20 @@ struct PrefillArgs {
     Divisor byH, byG;
 };
 
-__device__ __forceinline__ floatx4 mma(bf16x8 a, bf16x8 b, floatx4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ floatx4 mma4(float a, float b, floatx4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// element e of h and l <- the two bf16 parts of x
-template <class V>
-__device__ __forceinline__ void split(float x, V &h, V &l, int e)
-{
-    const __bf16 hi = (__bf16)x;
-    h[e] = hi;
-    l[e] = (__bf16)(x - (float)hi);
-}
-
-// Operand in the permuted slot order: 4 values at p, then 4 at p + 16.
-__device__ __forceinline__ bf16x8 ld_pair(const __bf16 *p)
-{
-    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
-    const bf16x4 y = *reinterpret_cast<const bf16x4 *>(p + 16);
-    return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-}
-
-__device__ __forceinline__ bf16x8 ld8(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
-
-// Lower 16x16 tiles (I >= J) of a 64x64 chunk matrix.
-__constant__ unsigned char kTileI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ unsigned char kTileJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
 template <int D>
-__global__ __launch_bounds__(D * 4, 1) void prefill_kernel(PrefillArgs A)
+__global__ __launch_bounds__(D * 2, 1) void prefill_kernel(PrefillArgs A)
 {
     using Lds = PrefillLds<D>;
     constexpr int SD = Lds::SD, SC = Lds::SC, SF = Lds::SF;
-    constexpr int NW = D / 16, NT = NW * 64;
-    constexpr int KB = D / 32;  // 32-wide blocks along a head dim
-    constexpr int DT = D / 16;  // 16-row tiles along a head dim
-    static_assert(NT == CH * D / 16, "one 16-byte piece per thread per token pair");
+    constexpr int NW = D / 32, NT = NW * 64;  // waves; wave w owns value columns 32w..32w+31
+    constexpr int KB = D / 32;                // 32-wide blocks along a head dim
+    constexpr int DT = D / 16;                // 16-row tiles along a head dim
+    static_assert(DT == 2 * NW, "two key-row tiles of W per wave");
     __shared__ Lds L;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lg = lane >> 4, ln = lane & 15;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const unsigned bh = blockIdx.x;
     const unsigned bb = div_by(bh, A.byH), hh = bh - bb * (unsigned)A.H;
     const unsigned kh = div_by(hh, A.byG);  // key head within the batch entry
@@ -147,7 +180,8 @@ __global__ __launch_bounds__(D * 4, 1) void prefill_kernel(PrefillArgs A)
     const float *ag = A.a + (size_t)bb * T * A.H + hh;
     const float *bg = A.b + (size_t)bb * T * A.H + hh;
     float *Sg = A.S + (size_t)bh * D * D;
-    const int e0 = 16 * wave;  // this wave's value columns
+    const int e0 = 32 * wave;  // value columns e0 + 16 et + ln, et = 0, 1
+    int lg = (tid & 63) >> 4, ln = tid & 15;
 
     // P's upper tiles are never written: clear them once.
     for (int x = tid; x < CH * SC; x += NT) {
@@ -155,120 +189,146 @@ __global__ __launch_bounds__(D * 4, 1) void prefill_kernel(PrefillArgs A)
         L.pl[x] = (__bf16)0.0f;
     }
 
-    // state columns e0..e0+15: S[dt][r] = S[16dt + 4lg + r][e0 + ln]
-    floatx4 S[DT];
+    // S[et][dt][r] = S[16 dt + 4 lg + r][e0 + 16 et + ln] (MFMA accumulator layout)
+    floatx4 S[2][DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; dt++)
+    for (int et = 0; et < 2; et++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) S[dt][r] = Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + ln];
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                S[et][dt][r] = Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + 16 * et + ln];
 
-    // chunk loads: thread -> tokens 2p, 2p+1 (p = tid % 32), columns 8c..8c+7 (c = tid / 32)
-    const int jp = 2 * (tid & 31), cp = 8 * (tid >> 5);
-    u32x4 rk[2], rq[2], rv[2];
-    float ra = 1.0f, rb = 0.0f;
-    auto load = [&](int c0) {
+    // identity operands of the transposes: eye[h] holds B[k][n] = (k == n + 16 h)
+    bf16x8 eye[2];
 #pragma unroll
-        for (int s = 0; s < 2; s++) {
-            const int t = c0 + jp + s;
-            if (t < T) {
-                rk[s] = *reinterpret_cast<const u32x4 *>(kg + (size_t)t * tk + cp);
-                rq[s] = *reinterpret_cast<const u32x4 *>(qg + (size_t)t * tk + cp);
-                rv[s] = *reinterpret_cast<const u32x4 *>(vg + (size_t)t * tv + cp);
-            } else {
-                rk[s] = rq[s] = rv[s] = u32x4{0u, 0u, 0u, 0u};
-            }
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) eye[h][i] = (__bf16)(8 * lg + i == ln + 16 * h ? 1.0f : 0.0f);
+
+    // Chunk loads.  Wave w takes pieces p = 4w..4w+3 of each of K, Q, V: token
+    // group p / KB (16 tokens), channel block p % KB (32 channels); lane
+    // (lg, ln) takes token 16 tg + ln, channels 32 db + 8 lg .. +7, i.e. a
+    // 16 x 32 tile in the A-operand layout, 64 contiguous bytes per token.
+    // Lanes of wave 0 also take the gate and beta of token lane.  Every load
+    // is unconditional (rows past the end are clamped) and those rows are
+    // zeroed only when staged, so the compiler counts the loads and waits for
+    // them at staging alone.
+    auto load = [=](int c0, int which, ChunkRegs &r) {
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            const int p = 4 * wave + s, tg = p / KB, db = p % KB;
+            const size_t u = (size_t)min(c0 + 16 * tg + ln, T - 1);
+            const int off = 32 * db + 8 * lg;
+            if (which == 0) r.k[s] = *reinterpret_cast<const u32x4 *>(kg + u * tk + off);
+            if (which == 1) r.q[s] = *reinterpret_cast<const u32x4 *>(qg + u * tk + off);
+            if (which == 2) r.v[s] = *reinterpret_cast<const u32x4 *>(vg + u * tv + off);
         }
-        if (tid < CH) {
-            const int t = c0 + tid;
-            ra = t < T ? ag[(size_t)t * A.H] : 1.0f;  // padding: gate 1, beta 0
-            rb = t < T ? bg[(size_t)t * A.H] : 0.0f;
+        if (which == 2) {
+            const size_t ua = (size_t)min(c0 + (tid & 63), T - 1);
+            r.a = ag[ua * A.H];
+            r.b = bg[ua * A.H];
         }
     };
 
-    load(0);
+    ChunkRegs nx;
+    load(0, 0, nx);
+    load(0, 1, nx);
+    load(0, 2, nx);
     for (int c0 = 0; c0 < T; c0 += CH) {
         __syncthreads();  // the previous chunk is done with every LDS tile
-        // ---- stage the chunk: K, Q token-major; K, V transposed (token pairs packed)
+        // Lane indices pass through an empty asm each chunk, so the LDS
+        // addresses built from them are formed inside the loop: hoisted out
+        // of it, the few dozen distinct addresses would not fit in registers.
+        asm volatile("" : "+v"(lg), "+v"(ln));
+        const int lane = 16 * lg + ln;
+
+        // ---- stage the chunk: K, Q token-major; K^T, V^T through the matrix
+        // cores (X E_h puts 4 consecutive tokens of one channel in each lane;
+        // exact: one product by 1 per output); rows past the end are zero
 #pragma unroll
-        for (int s = 0; s < 2; s++) {
-            *reinterpret_cast<u32x4 *>(&L.kr[(jp + s) * SD + cp]) = rk[s];
-            *reinterpret_cast<u32x4 *>(&L.qr[(jp + s) * SD + cp]) = rq[s];
-        }
+        for (int s = 0; s < 4; s++) {
+            const int p = 4 * wave + s, tg = p / KB, db = p % KB;
+            const bool ok = c0 + 16 * tg + ln < T;
+            const u32x4 kx = keep(nx.k[s], ok), qx = keep(nx.q[s], ok), vx = keep(nx.v[s], ok);
+            const int row = (16 * tg + ln) * SD + 32 * db + 8 * lg;
+            *reinterpret_cast<u32x4 *>(&L.kr[row]) = kx;
+            *reinterpret_cast<u32x4 *>(&L.qr[row]) = qx;
 #pragma unroll
-        for (int x = 0; x < 4; x++) {
-            // dword x of a piece holds columns 2x, 2x+1; pack token pairs per column
-            const unsigned k0 = rk[0][x], k1 = rk[1][x], v0 = rv[0][x], v1 = rv[1][x];
-            *reinterpret_cast<unsigned *>(&L.kt[(cp + 2 * x) * SC + jp]) = (k0 & 0xffffu) | (k1 << 16);
-            *reinterpret_cast<unsigned *>(&L.kt[(cp + 2 * x + 1) * SC + jp]) = (k0 >> 16) | (k1 & 0xffff0000u);
-            *reinterpret_cast<unsigned *>(&L.vt[(cp + 2 * x) * SC + jp]) = (v0 & 0xffffu) | (v1 << 16);
-            *reinterpret_cast<unsigned *>(&L.vt[(cp + 2 * x + 1) * SC + jp]) = (v0 >> 16) | (v1 & 0xffff0000u);
-        }
-        if (wave == 0) {  // cumulative log-gates over the chunk (inclusive scan)
-            float x = logf(ra);
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float y = __shfl_up(x, o, 64);
-                if (lane >= o) x += y;
+            for (int h = 0; h < 2; h++) {
+                const floatx4 tkx = mma(__builtin_bit_cast(bf16x8, kx), eye[h], floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+                const floatx4 tvx = mma(__builtin_bit_cast(bf16x8, vx), eye[h], floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+                const int col = (32 * db + 16 * h + ln) * SC + 16 * tg + 4 * lg;
+                *reinterpret_cast<bf16x4 *>(&L.kt[col]) =
+                    bf16x4{(__bf16)tkx[0], (__bf16)tkx[1], (__bf16)tkx[2], (__bf16)tkx[3]};
+                *reinterpret_cast<bf16x4 *>(&L.vt[col]) =
+                    bf16x4{(__bf16)tvx[0], (__bf16)tvx[1], (__bf16)tvx[2], (__bf16)tvx[3]};
             }
-            const float glast = __shfl(x, 63, 64);
+        }
+        if (wave == 0) {  // cumulative log2-gates over the chunk (inclusive scan)
+            const bool ok = c0 + lane < T;
+            const float x = scan64(__builtin_amdgcn_logf(ok ? nx.a : 1.0f));  // padding: gate 1, beta 0
+            const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
             L.g[lane] = x;
-            L.eg[lane] = expf(x);
-            L.gam[lane] = expf(glast - x);
-            L.beta[lane] = rb;
+            L.eg[lane] = __builtin_amdgcn_exp2f(x);
+            L.gam[lane] = __builtin_amdgcn_exp2f(glast - x);
+            L.beta[lane] = ok ? nx.b : 0.0f;
         }
         __syncthreads();
-        if (c0 + CH < T) load(c0 + CH);  // next chunk in flight during this one
+        // the next chunk's loads go out in three parts spread over this chunk:
+        // all at once, every workgroup's burst fills the memory queues and the
+        // waves stall on issue
+        const bool more = c0 + CH < T;
+        if (more) load(c0 + CH, 0, nx);
 
-        // ---- A = strictly lower diag(beta)(K K^T . Gam) (fp32) and P (split);
-        // tile (I, J) is computed transposed (rows j, columns i) so each lane
-        // holds 4 consecutive j of one i
-        for (int job = wave; job < 20; job += NW) {
-            const bool isP = job >= 10;
-            const int tix = isP ? job - 10 : job;
-            const int I = kTileI[tix], J = kTileJ[tix];
-            const __bf16 *src = isP ? L.qr : L.kr;
-            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        // ---- A = strictly lower diag(beta)(K K^T . Gam) (fp32) and P (split),
+        // one lower 16x16 tile (I, J) of both per job; the tile is computed
+        // transposed (rows j, columns i) so each lane holds 4 consecutive j
+        // of one i
+        for (int job = wave; job < 10; job += NW) {
+            const int I = tile_i(job), J = tile_j(job);
+            floatx4 gk = {0.0f, 0.0f, 0.0f, 0.0f}, gq = gk;
 #pragma unroll
-            for (int kb = 0; kb < KB; kb++)
-                acc = mma(ld8(&L.kr[(16 * J + ln) * SD + 32 * kb + 8 * lg]),
-                          ld8(&src[(16 * I + ln) * SD + 32 * kb + 8 * lg]), acc);
-            const int i = 16 * I + ln, j0 = 16 * J + 4 * lg;
-            const float gi = L.g[i];
-            if (!isP) {
-                const float bi = L.beta[i];
-                floatx4 out;
-#pragma unroll
-                for (int r = 0; r < 4; r++)
-                    out[r] = i > j0 + r ? (bi * acc[r]) * expf(gi - L.g[j0 + r]) : 0.0f;
-                *reinterpret_cast<floatx4 *>(&L.u.inv.a[i * SF + j0]) = out;
-            } else {
-                bf16x4 h, l;
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const float p = i >= j0 + r ? acc[r] * expf(gi - L.g[j0 + r]) : 0.0f;
-                    split(p, h, l, r);
-                }
-                *reinterpret_cast<bf16x4 *>(&L.ph[i * SC + j0]) = h;
-                *reinterpret_cast<bf16x4 *>(&L.pl[i * SC + j0]) = l;
+            for (int kb = 0; kb < KB; kb++) {
+                const bf16x8 kj = ld8(&L.kr[(16 * J + ln) * SD + 32 * kb + 8 * lg]);
+                gk = mma(kj, ld8(&L.kr[(16 * I + ln) * SD + 32 * kb + 8 * lg]), gk);
+                gq = mma(kj, ld8(&L.qr[(16 * I + ln) * SD + 32 * kb + 8 * lg]), gq);
             }
+            const int i = 16 * I + ln, j0 = 16 * J + 4 * lg;
+            const float gi = L.g[i], bi = L.beta[i];
+            const floatx4 gj = *reinterpret_cast<const floatx4 *>(&L.g[j0]);
+            floatx4 out;
+            bf16x4 h, l;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float gam = __builtin_amdgcn_exp2f(gi - gj[r]);
+                out[r] = i > j0 + r ? (bi * gk[r]) * gam : 0.0f;
+                split(i >= j0 + r ? gq[r] * gam : 0.0f, h, l, r);
+            }
+            *reinterpret_cast<floatx4 *>(&L.u.inv.a[i * SF + j0]) = out;
+            *reinterpret_cast<bf16x4 *>(&L.ph[i * SC + j0]) = h;
+            *reinterpret_cast<bf16x4 *>(&L.pl[i * SC + j0]) = l;
         }
         __syncthreads();
 
         // ---- T = (I + A)^{-1}.  Level 0: the four 16x16 diagonal blocks by
-        // forward substitution, lane = (block lg, column ln)
+        // forward substitution, lane = (block lg, column c = ln).  y = T e_c - e_c
+        // solves y_r = -A_rc - sum_{s<r} A_rs y_s (A's diagonal blocks are
+        // strictly lower, so y_r = 0 for r <= c); the sums are updated
+        // right-looking, so the dependent chain is 16 steps long.
         if (wave == 0) {
             const float *Ab = &L.u.inv.a[16 * lg * SF + 16 * lg];
-            float x[16];
+            float y[16];
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                float acc = r == ln ? 1.0f : 0.0f;
+            for (int r = 0; r < 16; r++) y[r] = -Ab[r * SF + ln];
 #pragma unroll
-                for (int s = 0; s < r; s++) acc = fmaf(-Ab[r * SF + s], x[s], acc);
-                x[r] = acc;
-            }
+            for (int s = 0; s < 15; s++)
+#pragma unroll
+                for (int r = s + 1; r < 16; r++) y[r] = fmaf(-Ab[r * SF + s], y[s], y[r]);
             float *Tb = &L.u.inv.t[16 * lg * SF + 16 * lg];
 #pragma unroll
-            for (int r = 0; r < 16; r++) Tb[r * SF + ln] = x[r];
+            for (int r = 0; r < 16; r++) Tb[r * SF + ln] = y[r];
+            Tb[ln * SF + ln] = 1.0f;
         }
         __syncthreads();
         // Level 1: T_{b+1,b} = -T_{b+1,b+1} A_{b+1,b} T_{b,b} for b = 0, 2
@@ -313,9 +373,12 @@ __global__ __launch_bounds__(D * 4, 1) void prefill_kernel(PrefillArgs A)
         }
         __syncthreads();
 
+        if (more) load(c0 + CH, 1, nx);
+
         // ---- T1 = T diag(beta e^g), T2 = T diag(beta), split; T's upper part is 0
-        for (int x = tid; x < CH * CH / 8; x += NT) {
-            const int i = x >> 3, j0 = 8 * (x & 7);
+#pragma unroll
+        for (int sx = 0; sx < CH * CH / 8 / NT; sx++) {
+            const int x = tid + sx * NT, i = x >> 3, j0 = 8 * (x & 7);
             bf16x8 h1, l1, h2, l2;
 #pragma unroll
             for (int e = 0; e < 8; e++) {
@@ -333,131 +396,215 @@ __global__ __launch_bounds__(D * 4, 1) void prefill_kernel(PrefillArgs A)
         }
         __syncthreads();
 
-        // ---- W^T = K^T T1^T: wave owns key rows 16w..16w+15 (DT == NW); store -W split
+        // ---- W^T = K^T T1^T: wave w makes key-row tiles 2w, 2w+1; store -W split
         {
-            floatx4 acc[4];
+            floatx4 acc[2][4];
 #pragma unroll
-            for (int it = 0; it < 4; it++) acc[it] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int x = 0; x < 2; x++)
+#pragma unroll
+                for (int it = 0; it < 4; it++) acc[x][it] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int jb = 0; jb < 2; jb++) {
-                const bf16x8 av = ld8(&L.kt[(16 * wave + ln) * SC + 32 * jb + 8 * lg]);
+                bf16x8 av[2];
+#pragma unroll
+                for (int x = 0; x < 2; x++) av[x] = ld8(&L.kt[(16 * (2 * wave + x) + ln) * SC + 32 * jb + 8 * lg]);
+                bf16x8 bh[4], bl[4];
 #pragma unroll
                 for (int it = 0; it < 4; it++) {
-                    acc[it] = mma(av, ld8(&L.t1h[(16 * it + ln) * SC + 32 * jb + 8 * lg]), acc[it]);
-                    acc[it] = mma(av, ld8(&L.t1l[(16 * it + ln) * SC + 32 * jb + 8 * lg]), acc[it]);
+                    bh[it] = ld8(&L.t1h[(16 * it + ln) * SC + 32 * jb + 8 * lg]);
+                    bl[it] = ld8(&L.t1l[(16 * it + ln) * SC + 32 * jb + 8 * lg]);
                 }
+#pragma unroll
+                for (int it = 0; it < 4; it++)
+#pragma unroll
+                    for (int x = 0; x < 2; x++) acc[x][it] = mma(av[x], bh[it], acc[x][it]);
+#pragma unroll
+                for (int it = 0; it < 4; it++)
+#pragma unroll
+                    for (int x = 0; x < 2; x++) acc[x][it] = mma(av[x], bl[it], acc[x][it]);
             }
 #pragma unroll
-            for (int it = 0; it < 4; it++) {
-                bf16x4 h, l;
+            for (int x = 0; x < 2; x++)
 #pragma unroll
-                for (int r = 0; r < 4; r++) split(-acc[it][r], h, l, r);
-                const int off = (16 * it + ln) * SD + 16 * wave + 4 * lg;
-                *reinterpret_cast<bf16x4 *>(&L.u.w.h[off]) = h;
-                *reinterpret_cast<bf16x4 *>(&L.u.w.l[off]) = l;
-            }
+                for (int it = 0; it < 4; it++) {
+                    bf16x4 h, l;
+#pragma unroll
+                    for (int r = 0; r < 4; r++) split(-acc[x][it][r], h, l, r);
+                    const int off = (16 * it + ln) * SD + 16 * (2 * wave + x) + 4 * lg;
+                    *reinterpret_cast<bf16x4 *>(&L.u.w.h[off]) = h;
+                    *reinterpret_cast<bf16x4 *>(&L.u.w.l[off]) = l;
+                }
         }
         // ---- U = T2 V for this wave's value columns (accumulators become U')
-        floatx4 U[4];
+        floatx4 U[2][4];
 #pragma unroll
-        for (int it = 0; it < 4; it++) U[it] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int it = 0; it < 4; it++) U[et][it] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int jb = 0; jb < 2; jb++) {
-            const bf16x8 bv = ld8(&L.vt[(e0 + ln) * SC + 32 * jb + 8 * lg]);
+            bf16x8 bv[2];
+#pragma unroll
+            for (int et = 0; et < 2; et++) bv[et] = ld8(&L.vt[(e0 + 16 * et + ln) * SC + 32 * jb + 8 * lg]);
+            bf16x8 th[4], tl[4];
 #pragma unroll
             for (int it = 0; it < 4; it++) {
-                U[it] = mma(ld8(&L.t2h[(16 * it + ln) * SC + 32 * jb + 8 * lg]), bv, U[it]);
-                U[it] = mma(ld8(&L.t2l[(16 * it + ln) * SC + 32 * jb + 8 * lg]), bv, U[it]);
+                th[it] = ld8(&L.t2h[(16 * it + ln) * SC + 32 * jb + 8 * lg]);
+                tl[it] = ld8(&L.t2l[(16 * it + ln) * SC + 32 * jb + 8 * lg]);
             }
+#pragma unroll
+            for (int it = 0; it < 4; it++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) U[et][it] = mma(th[it], bv[et], U[et][it]);
+#pragma unroll
+            for (int it = 0; it < 4; it++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) U[et][it] = mma(tl[it], bv[et], U[et][it]);
         }
         __syncthreads();  // -W complete
+        if (more) load(c0 + CH, 2, nx);
 
         // ---- state operand (contraction over key rows, permuted slots)
-        bf16x8 Sh[KB], Sl[KB];
+        bf16x8 Sh[2][KB], Sl[2][KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; kb++)
+        for (int et = 0; et < 2; et++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                split(S[2 * kb][r], Sh[kb], Sl[kb], r);
-                split(S[2 * kb + 1][r], Sh[kb], Sl[kb], 4 + r);
+            for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    split(S[et][2 * kb][r], Sh[et][kb], Sl[et][kb], r);
+                    split(S[et][2 * kb + 1][r], Sh[et][kb], Sl[et][kb], 4 + r);
+                }
+        // ---- U' = U - W S and Q S (each operand read from LDS feeds both column tiles)
+        floatx4 O[2][4];
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int it = 0; it < 4; it++) O[et][it] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < KB; kb++) {
+            bf16x8 wh[4], wl[4], qa[4];
+#pragma unroll
+            for (int it = 0; it < 4; it++) {
+                const int row = (16 * it + ln) * SD + 4 * lg + 32 * kb;
+                wh[it] = ld_pair(&L.u.w.h[row]);
+                wl[it] = ld_pair(&L.u.w.l[row]);
+                qa[it] = ld_pair(&L.qr[row]);
             }
-        // ---- U' = U - W S and Q S
-        floatx4 O[4];
+            // 16 independent accumulators; each product order keeps a
+            // chain's consecutive products 16 instructions apart
+#pragma unroll
+            for (int it = 0; it < 4; it++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) {
+                    U[et][it] = mma(wh[it], Sh[et][kb], U[et][it]);
+                    O[et][it] = mma(qa[it], Sh[et][kb], O[et][it]);
+                }
+#pragma unroll
+            for (int it = 0; it < 4; it++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) {
+                    U[et][it] = mma(wh[it], Sl[et][kb], U[et][it]);
+                    O[et][it] = mma(qa[it], Sl[et][kb], O[et][it]);
+                }
+#pragma unroll
+            for (int it = 0; it < 4; it++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) U[et][it] = mma(wl[it], Sh[et][kb], U[et][it]);
+        }
 #pragma unroll
         for (int it = 0; it < 4; it++) {
-            floatx4 qs = {0.0f, 0.0f, 0.0f, 0.0f};
-            const int row = (16 * it + ln) * SD + 4 * lg;
+            const floatx4 eg = *reinterpret_cast<const floatx4 *>(&L.eg[16 * it + 4 * lg]);
 #pragma unroll
-            for (int kb = 0; kb < KB; kb++) {
-                const bf16x8 wh = ld_pair(&L.u.w.h[row + 32 * kb]);
-                const bf16x8 wl = ld_pair(&L.u.w.l[row + 32 * kb]);
-                const bf16x8 qa = ld_pair(&L.qr[row + 32 * kb]);
-                U[it] = mma(wh, Sh[kb], U[it]);
-                U[it] = mma(wh, Sl[kb], U[it]);
-                U[it] = mma(wl, Sh[kb], U[it]);
-                qs = mma(qa, Sh[kb], qs);
-                qs = mma(qa, Sl[kb], qs);
-            }
+            for (int et = 0; et < 2; et++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) qs[r] *= L.eg[16 * it + 4 * lg + r];
-            O[it] = qs;
+                for (int r = 0; r < 4; r++) O[et][it][r] *= eg[r];
         }
         // ---- U' as an operand (contraction over tokens), plain and scaled by e^{g_C - g_j}
-        bf16x8 Vh[2], Vl[2], Gh[2], Gl[2];
+        bf16x8 Vh[2][2], Vl[2][2], Gh[2][2], Gl[2][2];
 #pragma unroll
-        for (int jb = 0; jb < 2; jb++)
+        for (int jb = 0; jb < 2; jb++) {
+            const floatx4 ga = *reinterpret_cast<const floatx4 *>(&L.gam[32 * jb + 4 * lg]);
+            const floatx4 gc = *reinterpret_cast<const floatx4 *>(&L.gam[32 * jb + 16 + 4 * lg]);
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int ja = 32 * jb + 4 * lg + r, jc = ja + 16;
-                split(U[2 * jb][r], Vh[jb], Vl[jb], r);
-                split(U[2 * jb + 1][r], Vh[jb], Vl[jb], 4 + r);
-                split(U[2 * jb][r] * L.gam[ja], Gh[jb], Gl[jb], r);
-                split(U[2 * jb + 1][r] * L.gam[jc], Gh[jb], Gl[jb], 4 + r);
-            }
+            for (int et = 0; et < 2; et++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    split(U[et][2 * jb][r], Vh[et][jb], Vl[et][jb], r);
+                    split(U[et][2 * jb + 1][r], Vh[et][jb], Vl[et][jb], 4 + r);
+                    split(U[et][2 * jb][r] * ga[r], Gh[et][jb], Gl[et][jb], r);
+                    split(U[et][2 * jb + 1][r] * gc[r], Gh[et][jb], Gl[et][jb], 4 + r);
+                }
+        }
         // ---- O += P U' (causal: token block jb only feeds rows i >= 32 jb)
 #pragma unroll
-        for (int it = 0; it < 4; it++) {
-            const int row = (16 * it + ln) * SC + 4 * lg;
+        for (int jb = 0; jb < 2; jb++) {
+            bf16x8 phv[4], plv[4];
 #pragma unroll
-            for (int jb = 0; jb < 2; jb++) {
-                if (32 * jb > 16 * it + 15) continue;
-                const bf16x8 phv = ld_pair(&L.ph[row + 32 * jb]);
-                const bf16x8 plv = ld_pair(&L.pl[row + 32 * jb]);
-                O[it] = mma(phv, Vh[jb], O[it]);
-                O[it] = mma(phv, Vl[jb], O[it]);
-                O[it] = mma(plv, Vh[jb], O[it]);
+            for (int it = 2 * jb; it < 4; it++) {
+                const int row = (16 * it + ln) * SC + 4 * lg + 32 * jb;
+                phv[it] = ld_pair(&L.ph[row]);
+                plv[it] = ld_pair(&L.pl[row]);
             }
+#pragma unroll
+            for (int it = 2 * jb; it < 4; it++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) O[et][it] = mma(phv[it], Vh[et][jb], O[et][it]);
+#pragma unroll
+            for (int it = 2 * jb; it < 4; it++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) O[et][it] = mma(phv[it], Vl[et][jb], O[et][it]);
+#pragma unroll
+            for (int it = 2 * jb; it < 4; it++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) O[et][it] = mma(plv[it], Vh[et][jb], O[et][it]);
         }
-        // ---- outputs of the chunk's tokens
+        // ---- outputs of the chunk's tokens: through LDS (K's token-major tile
+        // is free after the A/P tiles), then 16-byte coalesced stores
 #pragma unroll
-        for (int it = 0; it < 4; it++)
+        for (int et = 0; et < 2; et++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int t = c0 + 16 * it + 4 * lg + r;
-                if (t < T) og[(size_t)t * tv + e0 + ln] = (__bf16)O[it][r];
-            }
+            for (int it = 0; it < 4; it++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) L.kr[(16 * it + 4 * lg + r) * SD + e0 + 16 * et + ln] = (__bf16)O[et][it][r];
         // ---- S <- e^{g_C} S + K^T diag(e^{g_C - g}) U'
         const float egc = L.eg[CH - 1];
 #pragma unroll
-        for (int dt = 0; dt < DT; dt++) {
-            floatx4 acc = S[dt] * egc;
+        for (int et = 0; et < 2; et++)
 #pragma unroll
-            for (int jb = 0; jb < 2; jb++) {
-                const bf16x8 ka = ld_pair(&L.kt[(16 * dt + ln) * SC + 32 * jb + 4 * lg]);
-                acc = mma(ka, Gh[jb], acc);
-                acc = mma(ka, Gl[jb], acc);
-            }
-            S[dt] = acc;
+            for (int dt = 0; dt < DT; dt++) S[et][dt] *= egc;
+#pragma unroll
+        for (int jb = 0; jb < 2; jb++) {
+            bf16x8 ka[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) ka[dt] = ld_pair(&L.kt[(16 * dt + ln) * SC + 32 * jb + 4 * lg]);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) S[et][dt] = mma(ka[dt], Gh[et][jb], S[et][dt]);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) S[et][dt] = mma(ka[dt], Gl[et][jb], S[et][dt]);
+        }
+        __syncthreads();  // the outputs are staged
+#pragma unroll
+        for (int x = tid; x < CH * D / 8; x += NT) {
+            const int t = x / (D / 8), c = 8 * (x % (D / 8));
+            if (c0 + t < T)
+                *reinterpret_cast<u32x4 *>(og + (size_t)(c0 + t) * tv + c) =
+                    *reinterpret_cast<const u32x4 *>(&L.kr[t * SD + c]);
         }
     }
 
 #pragma unroll
-    for (int dt = 0; dt < DT; dt++)
+    for (int et = 0; et < 2; et++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + ln] = S[dt][r];
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + 16 * et + ln] = S[et][dt][r];
 }
-
-}  // namespace
 
 hipError_t launch_prefill(const gdnq_desc &d, float *S, const void *q, const void *k, const void *v,
                           const float *a, const float *b, void *o, int T, hipStream_t st)
@@ -477,9 +624,9 @@ hipError_t launch_prefill(const gdnq_desc &d, float *S, const void *q, const voi
                   make_divisor((unsigned)(d.H / hk))};
     const unsigned grid = (unsigned)d.B * (unsigned)d.H;
     if (d.dk == 128) {
-        hipLaunchKernelGGL(prefill_kernel<128>, dim3(grid), dim3(512), 0, st, A);
+        hipLaunchKernelGGL(prefill_kernel<128>, dim3(grid), dim3(256), 0, st, A);
     } else {
-        hipLaunchKernelGGL(prefill_kernel<64>, dim3(grid), dim3(256), 0, st, A);
+        hipLaunchKernelGGL(prefill_kernel<64>, dim3(grid), dim3(128), 0, st, A);
     }
     return hipGetLastError();
 }

@@ -21,6 +21,7 @@
 // "slot" with key-side vector and value-side vector, like a buffered token.
 #include "codec.hpp"
 #include "launch.hpp"
+#include "launchers.hpp"
 
 namespace gdnq {
 

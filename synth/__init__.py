@@ -18,10 +18,11 @@ q, k, v are then rounded to the I/O dtype (fp32 or bf16, round to nearest
 even); the arrays returned are fp32 holding those exact values, plus the
 raw bf16 bit patterns when the I/O dtype is bf16.
 
-The workloads below are the five shapes the method is exercised on: a tiny
+The workloads below are the shapes the method is exercised on: a tiny
 per-step decode, a Gated-DeltaNet serving decode in window mode, a
 per-channel-decay (KDA) decode in window mode, a prefix-cache serving step
-over many independent states, and a long decode with DAMP rows.
+over many independent states, a long decode with DAMP rows, and a prefill
+of long sequences.
 """
 from __future__ import annotations
 
@@ -50,6 +51,10 @@ WORKLOADS = {
     "prefix_cache": dict(B=1024, H=32, dk=128, dv=128, T=1, calls=100, io="bf16",
                          decay="scalar", a_lo=0.90, W=1, r=0, seed=3, s0="prefill",
                          outlier_rows=4, outlier_cols=4, outlier_scale=50.0),
+    # Prefill: T tokens of 8 sequences x 32 heads through the chunkwise
+    # prefill from a zero state (the state then goes through the codec).
+    "prefill": dict(B=8, H=32, dk=128, dv=128, T=4096, io="bf16", decay="scalar", a_lo=0.90,
+                    W=1, r=0, seed=5, s0="zero"),
     # Long decode with DAMP rows: 8 fp16 key rows per head from calibration
     # over 256 steps, window mode W=16 with 2 compensators, KDA decay.
     "damp": dict(B=256, H=32, dk=128, dv=128, T=8192, io="bf16", decay="channel", a_lo=0.80,
@@ -112,6 +117,26 @@ def steps_inputs(cfg: dict, t0: int, n: int, heads=None, seed=None):
     """Stack ``n`` steps from ``t0``: arrays get a leading [n] axis."""
     parts = [step_inputs(cfg, t0 + t, heads, seed) for t in range(n)]
     return {key: np.stack([p[key] for p in parts]) for key in parts[0]}
+
+
+def token_major_inputs(cfg: dict, T: int):
+    """The draws of steps 0..T-1 (``step_inputs``) laid out token-major for
+    a whole sequence: q16, k16, v16 as bf16 bit patterns [B,T,H,d], a and b
+    fp32 [B,T,H] (a: the scalar gate).  Filled one step at a time, so the
+    fp32 copies of the whole sequence are never held."""
+    B, H, dk, dv = cfg["B"], cfg["H"], cfg["dk"], cfg["dv"]
+    if cfg["io"] != "bf16" or cfg["decay"] != "scalar":
+        raise ValueError("token-major inputs are built for bf16 I/O and the scalar gate")
+    out = dict(q16=np.empty((B, T, H, dk), np.uint16), k16=np.empty((B, T, H, dk), np.uint16),
+               v16=np.empty((B, T, H, dv), np.uint16), a=np.empty((B, T, H), np.float32),
+               b=np.empty((B, T, H), np.float32))
+    for t in range(T):
+        x = step_inputs(cfg, t)
+        for name in ("q16", "k16", "v16"):
+            out[name][:, t] = x[name].reshape(B, H, -1)
+        out["a"][:, t] = x["a"].reshape(B, H)
+        out["b"][:, t] = x["b"].reshape(B, H)
+    return out
 
 
 def calib_inputs(cfg: dict, n: int, heads=None):

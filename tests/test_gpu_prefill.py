@@ -191,3 +191,32 @@ def test_prefill_rejects(D):
                       (dict(dv=64 if D == 128 else 128), "dk == dv")):
         with pytest.raises(g.GdnqError, match=msg):
             g.gdn_prefill(desc_for(cfg, **over), S, x, x, x, ab, ab, x.clone(), 8)
+
+
+def test_prefill_full_size_sampled():
+    """The benchmark's workload (8 sequences x 32 heads x 4096 tokens, zero
+    initial state) in the benchmark's launch, checked on sampled heads
+    against the oracle's 4096-step recurrence."""
+    torch = torch_cuda()
+    g = lib()
+    cfg = synth.WORKLOADS["prefill"]
+    B, H, D, T = cfg["B"], cfg["H"], cfg["dk"], cfg["T"]
+    x = synth.token_major_inputs(cfg, T)
+    S = torch.zeros((B * H, D, D), dtype=torch.float32, device="cuda")
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    say("prefill full size", B, H, T)
+    g.gdn_prefill(desc_for(dict(cfg, W=1, r=0)), S, _bf16_dev(x["q16"]), _bf16_dev(x["k16"]), _bf16_dev(x["v16"]),
+                  dev(x["a"]), dev(x["b"]), o, T)
+    torch.cuda.synchronize()
+    S_got = host(S)
+    for b, h in ((0, 0), (3, 17), (7, 31)):
+        f = lambda name: np.ascontiguousarray(synth.bf16_to_f32(x[name][b, :, h])[:, None, :])
+        S_ref, o_ref = oracle.recur(np.zeros((1, D, D), np.float32), f("q16"), f("k16"), f("v16"),
+                                    x["a"][b, :, h, None, None], x["b"][b, :, h, None])
+        rel_S = per_head_rel(S_got[b * H + h][None], S_ref)
+        assert rel_S.max() <= 1e-4, (b, h, rel_S.max())
+        got = synth.bf16_to_f32(o[b, :, h].view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+        ref = o_ref[:, 0]
+        rowmax = np.abs(ref).max(axis=1, keepdims=True)
+        bound = bf16_half_ulp(np.maximum(np.abs(ref), np.abs(got))) + 1e-4 * rowmax
+        assert not (np.abs(got - ref) > bound).any(), (b, h, np.abs(got - ref).max())
