@@ -361,12 +361,11 @@ def prefill_data():
 
 
 def cpu_prefill_baseline(cfg: dict, x: dict, budget_s: float = 10.0) -> dict:
-    """The oracle's sequential recurrence (fp64, one thread) on the first 8
-    heads of sequence 0, 128 tokens at a time until the time budget is
-    spent."""
+    """The oracle's sequential recurrence (fp64, one thread) on the heads of
+    sequence 0, 128 tokens at a time until the time budget is spent."""
     import oracle
 
-    D, nh, step = cfg["dk"], 8, 128
+    D, nh, step = cfg["dk"], cfg["H"], 128
     S = np.zeros((nh, D, D), np.float32)
     done, t, t0 = 0, 0, time.perf_counter()
     while time.perf_counter() - t0 < budget_s and t < cfg["T"]:
@@ -377,7 +376,7 @@ def cpu_prefill_baseline(cfg: dict, x: dict, budget_s: float = 10.0) -> dict:
         done += n * nh
     dt = time.perf_counter() - t0
     return {"value": done / dt, "unit": "token-head updates/s", "cores": 1, "kind": "oracle",
-            "sample": f"heads 0-7 of sequence 0, tokens 0-{t - 1} of the sequential recurrence in fp64 "
+            "sample": f"heads 0-{nh - 1} of sequence 0, tokens 0-{t - 1} of the sequential recurrence in fp64 "
                       f"({done} token-head updates) in {dt:.1f} s, one thread"}
 
 

@@ -131,7 +131,7 @@ struct PrefillLds {
     __bf16 vt[D * SC];   // V^T, value-channel-major
     union {
         struct {
-            float a[CH * SF];  // A (strictly lower)
+            float a[CH * SF];  // A^T (A strictly lower): a[j * SF + i] = A_ij
             float t[CH * SF];  // T = (I + A)^{-1} (lower)
         } inv;
         struct {
@@ -281,33 +281,42 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kernel(PrefillArgs A)
         const bool more = c0 + CH < T;
         if (more) load(c0 + CH, 0, nx);
 
-        // ---- A = strictly lower diag(beta)(K K^T . Gam) (fp32) and P (split),
-        // one lower 16x16 tile (I, J) of both per job; the tile is computed
-        // transposed (rows j, columns i) so each lane holds 4 consecutive j
-        // of one i
+        // ---- A = strictly lower diag(beta)(K K^T . Gam), stored transposed
+        // (fp32), and P = (Q K^T . Gam . [i >= j]) (split), one lower 16x16
+        // tile (I, J) of both per job.  The K K^T tile is computed with rows i
+        // and the P tile transposed (rows j), so that each lane holds 4
+        // consecutive i of one j for A^T and 4 consecutive j of one i for P.
         for (int job = wave; job < 10; job += NW) {
             const int I = tile_i(job), J = tile_j(job);
             floatx4 gk = {0.0f, 0.0f, 0.0f, 0.0f}, gq = gk;
 #pragma unroll
             for (int kb = 0; kb < KB; kb++) {
                 const bf16x8 kj = ld8(&L.kr[(16 * J + ln) * SD + 32 * kb + 8 * lg]);
-                gk = mma(kj, ld8(&L.kr[(16 * I + ln) * SD + 32 * kb + 8 * lg]), gk);
+                gk = mma(ld8(&L.kr[(16 * I + ln) * SD + 32 * kb + 8 * lg]), kj, gk);
                 gq = mma(kj, ld8(&L.qr[(16 * I + ln) * SD + 32 * kb + 8 * lg]), gq);
             }
-            const int i = 16 * I + ln, j0 = 16 * J + 4 * lg;
-            const float gi = L.g[i], bi = L.beta[i];
-            const floatx4 gj = *reinterpret_cast<const floatx4 *>(&L.g[j0]);
-            floatx4 out;
-            bf16x4 h, l;
+            {   // A^T: lane (lg, ln) has G[16I + 4lg + r][16J + ln]
+                const int i0 = 16 * I + 4 * lg, j = 16 * J + ln;
+                const floatx4 gi = *reinterpret_cast<const floatx4 *>(&L.g[i0]);
+                const floatx4 bi = *reinterpret_cast<const floatx4 *>(&L.beta[i0]);
+                const float gj = L.g[j];
+                floatx4 out;
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const float gam = __builtin_amdgcn_exp2f(gi - gj[r]);
-                out[r] = i > j0 + r ? (bi * gk[r]) * gam : 0.0f;
-                split(i >= j0 + r ? gq[r] * gam : 0.0f, h, l, r);
+                for (int r = 0; r < 4; r++)
+                    out[r] = i0 + r > j ? (bi[r] * gk[r]) * __builtin_amdgcn_exp2f(gi[r] - gj) : 0.0f;
+                *reinterpret_cast<floatx4 *>(&L.u.inv.a[j * SF + i0]) = out;
             }
-            *reinterpret_cast<floatx4 *>(&L.u.inv.a[i * SF + j0]) = out;
-            *reinterpret_cast<bf16x4 *>(&L.ph[i * SC + j0]) = h;
-            *reinterpret_cast<bf16x4 *>(&L.pl[i * SC + j0]) = l;
+            {   // P: lane (lg, ln) has (Q K^T)[16I + ln][16J + 4lg + r]
+                const int i = 16 * I + ln, j0 = 16 * J + 4 * lg;
+                const float gi = L.g[i];
+                const floatx4 gj = *reinterpret_cast<const floatx4 *>(&L.g[j0]);
+                bf16x4 h, l;
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    split(i >= j0 + r ? gq[r] * __builtin_amdgcn_exp2f(gi - gj[r]) : 0.0f, h, l, r);
+                *reinterpret_cast<bf16x4 *>(&L.ph[i * SC + j0]) = h;
+                *reinterpret_cast<bf16x4 *>(&L.pl[i * SC + j0]) = l;
+            }
         }
         __syncthreads();
 
@@ -315,16 +324,33 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kernel(PrefillArgs A)
         // forward substitution, lane = (block lg, column c = ln).  y = T e_c - e_c
         // solves y_r = -A_rc - sum_{s<r} A_rs y_s (A's diagonal blocks are
         // strictly lower, so y_r = 0 for r <= c); the sums are updated
-        // right-looking, so the dependent chain is 16 steps long.
+        // right-looking (column s of A is row s of the stored A^T, read with
+        // 16-byte loads), so the dependent chain is 16 steps long.
         if (wave == 0) {
-            const float *Ab = &L.u.inv.a[16 * lg * SF + 16 * lg];
-            float y[16];
+            const float *At = &L.u.inv.a[16 * lg * SF + 16 * lg];  // At[s * SF + r] = A_rs
+            // all loads first (40 x 16 bytes, broadcast within a block): left to
+            // the scheduler they go out one step ahead and the 16 steps wait
+            // on 16 LDS round trips
+            floatx4 yv[4], col[15][4];
 #pragma unroll
-            for (int r = 0; r < 16; r++) y[r] = -Ab[r * SF + ln];
+            for (int q = 0; q < 4; q++) yv[q] = *reinterpret_cast<const floatx4 *>(&At[ln * SF + 4 * q]);
 #pragma unroll
             for (int s = 0; s < 15; s++)
 #pragma unroll
-                for (int r = s + 1; r < 16; r++) y[r] = fmaf(-Ab[r * SF + s], y[s], y[r]);
+                for (int q = (s + 1) / 4; q < 4; q++) col[s][q] = *reinterpret_cast<const floatx4 *>(&At[s * SF + 4 * q]);
+            __builtin_amdgcn_sched_barrier(0);
+            float y[16];
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) y[4 * q + e] = -yv[q][e];
+#pragma unroll
+            for (int s = 0; s < 15; s++)
+#pragma unroll
+                for (int q = (s + 1) / 4; q < 4; q++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        if (4 * q + e > s) y[4 * q + e] = fmaf(-col[s][q][e], y[s], y[4 * q + e]);
             float *Tb = &L.u.inv.t[16 * lg * SF + 16 * lg];
 #pragma unroll
             for (int r = 0; r < 16; r++) Tb[r * SF + ln] = y[r];
@@ -337,7 +363,7 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kernel(PrefillArgs A)
             floatx4 X = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < 4; s++)
-                X = mma4(L.u.inv.a[(b0 + 16 + ln) * SF + b0 + 4 * s + lg], L.u.inv.t[(b0 + 4 * s + lg) * SF + b0 + ln], X);
+                X = mma4(L.u.inv.a[(b0 + 4 * s + lg) * SF + b0 + 16 + ln], L.u.inv.t[(b0 + 4 * s + lg) * SF + b0 + ln], X);
             floatx4 Y = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < 4; s++) Y = mma4(L.u.inv.t[(b0 + 16 + ln) * SF + b0 + 16 + 4 * lg + s], X[s], Y);
@@ -354,8 +380,8 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kernel(PrefillArgs A)
 #pragma unroll
                 for (int s = 0; s < 4; s++) {
                     const float bt = L.u.inv.t[(16 * K + 4 * s + lg) * SF + 16 * J + ln];
-                    X2 = mma4(L.u.inv.a[(32 + ln) * SF + 16 * K + 4 * s + lg], bt, X2);
-                    X3 = mma4(L.u.inv.a[(48 + ln) * SF + 16 * K + 4 * s + lg], bt, X3);
+                    X2 = mma4(L.u.inv.a[(16 * K + 4 * s + lg) * SF + 32 + ln], bt, X2);
+                    X3 = mma4(L.u.inv.a[(16 * K + 4 * s + lg) * SF + 48 + ln], bt, X3);
                 }
             }
             floatx4 Y2 = {0.0f, 0.0f, 0.0f, 0.0f}, Y3 = Y2;
@@ -381,13 +407,18 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kernel(PrefillArgs A)
             const int x = tid + sx * NT, i = x >> 3, j0 = 8 * (x & 7);
             bf16x8 h1, l1, h2, l2;
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const int j = j0 + e;
-                const float t = j <= i ? L.u.inv.t[i * SF + j] : 0.0f;
-                const float t2 = t * L.beta[j];
-                const float t1 = t2 * L.eg[j];
-                split(t1, h1, l1, e);
-                split(t2, h2, l2, e);
+            for (int q = 0; q < 2; q++) {
+                const floatx4 tv = *reinterpret_cast<const floatx4 *>(&L.u.inv.t[i * SF + j0 + 4 * q]);
+                const floatx4 bv = *reinterpret_cast<const floatx4 *>(&L.beta[j0 + 4 * q]);
+                const floatx4 ev = *reinterpret_cast<const floatx4 *>(&L.eg[j0 + 4 * q]);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const float t = j0 + 4 * q + e <= i ? tv[e] : 0.0f;  // T's upper part is 0
+                    const float t2 = t * bv[e];
+                    const float t1 = t2 * ev[e];
+                    split(t1, h1, l1, 4 * q + e);
+                    split(t2, h2, l2, 4 * q + e);
+                }
             }
             *reinterpret_cast<bf16x8 *>(&L.t1h[i * SC + j0]) = h1;
             *reinterpret_cast<bf16x8 *>(&L.t1l[i * SC + j0]) = l1;
