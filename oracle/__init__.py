@@ -277,3 +277,49 @@ def calibrate(S0, k, v, a, b, n_hp):
     lib().orc_calibrate(nh, dk, dv, kda, n, n_hp, _p(S0), _p(k), _p(v), _p(a), _p(b), _p(idx),
                         _p(score))
     return idx, score
+
+
+# ------------------------------------------------------------ static scales (f4)
+def quantize_static(X, rho, iota, bits=8):
+    """Codes of tiles X [nh,dk,dv] under fixed rho [nh,dk], iota [nh,dv]
+    (orc_quantize_static): rint of (X rho) iota, clamped."""
+    X = _f32(X)
+    nh, dk, dv = X.shape
+    rho, iota = _f32(rho), _f32(iota)
+    Q = np.empty((nh, dk, dv), np.int8)
+    lib().orc_quantize_static(nh, dk, dv, int(bits), _p(X), _p(rho), _p(iota), _p(Q))
+    return Q
+
+
+def fit_static(S0, q, k, v, a, b, bits=8):
+    """Static-scale fit (orc_fit_static) over n calibration steps from S0.
+    q, k: [n,nh,dk]; v: [n,nh,dv]; a: [n,nh,1|dk]; b: [n,nh].  Returns dict
+    s, rho [nh,dk]; c, iota, choice [nh,dv]; err, cand_c, cand_iota [nh,9,dv]."""
+    S0 = _f32(S0)
+    nh, dk, dv = S0.shape
+    q, k, v, a, b = _f32(q), _f32(k), _f32(v), _f32(a), _f32(b)
+    n = k.shape[0]
+    kda = _a_width(a, dk)
+    out = dict(s=np.empty((nh, dk), np.float32), rho=np.empty((nh, dk), np.float32),
+               c=np.empty((nh, dv), np.float32), iota=np.empty((nh, dv), np.float32),
+               choice=np.empty((nh, dv), np.int32), err=np.empty((nh, 9, dv), np.float64),
+               cand_c=np.empty((nh, 9, dv), np.float32), cand_iota=np.empty((nh, 9, dv), np.float32))
+    lib().orc_fit_static(nh, dk, dv, kda, int(bits), n, _p(S0), _p(q), _p(k), _p(v), _p(a), _p(b),
+                         _p(out["s"]), _p(out["rho"]), _p(out["c"]), _p(out["iota"]), _p(out["choice"]),
+                         _p(out["err"]), _p(out["cand_c"]), _p(out["cand_iota"]))
+    return out
+
+
+def quant_step_static(Q, s, c, rho, iota, q, k, v, a, b, bits=8):
+    """One per-step decode under static scales (orc_quant_step_static) on a
+    copy of Q.  Returns dict(Q, o (fp64), S_f32)."""
+    Q = np.ascontiguousarray(Q, np.int8).copy()
+    nh, dk, dv = Q.shape
+    s, c, rho, iota = _f32(s), _f32(c), _f32(rho), _f32(iota)
+    q, k, v, a, b = _f32(q), _f32(k), _f32(v), _f32(a), _f32(b)
+    kda = _a_width(a, dk)
+    o = np.empty((nh, dv), np.float64)
+    S_f32 = np.empty((nh, dk, dv), np.float32)
+    lib().orc_quant_step_static(nh, dk, dv, kda, int(bits), _p(Q), _p(s), _p(c), _p(rho), _p(iota), _p(q), _p(k),
+                                _p(v), _p(a), _p(b), _p(o), _p(S_f32))
+    return dict(Q=Q, o=o, S_f32=S_f32)

@@ -749,3 +749,188 @@ void orc_calibrate(int nh, int dk, int dv, int kda, int n_steps, int n_hp, const
     free(sc);
     free(taken);
 }
+
+/* ======================================================================
+ * f4: static scales.  [STEP] (opening section): key-row and value-column
+ * scales are fitted jointly and offline, from the state distribution and
+ * from each key row's impact on the output error; precision follows the
+ * error's size and how long it persists.  The page gives no formula.
+ * Reading taken:
+ *  - a head's stored parameters are s (dk), rho = 1/s (dk), c (dv) and
+ *    iota (dv), with c_j = mc_j / Qb and iota_j = Qb / mc_j for a column
+ *    range mc_j (zero column: c = iota = 0);
+ *  - codes of a state X under fixed parameters: Y_ij = X_ij rho_i (one fp32
+ *    product), Q_ij = the integer nearest to the exact product Y_ij iota_j
+ *    (ties to even), clamped to [-Qb, Qb]; dequantization as in c2;
+ *  - the fit runs n steps of the recurrence from S0 and takes the fp32
+ *    state after each step as a calibration state X_t:
+ *      s_i   = sqrt(max_t max_j |X_t,ij|), rho_i = 1/s_i (0 for a zero row);
+ *      m_j   = max_t max_i |X_t,ij rho_i|;
+ *      candidate ranges mc_j(k) = m_j (16-k)/16, k = 0..8 (one fp32 product);
+ *      omega_i = (mean_t q_t,i^2) / max(1 - abar_i, 1e-6): the weight of key
+ *      row i in the output o = S^T q times the lifetime of an error in that
+ *      row under its gate (abar_i = mean gate of key channel i);
+ *      E_j(k) = sum_t sum_i omega_i (X_t,ij - D_t,ij(k))^2 with the codes
+ *      and dequantized values of column j under candidate k;
+ *      keep the candidate with the least E_j (smallest k on ties).
+ * ==================================================================== */
+static void quantize_tile_static(int dk, int dv, int qmax, const float *X, const float *rho,
+                                 const float *iota, int8_t *Q)
+{
+    for (int i = 0; i < dk; i++)
+        for (int j = 0; j < dv; j++) {
+            float Y = f32_mul(X[i * dv + j], rho[i]);                 /* Y_ij = X_ij rho_i */
+            double qv = round_half_even((double)Y * (double)iota[j]); /* exact product    */
+            if (qv > qmax) qv = qmax;
+            if (qv < -qmax) qv = -qmax;
+            Q[i * dv + j] = (int8_t)qv;
+        }
+}
+
+/* codes of nh tiles X [nh][dk][dv] under fixed rho [nh][dk], iota [nh][dv] */
+void orc_quantize_static(int nh, int dk, int dv, int bits, const float *X, const float *rho, const float *iota,
+                         int8_t *Q)
+{
+    size_t E = (size_t)dk * dv;
+    for (int h = 0; h < nh; h++)
+        quantize_tile_static(dk, dv, code_qmax(bits), X + h * E, rho + (size_t)h * dk, iota + (size_t)h * dv,
+                             Q + h * E);
+}
+
+/* Fit of the reading above.  q, k: [n][nh][dk], v: [n][nh][dv], a: [n][nh][1|dk],
+ * b: [n][nh].  Outputs per head: s, rho [nh][dk]; c, iota [nh][dv]; choice
+ * [nh][dv] (the chosen k); err (nullable) [nh][9][dv] the E_j(k); cand_c and
+ * cand_iota (nullable) [nh][9][dv] the candidates' scales. */
+void orc_fit_static(int nh, int dk, int dv, int kda, int bits, int n, const float *S0, const float *q,
+                    const float *k, const float *v, const float *a, const float *b, float *s, float *rho,
+                    float *c, float *iota, int32_t *choice, double *err, float *cand_c, float *cand_iota)
+{
+    size_t E = (size_t)dk * dv;
+    int na = kda ? dk : 1;
+    const int qmax = code_qmax(bits);
+    const float qm = (float)qmax;
+    double *S = (double *)malloc(sizeof(double) * E);
+    float *X = (float *)malloc(sizeof(float) * E);
+    double *om = (double *)malloc(sizeof(double) * dk);
+    double *Ej = (double *)malloc(sizeof(double) * 9 * dv);
+    float *cc = (float *)malloc(sizeof(float) * 9 * dv);
+    float *ci = (float *)malloc(sizeof(float) * 9 * dv);
+    for (int h = 0; h < nh; h++) {
+        float *sh = s + (size_t)h * dk, *rh = rho + (size_t)h * dk;
+        float *ch = c + (size_t)h * dv, *ih = iota + (size_t)h * dv;
+        /* pass 1: row maxima, output weights and gate means */
+        for (int i = 0; i < dk; i++) { sh[i] = 0.0f; om[i] = 0.0; }
+        double *ab = (double *)calloc((size_t)dk, sizeof(double));
+        for (size_t e = 0; e < E; e++) S[e] = (double)S0[h * E + e];
+        for (int t = 0; t < n; t++) {
+            size_t hs = (size_t)t * nh + h;
+            recur_step(dk, dv, kda, S, NULL, k + hs * dk, v + hs * dv, a + hs * na, b[hs], NULL, NULL);
+            for (int i = 0; i < dk; i++) {
+                for (int j = 0; j < dv; j++) {
+                    float x = fabsf((float)S[i * dv + j]);
+                    if (x > sh[i]) sh[i] = x;        /* sh holds the running max */
+                }
+                double qi = (double)q[hs * dk + i];
+                om[i] += qi * qi;
+                ab[i] += kda ? (double)a[hs * na + i] : (double)a[hs * na];
+            }
+        }
+        for (int i = 0; i < dk; i++) {
+            float r = sh[i];
+            sh[i] = (r > 0.0f) ? f32_sqrt(r) : 0.0f;
+            rh[i] = (sh[i] > 0.0f) ? f32_div(1.0f, sh[i]) : 0.0f;
+            double den = 1.0 - ab[i] / (double)n;
+            if (den < 1e-6) den = 1e-6;
+            om[i] = (om[i] / (double)n) / den;
+        }
+        free(ab);
+        /* pass 2: column maxima of the smoothed states */
+        float *m = (float *)calloc((size_t)dv, sizeof(float));
+        for (size_t e = 0; e < E; e++) S[e] = (double)S0[h * E + e];
+        for (int t = 0; t < n; t++) {
+            size_t hs = (size_t)t * nh + h;
+            recur_step(dk, dv, kda, S, NULL, k + hs * dk, v + hs * dv, a + hs * na, b[hs], NULL, NULL);
+            for (int i = 0; i < dk; i++)
+                for (int j = 0; j < dv; j++) {
+                    float y = fabsf(f32_mul((float)S[i * dv + j], rh[i]));
+                    if (y > m[j]) m[j] = y;
+                }
+        }
+        for (int j = 0; j < dv; j++)
+            for (int kk = 0; kk < 9; kk++) {
+                float mc = f32_mul(m[j], (float)(16 - kk) / 16.0f);
+                float cj = 0.0f, io = 0.0f;
+                if (mc > 0.0f) {
+                    io = f32_div(qm, mc);
+                    if (isinf(io)) io = 0.0f;
+                    else cj = f32_div(mc, qm);
+                }
+                cc[kk * dv + j] = cj;
+                ci[kk * dv + j] = io;
+                Ej[kk * dv + j] = 0.0;
+            }
+        free(m);
+        /* pass 3: weighted error of every candidate */
+        for (size_t e = 0; e < E; e++) S[e] = (double)S0[h * E + e];
+        for (int t = 0; t < n; t++) {
+            size_t hs = (size_t)t * nh + h;
+            recur_step(dk, dv, kda, S, NULL, k + hs * dk, v + hs * dv, a + hs * na, b[hs], NULL, NULL);
+            for (size_t e = 0; e < E; e++) X[e] = (float)S[e];
+            for (int i = 0; i < dk; i++)
+                for (int j = 0; j < dv; j++) {
+                    float Y = f32_mul(X[i * dv + j], rh[i]);
+                    for (int kk = 0; kk < 9; kk++) {
+                        double qv = round_half_even((double)Y * (double)ci[kk * dv + j]);
+                        if (qv > qmax) qv = qmax;
+                        if (qv < -qmax) qv = -qmax;
+                        float D = f32_mul(f32_mul((float)qv, cc[kk * dv + j]), sh[i]);
+                        double d = (double)X[i * dv + j] - (double)D;
+                        Ej[kk * dv + j] += om[i] * d * d;
+                    }
+                }
+        }
+        for (int j = 0; j < dv; j++) {
+            int best = 0;
+            for (int kk = 1; kk < 9; kk++)
+                if (Ej[kk * dv + j] < Ej[best * dv + j]) best = kk;
+            ch[j] = cc[best * dv + j];
+            ih[j] = ci[best * dv + j];
+            choice[(size_t)h * dv + j] = best;
+        }
+        if (err) memcpy(err + (size_t)h * 9 * dv, Ej, sizeof(double) * 9 * dv);
+        if (cand_c) memcpy(cand_c + (size_t)h * 9 * dv, cc, sizeof(float) * 9 * dv);
+        if (cand_iota) memcpy(cand_iota + (size_t)h * 9 * dv, ci, sizeof(float) * 9 * dv);
+    }
+    free(S);
+    free(X);
+    free(om);
+    free(Ej);
+    free(cc);
+    free(ci);
+}
+
+/* c3 with static scales: X = D(Q) with the fixed s, c; one c1 step in fp64;
+ * o from the updated fp64 state; round to fp32; codes under the fixed rho,
+ * iota (s, c, rho, iota unchanged).  S_f32 (nullable) receives the fp32
+ * tensor handed to the codec. */
+void orc_quant_step_static(int nh, int dk, int dv, int kda, int bits, int8_t *Q, const float *s, const float *c,
+                           const float *rho, const float *iota, const float *q, const float *k, const float *v,
+                           const float *a, const float *b, double *o, float *S_f32)
+{
+    size_t E = (size_t)dk * dv;
+    int na = kda ? dk : 1;
+    float *X = (float *)malloc(sizeof(float) * E);
+    double *S = (double *)malloc(sizeof(double) * E);
+    for (int h = 0; h < nh; h++) {
+        int8_t *Qh = Q + h * E;
+        dequantize_tile(dk, dv, Qh, s + (size_t)h * dk, c + (size_t)h * dv, X);
+        for (size_t e = 0; e < E; e++) S[e] = (double)X[e];
+        recur_step(dk, dv, kda, S, q + (size_t)h * dk, k + (size_t)h * dk, v + (size_t)h * dv,
+                   a + (size_t)h * na, b[h], o + (size_t)h * dv, NULL);
+        for (size_t e = 0; e < E; e++) X[e] = (float)S[e];
+        if (S_f32) memcpy(S_f32 + h * E, X, sizeof(float) * E);
+        quantize_tile_static(dk, dv, code_qmax(bits), X, rho + (size_t)h * dk, iota + (size_t)h * dv, Qh);
+    }
+    free(X);
+    free(S);
+}
