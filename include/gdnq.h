@@ -88,6 +88,8 @@ enum { GDNQ_LAYOUT_ROWCOL = 0, GDNQ_LAYOUT_DAMP = 1 };
 
 /* flags */
 #define GDNQ_DEBUG_PREQUANT 1u  /* also store the fp32 tensor the codec consumed */
+#define GDNQ_STATIC_SCALES 2u   /* keep fitted static scales (calibrate_static_scales);
+                                   per-step mode of layout 0 only */
 
 /* Problem description shared by all calls. */
 typedef struct {
@@ -100,7 +102,7 @@ typedef struct {
     int32_t layout;       /* GDNQ_LAYOUT_ROWCOL or GDNQ_LAYOUT_DAMP            */
     int32_t n_hp;         /* DAMP fp16 rows per head (layout 1), 1..dk/2       */
     int32_t power_iters;  /* power-iteration steps per compensator, 1..64      */
-    uint32_t flags;       /* GDNQ_DEBUG_PREQUANT or 0                          */
+    uint32_t flags;       /* GDNQ_DEBUG_PREQUANT | GDNQ_STATIC_SCALES, or 0    */
     int32_t bits;         /* code width b: 8 (0 also means 8), 6 or 4; layout 1
                              keeps 8-bit codes (DAMP: the rest in INT8)        */
     int32_t hk;           /* key/query heads, dividing H (0 means H): value
@@ -122,8 +124,13 @@ typedef struct {
  *                      32..47 in bytes dv/2+2k, +1.  Codes lie in [-(2^(b-1)-1),
  *                      2^(b-1)-1] (LeapQuant accuracy table: 8, 6 and 4
  *                      bit states), column scales c = m / (2^(b-1)-1).
- *   row_scale   fp32   [B,H,dk]        layout 0 only (smoothing scales s)
- *   col_scale   fp32   [B,H,dv]        value-column scales c
+ *   row_scale   fp32   [B,H,dk]        layout 0 only (smoothing scales s); with
+ *                                      GDNQ_STATIC_SCALES two planes [2][B,H,dk]:
+ *                                      s, then rho = 1/s
+ *   col_scale   fp32   [B,H,dv]        value-column scales c; with
+ *                                      GDNQ_STATIC_SCALES two planes [2][B,H,dv]:
+ *                                      c = range/Qb, then iota = Qb/range for
+ *                                      the fitted column range
  *   comp_k      fp32   [B,H,r,dk]      compensator key-side vectors p (r > 0)
  *   comp_v      fp32   [B,H,r,dv]      compensator value-side unit vectors w
  *   buf_k       fp32   [B,H,W,dk]      window buffer keys k_t / G_t, where
@@ -241,6 +248,32 @@ int gdn_state_dequantize(const gdnq_desc *desc, const gdnq_state *state, float *
 int calibrate_scales(const gdnq_desc *desc, const float *S0, const void *k, const void *v,
                      const float *a, const float *b, int32_t n_steps, int32_t *hp_idx_out,
                      float *row_score_out, void *stream);
+
+/*
+ * Static scales (STEPQuant page, opening section: key-row and value-column
+ * scales fitted jointly and offline from the state distribution and each key
+ * row's impact on the output error; no formula is given, the reading here is
+ * the library's).  Needs desc->flags & GDNQ_STATIC_SCALES (per-step mode,
+ * layout 0).  Runs n_steps of the fp32 recurrence from S0 [B,H,dk,dv] three
+ * times over the calibration inputs q, k (io_dtype [n_steps,B,hk,dk]), v
+ * (io_dtype [n_steps,B,H,dv]), a (fp32 [n_steps,B,H] or [n_steps,B,H,dk]), b
+ * (fp32 [n_steps,B,H]), all device pointers, and writes both planes of
+ * state->row_scale and state->col_scale:
+ *   s_i = sqrt(max_t max_j |S_t,ij|), rho_i = 1/s_i;
+ *   m_j = max_t max_i |S_t,ij rho_i|; candidate ranges m_j (16-k)/16,
+ *   k = 0..8, each with c = range/Qb and iota = Qb/range;
+ *   omega_i = (mean_t q_t,i^2) / max(1 - mean_t a_t,i, 1e-6);
+ *   E_j(k) = sum_t sum_i omega_i (S_t,ij - D_t,ij(k))^2 with
+ *   D = (Q c) s, Q = clamp(rint((S rho) iota), -Qb, Qb); the candidate with
+ *   the least E_j is kept (smallest k on ties).
+ * With the flag set, gdn_quant_decode_step (and its pool form) and
+ * gdn_state_quantize store codes under these fixed scales (the integer
+ * nearest to the exact product (x rho_i) iota_j, clamped to [-Qb, Qb]) and
+ * leave every scale unchanged; gdn_state_dequantize reads the first planes.
+ */
+int calibrate_static_scales(const gdnq_desc *desc, const float *S0, const void *q, const void *k,
+                            const void *v, const float *a, const float *b, int32_t n_steps,
+                            const gdnq_state *state, void *stream);
 
 /*
  * Baseline: one decode token on fp32 states S [B,H,dk,dv] (device, in

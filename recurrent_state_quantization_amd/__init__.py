@@ -21,6 +21,7 @@ DECAY_SCALAR, DECAY_CHANNEL = 0, 1
 IO_F32, IO_BF16 = 0, 1
 LAYOUT_ROWCOL, LAYOUT_DAMP = 0, 1
 DEBUG_PREQUANT = 1
+STATIC_SCALES = 2
 
 STATE_FIELDS = ("codes", "row_scale", "col_scale", "comp_k", "comp_v", "buf_k", "buf_u", "g_cur",
                 "hp_rows", "hp_idx", "prequant_out")
@@ -91,6 +92,7 @@ def _load():
         "calibrate_scales": [D, P, P, P, P, P, i32, P, P, P],
         "gdn_fp32_decode_step": [D, P, P, P, P, P, P, P, P],
         "gdn_prefill": [D, P, P, P, P, P, P, P, i32, P],
+        "calibrate_static_scales": [D, P, P, P, P, P, P, i32, S, P],
         "gdnq_state_sizes": [D, ctypes.POINTER(ctypes.c_size_t * 11)],
     }
     for name, args in sig.items():
@@ -196,6 +198,11 @@ def calibrate_scales(desc, S0, k, v, a, b, n_steps, hp_idx_out, row_score_out=No
 def gdn_fp32_decode_step(desc, S, q, k, v, a, b, o, stream=None):
     _check(lib.gdn_fp32_decode_step(ctypes.byref(_desc(desc)), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
                                     _ptr(b), _ptr(o), _stream(stream)))
+
+
+def calibrate_static_scales(desc, S0, q, k, v, a, b, n_steps, state, stream=None):
+    _check(lib.calibrate_static_scales(ctypes.byref(_desc(desc)), _ptr(S0), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                       _ptr(b), int(n_steps), _state(state), _stream(stream)))
 
 
 def gdn_prefill(desc, S, q, k, v, a, b, o, T, stream=None):

@@ -75,7 +75,10 @@ int check_desc(const gdnq_desc *d)
     }
     if (d->r > 0 && (d->power_iters < 1 || d->power_iters > 64))
         return fail(GDNQ_EINVAL, "power_iters must be in [1, 64] when r > 0 (got %d)", d->power_iters);
-    if (d->flags & ~GDNQ_DEBUG_PREQUANT) return fail(GDNQ_EINVAL, "unknown flag bits 0x%x", d->flags);
+    if (d->flags & ~(GDNQ_DEBUG_PREQUANT | GDNQ_STATIC_SCALES))
+        return fail(GDNQ_EINVAL, "unknown flag bits 0x%x", d->flags);
+    if ((d->flags & GDNQ_STATIC_SCALES) && (d->layout != GDNQ_LAYOUT_ROWCOL || d->W != 1 || d->r != 0))
+        return fail(GDNQ_EUNSUPPORTED, "static scales are for the per-step mode of layout 0 (W == 1, r == 0)");
     if (d->bits != 0 && d->bits != 8 && d->bits != 6 && d->bits != 4)
         return fail(GDNQ_EINVAL, "bits must be 8, 6 or 4 (0 means 8; got %d)", d->bits);
     if (d->layout == GDNQ_LAYOUT_DAMP && code_bits(*d) != 8)
@@ -93,8 +96,9 @@ void state_sizes(const gdnq_desc &d, size_t out[11])
     const bool window = !per_step(d) || damp;
     const size_t rows = damp ? (size_t)(d.dk - d.n_hp) : (size_t)d.dk;
     out[0] = nh * rows * d.dv * code_bits(d) / 8;                          // codes
-    out[1] = damp ? 0 : nh * d.dk * 4;                                     // row_scale
-    out[2] = nh * d.dv * 4;                                                // col_scale
+    const size_t planes = (d.flags & GDNQ_STATIC_SCALES) ? 2 : 1;        // static: s | rho, c | iota
+    out[1] = damp ? 0 : planes * nh * d.dk * 4;                            // row_scale
+    out[2] = planes * nh * d.dv * 4;                                       // col_scale
     out[3] = nh * (size_t)d.r * d.dk * 4;                                  // comp_k
     out[4] = nh * (size_t)d.r * d.dv * 4;                                  // comp_v
     out[5] = window ? nh * (size_t)d.W * d.dk * 4 : 0;                     // buf_k
@@ -382,6 +386,36 @@ int gdn_fp32_decode_step(const gdnq_desc *desc, float *S, const void *q, const v
     if ((rc = check_buf(S, nheads(d) * d.dk * d.dv * 4, "S", spans))) return rc;
     if ((rc = check_step_io(d, q, k, v, a, b, o, spans))) return rc;
     return launched(gdnq::launch_step_fp32(d, S, q, k, v, a, b, o, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int calibrate_static_scales(const gdnq_desc *desc, const float *S0, const void *q, const void *k, const void *v,
+                            const float *a, const float *b, int32_t n_steps, const gdnq_state *state, void *stream)
+{
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    const gdnq_desc &d = *desc;
+    if (!(d.flags & GDNQ_STATIC_SCALES))
+        return fail(GDNQ_EINVAL, "calibrate_static_scales needs a descriptor with GDNQ_STATIC_SCALES");
+    if (n_steps < 1) return fail(GDNQ_EINVAL, "n_steps must be >= 1 (got %d)", n_steps);
+    const size_t nh = nheads(d), es = io_size(d), ns = (size_t)n_steps;
+    const size_t na = d.decay == GDNQ_DECAY_CHANNEL ? (size_t)d.dk : 1;
+    std::vector<Span> spans;
+    bool need[11] = {false};
+    need[1] = need[2] = true;  // row_scale, col_scale (both planes)
+    if ((rc = check_state(d, state, need, spans))) return rc;
+    struct In {
+        const void *p;
+        size_t n;
+        const char *name;
+    } ins[6] = {{S0, nh * d.dk * d.dv * 4, "S0"},         {q, ns * nkheads(d) * d.dk * es, "q"},
+                {k, ns * nkheads(d) * d.dk * es, "k"},    {v, ns * nh * d.dv * es, "v"},
+                {a, ns * nh * na * 4, "a"},               {b, ns * nh * 4, "b"}};
+    for (const In &in : ins) {
+        std::vector<Span> tmp = spans;
+        if ((rc = check_buf(in.p, in.n, in.name, tmp))) return rc;
+    }
+    return launched(gdnq::launch_fit_static(d, S0, q, k, v, a, b, n_steps, state->row_scale, state->col_scale,
+                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
 int gdn_prefill(const gdnq_desc *desc, float *S, const void *q, const void *k, const void *v, const float *a,

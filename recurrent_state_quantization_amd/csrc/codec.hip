@@ -59,6 +59,23 @@ __global__ __launch_bounds__(G::NT, 2) void quantize_kernel(QuantArgs A)
     }
 }
 
+// Encode under fixed static scales: the rho plane follows the row scales and
+// the iota plane the column scales (row_scale + nh*DK, col_scale + nh*DV).
+template <class G, int BITS>
+__global__ __launch_bounds__(G::NT) void quantize_static_kernel(QuantArgs A, size_t nh)
+{
+    const Lane c = lane_coords<G>();
+    const size_t h = __builtin_amdgcn_workgroup_id_x();
+    constexpr size_t E = (size_t)G::DK * G::DV;
+    const int row0 = row0_of<G>(c);
+    float P[8][8], rho[8], io[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) load_f32x8(A.S + h * E + (size_t)row_of<G>(c, k) * G::DV + c.cb * 8, P[k]);
+    load_rows_f32<G>(A.row_scale + nh * G::DK + h * G::DK + row0, rho);
+    load_f32x8(A.col_scale + nh * G::DV + h * G::DV + c.cb * 8, io);
+    codec_static<G, false, BITS>(P, c, rho, io, A.codes + h * (size_t)G::DK * code_row_bytes<G, BITS>());
+}
+
 template <class G, bool DAMP, int BITS>
 __global__ __launch_bounds__(G::NT) void dequantize_kernel(QuantArgs A)
 {
@@ -126,7 +143,11 @@ hipError_t launch_quantize(const gdnq_desc &d, const float *S, const gdnq_state 
                 if constexpr (DAMP && BITS != 8) {
                     return hipErrorInvalidValue;
                 } else {
-                    hipLaunchKernelGGL((quantize_kernel<G, DAMP, BITS>), dim3(nh), dim3(G::NT), 0, st, A);
+                    if (!DAMP && (d.flags & GDNQ_STATIC_SCALES))
+                        hipLaunchKernelGGL((quantize_static_kernel<G, BITS>), dim3(nh), dim3(G::NT), 0, st, A,
+                                           (size_t)nh);
+                    else
+                        hipLaunchKernelGGL((quantize_kernel<G, DAMP, BITS>), dim3(nh), dim3(G::NT), 0, st, A);
                     return hipGetLastError();
                 }
             });

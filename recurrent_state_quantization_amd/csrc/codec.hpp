@@ -156,6 +156,28 @@ __device__ void codec_rowcol(float (&P)[8][8], const Lane &c, CodecLds<G> &L, in
     }
 }
 
+// Static-scale codec (the STEPQuant reading: row and column scales fitted
+// offline and kept): codes of P under the fixed reciprocals of the lane's
+// rows rho[k] and columns io[j] -- the integer nearest to the exact product
+// (P rho) io, clamped to [-Qb, Qb] (the med3 clamp on RINT_MAGIC + q keeps
+// the code in the low bits).  No reduction, no barrier; scales unchanged.
+template <class G, bool STREAM, int BITS>
+__device__ __forceinline__ void codec_static(const float (&P)[8][8], const Lane &c, const float (&rho)[8],
+                                             const float (&io)[8], int8_t *__restrict__ codes)
+{
+    constexpr float QB = (float)code_qmax<BITS>();
+    constexpr int RB = code_row_bytes<G, BITS>();
+    int8_t *rbase = codes + (size_t)row0_of<G>(c) * RB;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        float y[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            y[j] = __builtin_amdgcn_fmed3f(fmaf(P[k][j] * rho[k], io[j], RINT_MAGIC), RINT_MAGIC - QB, RINT_MAGIC + QB);
+        store_code8<G, BITS, STREAM>(rbase + koff<G>(k) * RB, c.cb, pack_code8<BITS>(y));
+    }
+}
+
 // fp32 -> IEEE fp16 bits, round to nearest even, saturating at +-65504.
 __device__ __forceinline__ uint16_t f32_to_f16_sat(float x)
 {

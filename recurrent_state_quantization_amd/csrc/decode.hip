@@ -35,6 +35,7 @@ struct StepArgs {
     float *prequant;  // nullable
     float *S;         // fp32 state (baseline kernel)
     HeadMap map;
+    size_t plane_r, plane_c;  // static scales: offsets of the rho and iota planes
 };
 
 // Column sums of R (retrieval) and O (output) partials plus k.q, reduced to
@@ -67,7 +68,7 @@ __device__ __forceinline__ void reduce_ro(const Lane &c, StepLds<G> &S, const fl
     if (c.lane == 0) S.red_kq[c.w] = kq_part;
 }
 
-template <class G, bool BF16, bool KDA, int BITS>
+template <class G, bool BF16, bool KDA, int BITS, bool STATIC>
 __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
 {
     __shared__ CodecLds<G> L;
@@ -98,6 +99,11 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     float *cs = A.col_scale + h * G::DV;
     const float si = rs[tr];
     const float cj = cs[tc];   // v_j and c_j serve the consumer lanes (t < DV; columns wrap)
+    float rho_t = 0.0f, io_t = 0.0f;  // static scales: one reciprocal per row / column, via LDS
+    if constexpr (STATIC) {
+        rho_t = A.row_scale[A.plane_r + h * G::DK + tr];
+        io_t = A.col_scale[A.plane_c + h * G::DV + tc];
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the codes'
 
     const int row0 = row0_of<G>(c);
@@ -116,6 +122,10 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
         SL.rv[2][c.t] = asi * qi;
         SL.rv[3][c.t] = ki;
         kq_row = ki * qi;
+    }
+    if constexpr (STATIC) {
+        if (c.t < G::DK) L.rho[c.t] = rho_t;
+        if (c.t < G::DV) L.iota[c.t] = io_t;
     }
     __syncthreads();
     float as[8], ask[8], asq[8], kk[8];
@@ -166,7 +176,13 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
 #pragma unroll
         for (int k = 0; k < 8; k++) store_f32x8(pq + koff<G>(k) * G::DV, X[k]);
     }
-    codec_rowcol<G, true, BITS>(X, c, L, codes, rs, cs);
+    if constexpr (STATIC) {
+        float srho[8], sio[8];  // the reciprocals of the lane's rows and columns
+        load_rows_f32<G>(&L.rho[row0], srho);
+        load_f32x8(&L.iota[c.cb * 8], sio);
+        codec_static<G, true, BITS>(X, c, srho, sio, codes);
+    } else
+        codec_rowcol<G, true, BITS>(X, c, L, codes, rs, cs);
 }
 
 template <class G, bool BF16, bool KDA>
@@ -249,18 +265,23 @@ hipError_t launch_step_fused(const gdnq_desc &d, const HeadMap &m, const gdnq_st
                              const void *k, const void *v, const float *a, const float *b, void *o,
                              hipStream_t st)
 {
+    // state heads: n_slots * H (n_slots = B for the plain call)
+    const size_t sh = (size_t)m.n_slots * (size_t)d.H;
     StepArgs A{q, k, v, a, b, o, s.codes, s.row_scale, s.col_scale,
-               (d.flags & GDNQ_DEBUG_PREQUANT) ? s.prequant_out : nullptr, nullptr, m};
+               (d.flags & GDNQ_DEBUG_PREQUANT) ? s.prequant_out : nullptr, nullptr, m,
+               sh * (size_t)d.dk, sh * (size_t)d.dv};
     const unsigned nh = (unsigned)d.B * (unsigned)d.H;
     return with_dims(d.dk, d.dv, [&](auto DK, auto DV) {
         using G = Geom<decltype(DK)::value, decltype(DV)::value>;
         return with_bool(d.io_dtype == GDNQ_IO_BF16, [&](auto bf) {
             return with_bool(d.decay == GDNQ_DECAY_CHANNEL, [&](auto kda) {
                 return with_bits(d.bits, [&](auto bits) {
-                    hipLaunchKernelGGL((step_fused_kernel<G, decltype(bf)::value, decltype(kda)::value,
-                                                          decltype(bits)::value>),
-                                       dim3(nh), dim3(G::NT), 0, st, A);
-                    return hipGetLastError();
+                    return with_bool((d.flags & GDNQ_STATIC_SCALES) != 0, [&](auto stat) {
+                        hipLaunchKernelGGL((step_fused_kernel<G, decltype(bf)::value, decltype(kda)::value,
+                                                              decltype(bits)::value, decltype(stat)::value>),
+                                           dim3(nh), dim3(G::NT), 0, st, A);
+                        return hipGetLastError();
+                    });
                 });
             });
         });
@@ -270,7 +291,7 @@ hipError_t launch_step_fused(const gdnq_desc &d, const HeadMap &m, const gdnq_st
 hipError_t launch_step_fp32(const gdnq_desc &d, float *S, const void *q, const void *k, const void *v,
                             const float *a, const float *b, void *o, hipStream_t st)
 {
-    StepArgs A{q, k, v, a, b, o, nullptr, nullptr, nullptr, nullptr, S, plain_map(d)};
+    StepArgs A{q, k, v, a, b, o, nullptr, nullptr, nullptr, nullptr, S, plain_map(d), 0, 0};
     const unsigned nh = (unsigned)d.B * (unsigned)d.H;
     return with_dims(d.dk, d.dv, [&](auto DK, auto DV) {
         using G = Geom<decltype(DK)::value, decltype(DV)::value>;

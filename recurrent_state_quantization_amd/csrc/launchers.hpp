@@ -24,6 +24,9 @@ hipError_t launch_dequantize(const gdnq_desc &d, const gdnq_state &s, float *S_o
 hipError_t launch_calibrate(const gdnq_desc &d, const float *S0, const void *k, const void *v,
                             const float *a, const float *b, int n_steps, int32_t *hp_idx,
                             float *score, hipStream_t st);
+hipError_t launch_fit_static(const gdnq_desc &d, const float *S0, const void *q, const void *k, const void *v,
+                             const float *a, const float *b, int n_steps, float *row_scale, float *col_scale,
+                             hipStream_t st);
 hipError_t launch_prefill(const gdnq_desc &d, float *S, const void *q, const void *k, const void *v,
                           const float *a, const float *b, void *o, int T, hipStream_t st);
 

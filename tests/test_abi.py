@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(g):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     out = subprocess.run(["nm", "-D", "--defined-only", g.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -251,3 +251,22 @@ def test_prefill_argument_errors(g):
     c, m = _err(lambda: call(args=args))
     assert c == 1 and "o overlaps S" in m
     g.gdn_prefill(d, S, None, None, None, None, None, None, 0, stream=0)   # T = 0: no launch
+
+
+def test_static_scale_arguments(g):
+    """GDNQ_STATIC_SCALES: per-step layout 0 only; both scale planes sized;
+    calibrate_static_scales needs the flag and n_steps >= 1."""
+    d = g.Desc(B=2, H=2, flags=g.STATIC_SCALES)
+    sz = g.gdnq_state_sizes(d)
+    base = g.gdnq_state_sizes(g.Desc(B=2, H=2))
+    assert sz[1] == 2 * base[1] and sz[2] == 2 * base[2]
+    c, m = _err(lambda: g.gdnq_state_sizes(g.Desc(B=2, H=2, W=4, flags=g.STATIC_SCALES)))
+    assert c == 2 and "static" in m
+    c, m = _err(lambda: g.gdnq_state_sizes(g.Desc(B=2, H=2, layout=g.LAYOUT_DAMP, n_hp=2, flags=g.STATIC_SCALES)))
+    assert c == 2
+    st = _fake_state(g, d)
+    io = [FAKE2 + i * (1 << 20) for i in range(6)]
+    c, m = _err(lambda: g.calibrate_static_scales(g.Desc(B=2, H=2), FAKE2 + (16 << 20), *io[:5], 4, st, stream=0))
+    assert c == 1 and "GDNQ_STATIC_SCALES" in m
+    c, m = _err(lambda: g.calibrate_static_scales(d, FAKE2 + (16 << 20), *io[:5], 0, st, stream=0))
+    assert c == 1 and "n_steps" in m
