@@ -273,9 +273,19 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
 
     dev_inputs = [up(i) for i in inputs]
     bits = cfg.get("bits", 8)
-    d = g.Desc(B=cfg["B"], H=cfg["H"], dk=dk, dv=dv, io_dtype=g.IO_BF16, bits=bits)
+    d = g.Desc(B=cfg["B"], H=cfg["H"], dk=dk, dv=dv, io_dtype=g.IO_BF16, bits=bits,
+               flags=g.STATIC_SCALES if args.static else 0)
     st = g.alloc_state(d)
     S_dev = torch.from_numpy(S).cuda()
+    if args.static:
+        # static scales fitted on 8 calibration steps (inputs of their own,
+        # steps 1000..1007 of the seeded stream) from the pre-filled states
+        log("fitting static scales on 8 calibration steps")
+        cal = synth.steps_inputs(cfg, 1000, 8)
+        cb = lambda n: torch.from_numpy(cal[n + "16"].view(np.int16)).cuda().view(torch.bfloat16)
+        g.calibrate_static_scales(d, S_dev, cb("q"), cb("k"), cb("v"), torch.from_numpy(cal["a"]).cuda(),
+                                  torch.from_numpy(cal["b"]).cuda(), 8, st)
+        del cal
     g.gdn_state_quantize(d, S_dev, st)
     o = torch.empty(nh * dv, dtype=torch.bfloat16, device="cuda")
     slots = None
@@ -318,7 +328,8 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
     value = nh * args.steps / wall
     res = {
         "metric": ("token-head state updates/s, INT8 GDN per-step decode (1 GPU)" if bits == 8 else
-                   f"token-head state updates/s, {bits}-bit GDN per-step decode (1 GPU)"),
+                   f"token-head state updates/s, {bits}-bit GDN per-step decode (1 GPU)")
+                  + (", static scales" if args.static else ""),
         "value": value,
         "unit": "token-head updates/s",
         "n_gpus": 1,
@@ -338,8 +349,10 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": b8 / per / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": b8 / per / 1e9 / HBM_PEAK_GBS,
-                     "traffic": stored_traffic("step_fused" + ("" if bits == 8 else f"_b{bits}"), "prefix_cache"),
-                     "kernel": f"step_fused_kernel<128x128, bf16, scalar gate, {bits}-bit codes>",
+                     "traffic": None if args.static else
+                                stored_traffic("step_fused" + ("" if bits == 8 else f"_b{bits}"), "prefix_cache"),
+                     "kernel": f"step_fused_kernel<128x128, bf16, scalar gate, {bits}-bit codes"
+                               + (", static scales>" if args.static else ">"),
                      "algorithmic_bytes_per_launch": b8, "mean_launch_s": per},
         "fp32_state": {"value": nh * args.steps / wall32, "ms_per_step": wall32 / args.steps * 1e3,
                        "achieved_GBs": b32 / per32 / 1e9, "frac": b32 / per32 / 1e9 / HBM_PEAK_GBS,
@@ -817,6 +830,9 @@ def main():
     ap.add_argument("--pool", type=int, default=0,
                     help="prefix_cache: keep the states in a pool of this many slots, the batch on a "
                          "seeded random subset (pool entry point)")
+    ap.add_argument("--static", action="store_true",
+                    help="prefix_cache: fit static scales on 8 calibration steps and time the per-step decode "
+                         "under them (GDNQ_STATIC_SCALES); no CPU leg")
     ap.add_argument("--stagger", action="store_true",
                     help="window workloads: entries at staggered window positions, each step followed "
                          "by a pool flush of the entries whose window ends (pool entry points)")
@@ -843,6 +859,9 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.workload, args.md)
         return
+    if args.static and (args.pool or args.workload != "prefix_cache"):
+        print("--static applies to the plain prefix_cache workload", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the decode path shards over independent "
               f"(batch, head) states with no exchange, and this build measures one GPU's share "
@@ -852,7 +871,7 @@ def main():
     if args.workload == "prefix_cache" and not args.copy_calibration:
         data = prefix_cache_data()
         data = (dict(data[0], bits=args.bits),) + data[1:]
-        if not args.no_cpu:
+        if not args.no_cpu and not args.static:
             log("timing the CPU oracle")
             cpu = cpu_baselines(*data)
     if args.workload == "prefill" and not args.copy_calibration:
