@@ -349,8 +349,8 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": b8 / per / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": b8 / per / 1e9 / HBM_PEAK_GBS,
-                     "traffic": None if args.static else
-                                stored_traffic("step_fused" + ("" if bits == 8 else f"_b{bits}"), "prefix_cache"),
+                     "traffic": stored_traffic("step_fused" + ("_static" if args.static else "")
+                                               + ("" if bits == 8 else f"_b{bits}"), "prefix_cache"),
                      "kernel": f"step_fused_kernel<128x128, bf16, scalar gate, {bits}-bit codes"
                                + (", static scales>" if args.static else ">"),
                      "algorithmic_bytes_per_launch": b8, "mean_launch_s": per},
@@ -751,10 +751,17 @@ def summarize_pmc(fetch_db: str, write_db: str, copy_fetch_db: str, copy_write_d
         lines.append(f"| {k} | {fetch[k]:.1f} | {write[k]:.1f} | {b:.4g} |")
         for tag in ("step_fused", "step_fp32", "window_step", "flush", "prefill"):
             if f"gdnq::{tag}_kernel" in k:
-                # the code width is the last template argument of the b-bit kernels
-                last = k.rstrip(">").split(",")[-1].strip()
-                if tag not in ("step_fp32", "prefill") and last in ("6", "4"):
-                    tag += "_b" + last
+                # template arguments after the geometry: the code width is the
+                # last one of the window kernels and the next-to-last of the
+                # fused step, whose last one is the static-scale flag
+                args = [x.strip() for x in k.rstrip(">").split(",")]
+                if tag == "step_fused":
+                    bits, static = args[-2], args[-1] == "true"
+                    tag += "_static" if static else ""
+                else:
+                    bits = args[-1]
+                if tag not in ("step_fp32", "prefill") and bits in ("6", "4"):
+                    tag += "_b" + bits
                 data.setdefault(workload, {})[tag] = {
                     "bytes_per_launch": b, "src_hash": src_hash(kernel_family(tag)), "fetch_kib": fetch[k],
                     "write_kib": write[k], "fetch_scale": fscale, "write_scale": wscale}
