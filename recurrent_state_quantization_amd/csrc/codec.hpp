@@ -36,7 +36,25 @@ struct CodecLds {
     float red[2][G::NW][G::DV];
     float iota[G::DV];
     int misc;
+    int flag[2][G::NW];  // per-wave flags of block_any, two sets used in turn
 };
+
+// Workgroup OR of a per-thread flag: each wave's ballot goes to its slot of
+// flag set `parity`, and after the barrier every thread ORs the slots.
+// Consecutive calls must alternate `parity`: the write to a set then
+// follows the barrier of the call in between, which every read of that
+// set precedes.
+template <class G>
+__device__ __forceinline__ bool block_any(CodecLds<G> &L, const Lane &c, bool x, int parity)
+{
+    const bool wave_any = __builtin_amdgcn_ballot_w64(x) != 0;
+    if (c.lane == 0) L.flag[parity][c.w] = wave_any ? 1 : 0;
+    __syncthreads();
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < G::NW; w++) any |= L.flag[parity][w];
+    return any != 0;
+}
 
 // Which of a thread's 8 rows are DAMP (fp16) rows, their slot in hp_idx and,
 // for the other rows, their index among the compacted INT8 rows.
@@ -338,7 +356,7 @@ __device__ void power_deflate(float (&P)[8][8], const Lane &c, CodecLds<G> &L, i
         for (int k = 0; k < 8; k++)
 #pragma unroll
             for (int j = 0; j < 8; j++) nz |= (P[k][j] != 0.0f);
-        const int any = __syncthreads_or(nz);
+        const bool any = block_any<G>(L, c, nz, cc & 1);
         float v[8], p[8];
         if (!any) {
 #pragma unroll
@@ -348,7 +366,7 @@ __device__ void power_deflate(float (&P)[8][8], const Lane &c, CodecLds<G> &L, i
 #pragma unroll
             for (int j = 0; j < 8; j++) v[j] = v0;
             // first step, with the restart rule; L.red[0] is free here (the
-            // barrier of __syncthreads_or follows every earlier read of it)
+            // barrier of block_any follows every earlier read of it)
             float n2 = power_step<G>(P, c, L.red[0], v);
             if (n2 == 0.0f) {  // uniform: every lane holds the same n2
                 float cn[8], cs[8];

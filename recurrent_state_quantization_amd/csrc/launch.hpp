@@ -39,7 +39,7 @@ inline Divisor make_divisor(unsigned d)
 
 __device__ __forceinline__ unsigned div_by(unsigned w, const Divisor &v)
 {
-    return v.d <= 1u ? w : (__umulhi(w, v.m) >> (v.l - 1u));
+    return v.d <= 1u ? w : ((unsigned)(((unsigned long long)w * v.m) >> 32) >> (v.l - 1u));
 }
 
 // Batch entry -> heads of one call.  Input head hi = b*H + hh (the

@@ -166,9 +166,9 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kernel(PrefillArgs A)
     static_assert(DT == 2 * NW, "two key-row tiles of W per wave");
     __shared__ Lds L;
 
-    const int tid = threadIdx.x;
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const unsigned bh = blockIdx.x;
+    const unsigned bh = __builtin_amdgcn_workgroup_id_x();
     const unsigned bb = div_by(bh, A.byH), hh = bh - bb * (unsigned)A.H;
     const unsigned kh = div_by(hh, A.byG);  // key head within the batch entry
     const int T = A.T;
