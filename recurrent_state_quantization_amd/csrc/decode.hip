@@ -13,11 +13,10 @@
 // straight off the codes:
 //   (S'^T k)_j = c_j sum_i (a_i s_i k_i) Q_ij
 //   o_j        = c_j sum_i (a_i s_i q_i) Q_ij + u_j (k . q)
-// which is S_t^T q of the updated fp32 state before requantization.  With
-// DV = 128 both column sums run on the matrix cores (mv_column_sums: the
-// codes are exact in bf16, the two vectors split into three bf16 planes
-// each), otherwise as fp32 FMAs plus cross-lane reductions.  The codec then
-// runs on P_ij = fma(k_i, u_j, (Q_ij c_j)(a_i s_i)).
+// which is S_t^T q of the updated fp32 state before requantization (fp32
+// FMAs over the thread's rows, then DPP / permlane reductions across the
+// lanes and LDS across the waves).  The codec then runs on
+// P_ij = fma(k_i, u_j, (Q_ij c_j)(a_i s_i)).
 //
 // The codes are read and written with non-temporal hints (each head's
 // codes are streamed once per call); measured on MI355X this is worth ~5%
@@ -49,7 +48,6 @@ struct StepLds {
     float red[G::NW][2][G::DV];
     float red_kq[G::NW];
     float u[G::DV];
-    alignas(8) uint16_t pl[8][G::DK];  // bf16 planes of a s k and a s q (matrix-core sums)
 };
 
 template <class G>
@@ -72,11 +70,8 @@ __device__ __forceinline__ void reduce_ro(const Lane &c, StepLds<G> &S, const fl
     if (c.lane == 0) S.red_kq[c.w] = kq_part;
 }
 
-// Occupancy: 8-bit codes fit 128 VGPRs (four workgroups per CU); the
-// bound also keeps the matrix-core results in VGPRs (no AGPR copies).  The
-// 6- and 4-bit unpackers need a few more registers: three per CU there.
 template <class G, bool BF16, bool KDA, int BITS, bool STATIC>
-__global__ __launch_bounds__(G::NT) __attribute__((amdgpu_waves_per_eu(BITS == 8 ? 4 : 3))) void step_fused_kernel(StepArgs A)
+__global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
 {
     __shared__ CodecLds<G> L;
     __shared__ StepLds<G> SL;
@@ -121,18 +116,13 @@ __global__ __launch_bounds__(G::NT) __attribute__((amdgpu_waves_per_eu(BITS == 8
     float cc[8];
     load_f32x8(cs + c.cb * 8, cc);
     const float bh = A.b[hi];
-    constexpr bool MV = G::NCB == 16;  // column sums on the matrix cores
     float kq_row = 0.0f;
     if (c.t < G::DK) {
         const float asi = ai * si;
         SL.rv[0][c.t] = asi;
+        SL.rv[1][c.t] = asi * ki;
+        SL.rv[2][c.t] = asi * qi;
         SL.rv[3][c.t] = ki;
-        if constexpr (MV) {
-            store_mv_planes<G>(SL.pl, c.t, asi * ki, asi * qi);
-        } else {
-            SL.rv[1][c.t] = asi * ki;
-            SL.rv[2][c.t] = asi * qi;
-        }
         kq_row = ki * qi;
     }
     if constexpr (STATIC) {
@@ -140,17 +130,11 @@ __global__ __launch_bounds__(G::NT) __attribute__((amdgpu_waves_per_eu(BITS == 8
         if (c.t < G::DV) L.iota[c.t] = io_t;
     }
     __syncthreads();
-    const float kq = row_sum<G>(kq_row);  // this lane's row group's share of k.q
+    const float kq = row_sum<G>(kq_row);  // this lane's row group's share: reduce_ro adds the rest
     float X[8][8];
 #pragma unroll
     for (int k = 0; k < 8; k++) unpack_code8<BITS>(qraw[k], X[k]);
-    if constexpr (MV) {
-        float s8[8];
-        mv_column_sums<G>(X, load_mv_planes<G>(SL.pl, c), s8);
-        if (c.lane < 32) store_f32x8(&SL.red[c.w][c.rgl][c.cb * 8], s8);  // lanes 0..15 R, 16..31 O
-        const float kq_w = col_allreduce<G, OpSum>(kq);
-        if (c.lane == 0) SL.red_kq[c.w] = kq_w;
-    } else {
+    {
         float ask[8], asq[8], R[8], O[8];
         load_rows_f32<G>(&SL.rv[1][row0], ask);
         load_rows_f32<G>(&SL.rv[2][row0], asq);

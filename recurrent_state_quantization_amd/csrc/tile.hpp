@@ -527,89 +527,6 @@ __device__ __forceinline__ CodeWord pack_code8(const float (&y)[8])
     return w;
 }
 
-// ------------------------------------------------ column sums on the MFMA
-// The per-step decode's two mat-vecs  sum_i x_i Q_ij  (x = a s k and
-// a s q over the key rows) read the codes off the register tile.  With
-// DV = 128 (NCB = 16) the 16 lanes of a row group hold the same 8 rows, so
-// v_mfma_f32_16x16x32_bf16 with B = the tile's column j (lane (g, cb): its
-// 8 codes of column 8cb+j, exact in bf16) and A = row-vector planes (lane
-// (g, m): plane m of the same 8 rows) sums a whole wave's 32 rows at once:
-// D[m][cb] = sum over the wave's rows of plane_m(row) * X(row, 8cb+j).
-// Each fp32 vector is carried as three bf16 planes (hi + mid + lo, the
-// first two differences exact), so the products are exact and the sum is
-// fp32-class; the matrix cores take the work off the VALU, which bounds
-// this kernel.
-typedef __bf16 mv_bf16x8 __attribute__((ext_vector_type(8)));
-typedef float mv_f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int mv_u32x4 __attribute__((ext_vector_type(4)));
-
-// x = hi + mid + lo + e, |e| <= 2^-24 |x| (hi, mid truncated: x - hi and
-// (x - hi) - mid are exact; lo rounded to nearest).
-__device__ __forceinline__ void split3_bf16(float x, uint16_t &h, uint16_t &m, uint16_t &l)
-{
-    const uint32_t xb = __float_as_uint(x);
-    const float r1 = x - __uint_as_float(xb & 0xFFFF0000u);
-    const uint32_t rb = __float_as_uint(r1);
-    const float r2 = r1 - __uint_as_float(rb & 0xFFFF0000u);
-    h = (uint16_t)(xb >> 16);
-    m = (uint16_t)(rb >> 16);
-    l = f32_to_bf16(r2);
-}
-
-// bf16 of two floats that are exact small integers (their high halves).
-__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi)
-{
-    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
-// Planes of the two row vectors in LDS, [8][DK] bf16: 0..2 the pieces of
-// the first vector, 4..6 those of the second, 3 and 7 zero.  Lane (g, m)
-// loads plane m (m < 8; a zero plane for m >= 8) of its 8 rows.
-template <class G>
-__device__ __forceinline__ mv_bf16x8 load_mv_planes(const uint16_t (&pl)[8][G::DK], const Lane &c)
-{
-    static_assert(G::NCB == 16, "matrix-core column sums need DV = 128");
-    const int p = c.cb < 8 ? c.cb : 3;
-    const int row0 = row0_of<G>(c);
-    const uint2 a = *reinterpret_cast<const uint2 *>(&pl[p][row0]);
-    const uint2 b = *reinterpret_cast<const uint2 *>(&pl[p][row0 + G::RGW * 4]);
-    return __builtin_bit_cast(mv_bf16x8, (mv_u32x4){a.x, a.y, b.x, b.y});
-}
-
-// Thread t < DK writes row t's planes of x (planes 0..2) and y (4..6).
-template <class G>
-__device__ __forceinline__ void store_mv_planes(uint16_t (&pl)[8][G::DK], int t, float x, float y)
-{
-    uint16_t h, m, l;
-    split3_bf16(x, h, m, l);
-    pl[0][t] = h;
-    pl[1][t] = m;
-    pl[2][t] = l;
-    pl[3][t] = 0;
-    split3_bf16(y, h, m, l);
-    pl[4][t] = h;
-    pl[5][t] = m;
-    pl[6][t] = l;
-    pl[7][t] = 0;
-}
-
-// The wave's column sums of X for both vectors: lanes 0..15 get the first
-// vector's sums of columns 8cb+j (j = 0..7) in s[j], lanes 16..31 the
-// second's; the other lanes hold zeros.
-template <class G>
-__device__ __forceinline__ void mv_column_sums(const float (&X)[8][8], mv_bf16x8 av, float (&s)[8])
-{
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const mv_u32x4 b = {pack_bf16_exact(X[0][j], X[1][j]), pack_bf16_exact(X[2][j], X[3][j]),
-                            pack_bf16_exact(X[4][j], X[5][j]), pack_bf16_exact(X[6][j], X[7][j])};
-        const mv_f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(mv_bf16x8, b),
-                                                                   (mv_f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-        s[j] = (d[2] + d[1]) + d[0];
-        if (j & 1) __builtin_amdgcn_sched_barrier(0);  // two products in flight: bounds the live operands
-    }
-}
-
 // fma(y, iota, 1.5*2^23) rounds the exact value y*iota + 1.5*2^23 once, at
 // unit spacing (the sum lies in [2^23, 2^24) for |y*iota| < 2^22), so it
 // equals 1.5*2^23 + rint_even(y*iota) with the product taken exactly; the
