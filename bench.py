@@ -12,7 +12,7 @@ the decode kernel against 8 TB/s HBM, and the plain fp64 CPU oracle timed
 on a bounded sample of the same workload).
 
     python bench.py [--steps 100] [--warmup 200] [--gpus 1]
-                    [--workload prefix_cache|gdn_serving|kda|damp|tiny|prefill]
+                    [--workload prefix_cache|gdn_serving|kda|damp|tiny|prefill|prefill_kda]
                     [--no-cpu] [--no-graph] [--no-diag] [--bits 8|6|4] [--copy-calibration]
 """
 from __future__ import annotations
@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "step": ("decode.hip", "tile.hpp", "codec.hpp", "launch.hpp"),
     "window": ("window.hip", "tile.hpp", "codec.hpp", "launch.hpp"),
     "prefill": ("prefill.hip", "launch.hpp"),
+    "prefill_kda": ("prefill_kda.hip", "launch.hpp"),
 }
 
 
@@ -53,6 +54,8 @@ def kernel_family(tag: str) -> str:
         return "step"
     if tag.startswith(("window_step", "flush")):
         return "window"
+    if tag.startswith("prefill_kda"):
+        return "prefill_kda"
     return "prefill"
 
 
@@ -122,13 +125,26 @@ def prefill_chunk_flops(D: int, C: int = 64) -> int:
     return gram + inv + 2 * (2 * C * C * D) + 2 * (2 * C * D * D) + (6 * C * C * D * 2) // 8 + 2 * D * C * D
 
 
+def prefill_kda_chunk_flops(D: int, C: int = 16) -> int:
+    """Algorithmic flops of one C-token chunk of one head in the per-channel
+    chunk form (each product counted once, second bf16 parts not counted):
+    the decayed Gram sums (A on the C(C-1)/2 pairs below the diagonal, P on
+    the C(C+1)/2 pairs with it, D channels each), the forward substitution,
+    W and U (C x C x D each), U - W S and (Q . e^G) S (C x D x D each), P U'
+    (C x C x D) and the state update (D x C x D)."""
+    gram = 2 * (C * (C - 1) // 2 + C * (C + 1) // 2) * D
+    inv = 2 * C * (C * (C - 1) // 2)
+    return gram + inv + 2 * (2 * C * C * D) + 2 * (2 * C * D * D) + 2 * C * C * D + 2 * D * C * D
+
+
 def prefill_bytes(cfg: dict, T: int) -> int:
     """Algorithmic HBM bytes of one prefill call: q, k, v read and o written
-    once (bf16), a and b read once, each head's fp32 state read and written
-    once."""
+    once (bf16), a (one value per head, or dk per head for the per-channel
+    gate) and b read once, each head's fp32 state read and written once."""
     B, H, D = cfg["B"], cfg["H"], cfg["dk"]
     hk = cfg.get("hk", H)
-    per_token = B * (hk * 2 * D * 2 + H * (2 * D * 2 + 8))
+    na = D if cfg["decay"] == "channel" else 1
+    per_token = B * (hk * 2 * D * 2 + H * (2 * D * 2 + 4 * na + 4))
     return T * per_token + B * H * 2 * D * D * 4
 
 
@@ -367,8 +383,8 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
     return res
 
 
-def prefill_data():
-    cfg = synth.WORKLOADS["prefill"]
+def prefill_data(name: str = "prefill"):
+    cfg = synth.WORKLOADS[name]
     log(f"generating {cfg['T']} tokens x {cfg['B'] * cfg['H']} heads of prefill input")
     return cfg, synth.token_major_inputs(cfg, cfg["T"])
 
@@ -384,7 +400,8 @@ def cpu_prefill_baseline(cfg: dict, x: dict, budget_s: float = 10.0) -> dict:
     while time.perf_counter() - t0 < budget_s and t < cfg["T"]:
         n = min(step, cfg["T"] - t)
         f = lambda name: np.ascontiguousarray(synth.bf16_to_f32(x[name][0, t:t + n, :nh]))
-        S, _ = oracle.recur(S, f("q16"), f("k16"), f("v16"), x["a"][0, t:t + n, :nh, None], x["b"][0, t:t + n, :nh])
+        ga = x["a"][0, t:t + n, :nh, None] if cfg["decay"] == "scalar" else x["a"][0, t:t + n, :nh]
+        S, _ = oracle.recur(S, f("q16"), f("k16"), f("v16"), np.ascontiguousarray(ga), x["b"][0, t:t + n, :nh])
         t += n
         done += n * nh
     dt = time.perf_counter() - t0
@@ -401,7 +418,8 @@ def bench_prefill(args, torch, g, cfg, x, cpu):
     a, b = torch.from_numpy(x["a"]).cuda(), torch.from_numpy(x["b"]).cuda()
     S = torch.zeros((nh, D, D), dtype=torch.float32, device="cuda")
     o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
-    d = g.Desc(B=B, H=H, dk=D, dv=D, io_dtype=g.IO_BF16)
+    kda = cfg["decay"] == "channel"
+    d = g.Desc(B=B, H=H, dk=D, dv=D, io_dtype=g.IO_BF16, decay=g.DECAY_CHANNEL if kda else g.DECAY_SCALAR)
     dc, sh = d.c(), torch.cuda.current_stream().cuda_stream
     p = [t.data_ptr() for t in (S, q, k, v, a, b, o)]
 
@@ -410,21 +428,27 @@ def bench_prefill(args, torch, g, cfg, x, cpu):
 
     log("timing the prefill")
     wall, per = time_launches(torch, call, args.steps, args.warmup)
-    flops = prefill_chunk_flops(D) * nh * ((T + 63) // 64)
+    if kda:
+        flops = prefill_kda_chunk_flops(D) * nh * ((T + 15) // 16)
+        tag, kernel = "prefill_kda", f"prefill_kda_kernel<{D}>"
+    else:
+        flops = prefill_chunk_flops(D) * nh * ((T + 63) // 64)
+        tag, kernel = "prefill", f"prefill_kernel<{D}>"
     nbytes = prefill_bytes(cfg, T)
     res = {
-        "metric": "token-head state updates/s, chunkwise GDN prefill (1 GPU)",
+        "metric": f"token-head state updates/s, chunkwise {'KDA' if kda else 'GDN'} prefill (1 GPU)",
         "value": nh * T * args.steps / wall, "unit": "token-head updates/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16 q/k/v/o, bf16 MFMA with split fp32 operands, fp32 state",
         "data": "synthetic (seeded; no weights)",
-        "config": {"workload": f"prefill: B={B} sequences x H={H} heads x T={T} tokens, dk=dv={D}, "
-                               "bf16 I/O, scalar gate, zero initial state", "B": B, "H": H, "T": T, "dk": D},
+        "config": {"workload": f"{tag}: B={B} sequences x H={H} heads x T={T} tokens, dk=dv={D}, bf16 I/O, "
+                               f"{'per-channel' if kda else 'scalar'} gate, zero initial state",
+                   "B": B, "H": H, "T": T, "dk": D},
         "roofline": {"bound": "mfma", "achieved": flops / per / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / per / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": stored_traffic("prefill", "prefill"),
-                     "kernel": f"prefill_kernel<{D}>", "algorithmic_flops_per_launch": flops,
+                     "traffic": stored_traffic(tag, tag),
+                     "kernel": kernel, "algorithmic_flops_per_launch": flops,
                      "mean_launch_s": per},
         "hbm": {"algorithmic_bytes_per_launch": nbytes, "achieved_GBs": nbytes / per / 1e9,
                 "frac": nbytes / per / 1e9 / HBM_PEAK_GBS},
@@ -749,7 +773,7 @@ def summarize_pmc(fetch_db: str, write_db: str, copy_fetch_db: str, copy_write_d
             continue
         b = fetch[k] * 1024 * fscale + write[k] * 1024 * wscale
         lines.append(f"| {k} | {fetch[k]:.1f} | {write[k]:.1f} | {b:.4g} |")
-        for tag in ("step_fused", "step_fp32", "window_step", "flush", "prefill"):
+        for tag in ("step_fused", "step_fp32", "window_step", "flush", "prefill", "prefill_kda"):
             if f"gdnq::{tag}_kernel" in k:
                 # template arguments after the geometry: the code width is the
                 # last one of the window kernels and the next-to-last of the
@@ -760,7 +784,7 @@ def summarize_pmc(fetch_db: str, write_db: str, copy_fetch_db: str, copy_write_d
                     tag += "_static" if static else ""
                 else:
                     bits = args[-1]
-                if tag not in ("step_fp32", "prefill") and bits in ("6", "4"):
+                if tag not in ("step_fp32", "prefill", "prefill_kda") and bits in ("6", "4"):
                     tag += "_b" + bits
                 data.setdefault(workload, {})[tag] = {
                     "bytes_per_launch": b, "src_hash": src_hash(kernel_family(tag)), "fetch_kib": fetch[k],
@@ -830,7 +854,7 @@ def main():
     # clocks; the first calls after start-up run up to ~40% slower
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="prefix_cache",
-                    choices=["prefix_cache", "gdn_serving", "kda", "damp", "tiny", "prefill"])
+                    choices=["prefix_cache", "gdn_serving", "kda", "damp", "tiny", "prefill", "prefill_kda"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--bits", type=int, default=8, choices=[8, 6, 4],
                     help="code width of the quantized state (default 8)")
@@ -881,8 +905,8 @@ def main():
         if not args.no_cpu and not args.static:
             log("timing the CPU oracle")
             cpu = cpu_baselines(*data)
-    if args.workload == "prefill" and not args.copy_calibration:
-        data = prefill_data()
+    if args.workload in ("prefill", "prefill_kda") and not args.copy_calibration:
+        data = prefill_data(args.workload)
         cpu = None
         if not args.no_cpu:
             log("timing the CPU oracle")
@@ -899,7 +923,7 @@ def main():
         return
     if args.workload == "prefix_cache":
         res = bench_prefix_cache(args, torch, g, *data, cpu)
-    elif args.workload == "prefill":
+    elif args.workload in ("prefill", "prefill_kda"):
         res = bench_prefill(args, torch, g, *data, cpu)
     elif args.workload == "tiny":
         res = bench_tiny(args, torch, g)

@@ -285,19 +285,21 @@ int gdn_fp32_decode_step(const gdnq_desc *desc, float *S, const void *q, const v
 /*
  * Prefill ("LinQuant: Functional Invariances for Low-Precision Linear
  * Recurrences", abstract: chunkwise-parallel prefill casts most of the
- * recurrence as dense matrix products; appendix Table 3, Gated DeltaNet
- * row).  Runs T tokens of the recurrence for all B*H heads at once, in
- * chunks of 64 tokens on the matrix cores, and writes every token's output:
+ * recurrence as dense matrix products; appendix Table 3, Gated DeltaNet and
+ * KDA rows).  Runs T tokens of the recurrence for all B*H heads at once,
+ * chunk by chunk on the matrix cores (64 tokens per chunk for the scalar
+ * gate, 16 for the per-channel gate), and writes every token's output:
  *   S      device fp32 [B,H,dk,dv], in place: the state before token 0 on
  *          entry (zeros for a new sequence, gdn_state_dequantize's output to
  *          continue a cached prefix), the state after token T-1 on return.
  *   q, k   device bf16 [B,T,hk,dk] (hk = H unless set); v device bf16 [B,T,H,dv]
- *   a      device fp32 [B,T,H], the scalar gate, 0 < a <= 1 (no bound on
- *          the product of gates: the chunk form works with log-gates)
+ *   a      device fp32, 0 < a <= 1: [B,T,H] for GDNQ_DECAY_SCALAR, [B,T,H,dk]
+ *          for GDNQ_DECAY_CHANNEL (no bound on the product of gates: the
+ *          chunk forms work with log-gates and only non-positive exponents)
  *   b      device fp32 [B,T,H]
  *   o      device bf16 [B,T,H,dv], o_t = S_t^T q_t
- * Supported: io_dtype GDNQ_IO_BF16, decay GDNQ_DECAY_SCALAR, dk == dv (64
- * or 128); other descriptors return GDNQ_EUNSUPPORTED.  W, r, layout,
+ * Supported: io_dtype GDNQ_IO_BF16, either decay, dk == dv (64 or 128);
+ * other descriptors return GDNQ_EUNSUPPORTED.  W, r, layout,
  * n_hp, bits and the state struct play no part.  Products run in bf16 with
  * fp32 accumulation, fp32 operands split into two bf16 parts, so results
  * stay near fp32 accuracy.  T == 0 is a no-op (the buffers may be NULL).

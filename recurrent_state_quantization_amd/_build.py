@@ -23,7 +23,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdnq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "decode.hip", "window.hip", "codec.hip", "calibrate.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "decode.hip", "window.hip", "codec.hip", "calibrate.hip", "prefill.hip", "prefill_kda.hip"]
 HEADERS = ["tile.hpp", "codec.hpp", "launch.hpp", "launchers.hpp"]
 
 COMMON = [

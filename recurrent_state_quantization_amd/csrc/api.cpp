@@ -52,6 +52,7 @@ size_t nheads(const gdnq_desc &d) { return (size_t)d.B * (size_t)d.H; }
 bool per_step(const gdnq_desc &d) { return d.W == 1 && d.r == 0; }
 int code_bits(const gdnq_desc &d) { return d.bits == 0 ? 8 : d.bits; }
 size_t nkheads(const gdnq_desc &d) { return (size_t)d.B * (size_t)(d.hk ? d.hk : d.H); }
+size_t agate(const gdnq_desc &d) { return d.decay == GDNQ_DECAY_CHANNEL ? (size_t)d.dk : 1; }  // gate values per head
 
 int check_desc(const gdnq_desc *d)
 {
@@ -425,7 +426,6 @@ int gdn_prefill(const gdnq_desc *desc, float *S, const void *q, const void *k, c
     if (rc) return rc;
     const gdnq_desc &d = *desc;
     if (d.io_dtype != GDNQ_IO_BF16) return fail(GDNQ_EUNSUPPORTED, "gdn_prefill takes bf16 q, k, v and o");
-    if (d.decay != GDNQ_DECAY_SCALAR) return fail(GDNQ_EUNSUPPORTED, "gdn_prefill implements the scalar gate");
     if (d.dk != d.dv) return fail(GDNQ_EUNSUPPORTED, "gdn_prefill needs dk == dv (got %d, %d)", d.dk, d.dv);
     if (T < 0) return fail(GDNQ_EINVAL, "T must be >= 0 (got %d)", T);
     const size_t nh = nheads(d), nt = (size_t)T;
@@ -438,13 +438,15 @@ int gdn_prefill(const gdnq_desc *desc, float *S, const void *q, const void *k, c
         size_t n;
         const char *name;
     } ins[5] = {{q, nt * nkheads(d) * d.dk * 2, "q"}, {k, nt * nkheads(d) * d.dk * 2, "k"},
-                {v, nt * nh * d.dv * 2, "v"}, {a, nt * nh * 4, "a"}, {b, nt * nh * 4, "b"}};
+                {v, nt * nh * d.dv * 2, "v"}, {a, nt * nh * agate(d) * 4, "a"}, {b, nt * nh * 4, "b"}};
     for (const In &in : ins) {
         std::vector<Span> tmp = spans;
         if ((rc = check_buf(in.p, in.n, in.name, tmp, T == 0))) return rc;
     }
     if (T == 0) return ok();
-    return launched(gdnq::launch_prefill(d, S, q, k, v, a, b, o, T, reinterpret_cast<hipStream_t>(stream)));
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (d.decay == GDNQ_DECAY_CHANNEL) return launched(gdnq::launch_prefill_kda(d, S, q, k, v, a, b, o, T, st));
+    return launched(gdnq::launch_prefill(d, S, q, k, v, a, b, o, T, st));
 }
 
 }  // extern "C"

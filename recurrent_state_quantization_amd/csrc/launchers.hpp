@@ -29,5 +29,7 @@ hipError_t launch_fit_static(const gdnq_desc &d, const float *S0, const void *q,
                              hipStream_t st);
 hipError_t launch_prefill(const gdnq_desc &d, float *S, const void *q, const void *k, const void *v,
                           const float *a, const float *b, void *o, int T, hipStream_t st);
+hipError_t launch_prefill_kda(const gdnq_desc &d, float *S, const void *q, const void *k, const void *v,
+                              const float *a, const float *b, void *o, int T, hipStream_t st);
 
 }  // namespace gdnq

@@ -1,0 +1,479 @@
+// prefill_kda.hip -- chunkwise-parallel prefill of the delta rule with a
+// per-key-channel gate (KDA) on the matrix cores (gdn_prefill with
+// GDNQ_DECAY_CHANNEL).
+//
+// The recurrence is the KDA row of Table 3 in "LinQuant: Functional
+// Invariances for Low-Precision Linear Recurrences" (appendix), in the
+// dk x dv orientation: S_t = diag(a_t) S_{t-1} + k_t u_t^T with
+// u_t = b_t (v_t - (diag(a_t) S_{t-1})^T k_t), o_t = S_t^T q_t.  That
+// page's abstract notes that chunkwise-parallel prefill turns most of it
+// into dense products; the chunk form is the WY/UT form of the delta rule
+// (Yang et al., "Parallelizing Linear Transformers with the Delta Rule
+// over Sequence Length", 2024) with the scalar decay of its gated variant
+// replaced by a diagonal one.  For a chunk of C = 16 tokens, with
+// G_tc = sum_{s<=t} log a_sc counted from the chunk start (per key channel
+// c), S the state at the chunk start and beta = b:
+//     A_ij = beta_i sum_c k_ic k_jc e^{G_ic - G_jc}    (i > j)
+//     P_ij = sum_c q_ic k_jc e^{G_ic - G_jc}           (i >= j)
+//     T  = (I + A)^{-1},  T1 = T diag(beta)
+//     W  = T1 (K . e^G),  U = T1 V,  U' = U - W S      (row i is u_i)
+//     O  = (Q . e^G) S + P U'
+//     S <- diag(e^{G_C}) S + (K . e^{G_C - G})^T U'
+// which is the token recurrence unrolled over the chunk: with
+// Gam_t = e^{G_t}, diag(a_t) S_{t-1} = diag(Gam_t) S
+// + sum_{j<t} diag(Gam_t / Gam_j) k_j u_j^T, so (I + A) U' =
+// diag(beta) V - diag(beta) (K . Gam) S, and S_t^T q_t gives O.  Every
+// exponent used is <= 0 (the decays of A and P are taken pair by pair,
+// never as a quotient of two chunk-wide factors), so no gate can overflow.
+//
+// Precision as in the scalar-gate kernel (prefill.hip): bf16 matrix products
+// with fp32 accumulation, q, k, v exact in bf16, every fp32 operand split
+// into two bf16 parts.  The decayed Gram sums A and P run on the VALU in
+// fp32 (one e^{G_ic - G_jc} per pair and channel: the per-channel decay
+// does not factor out of the contraction); T by forward substitution in
+// fp32.
+//
+// Mapping: one workgroup per (batch, head); wave w owns value columns
+// 32w..32w+31 of the state, kept in fp32 MFMA accumulators for the whole
+// sequence (the layout and the permuted contraction of the scalar-gate
+// kernel), and key channels 32w..32w+31 of the chunk-local work (its share
+// of the Gram sums and of W).  Products over the chunk's 16 tokens use
+// v_mfma_f32_16x16x16_bf16, whose accumulator layout is its own B operand
+// layout: U' feeds P U' and the state update straight from registers.
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+#include "launchers.hpp"
+
+namespace gdnq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int KC = 16;                    // tokens per chunk
+constexpr int NPAIR = KC * (KC + 1) / 2;  // pairs i >= j
+constexpr int SA = KC + 4;                // fp32 stride of the A^T tile
+
+__device__ __forceinline__ floatx4 mma32(bf16x8 a, bf16x8 b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mma16(bf16x4 a, bf16x4 b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, a), __builtin_bit_cast(short4v, b),
+                                                     c, 0, 0, 0);
+}
+
+// element e of h and l <- the two bf16 parts of x
+template <class V>
+__device__ __forceinline__ void split(float x, V &h, V &l, int e)
+{
+    const __bf16 hi = (__bf16)x;
+    h[e] = hi;
+    l[e] = (__bf16)(x - (float)hi);
+}
+
+// Operand in the permuted slot order: 4 values at p, then 4 at p + 16.
+__device__ __forceinline__ bf16x8 ld_pair(const __bf16 *p)
+{
+    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+    const bf16x4 y = *reinterpret_cast<const bf16x4 *>(p + 16);
+    return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+
+__device__ __forceinline__ bf16x8 ld8(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ bf16x4 ld4(const __bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
+__device__ __forceinline__ floatx4 ldf4(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
+
+// pair index p = i (i + 1) / 2 + j (j <= i) -> i
+__device__ __forceinline__ int pair_row(int p)
+{
+    int i = (int)((sqrtf(8.0f * (float)p + 1.0f) - 1.0f) * 0.5f);
+    if (i * (i + 1) / 2 > p) i--;
+    if ((i + 1) * (i + 2) / 2 <= p) i++;
+    return i;
+}
+
+}  // namespace
+
+template <int D>
+struct KdaLds {
+    static constexpr int NW = D / 32;
+    static constexpr int SD = D + 8;   // bf16 stride of token-major [KC][D] tiles (16-byte pad)
+    static constexpr int SG = D + 4;   // fp32 stride of the gate tile
+    static constexpr int ST = KC + 8;  // bf16 stride of channel-major [D][KC] and of [KC][KC] tiles
+    __bf16 kr[KC * SD];                // K, token-major (then the chunk's outputs)
+    __bf16 qr[KC * SD];                // Q, token-major
+    float g[KC * SG];                  // G in base 2: cumulative log2 gates from the chunk start
+    __bf16 vt[D * ST];                 // V^T
+    __bf16 qgh[KC * SD], qgl[KC * SD];  // Q . 2^G, split, token-major
+    __bf16 kgh[D * ST], kgl[D * ST];    // (K . 2^G)^T, split
+    __bf16 kch[D * ST], kcl[D * ST];    // (K . 2^(G_C - G))^T, split
+    __bf16 wh[KC * SD], wl[KC * SD];    // -W, split, token-major
+    __bf16 t1h[KC * ST], t1l[KC * ST];  // T1 = T diag(beta), split
+    __bf16 ph[KC * ST], pl[KC * ST];    // P, split (upper part zero)
+    float at[KC * SA];                  // A^T: at[j * SA + i] = A_ij (i > j), zero elsewhere
+    float part[NW][2][NPAIR];           // per-wave Gram sums (A without beta, P)
+    float beta[KC];
+};
+
+struct PrefillKdaArgs {
+    float *S;
+    const __bf16 *q, *k, *v;
+    const float *a, *b;
+    __bf16 *o;
+    int T, H, HK;
+    Divisor byH, byG;
+};
+
+template <int D>
+__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kda_kernel(PrefillKdaArgs A)
+{
+    using Lds = KdaLds<D>;
+    constexpr int SD = Lds::SD, SG = Lds::SG, ST = Lds::ST;
+    constexpr int NW = D / 32, NT = NW * 64;  // waves; wave w owns value columns and key channels 32w..32w+31
+    constexpr int KB = D / 32;                // 32-wide blocks along a head dim
+    constexpr int DT = D / 16;                // 16-row tiles along a head dim
+    constexpr int TPT = KC * D / NT;          // tokens per thread of the element-wise stage
+    static_assert(TPT == 8, "one thread takes 8 tokens of one channel");
+    __shared__ Lds L;
+
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const unsigned bh = __builtin_amdgcn_workgroup_id_x();
+    const unsigned bb = div_by(bh, A.byH), hh = bh - bb * (unsigned)A.H;
+    const unsigned kh = div_by(hh, A.byG);  // key head within the batch entry
+    const int T = A.T;
+    const size_t tk = (size_t)A.HK * D, tv = (size_t)A.H * D;  // token strides (elements)
+    const __bf16 *qg = A.q + (size_t)bb * T * tk + (size_t)kh * D;
+    const __bf16 *kg = A.k + (size_t)bb * T * tk + (size_t)kh * D;
+    const __bf16 *vg = A.v + (size_t)bb * T * tv + (size_t)hh * D;
+    __bf16 *og = A.o + (size_t)bb * T * tv + (size_t)hh * D;
+    const float *ag = A.a + (size_t)bb * T * tv + (size_t)hh * D;  // a: [B, T, H, D]
+    const float *bg = A.b + (size_t)bb * T * A.H + hh;
+    float *Sg = A.S + (size_t)bh * D * D;
+    const int e0 = 32 * wave;  // value columns e0 + 16 et + ln, et = 0, 1
+    int lg = (tid & 63) >> 4, ln = tid & 15;
+
+    // Entries never written by the chunk loop (P's upper part, A^T's
+    // diagonal and upper part) are cleared once.
+    for (int x = tid; x < KC * ST; x += NT) {
+        L.ph[x] = (__bf16)0.0f;
+        L.pl[x] = (__bf16)0.0f;
+    }
+    for (int x = tid; x < KC * SA; x += NT) L.at[x] = 0.0f;
+
+    // S[et][dt][r] = S[16 dt + 4 lg + r][e0 + 16 et + ln] (MFMA accumulator layout)
+    floatx4 S[2][DT];
+#pragma unroll
+    for (int et = 0; et < 2; et++)
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                S[et][dt][r] = Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + 16 * et + ln];
+
+    for (int c0 = 0; c0 < T; c0 += KC) {
+        __syncthreads();  // the previous chunk is done with every LDS tile
+        // Lane indices pass through an empty asm each chunk, so the LDS
+        // addresses built from them are formed inside the loop instead of
+        // being hoisted out and held in registers across it.
+        asm volatile("" : "+v"(lg), "+v"(ln));
+        const int nv = min(KC, T - c0);  // valid tokens of this chunk
+
+        // ---- stage K, Q token-major and V^T (tokens past the end are zero),
+        // the gates (thread c < D scans channel c; padding has gate 1) and beta
+        for (int x = tid; x < KC * D / 8; x += NT) {
+            const int t = x / (D / 8), c = 8 * (x % (D / 8));
+            const bool ok = t < nv;
+            const size_t u = (size_t)(c0 + (ok ? t : 0));
+            u32x4 kx = *reinterpret_cast<const u32x4 *>(kg + u * tk + c);
+            u32x4 qx = *reinterpret_cast<const u32x4 *>(qg + u * tk + c);
+            u32x4 vx = *reinterpret_cast<const u32x4 *>(vg + u * tv + c);
+            if (!ok) kx = qx = vx = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4 *>(&L.kr[t * SD + c]) = kx;
+            *reinterpret_cast<u32x4 *>(&L.qr[t * SD + c]) = qx;
+            const bf16x8 vv = __builtin_bit_cast(bf16x8, vx);
+#pragma unroll
+            for (int e = 0; e < 8; e++) L.vt[(c + e) * ST + t] = vv[e];
+        }
+        if (tid < D) {
+            float av[KC];
+#pragma unroll
+            for (int t = 0; t < KC; t++) av[t] = ag[(size_t)(c0 + min(t, nv - 1)) * tv + tid];
+            float acc = 0.0f;
+#pragma unroll
+            for (int t = 0; t < KC; t++) {
+                acc += t < nv ? __builtin_amdgcn_logf(av[t]) : 0.0f;
+                L.g[t * SG + tid] = acc;
+            }
+        }
+        if (tid < KC) L.beta[tid] = tid < nv ? bg[(size_t)(c0 + tid) * A.H] : 0.0f;
+        __syncthreads();
+
+        // ---- element-wise operands: Q . 2^G (token-major), (K . 2^G)^T and
+        // (K . 2^(G_C - G))^T (channel-major), all split; every exponent <= 0
+        {
+            const int c = tid % D, t0 = TPT * (tid / D);
+            const float gC = L.g[(KC - 1) * SG + c];
+            bf16x8 gh, gl, ch, cl;
+#pragma unroll
+            for (int e = 0; e < TPT; e++) {
+                const int t = t0 + e;
+                const float gv = L.g[t * SG + c];
+                const float kv = (float)L.kr[t * SD + c], qv = (float)L.qr[t * SD + c];
+                const float e1 = __builtin_amdgcn_exp2f(gv), e2 = __builtin_amdgcn_exp2f(gC - gv);
+                split(kv * e1, gh, gl, e);
+                split(kv * e2, ch, cl, e);
+                const float qe = qv * e1;
+                const __bf16 qh = (__bf16)qe;
+                L.qgh[t * SD + c] = qh;
+                L.qgl[t * SD + c] = (__bf16)(qe - (float)qh);
+            }
+            *reinterpret_cast<bf16x8 *>(&L.kgh[c * ST + t0]) = gh;
+            *reinterpret_cast<bf16x8 *>(&L.kgl[c * ST + t0]) = gl;
+            *reinterpret_cast<bf16x8 *>(&L.kch[c * ST + t0]) = ch;
+            *reinterpret_cast<bf16x8 *>(&L.kcl[c * ST + t0]) = cl;
+        }
+        // ---- the decayed Gram sums over this wave's 32 key channels: lane
+        // (i, jg) takes the pairs (i, j), j = jg + 4m <= i
+        {
+            const int lane = tid & 63, i = lane >> 2, jg = lane & 3;
+            float sa[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int cq = 0; cq < 4; cq++) {
+                const int c = 32 * wave + 8 * cq;
+                const bf16x8 kiv = ld8(&L.kr[i * SD + c]), qiv = ld8(&L.qr[i * SD + c]);
+                const floatx4 gi0 = ldf4(&L.g[i * SG + c]), gi1 = ldf4(&L.g[i * SG + c + 4]);
+#pragma unroll
+                for (int m = 0; m < 4; m++) {
+                    const int j = jg + 4 * m;
+                    if (j <= i) {
+                        const bf16x8 kjv = ld8(&L.kr[j * SD + c]);
+                        const floatx4 gj0 = ldf4(&L.g[j * SG + c]), gj1 = ldf4(&L.g[j * SG + c + 4]);
+#pragma unroll
+                        for (int e = 0; e < 8; e++) {
+                            const float gi = e < 4 ? gi0[e] : gi1[e - 4], gj = e < 4 ? gj0[e] : gj1[e - 4];
+                            const float ex = __builtin_amdgcn_exp2f(gi - gj);
+                            const float kj = (float)kjv[e];
+                            sa[m] = fmaf((float)kiv[e] * kj, ex, sa[m]);  // k_ic k_jc is exact in fp32
+                            sp[m] = fmaf((float)qiv[e] * kj, ex, sp[m]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                const int j = jg + 4 * m;
+                if (j <= i) {
+                    const int p = i * (i + 1) / 2 + j;
+                    L.part[wave][0][p] = sa[m];
+                    L.part[wave][1][p] = sp[m];
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- A (transposed, with beta) and P (split) from the wave partials
+        for (int p = tid; p < NPAIR; p += NT) {
+            const int i = pair_row(p), j = p - i * (i + 1) / 2;
+            float sa = L.part[0][0][p], sp = L.part[0][1][p];
+#pragma unroll
+            for (int w = 1; w < NW; w++) {
+                sa += L.part[w][0][p];
+                sp += L.part[w][1][p];
+            }
+            if (j < i) L.at[j * SA + i] = L.beta[i] * sa;
+            const __bf16 h = (__bf16)sp;
+            L.ph[i * ST + j] = h;
+            L.pl[i * ST + j] = (__bf16)(sp - (float)h);
+        }
+        __syncthreads();
+
+        // ---- T = (I + A)^{-1} by forward substitution, lane c of wave 0 its
+        // column: y = T e_c - e_c solves y_r = -A_rc - sum_{s<r} A_rs y_s (A
+        // strictly lower: y_r = 0 for r <= c), updated right-looking with
+        // A's columns read as rows of A^T; then T1 = T diag(beta), split.
+        if (tid < KC) {
+            const int c = tid;
+            float y[KC];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const floatx4 yv = ldf4(&L.at[c * SA + 4 * q]);
+#pragma unroll
+                for (int e = 0; e < 4; e++) y[4 * q + e] = -yv[e];
+            }
+#pragma unroll
+            for (int s = 0; s < KC - 1; s++)
+#pragma unroll
+                for (int q = (s + 1) / 4; q < 4; q++) {
+                    const floatx4 col = ldf4(&L.at[s * SA + 4 * q]);  // A_{4q+e, s}
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        if (4 * q + e > s) y[4 * q + e] = fmaf(-col[e], y[s], y[4 * q + e]);
+                }
+            const float bc = L.beta[c];
+#pragma unroll
+            for (int r = 0; r < KC; r++) {
+                const float t1 = (r > c ? y[r] : (r == c ? 1.0f : 0.0f)) * bc;
+                const __bf16 h = (__bf16)t1;
+                L.t1h[r * ST + c] = h;
+                L.t1l[r * ST + c] = (__bf16)(t1 - (float)h);
+            }
+        }
+        __syncthreads();
+
+        // ---- U = T1 V (this wave's value columns) and -W = -T1 (K . 2^G) (this
+        // wave's key channels, stored split, token-major)
+        floatx4 U[2];
+        {
+            const bf16x4 th = ld4(&L.t1h[ln * ST + 4 * lg]), tl = ld4(&L.t1l[ln * ST + 4 * lg]);
+#pragma unroll
+            for (int et = 0; et < 2; et++) {
+                const bf16x4 vb = ld4(&L.vt[(e0 + 16 * et + ln) * ST + 4 * lg]);
+                U[et] = mma16(th, vb, floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+                U[et] = mma16(tl, vb, U[et]);
+            }
+#pragma unroll
+            for (int x = 0; x < 2; x++) {
+                const int c0w = 32 * wave + 16 * x;
+                const bf16x4 gbh = ld4(&L.kgh[(c0w + ln) * ST + 4 * lg]), gbl = ld4(&L.kgl[(c0w + ln) * ST + 4 * lg]);
+                floatx4 Wx = mma16(th, gbh, floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+                Wx = mma16(th, gbl, Wx);
+                Wx = mma16(tl, gbh, Wx);
+#pragma unroll
+                for (int r = 0; r < 4; r++) {  // Wx[r] = W[4 lg + r][c0w + ln]
+                    const float w = -Wx[r];
+                    const __bf16 h = (__bf16)w;
+                    L.wh[(4 * lg + r) * SD + c0w + ln] = h;
+                    L.wl[(4 * lg + r) * SD + c0w + ln] = (__bf16)(w - (float)h);
+                }
+            }
+        }
+        __syncthreads();  // -W complete
+
+        // ---- state operand (contraction over key rows, permuted slots)
+        bf16x8 Sh[2][KB], Sl[2][KB];
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    split(S[et][2 * kb][r], Sh[et][kb], Sl[et][kb], r);
+                    split(S[et][2 * kb + 1][r], Sh[et][kb], Sl[et][kb], 4 + r);
+                }
+        // ---- U' = U - W S and O = (Q . 2^G) S
+        floatx4 O[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int kb = 0; kb < KB; kb++) {
+            const int row = ln * SD + 4 * lg + 32 * kb;
+            const bf16x8 wh = ld_pair(&L.wh[row]), wl = ld_pair(&L.wl[row]);
+            const bf16x8 qh = ld_pair(&L.qgh[row]), ql = ld_pair(&L.qgl[row]);
+#pragma unroll
+            for (int et = 0; et < 2; et++) {
+                U[et] = mma32(wh, Sh[et][kb], U[et]);
+                O[et] = mma32(qh, Sh[et][kb], O[et]);
+            }
+#pragma unroll
+            for (int et = 0; et < 2; et++) {
+                U[et] = mma32(wh, Sl[et][kb], U[et]);
+                O[et] = mma32(qh, Sl[et][kb], O[et]);
+            }
+#pragma unroll
+            for (int et = 0; et < 2; et++) {
+                U[et] = mma32(wl, Sh[et][kb], U[et]);
+                O[et] = mma32(ql, Sh[et][kb], O[et]);
+            }
+        }
+        // ---- U' as the B operand over tokens (its accumulator layout), split
+        bf16x4 Vh[2], Vl[2];
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) split(U[et][r], Vh[et], Vl[et], r);
+        // ---- O += P U'; outputs staged token-major in K's tile (free now)
+        {
+            const bf16x4 pah = ld4(&L.ph[ln * ST + 4 * lg]), pal = ld4(&L.pl[ln * ST + 4 * lg]);
+#pragma unroll
+            for (int et = 0; et < 2; et++) {
+                O[et] = mma16(pah, Vh[et], O[et]);
+                O[et] = mma16(pah, Vl[et], O[et]);
+                O[et] = mma16(pal, Vh[et], O[et]);
+            }
+        }
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) L.kr[(4 * lg + r) * SD + e0 + 16 * et + ln] = (__bf16)O[et][r];
+        // ---- S <- diag(2^{G_C}) S + (K . 2^(G_C - G))^T U'
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            const floatx4 gc = ldf4(&L.g[(KC - 1) * SG + 16 * dt + 4 * lg]);
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float e = __builtin_amdgcn_exp2f(gc[r]);
+#pragma unroll
+                for (int et = 0; et < 2; et++) S[et][dt][r] *= e;
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            const bf16x4 kah = ld4(&L.kch[(16 * dt + ln) * ST + 4 * lg]);
+            const bf16x4 kal = ld4(&L.kcl[(16 * dt + ln) * ST + 4 * lg]);
+#pragma unroll
+            for (int et = 0; et < 2; et++) {
+                S[et][dt] = mma16(kah, Vh[et], S[et][dt]);
+                S[et][dt] = mma16(kah, Vl[et], S[et][dt]);
+                S[et][dt] = mma16(kal, Vh[et], S[et][dt]);
+            }
+        }
+        __syncthreads();  // the outputs are staged
+        for (int x = tid; x < KC * D / 8; x += NT) {
+            const int t = x / (D / 8), c = 8 * (x % (D / 8));
+            if (t < nv)
+                *reinterpret_cast<u32x4 *>(og + (size_t)(c0 + t) * tv + c) =
+                    *reinterpret_cast<const u32x4 *>(&L.kr[t * SD + c]);
+        }
+    }
+
+#pragma unroll
+    for (int et = 0; et < 2; et++)
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + 16 * et + ln] = S[et][dt][r];
+}
+
+hipError_t launch_prefill_kda(const gdnq_desc &d, float *S, const void *q, const void *k, const void *v,
+                              const float *a, const float *b, void *o, int T, hipStream_t st)
+{
+    const int hk = d.hk ? d.hk : d.H;
+    PrefillKdaArgs A{S,
+                     static_cast<const __bf16 *>(q),
+                     static_cast<const __bf16 *>(k),
+                     static_cast<const __bf16 *>(v),
+                     a,
+                     b,
+                     static_cast<__bf16 *>(o),
+                     T,
+                     d.H,
+                     hk,
+                     make_divisor((unsigned)d.H),
+                     make_divisor((unsigned)(d.H / hk))};
+    const unsigned grid = (unsigned)d.B * (unsigned)d.H;
+    if (d.dk == 128) {
+        hipLaunchKernelGGL(prefill_kda_kernel<128>, dim3(grid), dim3(256), 0, st, A);
+    } else {
+        hipLaunchKernelGGL(prefill_kda_kernel<64>, dim3(grid), dim3(128), 0, st, A);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gdnq

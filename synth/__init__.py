@@ -55,6 +55,10 @@ WORKLOADS = {
     # prefill from a zero state (the state then goes through the codec).
     "prefill": dict(B=8, H=32, dk=128, dv=128, T=4096, io="bf16", decay="scalar", a_lo=0.90,
                     W=1, r=0, seed=5, s0="zero"),
+    # The same prefill with the per-key-channel gate of the KDA workload
+    # (entries U[0.80, 1.00]).
+    "prefill_kda": dict(B=8, H=32, dk=128, dv=128, T=4096, io="bf16", decay="channel", a_lo=0.80,
+                        W=1, r=0, seed=6, s0="zero"),
     # Long decode with DAMP rows: 8 fp16 key rows per head from calibration
     # over 256 steps, window mode W=16 with 2 compensators, KDA decay.
     "damp": dict(B=256, H=32, dk=128, dv=128, T=8192, io="bf16", decay="channel", a_lo=0.80,
@@ -121,20 +125,22 @@ def steps_inputs(cfg: dict, t0: int, n: int, heads=None, seed=None):
 
 def token_major_inputs(cfg: dict, T: int):
     """The draws of steps 0..T-1 (``step_inputs``) laid out token-major for
-    a whole sequence: q16, k16, v16 as bf16 bit patterns [B,T,H,d], a and b
-    fp32 [B,T,H] (a: the scalar gate).  Filled one step at a time, so the
-    fp32 copies of the whole sequence are never held."""
+    a whole sequence: q16, k16, v16 as bf16 bit patterns [B,T,H,d], b fp32
+    [B,T,H] and a fp32 [B,T,H] (scalar gate) or [B,T,H,dk] (per-channel
+    gate).  Filled one step at a time, so the fp32 copies of the whole
+    sequence are never held."""
     B, H, dk, dv = cfg["B"], cfg["H"], cfg["dk"], cfg["dv"]
-    if cfg["io"] != "bf16" or cfg["decay"] != "scalar":
-        raise ValueError("token-major inputs are built for bf16 I/O and the scalar gate")
+    if cfg["io"] != "bf16":
+        raise ValueError("token-major inputs are built for bf16 I/O")
+    ashape = (B, T, H) if cfg["decay"] == "scalar" else (B, T, H, dk)
     out = dict(q16=np.empty((B, T, H, dk), np.uint16), k16=np.empty((B, T, H, dk), np.uint16),
-               v16=np.empty((B, T, H, dv), np.uint16), a=np.empty((B, T, H), np.float32),
+               v16=np.empty((B, T, H, dv), np.uint16), a=np.empty(ashape, np.float32),
                b=np.empty((B, T, H), np.float32))
     for t in range(T):
         x = step_inputs(cfg, t)
         for name in ("q16", "k16", "v16"):
             out[name][:, t] = x[name].reshape(B, H, -1)
-        out["a"][:, t] = x["a"].reshape(B, H)
+        out["a"][:, t] = x["a"].reshape(ashape[:1] + ashape[2:])
         out["b"][:, t] = x["b"].reshape(B, H)
     return out
 

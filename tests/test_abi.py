@@ -233,8 +233,7 @@ def test_prefill_argument_errors(g):
     S = FAKE
     io = [FAKE2 + i * (64 << 20) for i in range(6)]     # q, k, v, a, b, o
     call = lambda desc=d, s=S, args=io, T=16: g.gdn_prefill(desc, s, *args, T, stream=0)
-    for over, msg in ((dict(io_dtype=g.IO_F32), "bf16"), (dict(decay=g.DECAY_CHANNEL), "scalar gate"),
-                      (dict(dv=64), "dk == dv")):
+    for over, msg in ((dict(io_dtype=g.IO_F32), "bf16"), (dict(dv=64), "dk == dv")):
         dd = g.Desc(B=2, H=4, io_dtype=g.IO_BF16, hk=2)
         for k, v in over.items():
             setattr(dd, k, v)
@@ -251,6 +250,13 @@ def test_prefill_argument_errors(g):
     c, m = _err(lambda: call(args=args))
     assert c == 1 and "o overlaps S" in m
     g.gdn_prefill(d, S, None, None, None, None, None, None, 0, stream=0)   # T = 0: no launch
+    # the gate is [B,T,H] for the scalar decay and [B,T,H,dk] per channel:
+    # o placed right after a scalar gate overlaps a per-channel one
+    args = list(io)
+    args[5] = args[3] + 16 * 8 * 4
+    dk = g.Desc(B=2, H=4, io_dtype=g.IO_BF16, hk=2, decay=g.DECAY_CHANNEL)
+    c, m = _err(lambda: call(desc=dk, args=args))
+    assert c == 1 and "overlaps" in m, m
 
 
 def test_static_scale_arguments(g):

@@ -1,18 +1,22 @@
 """Chunkwise prefill (gdn_prefill) through the C ABI against the oracle's
-sequential recurrence (oracle.recur: the Gated DeltaNet row of LinQuant's
-Table 3 run token by token in fp64).
+sequential recurrence (oracle.recur: the Gated DeltaNet and KDA rows of
+LinQuant's Table 3 run token by token in fp64).
 
-The kernel computes the same recurrence 64 tokens at a time with bf16
-matrix products whose fp32 operands are split in two bf16 parts (operand
-error near 2^-17), so the bars are those of fp32 arithmetic on bf16 inputs:
+The kernels compute the same recurrence 64 tokens (scalar gate) or 16
+tokens (per-channel gate) at a time with bf16 matrix products whose fp32
+operands are split in two bf16 parts (operand error near 2^-17), so the
+bars are those of fp32 arithmetic on bf16 inputs:
   * state after the last token: l2-relative error per head <= 1e-4;
   * outputs (bf16): every element is a correct bf16 rounding of a value
     within 1e-4 of its token's largest |o| of the oracle, and per head the
     l2 gap to the oracle's output rounded to bf16 is <= 2e-3 of its norm.
-Cases: several chunks with a ragged tail, one partial chunk, one token,
-exact chunk multiples, both head sizes, shared key heads, T = 0, the
-identity gates (a = 1, b = 0 keep the state bit for bit), prefill followed
-by gdn_state_quantize, and sampled heads of the full-size workload.
+Cases, for both gates: several chunks with a ragged tail, one partial
+chunk, one token, exact chunk multiples, both head sizes, shared key heads,
+the identity gates (a = 1, b = 0 keep the state bit for bit), sampled heads
+of the full-size workloads; and T = 0, prefill followed by
+gdn_state_quantize, a per-channel gate whose channels are all equal (the
+scalar-gate kernel's result within the bars), and gates small enough that
+a chunk's decay underflows.
 """
 import numpy as np
 import pytest
@@ -24,8 +28,9 @@ from tests._gpu import bf16_half_ulp, desc_for, dev, host, lib, per_head_rel, sa
 pytestmark = pytest.mark.gpu
 
 
-def _cfg(B, H, D, seed):
-    return dict(B=B, H=H, dk=D, dv=D, io="bf16", decay="scalar", a_lo=0.90, W=1, r=0, seed=seed)
+def _cfg(B, H, D, seed, decay="scalar"):
+    return dict(B=B, H=H, dk=D, dv=D, io="bf16", decay=decay, a_lo=0.90 if decay == "scalar" else 0.80, W=1, r=0,
+                seed=seed)
 
 
 def _inputs(cfg, T, hk=None):
@@ -48,7 +53,7 @@ def _inputs(cfg, T, hk=None):
         out[name] = np.ascontiguousarray(np.swapaxes(rep, 0, 1).reshape(T, B * H, D))
     out["v16"] = bt(inp["v16"])
     out["v"] = inp["v"]
-    out["a_dev"] = bt(inp["a"][..., 0])
+    out["a_dev"] = bt(inp["a"][..., 0] if cfg["decay"] == "scalar" else inp["a"])
     out["b_dev"] = bt(inp["b"])
     out["a"], out["b"] = inp["a"], inp["b"]
     return out
@@ -67,7 +72,7 @@ def _run(cfg, T, S0, hk=None):
     d = desc_for(cfg, hk=hk or 0)
     S = dev(S0.copy())
     o = torch.full((B, T, H, D), 3.0, dtype=torch.bfloat16, device="cuda")
-    say("prefill", f"B={B} H={H} D={D} T={T} hk={hk}")
+    say("prefill", cfg["decay"], f"B={B} H={H} D={D} T={T} hk={hk}")
     g.gdn_prefill(d, S, _bf16_dev(inp["q16"]), _bf16_dev(inp["k16"]), _bf16_dev(inp["v16"]), dev(inp["a_dev"]),
                   dev(inp["b_dev"]), o, T)
     torch.cuda.synchronize()
@@ -94,28 +99,82 @@ def _check(cfg, T, inp, S_got, o_got, S0, heads=None):
     return rel_S.max(), like.max()
 
 
-@pytest.mark.parametrize("D,T", [(128, 150), (128, 64), (128, 37), (128, 1), (64, 200), (64, 128)])
-def test_prefill_parity(D, T):
-    cfg = _cfg(2, 3, D, seed=21 + T)
+DECAYS = ["scalar", "channel"]
+
+
+@pytest.mark.parametrize("decay", DECAYS)
+@pytest.mark.parametrize("D,T", [(128, 150), (128, 64), (128, 37), (128, 16), (128, 1), (64, 200), (64, 128),
+                                 (64, 9)])
+def test_prefill_parity(D, T, decay):
+    cfg = _cfg(2, 3, D, seed=21 + T, decay=decay)
     S0 = synth.random_states(5 + T, cfg["B"] * cfg["H"], D, D, scale=0.5)
     inp, S, o = _run(cfg, T, S0)
     _check(cfg, T, inp, S, o, S0)
 
 
-def test_prefill_zero_state_long():
-    cfg = _cfg(1, 2, 128, seed=31)
+@pytest.mark.parametrize("decay", DECAYS)
+def test_prefill_zero_state_long(decay):
+    cfg = _cfg(1, 2, 128, seed=31, decay=decay)
     T = 700
     S0 = np.zeros((2, 128, 128), np.float32)
     inp, S, o = _run(cfg, T, S0)
     _check(cfg, T, inp, S, o, S0)
 
 
-def test_prefill_shared_key_heads():
-    cfg = _cfg(2, 4, 128, seed=41)
+@pytest.mark.parametrize("decay", DECAYS)
+def test_prefill_shared_key_heads(decay):
+    cfg = _cfg(2, 4, 128, seed=41, decay=decay)
     T = 100
     S0 = synth.random_states(7, 8, 128, 128, scale=0.5)
     inp, S, o = _run(cfg, T, S0, hk=2)
     _check(cfg, T, inp, S, o, S0)
+
+
+def test_prefill_equal_channel_gates_match_scalar_gate():
+    """A per-channel gate whose channels are all equal is the scalar gate:
+    the KDA kernel's result meets the oracle's scalar-gate bars too."""
+    cfg = _cfg(1, 3, 128, seed=43)
+    T = 90
+    S0 = synth.random_states(17, 3, 128, 128, scale=0.5)
+    inp = _inputs(cfg, T)
+    kcfg = dict(cfg, decay="channel")
+    kin = dict(inp, a_dev=np.ascontiguousarray(np.repeat(inp["a_dev"][..., None], 128, axis=3)))
+    torch = torch_cuda()
+    g = lib()
+    S = dev(S0.copy())
+    o = torch.empty((1, T, 3, 128), dtype=torch.bfloat16, device="cuda")
+    say("prefill equal channel gates")
+    g.gdn_prefill(desc_for(kcfg), S, _bf16_dev(kin["q16"]), _bf16_dev(kin["k16"]), _bf16_dev(kin["v16"]),
+                  dev(kin["a_dev"]), dev(kin["b_dev"]), o, T)
+    torch.cuda.synchronize()
+    o_host = synth.bf16_to_f32(o.view(torch.int16).cpu().numpy().view(np.uint16))
+    _check(cfg, T, inp, host(S), o_host, S0)
+
+
+def test_prefill_kda_underflowing_gates():
+    """Per-channel gates down to 1e-4: a 16-token chunk's decay reaches
+    1e-64 (below fp32's range) in some channels; the kernel takes only
+    non-positive exponents, so it neither overflows nor loses the state."""
+    cfg = _cfg(1, 2, 128, seed=47, decay="channel")
+    T = 80
+    S0 = synth.random_states(19, 2, 128, 128, scale=0.5)
+    inp = _inputs(cfg, T)
+    rng = synth.misc_rng(47, 1)
+    small = rng.uniform(1e-4, 1.0, inp["a"].shape).astype(np.float32)
+    mask = rng.uniform(size=inp["a"].shape) < 0.1        # one channel in ten decays fast
+    inp["a"] = np.where(mask, small, inp["a"]).astype(np.float32)
+    inp["a_dev"] = np.ascontiguousarray(np.swapaxes(inp["a"].reshape(T, 1, 2, 128), 0, 1))
+    torch = torch_cuda()
+    g = lib()
+    S = dev(S0.copy())
+    o = torch.empty((1, T, 2, 128), dtype=torch.bfloat16, device="cuda")
+    say("prefill kda small gates")
+    g.gdn_prefill(desc_for(cfg), S, _bf16_dev(inp["q16"]), _bf16_dev(inp["k16"]), _bf16_dev(inp["v16"]),
+                  dev(inp["a_dev"]), dev(inp["b_dev"]), o, T)
+    torch.cuda.synchronize()
+    o_host = synth.bf16_to_f32(o.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert np.isfinite(host(S)).all()
+    _check(cfg, T, inp, host(S), o_host, S0)
 
 
 def test_prefill_empty_is_noop():
@@ -130,12 +189,13 @@ def test_prefill_empty_is_noop():
     assert np.array_equal(host(S), S0)
 
 
-def test_prefill_identity_gates_keep_state():
+@pytest.mark.parametrize("decay", DECAYS)
+def test_prefill_identity_gates_keep_state(decay):
     """a = 1, b = 0: every update is zero and the decay is e^0 = 1, so the
     state comes back bit for bit (outputs still checked against the oracle)."""
     torch = torch_cuda()
     g = lib()
-    cfg = _cfg(1, 2, 128, seed=61)
+    cfg = _cfg(1, 2, 128, seed=61, decay=decay)
     T = 90
     S0 = synth.random_states(11, 2, 128, 128)
     inp = _inputs(cfg, T)
@@ -187,32 +247,33 @@ def test_prefill_rejects(D):
     S = torch.zeros((2, D, D), device="cuda")
     x = torch.zeros((1, 8, 2, D), dtype=torch.bfloat16, device="cuda")
     ab = torch.ones((1, 8, 2), device="cuda")
-    for over, msg in ((dict(io_dtype=g.IO_F32), "bf16"), (dict(decay=g.DECAY_CHANNEL), "scalar"),
-                      (dict(dv=64 if D == 128 else 128), "dk == dv")):
+    for over, msg in ((dict(io_dtype=g.IO_F32), "bf16"), (dict(dv=64 if D == 128 else 128), "dk == dv")):
         with pytest.raises(g.GdnqError, match=msg):
             g.gdn_prefill(desc_for(cfg, **over), S, x, x, x, ab, ab, x.clone(), 8)
 
 
-def test_prefill_full_size_sampled():
-    """The benchmark's workload (8 sequences x 32 heads x 4096 tokens, zero
-    initial state) in the benchmark's launch, checked on sampled heads
-    against the oracle's 4096-step recurrence."""
+@pytest.mark.parametrize("wl", ["prefill", "prefill_kda"])
+def test_prefill_full_size_sampled(wl):
+    """The benchmark's workloads (8 sequences x 32 heads x 4096 tokens, zero
+    initial state, scalar or per-channel gate) in the benchmark's launch,
+    checked on sampled heads against the oracle's 4096-step recurrence."""
     torch = torch_cuda()
     g = lib()
-    cfg = synth.WORKLOADS["prefill"]
+    cfg = synth.WORKLOADS[wl]
     B, H, D, T = cfg["B"], cfg["H"], cfg["dk"], cfg["T"]
     x = synth.token_major_inputs(cfg, T)
     S = torch.zeros((B * H, D, D), dtype=torch.float32, device="cuda")
     o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
-    say("prefill full size", B, H, T)
+    say("prefill full size", wl, B, H, T)
     g.gdn_prefill(desc_for(dict(cfg, W=1, r=0)), S, _bf16_dev(x["q16"]), _bf16_dev(x["k16"]), _bf16_dev(x["v16"]),
                   dev(x["a"]), dev(x["b"]), o, T)
     torch.cuda.synchronize()
     S_got = host(S)
     for b, h in ((0, 0), (3, 17), (7, 31)):
         f = lambda name: np.ascontiguousarray(synth.bf16_to_f32(x[name][b, :, h])[:, None, :])
+        ga = x["a"][b, :, h, None, None] if cfg["decay"] == "scalar" else x["a"][b, :, h, None, :]
         S_ref, o_ref = oracle.recur(np.zeros((1, D, D), np.float32), f("q16"), f("k16"), f("v16"),
-                                    x["a"][b, :, h, None, None], x["b"][b, :, h, None])
+                                    np.ascontiguousarray(ga), x["b"][b, :, h, None])
         rel_S = per_head_rel(S_got[b * H + h][None], S_ref)
         assert rel_S.max() <= 1e-4, (b, h, rel_S.max())
         got = synth.bf16_to_f32(o[b, :, h].view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
