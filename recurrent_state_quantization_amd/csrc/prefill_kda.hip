@@ -30,14 +30,13 @@
 // with fp32 accumulation, q, k, v exact in bf16, every fp32 operand split
 // into two bf16 parts.  The decayed Gram sums A and P run on the VALU in
 // fp32 (one e^{G_ic - G_jc} per pair and channel: the per-channel decay
-// does not factor out of the contraction); T by forward substitution in
-// fp32.
+// does not factor out of the contraction), D/8 lanes per pair with a DPP
+// sum; T by forward substitution in fp32.
 //
 // Mapping: one workgroup per (batch, head); wave w owns value columns
 // 32w..32w+31 of the state, kept in fp32 MFMA accumulators for the whole
 // sequence (the layout and the permuted contraction of the scalar-gate
-// kernel), and key channels 32w..32w+31 of the chunk-local work (its share
-// of the Gram sums and of W).  Products over the chunk's 16 tokens use
+// kernel), and key channels 32w..32w+31 of W.  Products over the chunk's 16 tokens use
 // v_mfma_f32_16x16x16_bf16, whose accumulator layout is its own B operand
 // layout: U' feeds P U' and the state update straight from registers.
 #include <hip/hip_runtime.h>
@@ -90,6 +89,36 @@ __device__ __forceinline__ bf16x8 ld8(const __bf16 *p) { return *reinterpret_cas
 __device__ __forceinline__ bf16x4 ld4(const __bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
 __device__ __forceinline__ floatx4 ldf4(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
 
+// One thread's share of a chunk's inputs, held in registers while the
+// previous chunk is computed: one 16-byte piece of each of K, Q, V (token
+// x / (D/8), channels 8 (x % (D/8)) .. +7), and for thread c < D the 16
+// gates of key channel c; b for thread t < KC.
+struct KdaChunkRegs {
+    u32x4 k, q, v;
+    float a[KC];
+    float b;
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over aligned groups of N = 8 or 16 lanes, every lane of a group gets
+// it: xor-1 and xor-2 (quad_perm), then row_half_mirror (xor-4 once the
+// quads hold equal values) and, for 16, row_mirror.
+template <int N>
+__device__ __forceinline__ float group_sum(float x)
+{
+    static_assert(N == 8 || N == 16, "groups of 8 or 16 lanes");
+    x += dppf<0xB1>(x);
+    x += dppf<0x4E>(x);
+    x += dppf<0x141>(x);
+    if constexpr (N == 16) x += dppf<0x140>(x);
+    return x;
+}
+
 // pair index p = i (i + 1) / 2 + j (j <= i) -> i
 __device__ __forceinline__ int pair_row(int p)
 {
@@ -117,9 +146,10 @@ struct KdaLds {
     __bf16 wh[KC * SD], wl[KC * SD];    // -W, split, token-major
     __bf16 t1h[KC * ST], t1l[KC * ST];  // T1 = T diag(beta), split
     __bf16 ph[KC * ST], pl[KC * ST];    // P, split (upper part zero)
+    float egc[D];                       // 2^(G_C): the chunk's decay of each key row of S
     float at[KC * SA];                  // A^T: at[j * SA + i] = A_ij (i > j), zero elsewhere
-    float part[NW][2][NPAIR];           // per-wave Gram sums (A without beta, P)
     float beta[KC];
+    uint8_t pij[NPAIR];                 // pair p -> i | j << 4
 };
 
 struct PrefillKdaArgs {
@@ -132,15 +162,13 @@ struct PrefillKdaArgs {
 };
 
 template <int D>
-__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kda_kernel(PrefillKdaArgs A)
+__global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
 {
     using Lds = KdaLds<D>;
     constexpr int SD = Lds::SD, SG = Lds::SG, ST = Lds::ST;
     constexpr int NW = D / 32, NT = NW * 64;  // waves; wave w owns value columns and key channels 32w..32w+31
     constexpr int KB = D / 32;                // 32-wide blocks along a head dim
     constexpr int DT = D / 16;                // 16-row tiles along a head dim
-    constexpr int TPT = KC * D / NT;          // tokens per thread of the element-wise stage
-    static_assert(TPT == 8, "one thread takes 8 tokens of one channel");
     __shared__ Lds L;
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
@@ -167,6 +195,29 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2))) void
         L.pl[x] = (__bf16)0.0f;
     }
     for (int x = tid; x < KC * SA; x += NT) L.at[x] = 0.0f;
+    for (int p = tid; p < NPAIR; p += NT) {
+        const int i = pair_row(p);
+        L.pij[p] = (uint8_t)(i | (p - i * (i + 1) / 2) << 4);
+    }
+
+    // Chunk loads: every load is unconditional (tokens past the end are
+    // clamped to the last one) and zeroed only when staged, so the compiler
+    // counts them and waits for them at staging alone.
+    auto load = [=](int c0, KdaChunkRegs &r) {
+        {
+            const int t = tid / (D / 8), c = 8 * (tid % (D / 8));
+            const size_t u = (size_t)min(c0 + t, T - 1);
+            r.k = *reinterpret_cast<const u32x4 *>(kg + u * tk + c);
+            r.q = *reinterpret_cast<const u32x4 *>(qg + u * tk + c);
+            r.v = *reinterpret_cast<const u32x4 *>(vg + u * tv + c);
+        }
+        if (tid < D) {
+#pragma unroll
+            for (int t = 0; t < KC; t++) r.a[t] = ag[(size_t)min(c0 + t, T - 1) * tv + tid];
+        }
+        r.b = bg[(size_t)min(c0 + (tid & (KC - 1)), T - 1) * A.H];
+    };
+    static_assert(KC * D / 8 == NT, "one 16-byte piece of K, Q and V per thread");
 
     // S[et][dt][r] = S[16 dt + 4 lg + r][e0 + 16 et + ln] (MFMA accumulator layout)
     floatx4 S[2][DT];
@@ -178,6 +229,8 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2))) void
             for (int r = 0; r < 4; r++)
                 S[et][dt][r] = Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + 16 * et + ln];
 
+    KdaChunkRegs nx;
+    load(0, nx);
     for (int c0 = 0; c0 < T; c0 += KC) {
         __syncthreads();  // the previous chunk is done with every LDS tile
         // Lane indices pass through an empty asm each chunk, so the LDS
@@ -188,39 +241,39 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2))) void
 
         // ---- stage K, Q token-major and V^T (tokens past the end are zero),
         // the gates (thread c < D scans channel c; padding has gate 1) and beta
-        for (int x = tid; x < KC * D / 8; x += NT) {
-            const int t = x / (D / 8), c = 8 * (x % (D / 8));
+        {
+            const int t = tid / (D / 8), c = 8 * (tid % (D / 8));
             const bool ok = t < nv;
-            const size_t u = (size_t)(c0 + (ok ? t : 0));
-            u32x4 kx = *reinterpret_cast<const u32x4 *>(kg + u * tk + c);
-            u32x4 qx = *reinterpret_cast<const u32x4 *>(qg + u * tk + c);
-            u32x4 vx = *reinterpret_cast<const u32x4 *>(vg + u * tv + c);
-            if (!ok) kx = qx = vx = u32x4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4 *>(&L.kr[t * SD + c]) = kx;
-            *reinterpret_cast<u32x4 *>(&L.qr[t * SD + c]) = qx;
-            const bf16x8 vv = __builtin_bit_cast(bf16x8, vx);
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4 *>(&L.kr[t * SD + c]) = ok ? nx.k : z;
+            *reinterpret_cast<u32x4 *>(&L.qr[t * SD + c]) = ok ? nx.q : z;
+            const bf16x8 vv = __builtin_bit_cast(bf16x8, ok ? nx.v : z);
 #pragma unroll
             for (int e = 0; e < 8; e++) L.vt[(c + e) * ST + t] = vv[e];
         }
         if (tid < D) {
-            float av[KC];
-#pragma unroll
-            for (int t = 0; t < KC; t++) av[t] = ag[(size_t)(c0 + min(t, nv - 1)) * tv + tid];
             float acc = 0.0f;
 #pragma unroll
             for (int t = 0; t < KC; t++) {
-                acc += t < nv ? __builtin_amdgcn_logf(av[t]) : 0.0f;
+                acc += t < nv ? __builtin_amdgcn_logf(nx.a[t]) : 0.0f;
                 L.g[t * SG + tid] = acc;
             }
         }
-        if (tid < KC) L.beta[tid] = tid < nv ? bg[(size_t)(c0 + tid) * A.H] : 0.0f;
+        if (tid < KC) L.beta[tid] = tid < nv ? nx.b : 0.0f;
         __syncthreads();
+        if (c0 + KC < T) load(c0 + KC, nx);  // in flight while this chunk is computed
 
         // ---- element-wise operands: Q . 2^G (token-major), (K . 2^G)^T and
-        // (K . 2^(G_C - G))^T (channel-major), all split; every exponent <= 0
+        // (K . 2^(G_C - G))^T (channel-major), all split; every exponent <= 0.
+        // Thread c, 8 tokens of key channel c (the channel-major tiles take one
+        // 16-byte store per thread); threads c < D also keep the chunk decay
+        // 2^(G_C) of key row c of S.
         {
+            constexpr int TPT = KC * D / NT;
+            static_assert(TPT == 8, "one thread takes 8 tokens of one channel");
             const int c = tid % D, t0 = TPT * (tid / D);
             const float gC = L.g[(KC - 1) * SG + c];
+            if (tid < D) L.egc[c] = __builtin_amdgcn_exp2f(gC);
             bf16x8 gh, gl, ch, cl;
 #pragma unroll
             for (int e = 0; e < TPT; e++) {
@@ -240,58 +293,55 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2))) void
             *reinterpret_cast<bf16x8 *>(&L.kch[c * ST + t0]) = ch;
             *reinterpret_cast<bf16x8 *>(&L.kcl[c * ST + t0]) = cl;
         }
-        // ---- the decayed Gram sums over this wave's 32 key channels: lane
-        // (i, jg) takes the pairs (i, j), j = jg + 4m <= i
+        // ---- the decayed Gram sums: D/8 lanes per pair (i, j), 8 key channels
+        // each, summed across the pair's lanes by DPP (all lanes take part: a
+        // slot past the last pair recomputes that pair and writes nothing);
+        // the pair's first lane stores A^T (with beta) and P (split).  Every
+        // pass's LDS reads go out first (one wave per SIMD: nothing else
+        // hides their latency).
         {
-            const int lane = tid & 63, i = lane >> 2, jg = lane & 3;
-            float sa[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            constexpr int LPP = D / 8, PPI = NT / LPP;  // lanes per pair, pairs per pass
+            constexpr int NP = (NPAIR + PPI - 1) / PPI;  // passes
+            const int cb = tid % LPP, slot = tid / LPP, c = 8 * cb;
+            int pi[NP], pj[NP];
+            bf16x8 kiv[NP], qiv[NP], kjv[NP];
+            floatx4 gi0[NP], gi1[NP], gj0[NP], gj1[NP];
 #pragma unroll
-            for (int cq = 0; cq < 4; cq++) {
-                const int c = 32 * wave + 8 * cq;
-                const bf16x8 kiv = ld8(&L.kr[i * SD + c]), qiv = ld8(&L.qr[i * SD + c]);
-                const floatx4 gi0 = ldf4(&L.g[i * SG + c]), gi1 = ldf4(&L.g[i * SG + c + 4]);
+            for (int n = 0; n < NP; n++) {
+                const int ij = L.pij[min(n * PPI + slot, NPAIR - 1)];
+                pi[n] = ij & 15;
+                pj[n] = ij >> 4;
+            }
 #pragma unroll
-                for (int m = 0; m < 4; m++) {
-                    const int j = jg + 4 * m;
-                    if (j <= i) {
-                        const bf16x8 kjv = ld8(&L.kr[j * SD + c]);
-                        const floatx4 gj0 = ldf4(&L.g[j * SG + c]), gj1 = ldf4(&L.g[j * SG + c + 4]);
+            for (int n = 0; n < NP; n++) {
+                kiv[n] = ld8(&L.kr[pi[n] * SD + c]);
+                qiv[n] = ld8(&L.qr[pi[n] * SD + c]);
+                kjv[n] = ld8(&L.kr[pj[n] * SD + c]);
+                gi0[n] = ldf4(&L.g[pi[n] * SG + c]);
+                gi1[n] = ldf4(&L.g[pi[n] * SG + c + 4]);
+                gj0[n] = ldf4(&L.g[pj[n] * SG + c]);
+                gj1[n] = ldf4(&L.g[pj[n] * SG + c + 4]);
+            }
 #pragma unroll
-                        for (int e = 0; e < 8; e++) {
-                            const float gi = e < 4 ? gi0[e] : gi1[e - 4], gj = e < 4 ? gj0[e] : gj1[e - 4];
-                            const float ex = __builtin_amdgcn_exp2f(gi - gj);
-                            const float kj = (float)kjv[e];
-                            sa[m] = fmaf((float)kiv[e] * kj, ex, sa[m]);  // k_ic k_jc is exact in fp32
-                            sp[m] = fmaf((float)qiv[e] * kj, ex, sp[m]);
-                        }
-                    }
+            for (int n = 0; n < NP; n++) {
+                const int i = pi[n], j = pj[n];
+                float sa = 0.0f, sp = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const float gi = e < 4 ? gi0[n][e] : gi1[n][e - 4], gj = e < 4 ? gj0[n][e] : gj1[n][e - 4];
+                    const float t = (float)kjv[n][e] * __builtin_amdgcn_exp2f(gi - gj);
+                    sa = fmaf((float)kiv[n][e], t, sa);
+                    sp = fmaf((float)qiv[n][e], t, sp);
+                }
+                sa = group_sum<LPP>(sa);
+                sp = group_sum<LPP>(sp);
+                if (cb == 0 && n * PPI + slot < NPAIR) {
+                    if (j < i) L.at[j * SA + i] = L.beta[i] * sa;
+                    const __bf16 h = (__bf16)sp;
+                    L.ph[i * ST + j] = h;
+                    L.pl[i * ST + j] = (__bf16)(sp - (float)h);
                 }
             }
-#pragma unroll
-            for (int m = 0; m < 4; m++) {
-                const int j = jg + 4 * m;
-                if (j <= i) {
-                    const int p = i * (i + 1) / 2 + j;
-                    L.part[wave][0][p] = sa[m];
-                    L.part[wave][1][p] = sp[m];
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- A (transposed, with beta) and P (split) from the wave partials
-        for (int p = tid; p < NPAIR; p += NT) {
-            const int i = pair_row(p), j = p - i * (i + 1) / 2;
-            float sa = L.part[0][0][p], sp = L.part[0][1][p];
-#pragma unroll
-            for (int w = 1; w < NW; w++) {
-                sa += L.part[w][0][p];
-                sp += L.part[w][1][p];
-            }
-            if (j < i) L.at[j * SA + i] = L.beta[i] * sa;
-            const __bf16 h = (__bf16)sp;
-            L.ph[i * ST + j] = h;
-            L.pl[i * ST + j] = (__bf16)(sp - (float)h);
         }
         __syncthreads();
 
@@ -301,22 +351,27 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2))) void
         // A's columns read as rows of A^T; then T1 = T diag(beta), split.
         if (tid < KC) {
             const int c = tid;
-            float y[KC];
+            // every load first (broadcast reads): issued step by step, the 15
+            // steps would wait on 15 LDS round trips
+            floatx4 yv[4], col[KC - 1][4];
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const floatx4 yv = ldf4(&L.at[c * SA + 4 * q]);
-#pragma unroll
-                for (int e = 0; e < 4; e++) y[4 * q + e] = -yv[e];
-            }
+            for (int q = 0; q < 4; q++) yv[q] = ldf4(&L.at[c * SA + 4 * q]);
 #pragma unroll
             for (int s = 0; s < KC - 1; s++)
 #pragma unroll
-                for (int q = (s + 1) / 4; q < 4; q++) {
-                    const floatx4 col = ldf4(&L.at[s * SA + 4 * q]);  // A_{4q+e, s}
+                for (int q = (s + 1) / 4; q < 4; q++) col[s][q] = ldf4(&L.at[s * SA + 4 * q]);  // A_{4q+e, s}
+            float y[KC];
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) y[4 * q + e] = -yv[q][e];
+#pragma unroll
+            for (int s = 0; s < KC - 1; s++)
+#pragma unroll
+                for (int q = (s + 1) / 4; q < 4; q++)
 #pragma unroll
                     for (int e = 0; e < 4; e++)
-                        if (4 * q + e > s) y[4 * q + e] = fmaf(-col[e], y[s], y[4 * q + e]);
-                }
+                        if (4 * q + e > s) y[4 * q + e] = fmaf(-col[s][q][e], y[s], y[4 * q + e]);
             const float bc = L.beta[c];
 #pragma unroll
             for (int r = 0; r < KC; r++) {
@@ -414,13 +469,11 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2))) void
         // ---- S <- diag(2^{G_C}) S + (K . 2^(G_C - G))^T U'
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) {
-            const floatx4 gc = ldf4(&L.g[(KC - 1) * SG + 16 * dt + 4 * lg]);
+            const floatx4 ec = ldf4(&L.egc[16 * dt + 4 * lg]);
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const float e = __builtin_amdgcn_exp2f(gc[r]);
+            for (int r = 0; r < 4; r++)
 #pragma unroll
-                for (int et = 0; et < 2; et++) S[et][dt][r] *= e;
-            }
+                for (int et = 0; et < 2; et++) S[et][dt][r] *= ec[r];
         }
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) {
