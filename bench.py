@@ -248,24 +248,26 @@ def cpu_baselines(cfg: dict, S: np.ndarray, inputs: list) -> dict:
 
 def time_launches(torch, fn, steps: int, warmup: int):
     """Run `warmup` untimed calls, then time exactly `steps` calls: the wall
-    time from a synchronize before to a synchronize after, and each call's
-    duration from HIP events recorded around it on the launch stream (the
-    library launches on torch's current stream).  Returns (wall seconds,
-    mean per-call seconds) of the same `steps` calls."""
+    time from a synchronize before to a synchronize after, and the mean
+    duration of a call from two HIP events recorded on the launch stream
+    (the library launches on torch's current stream), one before the first
+    timed call and one after the last, divided by `steps`.  Events between
+    the calls would sit in the stream between the launches and add their
+    own cost to every call.  Returns (wall seconds, mean per-call seconds)
+    of the same `steps` calls."""
     for i in range(warmup):
         fn(i)
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         fn(warmup + i)
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [a.elapsed_time(b) * 1e-3 for a, b in ev]
-    return wall, float(np.mean(per))
+    return wall, e0.elapsed_time(e1) * 1e-3 / steps
 
 
 def prefix_cache_data():

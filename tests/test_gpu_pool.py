@@ -233,3 +233,69 @@ def test_shared_key_heads_window():
     o_ref, _, _ = oracle.window(X0, _expand(kq["q"], H, hk), _expand(kq["k"], H, hk), vab["v"], vab["a"], vab["b"])
     for t in range(n):
         check_outputs(host_io(outs[t], True), o_ref[t], True)
+
+
+def test_pool_per_step_static_scales():
+    """Static scales through the pool entry point: the row and column scale
+    arrays hold two planes ([scales of every slot][reciprocals of every
+    slot]); the pool step on permuted and skipped slots equals the plain
+    static step on twin states holding each slot's codes and both planes,
+    bit for bit, and the scales are never rewritten."""
+    torch = torch_cuda()
+    g = lib()
+    cfg = sub_cfg(synth.WORKLOADS["prefix_cache"], B=1, H=4)
+    H, dk, dv = cfg["H"], cfg["dk"], cfg["dv"]
+    n_slots = 7
+    slots = [5, 0, 3, -1, 9]
+    nb = len(slots)
+    F = g.STATIC_SCALES
+    d = desc_for(cfg, B=nb, W=1, r=0, flags=F)
+    dpool = desc_for(cfg, B=n_slots, W=1, r=0, flags=F)
+    d1 = desc_for(cfg, B=1, W=1, r=0, flags=F)
+    S = synth.prefill_states(dict(cfg, B=n_slots), heads=range(n_slots * H))
+    cal = synth.steps_inputs(dict(cfg, B=n_slots), 300, 4)
+    pool = g.alloc_state(dpool)
+    say("pool static fit")
+    g.calibrate_static_scales(dpool, dev(S), dev_io(cal, "q", True), dev_io(cal, "k", True), dev_io(cal, "v", True),
+                              dev(cal["a"]), dev(cal["b"]), 4, pool)
+    g.gdn_state_quantize(dpool, dev(S), pool)
+
+    def planes(st, name, slot, n):
+        t = st[name].view(2, n, -1)
+        return t[0, slot], t[1, slot]
+
+    twins = {}
+    for e, s in enumerate(slots):
+        if 0 <= s < n_slots:
+            st = g.alloc_state(d1)
+            st["codes"].copy_(_slot_view(pool, "codes", s, n_slots))
+            for name in ("row_scale", "col_scale"):
+                p0, p1 = planes(pool, name, s, n_slots)
+                st[name].view(2, -1)[0].copy_(p0)
+                st[name].view(2, -1)[1].copy_(p1)
+            twins[e] = st
+    scales = (pool["row_scale"].clone(), pool["col_scale"].clone())
+    codes_before = pool["codes"].clone()
+    inp, args = _inputs(torch, cfg, nb, 0, True)
+    o = torch.full((nb * H * dv,), 7.0, dtype=torch.bfloat16, device="cuda")
+    sl = torch.tensor(slots, dtype=torch.int32, device="cuda")
+    say("pool static step")
+    g.gdn_quant_decode_step_pool(d, pool, n_slots, sl, None, *args, o)
+    for e, st1 in twins.items():
+        o1 = torch.empty(H * dv, dtype=torch.bfloat16, device="cuda")
+        one = {k: v.reshape(nb, H, -1)[e] for k, v in inp.items()}
+        g.gdn_quant_decode_step(d1, st1, dev_io(one, "q", True), dev_io(one, "k", True), dev_io(one, "v", True),
+                                dev(one["a"]), dev(one["b"]), o1, 0)
+        torch.cuda.synchronize()
+        assert _bytes_equal(o.view(nb, H * dv)[e], o1), e
+        assert _bytes_equal(_slot_view(pool, "codes", slots[e], n_slots), st1["codes"]), e
+    torch.cuda.synchronize()
+    assert torch.equal(scales[0], pool["row_scale"]) and torch.equal(scales[1], pool["col_scale"])
+    used = {s for s in slots if 0 <= s < n_slots}
+    for s in range(n_slots):
+        if s not in used:
+            assert _bytes_equal(_slot_view(pool, "codes", s, n_slots), _slot_view({"codes": codes_before}, "codes", s,
+                                                                                   n_slots)), s
+    for e, s in enumerate(slots):
+        if not 0 <= s < n_slots:
+            assert torch.all(o.view(nb, H * dv)[e] == 7.0)
