@@ -33,10 +33,12 @@
 // does not factor out of the contraction), D/8 lanes per pair with a DPP
 // sum; T by forward substitution in fp32.
 //
-// Mapping: one workgroup per (batch, head); wave w owns value columns
-// 32w..32w+31 of the state, kept in fp32 MFMA accumulators for the whole
-// sequence (the layout and the permuted contraction of the scalar-gate
-// kernel), and key channels 32w..32w+31 of W.  Products over the chunk's 16 tokens use
+// Mapping: one workgroup per (batch, head) of D/16 waves (two per SIMD:
+// the chunk-local phases are latency-bound, and a second wave on each SIMD
+// hides part of it); wave w owns value columns 16w..16w+15 of the state,
+// kept in fp32 MFMA accumulators for the whole sequence (the layout and the
+// permuted contraction of the scalar-gate kernel), and key channels
+// 16w..16w+15 of W.  Products over the chunk's 16 tokens use
 // v_mfma_f32_16x16x16_bf16, whose accumulator layout is its own B operand
 // layout: U' feeds P U' and the state update straight from registers.
 #include <hip/hip_runtime.h>
@@ -90,11 +92,12 @@ __device__ __forceinline__ bf16x4 ld4(const __bf16 *p) { return *reinterpret_cas
 __device__ __forceinline__ floatx4 ldf4(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
 
 // One thread's share of a chunk's inputs, held in registers while the
-// previous chunk is computed: one 16-byte piece of each of K, Q, V (token
-// x / (D/8), channels 8 (x % (D/8)) .. +7), and for thread c < D the 16
+// previous chunk is computed: one 8-byte piece of each of K, Q, V (token
+// x / (D/4), channels 4 (x % (D/4)) .. +3), and for thread c < D the 16
 // gates of key channel c; b for thread t < KC.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 struct KdaChunkRegs {
-    u32x4 k, q, v;
+    u32x2 k, q, v;
     float a[KC];
     float b;
 };
@@ -132,7 +135,6 @@ __device__ __forceinline__ int pair_row(int p)
 
 template <int D>
 struct KdaLds {
-    static constexpr int NW = D / 32;
     static constexpr int SD = D + 8;   // bf16 stride of token-major [KC][D] tiles (16-byte pad)
     static constexpr int SG = D + 4;   // fp32 stride of the gate tile
     static constexpr int ST = KC + 8;  // bf16 stride of channel-major [D][KC] and of [KC][KC] tiles
@@ -146,11 +148,25 @@ struct KdaLds {
     __bf16 wh[KC * SD], wl[KC * SD];    // -W, split, token-major
     __bf16 t1h[KC * ST], t1l[KC * ST];  // T1 = T diag(beta), split
     __bf16 ph[KC * ST], pl[KC * ST];    // P, split (upper part zero)
+    float xf[KC * SG];                  // K . 2^(G - G_m), token-major (m: the chunk's reference token)
+    float yf[KC * SG];                  // K . 2^(G_m - G), token-major
+    float zf[KC * SG];                  // Q . 2^(G - G_m), token-major
     float egc[D];                       // 2^(G_C): the chunk's decay of each key row of S
     float at[KC * SA];                  // A^T: at[j * SA + i] = A_ij (i > j), zero elsewhere
     float beta[KC];
     uint8_t pij[NPAIR];                 // pair p -> i | j << 4
+    int pairwise;                       // c0 + 1 when chunk c0 takes the pairwise Gram sums
 };
+
+// The decayed Gram sums of a chunk factor through its reference token m:
+// 2^(G_i - G_j) = 2^(G_i - G_m) 2^(G_m - G_j), which makes A and P two dense
+// products.  Every factor lies in [2^-R, 2^R] when no channel decays by more
+// than 2^-R over the chunk (|G_i - G_m| <= -G_C), so with R = 60 no factor
+// or product leaves fp32's normal range.  A chunk that decays
+// further in some channel takes the pairwise sums, whose exponents are all
+// <= 0.
+constexpr float kFactorRange = 60.0f;
+constexpr int kRefToken = KC / 2 - 1;
 
 struct PrefillKdaArgs {
     float *S;
@@ -161,17 +177,24 @@ struct PrefillKdaArgs {
     Divisor byH, byG;
 };
 
+// threads per workgroup: D/16 waves
 template <int D>
-__global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
+constexpr int kda_threads() { return D / 16 * 64; }
+
+template <int D>
+__global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(PrefillKdaArgs A)
 {
     using Lds = KdaLds<D>;
     constexpr int SD = Lds::SD, SG = Lds::SG, ST = Lds::ST;
-    constexpr int NW = D / 32, NT = NW * 64;  // waves; wave w owns value columns and key channels 32w..32w+31
+    constexpr int ET = 1;                     // 16-column tiles of the state per wave
+    constexpr int CW = 16 * ET;               // value columns (and key channels of W) per wave
+    constexpr int NW = D / CW, NT = NW * 64;  // waves; wave w owns columns and channels CW w .. CW w + CW - 1
+    static_assert(NT == kda_threads<D>(), "block size");
     constexpr int KB = D / 32;                // 32-wide blocks along a head dim
     constexpr int DT = D / 16;                // 16-row tiles along a head dim
     __shared__ Lds L;
 
-    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int tid0 = (int)__builtin_amdgcn_workitem_id_x(), tid = tid0;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const unsigned bh = __builtin_amdgcn_workgroup_id_x();
     const unsigned bb = div_by(bh, A.byH), hh = bh - bb * (unsigned)A.H;
@@ -185,7 +208,7 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
     const float *ag = A.a + (size_t)bb * T * tv + (size_t)hh * D;  // a: [B, T, H, D]
     const float *bg = A.b + (size_t)bb * T * A.H + hh;
     float *Sg = A.S + (size_t)bh * D * D;
-    const int e0 = 32 * wave;  // value columns e0 + 16 et + ln, et = 0, 1
+    const int e0 = CW * wave;  // value columns e0 + 16 et + ln, et < ET
     int lg = (tid & 63) >> 4, ln = tid & 15;
 
     // Entries never written by the chunk loop (P's upper part, A^T's
@@ -195,6 +218,7 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
         L.pl[x] = (__bf16)0.0f;
     }
     for (int x = tid; x < KC * SA; x += NT) L.at[x] = 0.0f;
+    if (tid == 0) L.pairwise = 0;
     for (int p = tid; p < NPAIR; p += NT) {
         const int i = pair_row(p);
         L.pij[p] = (uint8_t)(i | (p - i * (i + 1) / 2) << 4);
@@ -203,26 +227,28 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
     // Chunk loads: every load is unconditional (tokens past the end are
     // clamped to the last one) and zeroed only when staged, so the compiler
     // counts them and waits for them at staging alone.
-    auto load = [=](int c0, KdaChunkRegs &r) {
-        {
-            const int t = tid / (D / 8), c = 8 * (tid % (D / 8));
-            const size_t u = (size_t)min(c0 + t, T - 1);
-            r.k = *reinterpret_cast<const u32x4 *>(kg + u * tk + c);
-            r.q = *reinterpret_cast<const u32x4 *>(qg + u * tk + c);
-            r.v = *reinterpret_cast<const u32x4 *>(vg + u * tv + c);
-        }
+    // K, Q, V go out first; the gates and beta later in the chunk, so that
+    // their registers are not held through the Gram sums.
+    auto load_kqv = [=](int c0, int tid, KdaChunkRegs &r) {
+        const int t = tid / (D / 4), c = 4 * (tid % (D / 4));
+        const size_t u = (size_t)min(c0 + t, T - 1);
+        r.k = *reinterpret_cast<const u32x2 *>(kg + u * tk + c);
+        r.q = *reinterpret_cast<const u32x2 *>(qg + u * tk + c);
+        r.v = *reinterpret_cast<const u32x2 *>(vg + u * tv + c);
+    };
+    auto load_ab = [=](int c0, int tid, KdaChunkRegs &r) {
         if (tid < D) {
 #pragma unroll
             for (int t = 0; t < KC; t++) r.a[t] = ag[(size_t)min(c0 + t, T - 1) * tv + tid];
         }
         r.b = bg[(size_t)min(c0 + (tid & (KC - 1)), T - 1) * A.H];
     };
-    static_assert(KC * D / 8 == NT, "one 16-byte piece of K, Q and V per thread");
+    static_assert(KC * D / 4 == NT, "one 8-byte piece of K, Q and V per thread");
 
     // S[et][dt][r] = S[16 dt + 4 lg + r][e0 + 16 et + ln] (MFMA accumulator layout)
-    floatx4 S[2][DT];
+    floatx4 S[ET][DT];
 #pragma unroll
-    for (int et = 0; et < 2; et++)
+    for (int et = 0; et < ET; et++)
 #pragma unroll
         for (int dt = 0; dt < DT; dt++)
 #pragma unroll
@@ -230,26 +256,28 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
                 S[et][dt][r] = Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + 16 * et + ln];
 
     KdaChunkRegs nx;
-    load(0, nx);
+    load_kqv(0, tid, nx);
+    load_ab(0, tid, nx);
     for (int c0 = 0; c0 < T; c0 += KC) {
         __syncthreads();  // the previous chunk is done with every LDS tile
         // Lane indices pass through an empty asm each chunk, so the LDS
         // addresses built from them are formed inside the loop instead of
         // being hoisted out and held in registers across it.
-        asm volatile("" : "+v"(lg), "+v"(ln));
+        int tid = tid0;
+        asm volatile("" : "+v"(lg), "+v"(ln), "+v"(tid));
         const int nv = min(KC, T - c0);  // valid tokens of this chunk
 
         // ---- stage K, Q token-major and V^T (tokens past the end are zero),
         // the gates (thread c < D scans channel c; padding has gate 1) and beta
         {
-            const int t = tid / (D / 8), c = 8 * (tid % (D / 8));
+            const int t = tid / (D / 4), c = 4 * (tid % (D / 4));
             const bool ok = t < nv;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4 *>(&L.kr[t * SD + c]) = ok ? nx.k : z;
-            *reinterpret_cast<u32x4 *>(&L.qr[t * SD + c]) = ok ? nx.q : z;
-            const bf16x8 vv = __builtin_bit_cast(bf16x8, ok ? nx.v : z);
+            const u32x2 z = {0u, 0u};
+            *reinterpret_cast<u32x2 *>(&L.kr[t * SD + c]) = ok ? nx.k : z;
+            *reinterpret_cast<u32x2 *>(&L.qr[t * SD + c]) = ok ? nx.q : z;
+            const bf16x4 vv = __builtin_bit_cast(bf16x4, ok ? nx.v : z);
 #pragma unroll
-            for (int e = 0; e < 8; e++) L.vt[(c + e) * ST + t] = vv[e];
+            for (int e = 0; e < 4; e++) L.vt[(c + e) * ST + t] = vv[e];
         }
         if (tid < D) {
             float acc = 0.0f;
@@ -258,23 +286,26 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
                 acc += t < nv ? __builtin_amdgcn_logf(nx.a[t]) : 0.0f;
                 L.g[t * SG + tid] = acc;
             }
+            if (!(acc >= -kFactorRange)) L.pairwise = c0 + 1;  // every thread that writes, writes the same
         }
         if (tid < KC) L.beta[tid] = tid < nv ? nx.b : 0.0f;
         __syncthreads();
-        if (c0 + KC < T) load(c0 + KC, nx);  // in flight while this chunk is computed
+        const bool more = c0 + KC < T;
+        if (more) load_kqv(c0 + KC, tid, nx);  // in flight while this chunk is computed
 
         // ---- element-wise operands: Q . 2^G (token-major), (K . 2^G)^T and
         // (K . 2^(G_C - G))^T (channel-major), all split; every exponent <= 0.
-        // Thread c, 8 tokens of key channel c (the channel-major tiles take one
-        // 16-byte store per thread); threads c < D also keep the chunk decay
+        // Thread c, 4 tokens of key channel c (the channel-major tiles take one
+        // 8-byte store per thread); threads c < D also keep the chunk decay
         // 2^(G_C) of key row c of S.
+        const bool factored = __builtin_amdgcn_readfirstlane(L.pairwise) != c0 + 1;
         {
             constexpr int TPT = KC * D / NT;
-            static_assert(TPT == 8, "one thread takes 8 tokens of one channel");
+            static_assert(TPT == 4, "one thread takes 4 tokens of one channel");
             const int c = tid % D, t0 = TPT * (tid / D);
-            const float gC = L.g[(KC - 1) * SG + c];
+            const float gC = L.g[(KC - 1) * SG + c], gm = L.g[kRefToken * SG + c];
             if (tid < D) L.egc[c] = __builtin_amdgcn_exp2f(gC);
-            bf16x8 gh, gl, ch, cl;
+            bf16x4 gh, gl, ch, cl;
 #pragma unroll
             for (int e = 0; e < TPT; e++) {
                 const int t = t0 + e;
@@ -287,18 +318,61 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
                 const __bf16 qh = (__bf16)qe;
                 L.qgh[t * SD + c] = qh;
                 L.qgl[t * SD + c] = (__bf16)(qe - (float)qh);
+                if (factored) {
+                    const float fl = __builtin_amdgcn_exp2f(gv - gm), fr = __builtin_amdgcn_exp2f(gm - gv);
+                    L.xf[t * SG + c] = kv * fl;
+                    L.yf[t * SG + c] = kv * fr;
+                    L.zf[t * SG + c] = qv * fl;
+                }
             }
-            *reinterpret_cast<bf16x8 *>(&L.kgh[c * ST + t0]) = gh;
-            *reinterpret_cast<bf16x8 *>(&L.kgl[c * ST + t0]) = gl;
-            *reinterpret_cast<bf16x8 *>(&L.kch[c * ST + t0]) = ch;
-            *reinterpret_cast<bf16x8 *>(&L.kcl[c * ST + t0]) = cl;
+            *reinterpret_cast<bf16x4 *>(&L.kgh[c * ST + t0]) = gh;
+            *reinterpret_cast<bf16x4 *>(&L.kgl[c * ST + t0]) = gl;
+            *reinterpret_cast<bf16x4 *>(&L.kch[c * ST + t0]) = ch;
+            *reinterpret_cast<bf16x4 *>(&L.kcl[c * ST + t0]) = cl;
         }
-        // ---- the decayed Gram sums: D/8 lanes per pair (i, j), 8 key channels
+        // ---- the decayed Gram sums, factored: wave 0 forms A = X Y^T and wave 1
+        // P^T = Y Z^T (X = K . 2^(G - G_m), Y = K . 2^(G_m - G), Z = Q . 2^(G - G_m))
+        // with fp32 matrix products; lane group lg contracts over key channels
+        // D/4 lg .. D/4 lg + D/4 - 1, one per instruction.  Lane (lg, ln) then
+        // holds rows 4 lg .. 4 lg + 3 of column ln: A_ij with i = 4 lg + r,
+        // j = ln, which is A^T's row j, and P_ij with i = ln, j = 4 lg + r,
+        // which is P's row i.
+        if (factored) {
+            __syncthreads();  // X, Y, Z staged
+            if (wave < 2) {
+                constexpr int CPG = D / 4;  // channels per lane group
+                const float *xa = (wave == 0 ? L.xf : L.yf) + ln * SG + CPG * lg;
+                const float *yb = (wave == 0 ? L.yf : L.zf) + ln * SG + CPG * lg;
+                floatx4 m0 = {0.0f, 0.0f, 0.0f, 0.0f}, m1 = m0;
+#pragma unroll
+                for (int s4 = 0; s4 < CPG; s4 += 4) {
+                    const floatx4 xv = ldf4(xa + s4), yv = ldf4(yb + s4);
+                    m0 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[0], yv[0], m0, 0, 0, 0);
+                    m1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[1], yv[1], m1, 0, 0, 0);
+                    m0 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[2], yv[2], m0, 0, 0, 0);
+                    m1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[3], yv[3], m1, 0, 0, 0);
+                }
+                const floatx4 m = m0 + m1;
+                if (wave == 0) {
+                    const floatx4 bi = ldf4(&L.beta[4 * lg]);
+                    floatx4 w;
+#pragma unroll
+                    for (int r = 0; r < 4; r++) w[r] = 4 * lg + r > ln ? bi[r] * m[r] : 0.0f;
+                    *reinterpret_cast<floatx4 *>(&L.at[ln * SA + 4 * lg]) = w;
+                } else {
+                    bf16x4 h, l;
+#pragma unroll
+                    for (int r = 0; r < 4; r++) split(ln >= 4 * lg + r ? m[r] : 0.0f, h, l, r);
+                    *reinterpret_cast<bf16x4 *>(&L.ph[ln * ST + 4 * lg]) = h;
+                    *reinterpret_cast<bf16x4 *>(&L.pl[ln * ST + 4 * lg]) = l;
+                }
+            }
+        } else
+        // ---- the decayed Gram sums, pairwise: D/8 lanes per pair (i, j), 8 key channels
         // each, summed across the pair's lanes by DPP (all lanes take part: a
         // slot past the last pair recomputes that pair and writes nothing);
         // the pair's first lane stores A^T (with beta) and P (split).  Every
-        // pass's LDS reads go out first (one wave per SIMD: nothing else
-        // hides their latency).
+        // pass's LDS reads go out first.
         {
             constexpr int LPP = D / 8, PPI = NT / LPP;  // lanes per pair, pairs per pass
             constexpr int NP = (NPAIR + PPI - 1) / PPI;  // passes
@@ -344,6 +418,7 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
             }
         }
         __syncthreads();
+        if (more) load_ab(c0 + KC, tid, nx);
 
         // ---- T = (I + A)^{-1} by forward substitution, lane c of wave 0 its
         // column: y = T e_c - e_c solves y_r = -A_rc - sum_{s<r} A_rs y_s (A
@@ -351,27 +426,32 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
         // A's columns read as rows of A^T; then T1 = T diag(beta), split.
         if (tid < KC) {
             const int c = tid;
-            // every load first (broadcast reads): issued step by step, the 15
-            // steps would wait on 15 LDS round trips
-            floatx4 yv[4], col[KC - 1][4];
-#pragma unroll
-            for (int q = 0; q < 4; q++) yv[q] = ldf4(&L.at[c * SA + 4 * q]);
-#pragma unroll
-            for (int s = 0; s < KC - 1; s++)
-#pragma unroll
-                for (int q = (s + 1) / 4; q < 4; q++) col[s][q] = ldf4(&L.at[s * SA + 4 * q]);  // A_{4q+e, s}
+            // the loads of each half of the steps go out together (broadcast
+            // reads): issued step by step, the 15 steps would wait on 15 LDS
+            // round trips, and all at once they would not fit in registers
             float y[KC];
 #pragma unroll
-            for (int q = 0; q < 4; q++)
+            for (int q = 0; q < 4; q++) {
+                const floatx4 yv = ldf4(&L.at[c * SA + 4 * q]);
 #pragma unroll
-                for (int e = 0; e < 4; e++) y[4 * q + e] = -yv[q][e];
+                for (int e = 0; e < 4; e++) y[4 * q + e] = -yv[e];
+            }
 #pragma unroll
-            for (int s = 0; s < KC - 1; s++)
+            for (int h = 0; h < 2; h++) {
+                constexpr int HS = (KC - 1 + 1) / 2;  // steps per half
+                floatx4 col[HS][4];
 #pragma unroll
-                for (int q = (s + 1) / 4; q < 4; q++)
+                for (int s = h * HS; s < min(KC - 1, (h + 1) * HS); s++)
 #pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        if (4 * q + e > s) y[4 * q + e] = fmaf(-col[s][q][e], y[s], y[4 * q + e]);
+                    for (int q = (s + 1) / 4; q < 4; q++) col[s - h * HS][q] = ldf4(&L.at[s * SA + 4 * q]);  // A_{4q+e, s}
+#pragma unroll
+                for (int s = h * HS; s < min(KC - 1, (h + 1) * HS); s++)
+#pragma unroll
+                    for (int q = (s + 1) / 4; q < 4; q++)
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            if (4 * q + e > s) y[4 * q + e] = fmaf(-col[s - h * HS][q][e], y[s], y[4 * q + e]);
+            }
             const float bc = L.beta[c];
 #pragma unroll
             for (int r = 0; r < KC; r++) {
@@ -385,18 +465,18 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
 
         // ---- U = T1 V (this wave's value columns) and -W = -T1 (K . 2^G) (this
         // wave's key channels, stored split, token-major)
-        floatx4 U[2];
+        floatx4 U[ET];
         {
             const bf16x4 th = ld4(&L.t1h[ln * ST + 4 * lg]), tl = ld4(&L.t1l[ln * ST + 4 * lg]);
 #pragma unroll
-            for (int et = 0; et < 2; et++) {
+            for (int et = 0; et < ET; et++) {
                 const bf16x4 vb = ld4(&L.vt[(e0 + 16 * et + ln) * ST + 4 * lg]);
                 U[et] = mma16(th, vb, floatx4{0.0f, 0.0f, 0.0f, 0.0f});
                 U[et] = mma16(tl, vb, U[et]);
             }
 #pragma unroll
-            for (int x = 0; x < 2; x++) {
-                const int c0w = 32 * wave + 16 * x;
+            for (int x = 0; x < ET; x++) {
+                const int c0w = CW * wave + 16 * x;
                 const bf16x4 gbh = ld4(&L.kgh[(c0w + ln) * ST + 4 * lg]), gbl = ld4(&L.kgl[(c0w + ln) * ST + 4 * lg]);
                 floatx4 Wx = mma16(th, gbh, floatx4{0.0f, 0.0f, 0.0f, 0.0f});
                 Wx = mma16(th, gbl, Wx);
@@ -413,9 +493,9 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
         __syncthreads();  // -W complete
 
         // ---- state operand (contraction over key rows, permuted slots)
-        bf16x8 Sh[2][KB], Sl[2][KB];
+        bf16x8 Sh[ET][KB], Sl[ET][KB];
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int kb = 0; kb < KB; kb++)
 #pragma unroll
@@ -424,46 +504,48 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
                     split(S[et][2 * kb + 1][r], Sh[et][kb], Sl[et][kb], 4 + r);
                 }
         // ---- U' = U - W S and O = (Q . 2^G) S
-        floatx4 O[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+        floatx4 O[ET];
+#pragma unroll
+        for (int et = 0; et < ET; et++) O[et] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kb = 0; kb < KB; kb++) {
             const int row = ln * SD + 4 * lg + 32 * kb;
             const bf16x8 wh = ld_pair(&L.wh[row]), wl = ld_pair(&L.wl[row]);
             const bf16x8 qh = ld_pair(&L.qgh[row]), ql = ld_pair(&L.qgl[row]);
 #pragma unroll
-            for (int et = 0; et < 2; et++) {
+            for (int et = 0; et < ET; et++) {
                 U[et] = mma32(wh, Sh[et][kb], U[et]);
                 O[et] = mma32(qh, Sh[et][kb], O[et]);
             }
 #pragma unroll
-            for (int et = 0; et < 2; et++) {
+            for (int et = 0; et < ET; et++) {
                 U[et] = mma32(wh, Sl[et][kb], U[et]);
                 O[et] = mma32(qh, Sl[et][kb], O[et]);
             }
 #pragma unroll
-            for (int et = 0; et < 2; et++) {
+            for (int et = 0; et < ET; et++) {
                 U[et] = mma32(wl, Sh[et][kb], U[et]);
                 O[et] = mma32(ql, Sh[et][kb], O[et]);
             }
         }
         // ---- U' as the B operand over tokens (its accumulator layout), split
-        bf16x4 Vh[2], Vl[2];
+        bf16x4 Vh[ET], Vl[ET];
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int r = 0; r < 4; r++) split(U[et][r], Vh[et], Vl[et], r);
         // ---- O += P U'; outputs staged token-major in K's tile (free now)
         {
             const bf16x4 pah = ld4(&L.ph[ln * ST + 4 * lg]), pal = ld4(&L.pl[ln * ST + 4 * lg]);
 #pragma unroll
-            for (int et = 0; et < 2; et++) {
+            for (int et = 0; et < ET; et++) {
                 O[et] = mma16(pah, Vh[et], O[et]);
                 O[et] = mma16(pah, Vl[et], O[et]);
                 O[et] = mma16(pal, Vh[et], O[et]);
             }
         }
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int r = 0; r < 4; r++) L.kr[(4 * lg + r) * SD + e0 + 16 * et + ln] = (__bf16)O[et][r];
         // ---- S <- diag(2^{G_C}) S + (K . 2^(G_C - G))^T U'
@@ -473,14 +555,14 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
 #pragma unroll
             for (int r = 0; r < 4; r++)
 #pragma unroll
-                for (int et = 0; et < 2; et++) S[et][dt][r] *= ec[r];
+                for (int et = 0; et < ET; et++) S[et][dt][r] *= ec[r];
         }
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) {
             const bf16x4 kah = ld4(&L.kch[(16 * dt + ln) * ST + 4 * lg]);
             const bf16x4 kal = ld4(&L.kcl[(16 * dt + ln) * ST + 4 * lg]);
 #pragma unroll
-            for (int et = 0; et < 2; et++) {
+            for (int et = 0; et < ET; et++) {
                 S[et][dt] = mma16(kah, Vh[et], S[et][dt]);
                 S[et][dt] = mma16(kah, Vl[et], S[et][dt]);
                 S[et][dt] = mma16(kal, Vh[et], S[et][dt]);
@@ -496,7 +578,7 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kda_kernel(PrefillKdaArgs A)
     }
 
 #pragma unroll
-    for (int et = 0; et < 2; et++)
+    for (int et = 0; et < ET; et++)
 #pragma unroll
         for (int dt = 0; dt < DT; dt++)
 #pragma unroll
@@ -522,9 +604,9 @@ hipError_t launch_prefill_kda(const gdnq_desc &d, float *S, const void *q, const
                      make_divisor((unsigned)(d.H / hk))};
     const unsigned grid = (unsigned)d.B * (unsigned)d.H;
     if (d.dk == 128) {
-        hipLaunchKernelGGL(prefill_kda_kernel<128>, dim3(grid), dim3(256), 0, st, A);
+        hipLaunchKernelGGL(prefill_kda_kernel<128>, dim3(grid), dim3(kda_threads<128>()), 0, st, A);
     } else {
-        hipLaunchKernelGGL(prefill_kda_kernel<64>, dim3(grid), dim3(128), 0, st, A);
+        hipLaunchKernelGGL(prefill_kda_kernel<64>, dim3(grid), dim3(kda_threads<64>()), 0, st, A);
     }
     return hipGetLastError();
 }

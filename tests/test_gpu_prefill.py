@@ -177,6 +177,36 @@ def test_prefill_kda_underflowing_gates():
     _check(cfg, T, inp, host(S), o_host, S0)
 
 
+def test_prefill_kda_chunk_paths():
+    """A chunk whose decay in some channel passes 2^-60 takes the pairwise
+    Gram sums, every other chunk the factored ones: chunk 1 of head 0 decays
+    by about 2^-70 in channel 5 (three gates of 1e-7), chunk 2 of head 1 by
+    about 2^-59.8 in channel 100 (two gates of 1e-9, the chunk's others 1:
+    just inside the factored range, where its factors reach 2^+-59.8); both
+    heads in one call."""
+    cfg = _cfg(1, 2, 128, seed=53, decay="channel")
+    T = 80
+    S0 = synth.random_states(23, 2, 128, 128, scale=0.5)
+    inp = _inputs(cfg, T)
+    a = inp["a"].copy()                                   # [T, B*H, dk]
+    a[17:20, 0, 5] = 1e-7
+    a[32:48, 1, 100] = 1.0
+    a[40:42, 1, 100] = 1e-9
+    inp["a"] = a
+    inp["a_dev"] = np.ascontiguousarray(np.swapaxes(a.reshape(T, 1, 2, 128), 0, 1))
+    torch = torch_cuda()
+    g = lib()
+    S = dev(S0.copy())
+    o = torch.empty((1, T, 2, 128), dtype=torch.bfloat16, device="cuda")
+    say("prefill kda chunk paths")
+    g.gdn_prefill(desc_for(cfg), S, _bf16_dev(inp["q16"]), _bf16_dev(inp["k16"]), _bf16_dev(inp["v16"]),
+                  dev(inp["a_dev"]), dev(inp["b_dev"]), o, T)
+    torch.cuda.synchronize()
+    o_host = synth.bf16_to_f32(o.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert np.isfinite(host(S)).all()
+    _check(cfg, T, inp, host(S), o_host, S0)
+
+
 def test_prefill_empty_is_noop():
     torch = torch_cuda()
     g = lib()
