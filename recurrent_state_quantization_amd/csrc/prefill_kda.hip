@@ -92,9 +92,10 @@ __device__ __forceinline__ bf16x4 ld4(const __bf16 *p) { return *reinterpret_cas
 __device__ __forceinline__ floatx4 ldf4(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
 
 // One thread's share of a chunk's inputs, held in registers while the
-// previous chunk is computed: one 8-byte piece of each of K, Q, V (token
-// x / (D/4), channels 4 (x % (D/4)) .. +3), and for thread c < D the 16
-// gates of key channel c; b for thread t < KC.
+// previous chunk is computed: one 8-byte piece of each of K and Q (token
+// x / (D/4), channels 4 (x % (D/4)) .. +3) and of V (token x % KC, channels
+// 4 (x / KC) .. +3), and for the last D threads (c = x - (threads - D)) the
+// 16 gates of key channel c and, for c < KC, b of token c.
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 struct KdaChunkRegs {
     u32x2 k, q, v;
@@ -229,19 +230,23 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
     // counts them and waits for them at staging alone.
     // K, Q, V go out first; the gates and beta later in the chunk, so that
     // their registers are not held through the Gram sums.
+    // The gates go to the last D threads, whose waves wait idle while the
+    // first wave solves for T.
     auto load_kqv = [=](int c0, int tid, KdaChunkRegs &r) {
         const int t = tid / (D / 4), c = 4 * (tid % (D / 4));
         const size_t u = (size_t)min(c0 + t, T - 1);
         r.k = *reinterpret_cast<const u32x2 *>(kg + u * tk + c);
         r.q = *reinterpret_cast<const u32x2 *>(qg + u * tk + c);
-        r.v = *reinterpret_cast<const u32x2 *>(vg + u * tv + c);
+        const int tv_ = tid % KC, cv = 4 * (tid / KC);
+        r.v = *reinterpret_cast<const u32x2 *>(vg + (size_t)min(c0 + tv_, T - 1) * tv + cv);
     };
     auto load_ab = [=](int c0, int tid, KdaChunkRegs &r) {
-        if (tid < D) {
+        const int c = tid - (NT - D);
+        if (c >= 0) {
 #pragma unroll
-            for (int t = 0; t < KC; t++) r.a[t] = ag[(size_t)min(c0 + t, T - 1) * tv + tid];
+            for (int t = 0; t < KC; t++) r.a[t] = ag[(size_t)min(c0 + t, T - 1) * tv + c];
+            r.b = bg[(size_t)min(c0 + (c & (KC - 1)), T - 1) * A.H];
         }
-        r.b = bg[(size_t)min(c0 + (tid & (KC - 1)), T - 1) * A.H];
     };
     static_assert(KC * D / 4 == NT, "one 8-byte piece of K, Q and V per thread");
 
@@ -268,27 +273,29 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
         const int nv = min(KC, T - c0);  // valid tokens of this chunk
 
         // ---- stage K, Q token-major and V^T (tokens past the end are zero),
-        // the gates (thread c < D scans channel c; padding has gate 1) and beta
+        // the gates (the last D threads, one key channel each; padding has
+        // gate 1) and beta
         {
             const int t = tid / (D / 4), c = 4 * (tid % (D / 4));
             const bool ok = t < nv;
             const u32x2 z = {0u, 0u};
             *reinterpret_cast<u32x2 *>(&L.kr[t * SD + c]) = ok ? nx.k : z;
             *reinterpret_cast<u32x2 *>(&L.qr[t * SD + c]) = ok ? nx.q : z;
-            const bf16x4 vv = __builtin_bit_cast(bf16x4, ok ? nx.v : z);
+            const int tv_ = tid % KC, cv = 4 * (tid / KC);
+            const bf16x4 vv = __builtin_bit_cast(bf16x4, tv_ < nv ? nx.v : z);
 #pragma unroll
-            for (int e = 0; e < 4; e++) L.vt[(c + e) * ST + t] = vv[e];
+            for (int e = 0; e < 4; e++) L.vt[(cv + e) * ST + tv_] = vv[e];
         }
-        if (tid < D) {
+        if (const int c = tid - (NT - D); c >= 0) {
             float acc = 0.0f;
 #pragma unroll
             for (int t = 0; t < KC; t++) {
                 acc += t < nv ? __builtin_amdgcn_logf(nx.a[t]) : 0.0f;
-                L.g[t * SG + tid] = acc;
+                L.g[t * SG + c] = acc;
             }
             if (!(acc >= -kFactorRange)) L.pairwise = c0 + 1;  // every thread that writes, writes the same
+            if (c < KC) L.beta[c] = c < nv ? nx.b : 0.0f;
         }
-        if (tid < KC) L.beta[tid] = tid < nv ? nx.b : 0.0f;
         __syncthreads();
         const bool more = c0 + KC < T;
         if (more) load_kqv(c0 + KC, tid, nx);  // in flight while this chunk is computed
@@ -297,21 +304,27 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
         // (K . 2^(G_C - G))^T (channel-major), all split; every exponent <= 0.
         // Thread c, 4 tokens of key channel c (the channel-major tiles take one
         // 8-byte store per thread); threads c < D also keep the chunk decay
-        // 2^(G_C) of key row c of S.
+        // 2^(G_C) of key row c of S.  In a factored chunk every exponent lies
+        // within [-60, 60], and the factors are products of 2^(+-G_t) with the
+        // channel's 2^(+-G_m) and 2^(G_C).
         const bool factored = __builtin_amdgcn_readfirstlane(L.pairwise) != c0 + 1;
         {
             constexpr int TPT = KC * D / NT;
             static_assert(TPT == 4, "one thread takes 4 tokens of one channel");
             const int c = tid % D, t0 = TPT * (tid / D);
             const float gC = L.g[(KC - 1) * SG + c], gm = L.g[kRefToken * SG + c];
-            if (tid < D) L.egc[c] = __builtin_amdgcn_exp2f(gC);
+            const float egC = __builtin_amdgcn_exp2f(gC);
+            const float egm = __builtin_amdgcn_exp2f(gm), emg = __builtin_amdgcn_exp2f(-gm);
+            if (tid < D) L.egc[c] = egC;
             bf16x4 gh, gl, ch, cl;
 #pragma unroll
             for (int e = 0; e < TPT; e++) {
                 const int t = t0 + e;
                 const float gv = L.g[t * SG + c];
                 const float kv = (float)L.kr[t * SD + c], qv = (float)L.qr[t * SD + c];
-                const float e1 = __builtin_amdgcn_exp2f(gv), e2 = __builtin_amdgcn_exp2f(gC - gv);
+                const float e1 = __builtin_amdgcn_exp2f(gv);
+                const float ei = factored ? __builtin_amdgcn_exp2f(-gv) : 0.0f;
+                const float e2 = factored ? egC * ei : __builtin_amdgcn_exp2f(gC - gv);
                 split(kv * e1, gh, gl, e);
                 split(kv * e2, ch, cl, e);
                 const float qe = qv * e1;
@@ -319,7 +332,7 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
                 L.qgh[t * SD + c] = qh;
                 L.qgl[t * SD + c] = (__bf16)(qe - (float)qh);
                 if (factored) {
-                    const float fl = __builtin_amdgcn_exp2f(gv - gm), fr = __builtin_amdgcn_exp2f(gm - gv);
+                    const float fl = e1 * emg, fr = egm * ei;
                     L.xf[t * SG + c] = kv * fl;
                     L.yf[t * SG + c] = kv * fr;
                     L.zf[t * SG + c] = qv * fl;
