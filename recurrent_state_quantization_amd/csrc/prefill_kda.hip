@@ -139,15 +139,16 @@ struct KdaLds {
     static constexpr int SD = D + 8;   // bf16 stride of token-major [KC][D] tiles (16-byte pad)
     static constexpr int SG = D + 4;   // fp32 stride of the gate tile
     static constexpr int ST = KC + 8;  // bf16 stride of channel-major [D][KC] and of [KC][KC] tiles
+    static constexpr int SK = KC + 4;  // fp32 stride of channel-major [D][KC] tiles
     __bf16 kr[KC * SD];                // K, token-major (then the chunk's outputs)
     __bf16 qr[KC * SD];                // Q, token-major
     float g[KC * SG];                  // G in base 2: cumulative log2 gates from the chunk start
     __bf16 vt[D * ST];                 // V^T
     __bf16 qgh[KC * SD], qgl[KC * SD];  // Q . 2^G, split, token-major
-    __bf16 kgh[D * ST], kgl[D * ST];    // (K . 2^G)^T, split
+    float kgf[D * SK];                  // (K . 2^G)^T
     __bf16 kch[D * ST], kcl[D * ST];    // (K . 2^(G_C - G))^T, split
     __bf16 wh[KC * SD], wl[KC * SD];    // -W, split, token-major
-    __bf16 t1h[KC * ST], t1l[KC * ST];  // T1 = T diag(beta), split
+    float uf[KC * SG];                  // U = T1 V, token-major
     __bf16 ph[KC * ST], pl[KC * ST];    // P, split (upper part zero)
     float xf[KC * SG];                  // K . 2^(G - G_m), token-major (m: the chunk's reference token)
     float yf[KC * SG];                  // K . 2^(G_m - G), token-major
@@ -186,7 +187,7 @@ template <int D>
 __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(PrefillKdaArgs A)
 {
     using Lds = KdaLds<D>;
-    constexpr int SD = Lds::SD, SG = Lds::SG, ST = Lds::ST;
+    constexpr int SD = Lds::SD, SG = Lds::SG, ST = Lds::ST, SK = Lds::SK;
     constexpr int ET = 1;                     // 16-column tiles of the state per wave
     constexpr int CW = 16 * ET;               // value columns (and key channels of W) per wave
     constexpr int NW = D / CW, NT = NW * 64;  // waves; wave w owns columns and channels CW w .. CW w + CW - 1
@@ -300,10 +301,10 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
         const bool more = c0 + KC < T;
         if (more) load_kqv(c0 + KC, tid, nx);  // in flight while this chunk is computed
 
-        // ---- element-wise operands: Q . 2^G (token-major), (K . 2^G)^T and
-        // (K . 2^(G_C - G))^T (channel-major), all split; every exponent <= 0.
-        // Thread c, 4 tokens of key channel c (the channel-major tiles take one
-        // 8-byte store per thread); threads c < D also keep the chunk decay
+        // ---- element-wise operands: Q . 2^G (token-major, split), (K . 2^G)^T
+        // (fp32) and (K . 2^(G_C - G))^T (split, both channel-major); every
+        // exponent <= 0.  Thread c, 4 tokens of key channel c (one store per
+        // channel-major tile and thread); threads c < D also keep the chunk decay
         // 2^(G_C) of key row c of S.  In a factored chunk every exponent lies
         // within [-60, 60], and the factors are products of 2^(+-G_t) with the
         // channel's 2^(+-G_m) and 2^(G_C).
@@ -316,7 +317,8 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
             const float egC = __builtin_amdgcn_exp2f(gC);
             const float egm = __builtin_amdgcn_exp2f(gm), emg = __builtin_amdgcn_exp2f(-gm);
             if (tid < D) L.egc[c] = egC;
-            bf16x4 gh, gl, ch, cl;
+            floatx4 kgv;
+            bf16x4 ch, cl;
 #pragma unroll
             for (int e = 0; e < TPT; e++) {
                 const int t = t0 + e;
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
                 const float e1 = __builtin_amdgcn_exp2f(gv);
                 const float ei = factored ? __builtin_amdgcn_exp2f(-gv) : 0.0f;
                 const float e2 = factored ? egC * ei : __builtin_amdgcn_exp2f(gC - gv);
-                split(kv * e1, gh, gl, e);
+                kgv[e] = kv * e1;
                 split(kv * e2, ch, cl, e);
                 const float qe = qv * e1;
                 const __bf16 qh = (__bf16)qe;
@@ -338,8 +340,7 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
                     L.zf[t * SG + c] = qv * fl;
                 }
             }
-            *reinterpret_cast<bf16x4 *>(&L.kgh[c * ST + t0]) = gh;
-            *reinterpret_cast<bf16x4 *>(&L.kgl[c * ST + t0]) = gl;
+            *reinterpret_cast<floatx4 *>(&L.kgf[c * SK + t0]) = kgv;
             *reinterpret_cast<bf16x4 *>(&L.kch[c * ST + t0]) = ch;
             *reinterpret_cast<bf16x4 *>(&L.kcl[c * ST + t0]) = cl;
         }
@@ -433,25 +434,34 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
         __syncthreads();
         if (more) load_ab(c0 + KC, tid, nx);
 
-        // ---- T = (I + A)^{-1} by forward substitution, lane c of wave 0 its
-        // column: y = T e_c - e_c solves y_r = -A_rc - sum_{s<r} A_rs y_s (A
-        // strictly lower: y_r = 0 for r <= c), updated right-looking with
-        // A's columns read as rows of A^T; then T1 = T diag(beta), split.
-        if (tid < KC) {
-            const int c = tid;
-            // the loads of each half of the steps go out together (broadcast
-            // reads): issued step by step, the 15 steps would wait on 15 LDS
-            // round trips, and all at once they would not fit in registers
+        // ---- U = T1 V and W = T1 (K . 2^G), T1 = (I + A)^{-1} diag(beta), by
+        // forward substitution on their columns, (I + A) Y = diag(beta) R: one
+        // lane per value column (R = V) and one per key channel (R = K . 2^G),
+        // updated right-looking with A's columns read as rows of A^T.  U goes
+        // to LDS in fp32, -W split, both token-major.
+        if (tid < 2 * D) {
+            const bool isw = tid >= D;  // wave-uniform
+            const int c = isw ? tid - D : tid;
             float y[KC];
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const floatx4 yv = ldf4(&L.at[c * SA + 4 * q]);
+                const floatx4 bq = ldf4(&L.beta[4 * q]);
+                if (isw) {
+                    const floatx4 rq = ldf4(&L.kgf[c * SK + 4 * q]);
 #pragma unroll
-                for (int e = 0; e < 4; e++) y[4 * q + e] = -yv[e];
+                    for (int e = 0; e < 4; e++) y[4 * q + e] = bq[e] * rq[e];
+                } else {
+                    const bf16x4 rq = ld4(&L.vt[c * ST + 4 * q]);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) y[4 * q + e] = bq[e] * (float)rq[e];
+                }
             }
+            // the loads of each half of the steps go out together (broadcast
+            // reads): issued step by step, the 15 steps would wait on 15 LDS
+            // round trips, and all at once they would not fit in registers
 #pragma unroll
             for (int h = 0; h < 2; h++) {
-                constexpr int HS = (KC - 1 + 1) / 2;  // steps per half
+                constexpr int HS = KC / 2;  // steps per half
                 floatx4 col[HS][4];
 #pragma unroll
                 for (int s = h * HS; s < min(KC - 1, (h + 1) * HS); s++)
@@ -465,45 +475,25 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
                         for (int e = 0; e < 4; e++)
                             if (4 * q + e > s) y[4 * q + e] = fmaf(-col[s - h * HS][q][e], y[s], y[4 * q + e]);
             }
-            const float bc = L.beta[c];
+            if (isw) {
 #pragma unroll
-            for (int r = 0; r < KC; r++) {
-                const float t1 = (r > c ? y[r] : (r == c ? 1.0f : 0.0f)) * bc;
-                const __bf16 h = (__bf16)t1;
-                L.t1h[r * ST + c] = h;
-                L.t1l[r * ST + c] = (__bf16)(t1 - (float)h);
-            }
-        }
-        __syncthreads();
-
-        // ---- U = T1 V (this wave's value columns) and -W = -T1 (K . 2^G) (this
-        // wave's key channels, stored split, token-major)
-        floatx4 U[ET];
-        {
-            const bf16x4 th = ld4(&L.t1h[ln * ST + 4 * lg]), tl = ld4(&L.t1l[ln * ST + 4 * lg]);
-#pragma unroll
-            for (int et = 0; et < ET; et++) {
-                const bf16x4 vb = ld4(&L.vt[(e0 + 16 * et + ln) * ST + 4 * lg]);
-                U[et] = mma16(th, vb, floatx4{0.0f, 0.0f, 0.0f, 0.0f});
-                U[et] = mma16(tl, vb, U[et]);
-            }
-#pragma unroll
-            for (int x = 0; x < ET; x++) {
-                const int c0w = CW * wave + 16 * x;
-                const bf16x4 gbh = ld4(&L.kgh[(c0w + ln) * ST + 4 * lg]), gbl = ld4(&L.kgl[(c0w + ln) * ST + 4 * lg]);
-                floatx4 Wx = mma16(th, gbh, floatx4{0.0f, 0.0f, 0.0f, 0.0f});
-                Wx = mma16(th, gbl, Wx);
-                Wx = mma16(tl, gbh, Wx);
-#pragma unroll
-                for (int r = 0; r < 4; r++) {  // Wx[r] = W[4 lg + r][c0w + ln]
-                    const float w = -Wx[r];
+                for (int t = 0; t < KC; t++) {
+                    const float w = -y[t];
                     const __bf16 h = (__bf16)w;
-                    L.wh[(4 * lg + r) * SD + c0w + ln] = h;
-                    L.wl[(4 * lg + r) * SD + c0w + ln] = (__bf16)(w - (float)h);
+                    L.wh[t * SD + c] = h;
+                    L.wl[t * SD + c] = (__bf16)(w - (float)h);
                 }
+            } else {
+#pragma unroll
+                for (int t = 0; t < KC; t++) L.uf[t * SG + c] = y[t];
             }
         }
-        __syncthreads();  // -W complete
+        __syncthreads();  // U and -W complete
+        floatx4 U[ET];  // U[et][r] = U[4 lg + r][e0 + 16 et + ln]
+#pragma unroll
+        for (int et = 0; et < ET; et++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) U[et][r] = L.uf[(4 * lg + r) * SG + e0 + 16 * et + ln];
 
         // ---- state operand (contraction over key rows, permuted slots)
         bf16x8 Sh[ET][KB], Sl[ET][KB];
@@ -547,14 +537,19 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
         for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int r = 0; r < 4; r++) split(U[et][r], Vh[et], Vl[et], r);
-        // ---- O += P U'; outputs staged token-major in K's tile (free now)
+        // ---- O += P U' (its own accumulator, added on the VALU: a product
+        // that reads as its accumulator the result of a product of another
+        // shape, here 16x16x32 before 16x16x16, gets no wait from the
+        // compiler and may read it before it is complete); outputs staged
+        // token-major in K's tile (free now)
         {
             const bf16x4 pah = ld4(&L.ph[ln * ST + 4 * lg]), pal = ld4(&L.pl[ln * ST + 4 * lg]);
 #pragma unroll
             for (int et = 0; et < ET; et++) {
-                O[et] = mma16(pah, Vh[et], O[et]);
-                O[et] = mma16(pah, Vl[et], O[et]);
-                O[et] = mma16(pal, Vh[et], O[et]);
+                floatx4 pu = mma16(pah, Vh[et], floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+                pu = mma16(pah, Vl[et], pu);
+                pu = mma16(pal, Vh[et], pu);
+                O[et] += pu;
             }
         }
 #pragma unroll
