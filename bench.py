@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -59,14 +60,22 @@ def kernel_family(tag: str) -> str:
     return "prefill"
 
 
+def code_text(src: str) -> str:
+    """A source's code without its comments and with whitespace runs
+    collapsed (the kernel sources hold no comment markers inside literals)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def src_hash(family: str) -> str:
-    """Hash of one kernel family's sources, to tell whether stored counters
-    still describe the current kernels."""
+    """Hash of one kernel family's code (comments and layout aside), to tell
+    whether stored counters still describe the current kernels."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "recurrent_state_quantization_amd", "csrc")
     for f in KERNEL_SOURCES[family]:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update((f + "\n" + code_text(fh.read())).encode())
     return h.hexdigest()[:16]
 
 

@@ -28,19 +28,22 @@
 //
 // Precision as in the scalar-gate kernel (prefill.hip): bf16 matrix products
 // with fp32 accumulation, q, k, v exact in bf16, every fp32 operand split
-// into two bf16 parts.  The decayed Gram sums A and P run on the VALU in
-// fp32 (one e^{G_ic - G_jc} per pair and channel: the per-channel decay
-// does not factor out of the contraction), D/8 lanes per pair with a DPP
-// sum; T by forward substitution in fp32.
+// into two bf16 parts.  The decayed Gram sums A and P are fp32: as two fp32
+// matrix products of the chunk's operands scaled by per-token factors
+// around a reference token, or, in a chunk where some channel decays by
+// more than 2^-60, pair by pair on the VALU (one e^{G_ic - G_jc} per pair
+// and channel).  U and W by forward substitution in fp32.
 //
 // Mapping: one workgroup per (batch, head) of D/16 waves (two per SIMD:
 // the chunk-local phases are latency-bound, and a second wave on each SIMD
 // hides part of it); wave w owns value columns 16w..16w+15 of the state,
 // kept in fp32 MFMA accumulators for the whole sequence (the layout and the
-// permuted contraction of the scalar-gate kernel), and key channels
-// 16w..16w+15 of W.  Products over the chunk's 16 tokens use
-// v_mfma_f32_16x16x16_bf16, whose accumulator layout is its own B operand
-// layout: U' feeds P U' and the state update straight from registers.
+// permuted contraction of the scalar-gate kernel).  Products over the
+// chunk's 16 tokens use v_mfma_f32_16x16x16_bf16, whose accumulator layout
+// is its own B operand layout: U' feeds P U' and the state update straight
+// from registers.  No accumulator chain mixes instruction shapes: the
+// compiler inserts no wait between a product and one of another shape that
+// reads it as its accumulator.
 #include <hip/hip_runtime.h>
 
 #include "launch.hpp"
