@@ -156,6 +156,7 @@ struct KdaLds {
     float xf[KC * SG];                  // K . 2^(G - G_m), token-major (m: the chunk's reference token)
     float yf[KC * SG];                  // K . 2^(G_m - G), token-major
     float zf[KC * SG];                  // Q . 2^(G - G_m), token-major
+    float gp[2][KC * SA];               // second halves of A and P^T (factored Gram sums)
     float egc[D];                       // 2^(G_C): the chunk's decay of each key row of S
     float at[KC * SA];                  // A^T: at[j * SA + i] = A_ij (i > j), zero elsewhere
     float beta[KC];
@@ -347,19 +348,24 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
             *reinterpret_cast<bf16x4 *>(&L.kch[c * ST + t0]) = ch;
             *reinterpret_cast<bf16x4 *>(&L.kcl[c * ST + t0]) = cl;
         }
-        // ---- the decayed Gram sums, factored: wave 0 forms A = X Y^T and wave 1
-        // P^T = Y Z^T (X = K . 2^(G - G_m), Y = K . 2^(G_m - G), Z = Q . 2^(G - G_m))
-        // with fp32 matrix products; lane group lg contracts over key channels
-        // D/4 lg .. D/4 lg + D/4 - 1, one per instruction.  Lane (lg, ln) then
+        // ---- the decayed Gram sums, factored: waves 0 and 1 form A = X Y^T and
+        // waves 2 and 3 P^T = Y Z^T (X = K . 2^(G - G_m), Y = K . 2^(G_m - G),
+        // Z = Q . 2^(G - G_m)) with fp32 matrix products, each wave over half
+        // of the key channels and lane group lg over D/8 of them, one per
+        // instruction; the second half goes through LDS and is added to the
+        // first (in that order, so the sums are reproducible).  Lane (lg, ln) then
         // holds rows 4 lg .. 4 lg + 3 of column ln: A_ij with i = 4 lg + r,
         // j = ln, which is A^T's row j, and P_ij with i = ln, j = 4 lg + r,
         // which is P's row i.
         if (factored) {
             __syncthreads();  // X, Y, Z staged
-            if (wave < 2) {
-                constexpr int CPG = D / 4;  // channels per lane group
-                const float *xa = (wave == 0 ? L.xf : L.yf) + ln * SG + CPG * lg;
-                const float *yb = (wave == 0 ? L.yf : L.zf) + ln * SG + CPG * lg;
+            const bool isp = wave >= 2, first = (wave & 1) == 0;  // wave-uniform
+            floatx4 m = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (wave < 4) {
+                constexpr int CPG = D / 8;  // channels per lane group and half
+                const int cb = (wave & 1) * (D / 2) + CPG * lg;
+                const float *xa = (isp ? L.yf : L.xf) + ln * SG + cb;
+                const float *yb = (isp ? L.zf : L.yf) + ln * SG + cb;
                 floatx4 m0 = {0.0f, 0.0f, 0.0f, 0.0f}, m1 = m0;
 #pragma unroll
                 for (int s4 = 0; s4 < CPG; s4 += 4) {
@@ -369,8 +375,13 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
                     m0 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[2], yv[2], m0, 0, 0, 0);
                     m1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[3], yv[3], m1, 0, 0, 0);
                 }
-                const floatx4 m = m0 + m1;
-                if (wave == 0) {
+                m = m0 + m1;
+                if (!first) *reinterpret_cast<floatx4 *>(&L.gp[isp][ln * SA + 4 * lg]) = m;
+            }
+            __syncthreads();  // second halves staged
+            if (wave < 4 && first) {
+                m += ldf4(&L.gp[isp][ln * SA + 4 * lg]);
+                if (!isp) {
                     const floatx4 bi = ldf4(&L.beta[4 * lg]);
                     floatx4 w;
 #pragma unroll
