@@ -143,7 +143,8 @@ struct KdaLds {
     static constexpr int SG = D + 4;   // fp32 stride of the gate tile
     static constexpr int ST = KC + 8;  // bf16 stride of channel-major [D][KC] and of [KC][KC] tiles
     static constexpr int SK = KC + 4;  // fp32 stride of channel-major [D][KC] tiles
-    __bf16 kr[KC * SD];                // K, token-major (then the chunk's outputs)
+    __bf16 kr[KC * SD];                // K, token-major
+    __bf16 ob[KC * SD];                // the chunk's outputs, token-major
     __bf16 qr[KC * SD];                // Q, token-major
     float g[KC * SG];                  // G in base 2: cumulative log2 gates from the chunk start
     __bf16 vt[D * ST];                 // V^T
@@ -255,6 +256,37 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
     };
     static_assert(KC * D / 4 == NT, "one 8-byte piece of K, Q and V per thread");
 
+    // Staging of the chunk at cs from the registers: K, Q token-major and V^T
+    // (tokens past the end are zero), the gates (the last D threads, one key
+    // channel each: cumulative log2-gates from the chunk start, padding gate
+    // 1; a channel that decays by more than 2^-60 over the chunk flags it)
+    // and beta.  A chunk is staged while the previous one finishes its state
+    // products: by then no phase reads these tiles.
+    auto stage = [&](int cs, int tid, const KdaChunkRegs &r) {
+        const int nv = min(KC, T - cs);
+        {
+            const int t = tid / (D / 4), c = 4 * (tid % (D / 4));
+            const bool ok = t < nv;
+            const u32x2 z = {0u, 0u};
+            *reinterpret_cast<u32x2 *>(&L.kr[t * SD + c]) = ok ? r.k : z;
+            *reinterpret_cast<u32x2 *>(&L.qr[t * SD + c]) = ok ? r.q : z;
+            const int tv_ = tid % KC, cv = 4 * (tid / KC);
+            const bf16x4 vv = __builtin_bit_cast(bf16x4, tv_ < nv ? r.v : z);
+#pragma unroll
+            for (int e = 0; e < 4; e++) L.vt[(cv + e) * ST + tv_] = vv[e];
+        }
+        if (const int c = tid - (NT - D); c >= 0) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int t = 0; t < KC; t++) {
+                acc += t < nv ? __builtin_amdgcn_logf(r.a[t]) : 0.0f;
+                L.g[t * SG + c] = acc;
+            }
+            if (!(acc >= -kFactorRange)) L.pairwise = cs + 1;  // every thread that writes, writes the same
+            if (c < KC) L.beta[c] = c < nv ? r.b : 0.0f;
+        }
+    };
+
     // S[et][dt][r] = S[16 dt + 4 lg + r][e0 + 16 et + ln] (MFMA accumulator layout)
     floatx4 S[ET][DT];
 #pragma unroll
@@ -268,40 +300,16 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
     KdaChunkRegs nx;
     load_kqv(0, tid, nx);
     load_ab(0, tid, nx);
+    stage(0, tid, nx);
+    __syncthreads();
     for (int c0 = 0; c0 < T; c0 += KC) {
-        __syncthreads();  // the previous chunk is done with every LDS tile
         // Lane indices pass through an empty asm each chunk, so the LDS
         // addresses built from them are formed inside the loop instead of
         // being hoisted out and held in registers across it.
         int tid = tid0;
         asm volatile("" : "+v"(lg), "+v"(ln), "+v"(tid));
-        const int nv = min(KC, T - c0);  // valid tokens of this chunk
 
-        // ---- stage K, Q token-major and V^T (tokens past the end are zero),
-        // the gates (the last D threads, one key channel each; padding has
-        // gate 1) and beta
-        {
-            const int t = tid / (D / 4), c = 4 * (tid % (D / 4));
-            const bool ok = t < nv;
-            const u32x2 z = {0u, 0u};
-            *reinterpret_cast<u32x2 *>(&L.kr[t * SD + c]) = ok ? nx.k : z;
-            *reinterpret_cast<u32x2 *>(&L.qr[t * SD + c]) = ok ? nx.q : z;
-            const int tv_ = tid % KC, cv = 4 * (tid / KC);
-            const bf16x4 vv = __builtin_bit_cast(bf16x4, tv_ < nv ? nx.v : z);
-#pragma unroll
-            for (int e = 0; e < 4; e++) L.vt[(cv + e) * ST + tv_] = vv[e];
-        }
-        if (const int c = tid - (NT - D); c >= 0) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int t = 0; t < KC; t++) {
-                acc += t < nv ? __builtin_amdgcn_logf(nx.a[t]) : 0.0f;
-                L.g[t * SG + c] = acc;
-            }
-            if (!(acc >= -kFactorRange)) L.pairwise = c0 + 1;  // every thread that writes, writes the same
-            if (c < KC) L.beta[c] = c < nv ? nx.b : 0.0f;
-        }
-        __syncthreads();
+        const int nv = min(KC, T - c0);  // valid tokens of this chunk
         const bool more = c0 + KC < T;
         if (more) load_kqv(c0 + KC, tid, nx);  // in flight while this chunk is computed
 
@@ -555,7 +563,7 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
         // that reads as its accumulator the result of a product of another
         // shape, here 16x16x32 before 16x16x16, gets no wait from the
         // compiler and may read it before it is complete); outputs staged
-        // token-major in K's tile (free now)
+        // token-major in their own tile
         {
             const bf16x4 pah = ld4(&L.ph[ln * ST + 4 * lg]), pal = ld4(&L.pl[ln * ST + 4 * lg]);
 #pragma unroll
@@ -569,7 +577,7 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
 #pragma unroll
         for (int et = 0; et < ET; et++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) L.kr[(4 * lg + r) * SD + e0 + 16 * et + ln] = (__bf16)O[et][r];
+            for (int r = 0; r < 4; r++) L.ob[(4 * lg + r) * SD + e0 + 16 * et + ln] = (__bf16)O[et][r];
         // ---- S <- diag(2^{G_C}) S + (K . 2^(G_C - G))^T U'
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) {
@@ -590,12 +598,13 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
                 S[et][dt] = mma16(kal, Vh[et], S[et][dt]);
             }
         }
-        __syncthreads();  // the outputs are staged
+        if (more) stage(c0 + KC, tid, nx);
+        __syncthreads();  // the outputs and the next chunk are staged
         for (int x = tid; x < KC * D / 8; x += NT) {
             const int t = x / (D / 8), c = 8 * (x % (D / 8));
             if (t < nv)
                 *reinterpret_cast<u32x4 *>(og + (size_t)(c0 + t) * tv + c) =
-                    *reinterpret_cast<const u32x4 *>(&L.kr[t * SD + c]);
+                    *reinterpret_cast<const u32x4 *>(&L.ob[t * SD + c]);
         }
     }
 
