@@ -451,7 +451,8 @@ def bench_prefill(args, torch, g, cfg, x, cpu):
         "value": nh * T * args.steps / wall, "unit": "token-head updates/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 q/k/v/o, bf16 MFMA with split fp32 operands, fp32 state",
+        "dtype": "bf16 q/k/v/o, bf16 MFMA with split fp32 operands"
+                 + (", fp32 MFMA for the decayed Gram sums" if kda else "") + ", fp32 state",
         "data": "synthetic (seeded; no weights)",
         "config": {"workload": f"{tag}: B={B} sequences x H={H} heads x T={T} tokens, dk=dv={D}, bf16 I/O, "
                                f"{'per-channel' if kda else 'scalar'} gate, zero initial state",
