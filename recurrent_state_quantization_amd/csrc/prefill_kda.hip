@@ -553,6 +553,8 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
                 O[et] = mma32(ql, Sh[et][kb], O[et]);
             }
         }
+        // the next chunk's staging fills the time these products take
+        if (more) stage(c0 + KC, tid, nx);
         // ---- U' as the B operand over tokens (its accumulator layout), split
         bf16x4 Vh[ET], Vl[ET];
 #pragma unroll
@@ -598,7 +600,6 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
                 S[et][dt] = mma16(kal, Vh[et], S[et][dt]);
             }
         }
-        if (more) stage(c0 + KC, tid, nx);
         __syncthreads();  // the outputs and the next chunk are staged
         for (int x = tid; x < KC * D / 8; x += NT) {
             const int t = x / (D / 8), c = 8 * (x % (D / 8));
