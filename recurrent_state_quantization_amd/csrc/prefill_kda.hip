@@ -553,8 +553,17 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
                 O[et] = mma32(ql, Sh[et][kb], O[et]);
             }
         }
-        // the next chunk's staging fills the time these products take
+        // the next chunk's staging and the decay of S (whose split parts the
+        // products read) fill the time these products take
         if (more) stage(c0 + KC, tid, nx);
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            const floatx4 ec = ldf4(&L.egc[16 * dt + 4 * lg]);
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+#pragma unroll
+                for (int et = 0; et < ET; et++) S[et][dt][r] *= ec[r];
+        }
         // ---- U' as the B operand over tokens (its accumulator layout), split
         bf16x4 Vh[ET], Vl[ET];
 #pragma unroll
@@ -580,15 +589,7 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
         for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int r = 0; r < 4; r++) L.ob[(4 * lg + r) * SD + e0 + 16 * et + ln] = (__bf16)O[et][r];
-        // ---- S <- diag(2^{G_C}) S + (K . 2^(G_C - G))^T U'
-#pragma unroll
-        for (int dt = 0; dt < DT; dt++) {
-            const floatx4 ec = ldf4(&L.egc[16 * dt + 4 * lg]);
-#pragma unroll
-            for (int r = 0; r < 4; r++)
-#pragma unroll
-                for (int et = 0; et < ET; et++) S[et][dt][r] *= ec[r];
-        }
+        // ---- S <- diag(2^{G_C}) S + (K . 2^(G_C - G))^T U' (S already decayed)
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) {
             const bf16x4 kah = ld4(&L.kch[(16 * dt + ln) * ST + 4 * lg]);
