@@ -230,6 +230,9 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
         const int i = pair_row(p);
         L.pij[p] = (uint8_t)(i | (p - i * (i + 1) / 2) << 4);
     }
+    // The first chunk's staging may flag it for the pairwise sums: that
+    // write must follow the clear above.
+    __syncthreads();
 
     // Chunk loads: every load is unconditional (tokens past the end are
     // clamped to the last one) and zeroed only when staged, so the compiler

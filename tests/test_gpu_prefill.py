@@ -182,22 +182,25 @@ def test_prefill_kda_chunk_paths():
     Gram sums, every other chunk the factored ones: chunk 1 of head 0 decays
     by about 2^-70 in channel 5 (three gates of 1e-7), chunk 2 of head 1 by
     about 2^-59.8 in channel 100 (two gates of 1e-9, the chunk's others 1:
-    just inside the factored range, where its factors reach 2^+-59.8); both
-    heads in one call."""
-    cfg = _cfg(1, 2, 128, seed=53, decay="channel")
+    just inside the factored range, where its factors reach 2^+-59.8), and
+    chunk 0 of head 2 by about 2^-70 in channel 7 (the first chunk's flag is
+    set while the kernel's tables are first cleared); all heads in one
+    call."""
+    cfg = _cfg(1, 3, 128, seed=53, decay="channel")
     T = 80
-    S0 = synth.random_states(23, 2, 128, 128, scale=0.5)
+    S0 = synth.random_states(23, 3, 128, 128, scale=0.5)
     inp = _inputs(cfg, T)
     a = inp["a"].copy()                                   # [T, B*H, dk]
     a[17:20, 0, 5] = 1e-7
     a[32:48, 1, 100] = 1.0
     a[40:42, 1, 100] = 1e-9
+    a[2:5, 2, 7] = 1e-7
     inp["a"] = a
-    inp["a_dev"] = np.ascontiguousarray(np.swapaxes(a.reshape(T, 1, 2, 128), 0, 1))
+    inp["a_dev"] = np.ascontiguousarray(np.swapaxes(a.reshape(T, 1, 3, 128), 0, 1))
     torch = torch_cuda()
     g = lib()
     S = dev(S0.copy())
-    o = torch.empty((1, T, 2, 128), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((1, T, 3, 128), dtype=torch.bfloat16, device="cuda")
     say("prefill kda chunk paths")
     g.gdn_prefill(desc_for(cfg), S, _bf16_dev(inp["q16"]), _bf16_dev(inp["k16"]), _bf16_dev(inp["v16"]),
                   dev(inp["a_dev"]), dev(inp["b_dev"]), o, T)
