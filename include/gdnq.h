@@ -59,9 +59,9 @@
  *    gdnq_last_error().  Argument errors are found on the host before any
  *    launch, so a failed call has not touched device memory.
  *  - Inputs that are NaN or infinite give undefined results.  Gates must
- *    satisfy 0 < a <= 1 and the product of a window's gates must stay above
- *    1e-30 (per key channel for KDA): the window buffer stores each key
- *    divided by the cumulative gate up to its token.
+ *    satisfy 0 < a <= 1 (fp32 subnormal gates included); a window's gate
+ *    products may fall below fp32's range: the window buffer keeps each
+ *    product as a mantissa and a separate integer exponent.
  *  - bf16 inputs are widened exactly; a bf16 output is rounded to nearest
  *    even from fp32.
  */
@@ -133,19 +133,22 @@ typedef struct {
  *                                      the fitted column range
  *   comp_k      fp32   [B,H,r,dk]      compensator key-side vectors p (r > 0)
  *   comp_v      fp32   [B,H,r,dv]      compensator value-side unit vectors w
- *   buf_k       fp32   [B,H,W,dk]      window buffer keys k_t / G_t, where
- *                                      G_t is the gate product since the
- *                                      window start (per key channel)
+ *   With G_t the gate product a_1 ... a_t since the window start (one
+ *   value per head for the scalar gate, one per key channel for KDA),
+ *   written G_t = m_t 2^(e_t) with mantissa m_t in [0.5, 1) and integer
+ *   exponent e_t (so no product over- or underflows):
+ *   buf_k       fp32   [B,H,W,dk]      window buffer keys k_t / m_t
  *   buf_u       fp32   [B,H,W,dv]      window buffer updates u_t
- *   g_cur       fp32   [B,H] (scalar) or [B,H,dk] (channel): gate product
- *                                      since the window start
+ *   buf_g       int32  [B,H,W] (scalar) or [B,H,W,dk] (channel): e_t
+ *   g_cur       fp32   [B,H] (scalar) or [B,H,dk] (channel): m_t of the
+ *                                      last token (1 at a window start)
  *   hp_rows     uint16 [B,H,n_hp,dv]   layout 1: fp16 bit patterns
  *   hp_idx      int32  [B,H,n_hp]      layout 1: row indices, strictly
  *                                      ascending, in [0, dk)
  *   prequant_out fp32  [B,H,dk,dv]     with GDNQ_DEBUG_PREQUANT: the fp32
  *                                      tensor handed to the codec
- * Buffers for window mode (buf_k, buf_u, g_cur) are needed when W > 1,
- * r > 0 or layout == GDNQ_LAYOUT_DAMP.
+ * Buffers for window mode (buf_k, buf_u, buf_g, g_cur) are needed when
+ * W > 1, r > 0 or layout == GDNQ_LAYOUT_DAMP.
  */
 typedef struct {
     int8_t *codes;
@@ -155,6 +158,7 @@ typedef struct {
     float *comp_v;
     float *buf_k;
     float *buf_u;
+    int32_t *buf_g;
     float *g_cur;
     uint16_t *hp_rows;
     int32_t *hp_idx;
@@ -172,8 +176,8 @@ typedef struct {
  * Per-step mode: dequantize, update, emit o from the updated fp32 state,
  * requantize and store codes and scales in place (one fused kernel).
  * Window mode: read the fixed state, compensators and the t_in_window
- * buffered tokens, emit o, append (k_t, u_t) to buffer slot t_in_window
- * and update g_cur; the codes are not written.
+ * buffered tokens, emit o, append (k_t / m_t, u_t, e_t) to buffer slot
+ * t_in_window and store m_t in g_cur; the codes are not written.
  * Per-step mode with layout 1 runs the window step and a one-token flush.
  */
 int gdn_quant_decode_step(const gdnq_desc *desc, const gdnq_state *state, const void *q,
@@ -183,7 +187,8 @@ int gdn_quant_decode_step(const gdnq_desc *desc, const gdnq_state *state, const 
 /*
  * Window end: rebuild S_W = diag(G) (D(Q) + sum_c p_c w_c^T) +
  * sum_{t<n} ((G/G_t) . k_t) u_t^T from the first n_tokens buffer slots
- * (fp32 MFMA rank-(n+r) product), take r new Compensator Tokens out of it,
+ * (fp32 MFMA rank-(n+r) product; G = G_n, each ratio G/G_t formed as
+ * (m_n / m_t) 2^(e_n - e_t)), take r new Compensator Tokens out of it,
  * requantize the residual, store codes, scales and compensators, and reset
  * g_cur to 1.  n_tokens in 1..W; n_tokens < W gives a self-contained
  * snapshot of a partial window.  In per-step mode this is a no-op.
@@ -310,11 +315,11 @@ int gdn_prefill(const gdnq_desc *desc, float *S, const void *q, const void *k, c
                 const float *a, const float *b, void *o, int32_t T, void *stream);
 
 /*
- * Byte sizes of the 11 gdnq_state arrays for this descriptor, in field
- * order (codes, row_scale, col_scale, comp_k, comp_v, buf_k, buf_u, g_cur,
- * hp_rows, hp_idx, prequant_out); 0 where the array is unused.
+ * Byte sizes of the 12 gdnq_state arrays for this descriptor, in field
+ * order (codes, row_scale, col_scale, comp_k, comp_v, buf_k, buf_u, buf_g,
+ * g_cur, hp_rows, hp_idx, prequant_out); 0 where the array is unused.
  */
-int gdnq_state_sizes(const gdnq_desc *desc, size_t bytes_out[11]);
+int gdnq_state_sizes(const gdnq_desc *desc, size_t bytes_out[12]);
 
 /* Message of the last error on this thread ("" if none). */
 const char *gdnq_last_error(void);

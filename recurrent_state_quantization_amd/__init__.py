@@ -23,7 +23,7 @@ LAYOUT_ROWCOL, LAYOUT_DAMP = 0, 1
 DEBUG_PREQUANT = 1
 STATIC_SCALES = 2
 
-STATE_FIELDS = ("codes", "row_scale", "col_scale", "comp_k", "comp_v", "buf_k", "buf_u", "g_cur",
+STATE_FIELDS = ("codes", "row_scale", "col_scale", "comp_k", "comp_v", "buf_k", "buf_u", "buf_g", "g_cur",
                 "hp_rows", "hp_idx", "prequant_out")
 
 
@@ -93,7 +93,7 @@ def _load():
         "gdn_fp32_decode_step": [D, P, P, P, P, P, P, P, P],
         "gdn_prefill": [D, P, P, P, P, P, P, P, i32, P],
         "calibrate_static_scales": [D, P, P, P, P, P, P, i32, S, P],
-        "gdnq_state_sizes": [D, ctypes.POINTER(ctypes.c_size_t * 11)],
+        "gdnq_state_sizes": [D, ctypes.POINTER(ctypes.c_size_t * len(STATE_FIELDS))],
     }
     for name, args in sig.items():
         if not hasattr(lib, name):
@@ -150,7 +150,7 @@ def _desc(desc) -> _Desc:
 
 # ------------------------------------------------------------------ C ABI
 def gdnq_state_sizes(desc: Desc) -> list[int]:
-    out = (ctypes.c_size_t * 11)()
+    out = (ctypes.c_size_t * len(STATE_FIELDS))()
     _check(lib.gdnq_state_sizes(ctypes.byref(_desc(desc)), ctypes.byref(out)))
     return list(out)
 
@@ -211,7 +211,7 @@ def gdn_prefill(desc, S, q, k, v, a, b, o, T, stream=None):
 
 
 # --------------------------------------------------------------- plumbing
-_DTYPES = {"codes": "int8", "hp_rows": "int16", "hp_idx": "int32"}
+_DTYPES = {"codes": "int8", "hp_rows": "int16", "hp_idx": "int32", "buf_g": "int32"}
 
 
 def alloc_state(desc: Desc, device="cuda"):

@@ -89,8 +89,10 @@ int check_desc(const gdnq_desc *d)
     return GDNQ_OK;
 }
 
-// byte sizes of the 11 state arrays, 0 where unused
-void state_sizes(const gdnq_desc &d, size_t out[11])
+// byte sizes of the 12 state arrays, 0 where unused
+constexpr int NSTATE = 12;
+
+void state_sizes(const gdnq_desc &d, size_t out[NSTATE])
 {
     const size_t nh = nheads(d);
     const bool damp = d.layout == GDNQ_LAYOUT_DAMP;
@@ -104,16 +106,17 @@ void state_sizes(const gdnq_desc &d, size_t out[11])
     out[4] = nh * (size_t)d.r * d.dv * 4;                                  // comp_v
     out[5] = window ? nh * (size_t)d.W * d.dk * 4 : 0;                     // buf_k
     out[6] = window ? nh * (size_t)d.W * d.dv * 4 : 0;                     // buf_u
-    out[7] = window ? nh * (d.decay == GDNQ_DECAY_CHANNEL ? d.dk : 1) * 4 : 0;  // g_cur
-    out[8] = damp ? nh * (size_t)d.n_hp * d.dv * 2 : 0;                    // hp_rows
-    out[9] = damp ? nh * (size_t)d.n_hp * 4 : 0;                           // hp_idx
-    out[10] = (d.flags & GDNQ_DEBUG_PREQUANT) ? nh * d.dk * d.dv * 4 : 0;  // prequant_out
+    out[7] = window ? nh * (size_t)d.W * agate(d) * 4 : 0;                 // buf_g
+    out[8] = window ? nh * agate(d) * 4 : 0;                               // g_cur
+    out[9] = damp ? nh * (size_t)d.n_hp * d.dv * 2 : 0;                   // hp_rows
+    out[10] = damp ? nh * (size_t)d.n_hp * 4 : 0;                          // hp_idx
+    out[11] = (d.flags & GDNQ_DEBUG_PREQUANT) ? nh * d.dk * d.dv * 4 : 0;  // prequant_out
 }
 
-const char *kStateNames[11] = {"codes", "row_scale", "col_scale", "comp_k", "comp_v", "buf_k",
-                               "buf_u",  "g_cur",     "hp_rows",   "hp_idx", "prequant_out"};
+const char *kStateNames[NSTATE] = {"codes", "row_scale", "col_scale", "comp_k", "comp_v", "buf_k",
+                                   "buf_u", "buf_g",     "g_cur",     "hp_rows", "hp_idx", "prequant_out"};
 
-void state_ptrs(const gdnq_state &s, const void *out[11])
+void state_ptrs(const gdnq_state &s, const void *out[NSTATE])
 {
     out[0] = s.codes;
     out[1] = s.row_scale;
@@ -122,24 +125,38 @@ void state_ptrs(const gdnq_state &s, const void *out[11])
     out[4] = s.comp_v;
     out[5] = s.buf_k;
     out[6] = s.buf_u;
-    out[7] = s.g_cur;
-    out[8] = s.hp_rows;
-    out[9] = s.hp_idx;
-    out[10] = s.prequant_out;
+    out[7] = s.buf_g;
+    out[8] = s.g_cur;
+    out[9] = s.hp_rows;
+    out[10] = s.hp_idx;
+    out[11] = s.prequant_out;
+}
+
+// Which state arrays a call reads or writes.
+struct Need {
+    bool v[NSTATE];
+};
+
+// codes, scales and compensators (+ DAMP rows); `window` adds the window
+// buffer and gate arrays, `prequant` the debug output
+Need need_of(const gdnq_desc &d, bool window, bool prequant)
+{
+    const bool damp = d.layout == GDNQ_LAYOUT_DAMP;
+    return Need{{true, !damp, true, d.r > 0, d.r > 0, window, window, window, window, damp, damp, prequant}};
 }
 
 // Check the state arrays that `need[]` marks as used: non-NULL, 16-byte
 // aligned, pairwise disjoint; append them to `spans` for overlap checks
 // against the per-call buffers.
-int check_state(const gdnq_desc &d, const gdnq_state *s, const bool need[11], std::vector<Span> &spans)
+int check_state(const gdnq_desc &d, const gdnq_state *s, const Need &need, std::vector<Span> &spans)
 {
     if (!s) return fail(GDNQ_EINVAL, "state is NULL");
-    size_t sz[11];
-    const void *p[11];
+    size_t sz[NSTATE];
+    const void *p[NSTATE];
     state_sizes(d, sz);
     state_ptrs(*s, p);
-    for (int i = 0; i < 11; i++) {
-        if (!need[i] || sz[i] == 0) continue;
+    for (int i = 0; i < NSTATE; i++) {
+        if (!need.v[i] || sz[i] == 0) continue;
         if (!p[i]) return fail(GDNQ_EINVAL, "state->%s is NULL but required here", kStateNames[i]);
         if (!aligned16(p[i])) return fail(GDNQ_EINVAL, "state->%s is not 16-byte aligned", kStateNames[i]);
         Span sp{p[i], sz[i], kStateNames[i]};
@@ -201,7 +218,7 @@ extern "C" {
 
 const char *gdnq_last_error(void) { return g_err; }
 
-int gdnq_state_sizes(const gdnq_desc *desc, size_t bytes_out[11])
+int gdnq_state_sizes(const gdnq_desc *desc, size_t bytes_out[12])
 {
     int rc = check_desc(desc);
     if (rc) return rc;
@@ -221,9 +238,9 @@ int gdn_quant_decode_step(const gdnq_desc *desc, const gdnq_state *state, const 
     const bool fused = per_step(d) && !damp;
     if (t_in_window < 0 || t_in_window >= d.W)
         return fail(GDNQ_EINVAL, "t_in_window must be in [0, W-1] (got %d, W=%d)", t_in_window, d.W);
-    bool need[11] = {true, !damp, true, d.r > 0, d.r > 0, !fused, !fused, !fused, damp, damp,
-                     fused && (d.flags & GDNQ_DEBUG_PREQUANT)};
-    if (per_step(d) && damp) need[10] = (d.flags & GDNQ_DEBUG_PREQUANT) != 0;
+    // the debug output is written by the fused step and by the flush that
+    // follows a DAMP per-step decode
+    const Need need = need_of(d, !fused, (fused || per_step(d)) && (d.flags & GDNQ_DEBUG_PREQUANT));
     std::vector<Span> spans;
     if ((rc = check_state(d, state, need, spans))) return rc;
     if ((rc = check_step_io(d, q, k, v, a, b, o, spans))) return rc;
@@ -247,8 +264,7 @@ int gdn_quant_window_flush(const gdnq_desc *desc, const gdnq_state *state, int32
     if (per_step(d) && damp) return ok();  // the decode step already flushed
     if (n_tokens < 1 || n_tokens > d.W)
         return fail(GDNQ_EINVAL, "n_tokens must be in [1, W] (got %d, W=%d)", n_tokens, d.W);
-    bool need[11] = {true, !damp, true, d.r > 0, d.r > 0, true, true, true, damp, damp,
-                     (d.flags & GDNQ_DEBUG_PREQUANT) != 0};
+    const Need need = need_of(d, true, (d.flags & GDNQ_DEBUG_PREQUANT) != 0);
     std::vector<Span> spans;
     if ((rc = check_state(d, state, need, spans))) return rc;
     return launched(gdnq::launch_flush(d, gdnq::plain_map(d), *state, n_tokens, reinterpret_cast<hipStream_t>(stream)));
@@ -267,9 +283,7 @@ int gdn_quant_decode_step_pool(const gdnq_desc *desc, const gdnq_state *state, i
     const gdnq_desc &d = *desc;
     const bool damp = d.layout == GDNQ_LAYOUT_DAMP;
     const bool fused = per_step(d) && !damp;
-    bool need[11] = {true, !damp, true, d.r > 0, d.r > 0, !fused, !fused, !fused, damp, damp,
-                     fused && (d.flags & GDNQ_DEBUG_PREQUANT)};
-    if (per_step(d) && damp) need[10] = (d.flags & GDNQ_DEBUG_PREQUANT) != 0;
+    const Need need = need_of(d, !fused, (fused || per_step(d)) && (d.flags & GDNQ_DEBUG_PREQUANT));
     std::vector<Span> spans;
     if ((rc = check_state(pool, state, need, spans))) return rc;
     if ((rc = check_step_io(d, q, k, v, a, b, o, spans))) return rc;
@@ -301,8 +315,7 @@ int gdn_quant_window_flush_pool(const gdnq_desc *desc, const gdnq_state *state, 
     if (per_step(d)) return ok();   // per-step mode has no window to flush
     gdnq_desc pool = d;
     pool.B = n_slots;
-    bool need[11] = {true, !damp, true, d.r > 0, d.r > 0, true, true, true, damp, damp,
-                     (d.flags & GDNQ_DEBUG_PREQUANT) != 0};
+    const Need need = need_of(d, true, (d.flags & GDNQ_DEBUG_PREQUANT) != 0);
     std::vector<Span> spans;
     if ((rc = check_state(pool, state, need, spans))) return rc;
     if ((rc = check_buf(slots, (size_t)d.B * 4, "slots", spans))) return rc;
@@ -320,17 +333,16 @@ int gdn_state_quantize(const gdnq_desc *desc, const float *S, const gdnq_state *
     if (rc) return rc;
     const gdnq_desc &d = *desc;
     const bool damp = d.layout == GDNQ_LAYOUT_DAMP;
-    bool need[11] = {true, !damp, true, d.r > 0, d.r > 0, false, false, false, damp, damp,
-                     (d.flags & GDNQ_DEBUG_PREQUANT) != 0};
+    const Need need = need_of(d, false, (d.flags & GDNQ_DEBUG_PREQUANT) != 0);
     std::vector<Span> spans;
     if ((rc = check_state(d, state, need, spans))) return rc;
     if ((rc = check_buf(S, nheads(d) * d.dk * d.dv * 4, "S", spans))) return rc;
     // g_cur is optional here: reset to 1 when given
     if (state->g_cur) {
-        size_t sz[11];
+        size_t sz[NSTATE];
         state_sizes(d, sz);
-        size_t gsz = nheads(d) * (d.decay == GDNQ_DECAY_CHANNEL ? d.dk : 1) * 4;
-        if ((rc = check_buf(state->g_cur, sz[7] ? sz[7] : gsz, "state->g_cur", spans))) return rc;
+        size_t gsz = nheads(d) * agate(d) * 4;
+        if ((rc = check_buf(state->g_cur, sz[8] ? sz[8] : gsz, "state->g_cur", spans))) return rc;
     }
     return launched(gdnq::launch_quantize(d, S, *state, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -341,7 +353,7 @@ int gdn_state_dequantize(const gdnq_desc *desc, const gdnq_state *state, float *
     if (rc) return rc;
     const gdnq_desc &d = *desc;
     const bool damp = d.layout == GDNQ_LAYOUT_DAMP;
-    bool need[11] = {true, !damp, true, d.r > 0, d.r > 0, false, false, false, damp, damp, false};
+    const Need need = need_of(d, false, false);
     std::vector<Span> spans;
     if ((rc = check_state(d, state, need, spans))) return rc;
     if ((rc = check_buf(S_out, nheads(d) * d.dk * d.dv * 4, "S_out", spans))) return rc;
@@ -401,8 +413,8 @@ int calibrate_static_scales(const gdnq_desc *desc, const float *S0, const void *
     const size_t nh = nheads(d), es = io_size(d), ns = (size_t)n_steps;
     const size_t na = d.decay == GDNQ_DECAY_CHANNEL ? (size_t)d.dk : 1;
     std::vector<Span> spans;
-    bool need[11] = {false};
-    need[1] = need[2] = true;  // row_scale, col_scale (both planes)
+    Need need{};
+    need.v[1] = need.v[2] = true;  // row_scale, col_scale (both planes)
     if ((rc = check_state(d, state, need, spans))) return rc;
     struct In {
         const void *p;

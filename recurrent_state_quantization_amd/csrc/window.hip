@@ -13,10 +13,17 @@
 // (dequantized codes + DAMP fp16 rows + compensators).  Unrolling the
 // recurrence from X_0:
 //   S_t = diag(G_t) X_0 + sum_{l<=t} ((G_t/G_l) . k_l) u_l^T
-// so with the buffer holding k^_l = k_l / G_l (elementwise):
-//   S'^T k_t = X_0^T (G_t . k_t) + sum_{l<t} u_l (k^_l . (G_t . k_t))
-//   o_t      = X_0^T (G_t . q_t) + sum_{l<t} u_l (k^_l . (G_t . q_t)) + u_t (k_t . q_t)
-//   S_W      = diag(G_W) [ X_0 + sum_{l<=n} k^_l u_l^T ]
+// so
+//   S'^T k_t = X_0^T (G_t . k_t) + sum_{l<t} u_l (((G_t/G_l) . k_l) . k_t)
+//   o_t      = X_0^T (G_t . q_t) + sum_{l<t} u_l (((G_t/G_l) . k_l) . q_t) + u_t (k_t . q_t)
+//   S_W      = diag(G_W) X_0 + sum_{l<=n} ((G_W/G_l) . k_l) u_l^T
+// A gate product can leave fp32's range long before the ratios G_t/G_l
+// (all <= 1) do, so each is kept as G_t = m_t 2^(e_t): a mantissa m_t in
+// [0.5, 1) (the running product of the gates' mantissas, renormalized each
+// step, so it rounds exactly like a plain fp32 product) and an integer
+// exponent e_t.  The buffer holds k^_l = k_l / m_l and e_l; a ratio times a
+// key is then k^_l m_t scaled by 2^(e_t - e_l), an exact ldexp (a result
+// below fp32's range rounds to a subnormal or zero, the value it has).
 // Every rank-1 piece of X_0 (compensator p w^T, DAMP row e_i h_i^T) is a
 // "slot" with key-side vector and value-side vector, like a buffered token.
 #include "codec.hpp"
@@ -36,7 +43,9 @@ struct WinArgs {
     const int8_t *codes;
     const float *row_scale, *col_scale;
     const float *comp_k, *comp_v;
-    float *buf_k, *buf_u, *g_cur;
+    float *buf_k, *buf_u;
+    int32_t *buf_g;
+    float *g_cur;
     const uint16_t *hp_rows;
     const int32_t *hp_idx;
     int r, n_hp, W, t;
@@ -64,33 +73,66 @@ __device__ __forceinline__ void load_f16x8(const uint16_t *p, float (&out)[8])
     }
 }
 
+// Gate product after one more gate: (m, e) with m in [0.5, 1) from the
+// previous (mp, ep) (the window start is m = 1, e = 0) and a gate a in
+// (0, 1].  Both mantissas lie in [0.5, 1], so their product is a normal
+// number and rounds once, like the plain product of the two values.
+struct GateProd {
+    float m;
+    int e;
+};
+
+__device__ __forceinline__ GateProd gate_step(float mp, int ep, float a)
+{
+    const float p = mp * __builtin_amdgcn_frexp_mantf(a);
+    return GateProd{__builtin_amdgcn_frexp_mantf(p),
+                    ep + __builtin_amdgcn_frexp_expf(a) + __builtin_amdgcn_frexp_expf(p)};
+}
+
+__device__ __forceinline__ float ldexp_f(float x, int e) { return __builtin_amdgcn_ldexpf(x, e); }
+
 template <class G>
 struct WinLds {
     alignas(16) float sgk[G::DK];  // s_i G_i k_i and s_i G_i q_i (s = 1 for DAMP), read as float4
     alignas(16) float sgq[G::DK];
     alignas(16) float cs[G::DV];   // column scales
-    float ks[G::DK], qs[G::DK], gs[G::DK], gk[G::DK], gq[G::DK];
+    // raw k, q; m k, m q (token slots); G k, G q (fixed state, compensator
+    // and DAMP slots); per-row mantissa and exponent of G
+    float ks[G::DK], qs[G::DK], mk[G::DK], mq[G::DK], gk[G::DK], gq[G::DK], gm[G::DK];
+    int ge[G::DK];
     float alpha[MAX_SLOTS + 1], beta[MAX_SLOTS + 1];
     int hp[MAX_HP];
     float red[G::NW][2][G::DV];
 };
 
 // Key-side vector of slot l (a compensator or a buffered token), entries
-// l16*PER .. l16*PER+PER-1; false (nothing read) for a DAMP-row slot, the
-// k.q slot and l >= NS.
-template <class G>
+// l16*PER .. l16*PER+PER-1, and for a token its gate exponents (xe[0] for
+// the scalar gate, one per entry for KDA); false (nothing read) for a
+// DAMP-row slot, the k.q slot and l >= NS.
+template <class G, bool KDA>
 __device__ __forceinline__ bool slot_kvec(const WinArgs &A, size_t h, int l, int NS, int n_hp, int l16,
-                                          float (&x)[G::DK / 16])
+                                          float (&x)[G::DK / 16], int (&xe)[G::DK / 16])
 {
     constexpr int PER = G::DK / 16;
     const int r = A.r;
     if (l >= NS || (l >= r && l < r + n_hp)) return false;
-    const float *vec = (l < r) ? A.comp_k + ((h * r + l) * G::DK)
-                               : A.buf_k + ((h * A.W + (l - r - n_hp)) * G::DK);
+    const size_t tok = h * A.W + (l - r - n_hp);
+    const float *vec = (l < r) ? A.comp_k + ((h * r + l) * G::DK) : A.buf_k + tok * G::DK;
 #pragma unroll
     for (int e = 0; e < PER; e += 4) {
         const float4 v = *reinterpret_cast<const float4 *>(vec + l16 * PER + e);
         x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
+    }
+    if (l >= r) {
+        if constexpr (KDA) {
+#pragma unroll
+            for (int e = 0; e < PER; e += 4) {
+                const int4 v = *reinterpret_cast<const int4 *>(A.buf_g + tok * G::DK + l16 * PER + e);
+                xe[e] = v.x; xe[e + 1] = v.y; xe[e + 2] = v.z; xe[e + 3] = v.w;
+            }
+        } else {
+            xe[0] = A.buf_g[tok];
+        }
     }
     return true;
 }
@@ -176,7 +218,13 @@ __global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_ke
     const float kv = load1<BF16>(A.k, hk * G::DK + tr);
     const float qv = load1<BF16>(A.q, hk * G::DK + tr);
     const float av = KDA ? A.a[hi * G::DK + tr] : A.a[hi];
-    const float gprev = (t == 0) ? 1.0f : (KDA ? A.g_cur[h * G::DK + tr] : A.g_cur[h]);
+    // gate product of the previous token (the window start: 1 = 0.5 * 2^1)
+    float mprev = 1.0f;
+    int eprev = 0;
+    if (t > 0) {
+        mprev = KDA ? A.g_cur[h * G::DK + tr] : A.g_cur[h];
+        eprev = KDA ? A.buf_g[(h * A.W + (t - 1)) * G::DK + tr] : A.buf_g[h * A.W + (t - 1)];
+    }
     const float srow = DAMP ? 1.0f : A.row_scale[h * G::DK + tr];
     // column scales go through LDS (thread t < DV owns column t) so they
     // hold no registers during the mat-vecs
@@ -190,7 +238,8 @@ __global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_ke
     constexpr int PER = G::DK / 16;
     const int l16 = c.t & 15;
     float xk[PER];
-    const bool xk0 = slot_kvec<G>(A, h, c.t >> 4, NS, n_hp, l16, xk);
+    int xe[PER];
+    const bool xk0 = slot_kvec<G, KDA>(A, h, c.t >> 4, NS, n_hp, l16, xk, xe);
     constexpr int NRG = G::NW * G::RGW;
     const int rg = c.w * G::RGW + c.rgl;
     uint4 uvraw[2];
@@ -208,11 +257,15 @@ __global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_ke
 
     // per-row vectors: gate product, gated k and q (and times the row scale)
     if (c.t < G::DK) {
-        const float g = gprev * av;
-        const float gk = g * kv, gq = g * qv;
+        const GateProd g = gate_step(mprev, eprev, av);
+        const float mk = g.m * kv, mq = g.m * qv;
+        const float gk = ldexp_f(mk, g.e), gq = ldexp_f(mq, g.e);
         L.ks[c.t] = kv;
         L.qs[c.t] = qv;
-        L.gs[c.t] = g;
+        L.mk[c.t] = mk;
+        L.mq[c.t] = mq;
+        L.gm[c.t] = g.m;
+        L.ge[c.t] = g.e;
         L.gk[c.t] = gk;
         L.gq[c.t] = gq;
         L.sgk[c.t] = srow * gk;
@@ -226,12 +279,14 @@ __global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_ke
         load_tile_codes<G, true, BITS>(codes, c, rm, qraw);
     }
 
-    // slot dot products: alpha_l = kvec_l . (G.k), beta_l = kvec_l . (G.q);
-    // slot NS is k . q.  16 lanes per slot.
+    // slot dot products: alpha_l = kvec_l . (G.k), beta_l = kvec_l . (G.q)
+    // for the fixed state's slots; for a buffered token
+    // alpha_l = ((G_t/G_l) . k_l) . k_t = sum (k^_l m_t k_t) 2^(e_t - e_l)
+    // (beta with q_t); slot NS is k . q.  16 lanes per slot.
     for (int base = 0; base <= NS; base += G::NT / 16) {
         const int l = base + (c.t >> 4);
         if (l > NS) break;  // whole 16-lane groups leave together
-        const bool has = base == 0 ? xk0 : slot_kvec<G>(A, h, l, NS, n_hp, l16, xk);
+        const bool has = base == 0 ? xk0 : slot_kvec<G, KDA>(A, h, l, NS, n_hp, l16, xk, xe);
         float al = 0.0f, be = 0.0f;
         if (l == NS) {
 #pragma unroll
@@ -242,15 +297,35 @@ __global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_ke
                 al = L.gk[i];
                 be = L.gq[i];
             }
-        } else {
+        } else if (l < r) {  // compensator: part of the fixed state
 #pragma unroll
             for (int e = 0; e < PER; e++) {
                 al = fmaf(xk[e], L.gk[l16 * PER + e], al);
                 be = fmaf(xk[e], L.gq[l16 * PER + e], be);
             }
+        } else if constexpr (KDA) {
+#pragma unroll
+            for (int e = 0; e < PER; e++) {
+                const int i = l16 * PER + e;
+                const float x = ldexp_f(xk[e], L.ge[i] - xe[e]);
+                al = fmaf(x, L.mk[i], al);
+                be = fmaf(x, L.mq[i], be);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < PER; e++) {
+                al = fmaf(xk[e], L.mk[l16 * PER + e], al);
+                be = fmaf(xk[e], L.mq[l16 * PER + e], be);
+            }
         }
         al = sum16(al);
         be = sum16(be);
+        if constexpr (!KDA) {
+            if (has && l >= r) {  // the scalar gate's ratio, once per slot
+                al = ldexp_f(al, L.ge[0] - xe[0]);
+                be = ldexp_f(be, L.ge[0] - xe[0]);
+            }
+        }
         if (l16 == 0) {
             L.alpha[l] = al;
             L.beta[l] = be;
@@ -330,10 +405,15 @@ __global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_ke
         A.buf_u[(h * A.W + t) * G::DV + c.t] = u;
     }
     if (c.t < G::DK) {
-        const float g = L.gs[c.t];
-        A.buf_k[(h * A.W + t) * G::DK + c.t] = L.ks[c.t] / g;
-        if (KDA) A.g_cur[h * G::DK + c.t] = g;
-        else if (c.t == 0) A.g_cur[h] = g;
+        const float m = L.gm[c.t];
+        A.buf_k[(h * A.W + t) * G::DK + c.t] = L.ks[c.t] / m;
+        if (KDA) {
+            A.buf_g[(h * A.W + t) * G::DK + c.t] = L.ge[c.t];
+            A.g_cur[h * G::DK + c.t] = m;
+        } else if (c.t == 0) {
+            A.buf_g[h * A.W + t] = L.ge[0];
+            A.g_cur[h] = m;
+        }
     }
 }
 
@@ -342,6 +422,7 @@ struct FlushArgs {
     int8_t *codes;
     float *row_scale, *col_scale, *comp_k, *comp_v;
     const float *buf_k, *buf_u;
+    const int32_t *buf_g;
     float *g_cur;
     uint16_t *hp_rows;
     const int32_t *hp_idx;
@@ -352,20 +433,25 @@ struct FlushArgs {
 
 template <class G>
 struct FlushLds {
-    float gs[G::DK];
+    float gs[G::DK];   // G_n per row (a subnormal or zero when it underflows)
+    float gm[G::DK];   // its mantissa m_n and exponent e_n
+    int ge[G::DK];
     int hp[MAX_HP];
 };
 
-// Key-side value of slot l at row i (already multiplied by G_W,i) and the
-// 8 value-side entries at columns col..col+7.  Slots: r compensators, n_hp
-// DAMP rows, n buffered tokens; l >= K is a zero pad.
-template <class G>
+// Key-side value of slot l at row i (already multiplied by G_n,i; a token's
+// (G_n/G_l)_i k_l,i = m_n,i k^_l,i 2^(e_n,i - e_l,i)) and the 8 value-side
+// entries at columns col..col+7.  Slots: r compensators, n_hp DAMP rows,
+// n buffered tokens; l >= K is a zero pad.
+template <class G, bool KDA>
 __device__ __forceinline__ float slot_key(const FlushArgs &A, const FlushLds<G> &L, size_t h, int l, int i, int K)
 {
     if (l >= K) return 0.0f;
     if (l < A.r) return L.gs[i] * A.comp_k[(h * A.r + l) * G::DK + i];
     if (l < A.r + A.n_hp) return (L.hp[l - A.r] == i) ? L.gs[i] : 0.0f;
-    return L.gs[i] * A.buf_k[(h * A.W + (l - A.r - A.n_hp)) * G::DK + i];
+    const size_t tok = h * A.W + (l - A.r - A.n_hp);
+    const int el = KDA ? A.buf_g[tok * G::DK + i] : A.buf_g[tok];
+    return ldexp_f(L.gm[i] * A.buf_k[tok * G::DK + i], L.ge[i] - el);
 }
 
 template <class G>
@@ -405,7 +491,14 @@ __global__ __launch_bounds__(G::NT, (flush_min_blocks<G, DAMP>())) void flush_ke
     const int n = x.pos;
     const int n_hp = DAMP ? A.n_hp : 0;
     if (!DAMP) A.n_hp = 0;
-    if (c.t < G::DK) F.gs[c.t] = KDA ? A.g_cur[h * G::DK + c.t] : A.g_cur[h];
+    if (c.t < G::DK) {
+        // the gate product after the window's last token, n - 1
+        const float m = KDA ? A.g_cur[h * G::DK + c.t] : A.g_cur[h];
+        const int e = KDA ? A.buf_g[(h * A.W + (n - 1)) * G::DK + c.t] : A.buf_g[h * A.W + (n - 1)];
+        F.gm[c.t] = m;
+        F.ge[c.t] = e;
+        F.gs[c.t] = ldexp_f(m, e);
+    }
     if (DAMP && c.t < n_hp) F.hp[c.t] = A.hp_idx[h * n_hp + c.t];
     __syncthreads();
 
@@ -451,7 +544,7 @@ __global__ __launch_bounds__(G::NT, (flush_min_blocks<G, DAMP>())) void flush_ke
             const int l = kk + lk;
             float av[2], bv[8];
 #pragma unroll
-            for (int hb = 0; hb < 2; hb++) av[hb] = slot_key<G>(A, F, h, l, c.w * 32 + hb * 16 + lm, K);
+            for (int hb = 0; hb < 2; hb++) av[hb] = slot_key<G, KDA>(A, F, h, l, c.w * 32 + hb * 16 + lm, K);
             slot_val<G>(A, h, l, 8 * lm, K, bv);
 #pragma unroll
             for (int hb = 0; hb < 2; hb++)
@@ -469,7 +562,7 @@ __global__ __launch_bounds__(G::NT, (flush_min_blocks<G, DAMP>())) void flush_ke
         for (int l = 0; l < K; l++) {
             float kv[8], uv[8];
 #pragma unroll
-            for (int k = 0; k < 8; k++) kv[k] = slot_key<G>(A, F, h, l, row_of<G>(c, k), K);
+            for (int k = 0; k < 8; k++) kv[k] = slot_key<G, KDA>(A, F, h, l, row_of<G>(c, k), K);
             slot_val<G>(A, h, l, c.cb * 8, K, uv);
 #pragma unroll
             for (int k = 0; k < 8; k++)
@@ -500,7 +593,7 @@ hipError_t launch_window_step(const gdnq_desc &d, const HeadMap &m, const gdnq_s
                               int t_in_window, hipStream_t st)
 {
     WinArgs A{q, k, v, a, b, o, s.codes, s.row_scale, s.col_scale, s.comp_k, s.comp_v,
-              s.buf_k, s.buf_u, s.g_cur, s.hp_rows, s.hp_idx, d.r, d.n_hp, d.W, t_in_window, m};
+              s.buf_k, s.buf_u, s.buf_g, s.g_cur, s.hp_rows, s.hp_idx, d.r, d.n_hp, d.W, t_in_window, m};
     const unsigned nh = (unsigned)d.B * (unsigned)d.H;
     return with_dims(d.dk, d.dv, [&](auto DK, auto DV) {
         using G = Geom<decltype(DK)::value, decltype(DV)::value>;
@@ -527,7 +620,7 @@ hipError_t launch_window_step(const gdnq_desc &d, const HeadMap &m, const gdnq_s
 
 hipError_t launch_flush(const gdnq_desc &d, const HeadMap &m, const gdnq_state &s, int n_tokens, hipStream_t st)
 {
-    FlushArgs A{s.codes, s.row_scale, s.col_scale, s.comp_k, s.comp_v, s.buf_k, s.buf_u, s.g_cur,
+    FlushArgs A{s.codes, s.row_scale, s.col_scale, s.comp_k, s.comp_v, s.buf_k, s.buf_u, s.buf_g, s.g_cur,
                 s.hp_rows, s.hp_idx, (d.flags & GDNQ_DEBUG_PREQUANT) ? s.prequant_out : nullptr,
                 d.r, d.n_hp, d.W, n_tokens, d.power_iters, m};
     const unsigned nh = (unsigned)d.B * (unsigned)d.H;

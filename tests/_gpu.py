@@ -138,3 +138,36 @@ def check_outputs(got, ref, bf16: bool, fp32_tol=1e-4):
     assert like.max() <= 2e-3, like.max()
     assert rel.max() <= 2.0 ** -8, rel.max()
     return rel
+
+
+def _bits32(x) -> np.ndarray:
+    return np.ascontiguousarray(x, np.float32).view(np.uint32)
+
+
+def assert_encoding_is_oracle_codec(P, codes, col_scale, row_scale=None, bits=8, hp_idx=None, hp_rows=None):
+    """Fused requantization, bit for bit: the oracle's codec applied to the
+    fp32 tensor a kernel handed to its codec (P [nh,dk,dv], read back from
+    prequant_out) must reproduce the codes, scales and fp16 rows the kernel
+    stored.  Layout 0: oracle.quantize (codes packed by oracle.pack_codes
+    below 8 bits); DAMP layout: oracle.quantize_damp with the head's rows.
+    Every argument is a host array of the stored data for the same heads."""
+    import oracle
+
+    P = np.ascontiguousarray(P, np.float32)
+    nh, dk, dv = P.shape
+    if hp_idx is None:
+        Q, s, c = oracle.quantize(P, bits=bits)
+        want = Q.view(np.uint8) if bits == 8 else oracle.pack_codes(Q, bits)
+        got = np.ascontiguousarray(codes).view(np.uint8).reshape(want.shape)
+        bad = got != want
+        assert not bad.any(), f"{bad.sum()} code bytes differ from the oracle's codec on the kernel's input"
+        assert np.array_equal(_bits32(row_scale).reshape(nh, dk), _bits32(s)), "row scales differ"
+        assert np.array_equal(_bits32(col_scale).reshape(nh, dv), _bits32(c)), "column scales differ"
+    else:
+        Qc, c, rows = oracle.quantize_damp(P, hp_idx)
+        got = np.ascontiguousarray(codes).view(np.int8).reshape(Qc.shape)
+        bad = got != Qc
+        assert not bad.any(), f"{bad.sum()} codes differ from the oracle's DAMP codec on the kernel's input"
+        assert np.array_equal(_bits32(col_scale).reshape(nh, dv), _bits32(c)), "column scales differ"
+        assert np.array_equal(np.ascontiguousarray(hp_rows).view(np.uint16).reshape(rows.shape), rows), \
+            "fp16 rows differ"

@@ -76,15 +76,18 @@ def _err(fn):
 def test_state_sizes(g):
     d = g.Desc(B=2, H=3, dk=128, dv=64, W=4, r=2, decay=g.DECAY_CHANNEL)
     nh = 6
+    # codes, row/col scales, compensators, buf_k, buf_u, buf_g (one exponent
+    # per key channel and token), g_cur, hp_rows, hp_idx, prequant_out
     assert g.gdnq_state_sizes(d) == [nh * 128 * 64, nh * 128 * 4, nh * 64 * 4, nh * 2 * 128 * 4,
-                                     nh * 2 * 64 * 4, nh * 4 * 128 * 4, nh * 4 * 64 * 4, nh * 128 * 4,
-                                     0, 0, 0]
+                                     nh * 2 * 64 * 4, nh * 4 * 128 * 4, nh * 4 * 64 * 4, nh * 4 * 128 * 4,
+                                     nh * 128 * 4, 0, 0, 0]
     d = g.Desc(B=1, H=2, W=16, r=2, layout=g.LAYOUT_DAMP, n_hp=8, flags=g.DEBUG_PREQUANT)
     s = g.gdnq_state_sizes(d)
-    assert s[0] == 2 * 120 * 128 and s[1] == 0 and s[8] == 2 * 8 * 128 * 2 and s[9] == 2 * 8 * 4
-    assert s[10] == 2 * 128 * 128 * 4
+    assert s[0] == 2 * 120 * 128 and s[1] == 0 and s[9] == 2 * 8 * 128 * 2 and s[10] == 2 * 8 * 4
+    assert s[7] == 2 * 16 * 4 and s[8] == 2 * 4          # scalar gate: one exponent per token, one mantissa
+    assert s[11] == 2 * 128 * 128 * 4
     d = g.Desc(B=4, H=1)       # per-step: no window buffers
-    assert g.gdnq_state_sizes(d)[5:8] == [0, 0, 0]
+    assert g.gdnq_state_sizes(d)[5:9] == [0, 0, 0, 0]
     for bits, row in ((8, 128), (6, 96), (4, 64), (0, 128)):   # packed rows of 128 codes
         d = g.Desc(B=2, H=3, W=16, r=2, bits=bits)
         assert g.gdnq_state_sizes(d)[0] == 6 * 128 * row

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import synth
-from tests._gpu import dev, desc_for, host, lib, per_head_rel, say, sub_cfg, torch_cuda
+from tests._gpu import assert_encoding_is_oracle_codec, dev, desc_for, host, lib, per_head_rel, say, sub_cfg, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -143,21 +143,10 @@ def test_codec_with_compensators(layout, r):
     assert err.max() <= 1e-4, err
     R = host(st["prequant_out"]).reshape(nh, dk, dv)
     assert (np.sqrt(np.sum((R - ref["R"]) ** 2, axis=(1, 2))) / scale).max() <= 1e-4
-    # the codes are the GPU codec (pinned bit-exact above) applied to R
-    d0 = desc_for(dict(cfgc, W=1, r=0))
-    if hp is not None:
-        d0.layout, d0.n_hp = g.LAYOUT_DAMP, n_hp
-    st0 = g.alloc_state(d0)
-    if hp is not None:
-        st0["hp_idx"].copy_(st["hp_idx"])
-    g.gdn_state_quantize(d0, dev(R), st0)
-    torch.cuda.synchronize()
-    assert torch.equal(st0["codes"], st["codes"])
-    assert torch.equal(st0["col_scale"], st["col_scale"])
-    if hp is None:
-        assert torch.equal(st0["row_scale"], st["row_scale"])
-    else:
-        assert torch.equal(st0["hp_rows"], st["hp_rows"])
+    # the codes are the oracle's codec applied to the kernel's residual R
+    assert_encoding_is_oracle_codec(R, host(st["codes"]), host(st["col_scale"]),
+                                    None if hp is not None else host(st["row_scale"]), hp_idx=hp,
+                                    hp_rows=None if hp is None else host(st["hp_rows"]))
     # dequantize = D(Q) + compensators rebuilds X within the codec bound
     back = torch.empty((nh * dk * dv,), dtype=torch.float32, device="cuda")
     g.gdn_state_dequantize(d, st, back)

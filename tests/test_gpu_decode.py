@@ -8,9 +8,8 @@ Bars (l2-relative per head):
     the gap to the oracle's bf16-rounded output is <= 2e-3
     (tests/_gpu.check_outputs);
   * updated state before requantization: 1e-4;
-  * fused requantization: codes and scales equal the GPU codec's output on
-    the kernel's own pre-quantization tensor, bit for bit (the codec is
-    pinned to the oracle bit for bit in test_gpu_codec);
+  * fused requantization: codes and scales equal the oracle's codec
+    applied to the kernel's own pre-quantization tensor, bit for bit;
   * codes against the oracle's own codes: differences are +-1 and only at
     elements whose pre-rounding value is within 1e-3 of a rounding tie.
 """
@@ -19,8 +18,8 @@ import pytest
 
 import oracle
 import synth
-from tests._gpu import (check_outputs, desc_for, dev, dev_io, host, host_io, lib, near_tie_codes,
-                        per_head_rel, say, sub_cfg, torch_cuda)
+from tests._gpu import (assert_encoding_is_oracle_codec, check_outputs, desc_for, dev, dev_io, host, host_io,
+                        lib, near_tie_codes, per_head_rel, say, sub_cfg, torch_cuda)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,14 +91,8 @@ def test_fused_step_teacher_forced(case):
     check_outputs(host_io(o, bf), ref["o"], bf)
     P = host(st["prequant_out"]).reshape(nh, dk, dv)
     assert per_head_rel(P, ref["S_pre"]).max() <= 1e-4
-    # fused requantization == the GPU codec on the kernel's own input
-    d0 = desc_for(cfg, W=1, r=0)
-    st0 = g.alloc_state(d0)
-    g.gdn_state_quantize(d0, st["prequant_out"], st0)
-    torch.cuda.synchronize()
-    assert torch.equal(st0["codes"], st["codes"])
-    assert torch.equal(st0["row_scale"], st["row_scale"])
-    assert torch.equal(st0["col_scale"], st["col_scale"])
+    # fused requantization == the oracle's codec on the kernel's own input
+    assert_encoding_is_oracle_codec(P, host(st["codes"]), host(st["col_scale"]), host(st["row_scale"]))
     # and against the oracle's own codes: +-1 at near-ties only
     gQ = host(st["codes"]).reshape(nh, dk, dv).astype(np.int32)
     diff = gQ - ref["Q"].astype(np.int32)

@@ -7,8 +7,8 @@ import pytest
 
 import oracle
 import synth
-from tests._gpu import (check_outputs, desc_for, dev, dev_io, host, host_io, lib, near_tie_codes,
-                        per_head_rel, say, torch_cuda)
+from tests._gpu import (assert_encoding_is_oracle_codec, check_outputs, desc_for, dev, dev_io, host, host_io,
+                        lib, near_tie_codes, per_head_rel, say, torch_cuda)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,14 +27,17 @@ def _codes(st, nh, rows, dv, bits):
 @pytest.mark.parametrize("bits", [8, 6, 4])
 def test_prefix_cache_full_size(bits):
     """32768 pre-filled 128x128 states: quantize all, one fused per-step
-    decode (b-bit codes) and one fp32-state step over all of them."""
+    decode (b-bit codes) and one fp32-state step over all of them.  The
+    step also writes its codec input (the same kernel: that store is a
+    run-time branch), so the sampled heads' codes and scales are checked
+    bit for bit against the oracle's codec on it."""
     torch = torch_cuda()
     g = lib()
     cfg = synth.WORKLOADS["prefix_cache"]
     nh, dk, dv = cfg["B"] * cfg["H"], cfg["dk"], cfg["dv"]
     heads = _sample(nh)
     S = synth.prefill_states(cfg)
-    d = desc_for(cfg, bits=bits)
+    d = desc_for(cfg, bits=bits, flags=g.DEBUG_PREQUANT)
     st = g.alloc_state(d)
     Sd = dev(S)
     say("prefix_cache full: quantize", bits)
@@ -54,6 +57,11 @@ def test_prefix_cache_full_size(bits):
     sub = {k: v[heads] for k, v in inp.items()}
     ref = oracle.quant_step(Q, s, c, sub["q"], sub["k"], sub["v"], sub["a"], sub["b"], bits=bits)
     check_outputs(host_io(o, True).reshape(nh, dv)[heads], ref["o"], True)
+    hidx = torch.from_numpy(heads).cuda()
+    P = host(st["prequant_out"].view(nh, dk * dv)[hidx]).reshape(len(heads), dk, dv)
+    assert per_head_rel(P, ref["S_pre"]).max() <= 1e-4
+    assert_encoding_is_oracle_codec(P, host(st["codes"].view(nh, -1)[hidx]), host(st["col_scale"].view(nh, dv)[hidx]),
+                                    host(st["row_scale"].view(nh, dk)[hidx]), bits=bits)
     gQ = _codes(st, nh, dk, dv, bits)[heads].astype(np.int32)
     diff = gQ - ref["Q"].astype(np.int32)
     assert np.abs(diff).max() <= 1
@@ -132,5 +140,11 @@ def test_window_full_size(name, bits):
         check_outputs(host_io(outs[t], True).reshape(nh, dv)[heads], o_ref[t], True)
     ref = oracle.compress(SW, r, 20, hp_idx=None if hp is None else hp[heads], bits=bits)
     scale = np.sqrt(np.sum(SW ** 2, axis=(1, 2)))
-    R = host(st["prequant_out"]).reshape(nh, dk, dv)[heads].astype(np.float64)
-    assert (np.sqrt(np.sum((R - ref["R"]) ** 2, axis=(1, 2))) / scale).max() <= 1e-4
+    hidx = torch.from_numpy(heads).cuda()
+    R = host(st["prequant_out"].view(nh, dk * dv)[hidx]).reshape(len(heads), dk, dv)
+    assert (np.sqrt(np.sum((R.astype(np.float64) - ref["R"]) ** 2, axis=(1, 2))) / scale).max() <= 1e-4
+    # the flush's codes on the sampled heads: the oracle's codec on its residual
+    assert_encoding_is_oracle_codec(R, host(st["codes"].view(nh, -1)[hidx]), host(st["col_scale"].view(nh, dv)[hidx]),
+                                    None if hp is not None else host(st["row_scale"].view(nh, dk)[hidx]), bits=bits,
+                                    hp_idx=None if hp is None else hp[heads],
+                                    hp_rows=None if hp is None else host(st["hp_rows"].view(nh, -1)[hidx]))

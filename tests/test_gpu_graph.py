@@ -17,7 +17,7 @@ from tests._gpu import desc_for, lib, say, sub_cfg, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
-STATE_KEYS = ("codes", "row_scale", "col_scale", "comp_k", "comp_v", "buf_k", "buf_u", "g_cur", "hp_rows")
+STATE_KEYS = ("codes", "row_scale", "col_scale", "comp_k", "comp_v", "buf_k", "buf_u", "buf_g", "g_cur", "hp_rows")
 
 
 def _window(g, d, st, ins, outs, W):

@@ -2,12 +2,22 @@
 per-entry window positions and flush lengths, skipped entries) and shared
 key heads (desc.hk < H).
 
-Pool form: every pool call is compared bit for bit with the plain calls on
-twin states (one plain state per entry, holding a copy of that entry's
-slot): the same kernels run either way, so outputs, codes, scales,
-compensators, buffers and gates must be identical; slots no entry uses, and
-entries with an out-of-range slot, position or token count, stay untouched.
-The plain calls are pinned to the oracle by the other GPU tests.
+Pool form against the oracle: entries on permuted slots (one slot out of
+range, so skipped) run one per-step decode, and entries whose windows start
+at different steps (so each call holds them at different positions, and an
+entry before its start is skipped by its position) run to a flush that ends
+every window with its own token count (partial windows, and one entry with
+n_tokens = 0 left untouched).  Each active entry's outputs and buffered
+updates meet the per-step and window bars against the oracle on that slot's
+state, and the codes and scales the kernels store equal the oracle's codec
+applied to the fp32 tensor they handed to it, bit for bit.
+
+Pool form against the plain calls: every pool call is also compared bit for
+bit with the plain calls on twin states (one plain state per entry, holding
+a copy of that entry's slot): the same kernels run either way, so outputs,
+codes, scales, compensators, buffers and gates must be identical; slots no
+entry uses, and entries with an out-of-range slot, position or token count,
+stay untouched.
 
 Shared key heads: value head hh reads key head hh / (H / hk); the oracle is
 run with q and k repeated over their value heads (plain data movement in the
@@ -18,12 +28,12 @@ import pytest
 
 import oracle
 import synth
-from tests._gpu import (check_outputs, desc_for, dev, dev_io, host, host_io, lib, per_head_rel, say,
-                        sub_cfg, torch_cuda)
+from tests._gpu import (assert_encoding_is_oracle_codec, check_outputs, desc_for, dev, dev_io, host, host_io,
+                        lib, per_head_rel, say, sub_cfg, torch_cuda)
 
 pytestmark = pytest.mark.gpu
 
-KEYS = ("codes", "row_scale", "col_scale", "comp_k", "comp_v", "buf_k", "buf_u", "g_cur", "hp_rows")
+KEYS = ("codes", "row_scale", "col_scale", "comp_k", "comp_v", "buf_k", "buf_u", "buf_g", "g_cur", "hp_rows")
 
 
 def _slot_view(st, name, slot, n_slots):
@@ -299,3 +309,136 @@ def test_pool_per_step_static_scales():
     for e, s in enumerate(slots):
         if not 0 <= s < n_slots:
             assert torch.all(o.view(nb, H * dv)[e] == 7.0)
+
+
+def _heads(slot, H):
+    return np.arange(slot * H, (slot + 1) * H)
+
+
+def test_pool_per_step_against_oracle():
+    """Per-step decode through the pool entry point on permuted slots (one
+    out of range), each active entry checked against the oracle's per-step
+    decode of its slot's state: outputs, the pre-quantization state, and
+    codes and scales bit for bit against the oracle's codec on the kernel's
+    own input; slots no entry uses keep the oracle's encoding."""
+    torch = torch_cuda()
+    g = lib()
+    cfg = sub_cfg(synth.WORKLOADS["prefix_cache"], B=1, H=4)
+    H, dk, dv = cfg["H"], cfg["dk"], cfg["dv"]
+    n_slots = 6
+    slots = [4, 1, -1, 3, 0]
+    nb = len(slots)
+    d = desc_for(cfg, B=nb, W=1, r=0, flags=g.DEBUG_PREQUANT)
+    dpool = desc_for(cfg, B=n_slots, W=1, r=0, flags=g.DEBUG_PREQUANT)
+    S = synth.prefill_states(dict(cfg, B=n_slots), heads=range(n_slots * H))
+    Q, s_, c_ = oracle.quantize(S)
+    pool = g.alloc_state(dpool)
+    pool["codes"].copy_(torch.from_numpy(Q.reshape(-1)))
+    pool["row_scale"].copy_(torch.from_numpy(s_.reshape(-1)))
+    pool["col_scale"].copy_(torch.from_numpy(c_.reshape(-1)))
+    inp, args = _inputs(torch, cfg, nb, 2, True)
+    o = torch.full((nb * H * dv,), 7.0, dtype=torch.bfloat16, device="cuda")
+    say("pool per-step vs oracle")
+    g.gdn_quant_decode_step_pool(d, pool, n_slots, torch.tensor(slots, dtype=torch.int32, device="cuda"), None,
+                                 *args, o)
+    torch.cuda.synchronize()
+    o_host = host_io(o, True).reshape(nb, H, dv)
+    codes = host(pool["codes"]).reshape(n_slots * H, dk, dv)
+    rs = host(pool["row_scale"]).reshape(n_slots * H, dk)
+    cs = host(pool["col_scale"]).reshape(n_slots * H, dv)
+    P = host(pool["prequant_out"]).reshape(n_slots * H, dk, dv)
+    for e, slot in enumerate(slots):
+        if not 0 <= slot < n_slots:
+            assert np.all(o_host[e] == 7.0)
+            continue
+        hs, hi = _heads(slot, H), _heads(e, H)
+        ref = oracle.quant_step(Q[hs], s_[hs], c_[hs], inp["q"][hi], inp["k"][hi], inp["v"][hi], inp["a"][hi],
+                                inp["b"][hi])
+        check_outputs(o_host[e], ref["o"], True)
+        assert per_head_rel(P[hs], ref["S_pre"]).max() <= 1e-4
+        assert_encoding_is_oracle_codec(P[hs], codes[hs], cs[hs], rs[hs])
+    for slot in set(range(n_slots)) - set(slots):
+        hs = _heads(slot, H)
+        assert np.array_equal(codes[hs], Q[hs]) and np.array_equal(rs[hs], s_[hs])
+
+
+@pytest.mark.parametrize("name", ["gdn_serving", "kda"])
+def test_pool_window_staggered_against_oracle(name):
+    """Window mode through the pool entry points with staggered windows:
+    entry e starts its window at step start[e], so each decode call holds
+    the entries at different positions (an entry before its start has
+    position -1 and is skipped); one flush call then ends each window with
+    its own token count W - start[e] (partial windows), skips an entry on
+    an out-of-range slot, and leaves an entry with n_tokens = 0 untouched.
+    Against the oracle's window decode and flush of each slot's tokens."""
+    torch = torch_cuda()
+    g = lib()
+    cfg = sub_cfg(synth.WORKLOADS[name], B=1, H=2)
+    H, dk, dv, W, r = cfg["H"], cfg["dk"], cfg["dv"], cfg["W"], cfg["r"]
+    n_slots = 6
+    slots = [3, 0, 4, 9, 2]
+    start = [0, 3, W // 2 - 1, 0, 5]
+    ntok = [W - start[0], W - start[1], W - start[2], W, 0]
+    nb = len(slots)
+    d = desc_for(cfg, B=nb, flags=g.DEBUG_PREQUANT)
+    dpool = desc_for(cfg, B=n_slots, flags=g.DEBUG_PREQUANT)
+    S = synth.random_states(cfg["seed"] + 3, n_slots * H, dk, dv, scale=0.3).astype(np.float64)
+    enc = oracle.compress(S, r, 20)
+    pool = g.alloc_state(dpool)
+    for k, v in (("codes", enc["Q"]), ("row_scale", enc["s"]), ("col_scale", enc["c"]), ("comp_k", enc["p"]),
+                 ("comp_v", enc["w"])):
+        pool[k].copy_(torch.from_numpy(np.ascontiguousarray(v).reshape(-1)))
+    sl = torch.tensor(slots, dtype=torch.int32, device="cuda")
+    steps = synth.steps_inputs(dict(cfg, B=nb), 0, W)
+    outs = []
+    say("pool window staggered", name)
+    for i in range(W):
+        one = {k: v[i] for k, v in steps.items()}
+        pos = [i - start[e] if i >= start[e] else -1 for e in range(nb)]
+        o = torch.full((nb * H * dv,), 7.0, dtype=torch.bfloat16, device="cuda")
+        g.gdn_quant_decode_step_pool(d, pool, n_slots, sl, torch.tensor(pos, dtype=torch.int32, device="cuda"),
+                                     dev_io(one, "q", True), dev_io(one, "k", True), dev_io(one, "v", True),
+                                     dev(one["a"]), dev(one["b"]), o)
+        outs.append(o)
+    torch.cuda.synchronize()
+    before = {k: host(pool[k]).copy() for k in KEYS if pool.get(k) is not None}
+    say("pool flush staggered", name)
+    g.gdn_quant_window_flush_pool(d, pool, n_slots, sl, torch.tensor(ntok, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    o_all = np.stack([host_io(x, True).reshape(nb, H, dv) for x in outs])      # [W, nb, H, dv]
+    u_all = host(pool["buf_u"]).reshape(n_slots * H, W, dv)
+    P = host(pool["prequant_out"]).reshape(n_slots * H, dk, dv)
+    after = {k: host(pool[k]) for k in before}
+    for e, slot in enumerate(slots):
+        if not 0 <= slot < n_slots:
+            assert np.all(o_all[:, e] == 7.0)
+            continue
+        hs, hi = _heads(slot, H), _heads(e, H)
+        assert np.all(o_all[:start[e], e] == 7.0)
+        tk = slice(start[e], W)
+        n = W - start[e]
+        X0 = oracle.state_base(enc["Q"][hs], enc["s"][hs], enc["c"][hs], enc["p"][hs], enc["w"][hs])
+        o_ref, u_ref, SW = oracle.window(X0, steps["q"][tk][:, hi], steps["k"][tk][:, hi], steps["v"][tk][:, hi],
+                                         steps["a"][tk][:, hi], steps["b"][tk][:, hi])
+        for t in range(n):
+            check_outputs(o_all[start[e] + t, e], o_ref[t], True)
+        u_gpu = u_all[hs][:, :n].transpose(1, 0, 2)
+        assert per_head_rel(u_gpu.reshape(n * H, dv), u_ref.reshape(n * H, dv)).max() <= 1e-4
+        if ntok[e] == 0:
+            for k in before:      # not flushed: the whole slot is as the decode steps left it
+                per = before[k].size // n_slots
+                assert np.array_equal(after[k].reshape(-1)[slot * per:(slot + 1) * per],
+                                      before[k].reshape(-1)[slot * per:(slot + 1) * per]), k
+            continue
+        ref = oracle.compress(SW, r, 20)
+        scale = np.sqrt(np.sum(SW ** 2, axis=(1, 2)))
+        R = P[hs].astype(np.float64)
+        assert (np.sqrt(np.sum((R - ref["R"]) ** 2, axis=(1, 2))) / scale).max() <= 1e-4
+        pk = after["comp_k"].reshape(n_slots * H, r, dk)[hs].astype(np.float64)
+        wv = after["comp_v"].reshape(n_slots * H, r, dv)[hs].astype(np.float64)
+        C = np.einsum("hci,hcj->hij", pk, wv)
+        Cr = np.einsum("hci,hcj->hij", ref["p"].astype(np.float64), ref["w"].astype(np.float64))
+        assert (np.sqrt(np.sum((C - Cr) ** 2, axis=(1, 2))) / scale).max() <= 1e-4
+        assert_encoding_is_oracle_codec(P[hs], after["codes"].reshape(n_slots * H, dk, dv)[hs],
+                                        after["col_scale"].reshape(n_slots * H, dv)[hs],
+                                        after["row_scale"].reshape(n_slots * H, dk)[hs])
