@@ -196,63 +196,127 @@ def _slice_inputs(inputs: list, lo: int, hi: int) -> list:
     return [{k: v[lo:hi] for k, v in inp.items()} for inp in inputs]
 
 
-# (states, inputs, heads per worker, budget) shared with forked workers
+def _oracle_fp32_run(S: np.ndarray, inputs: list, budget_s: float):
+    """Consecutive steps of the unquantized recurrence (the fp32-state
+    comparator, kept in fp64 by the oracle) on the states S until budget_s
+    has passed: (updates, steps, s)."""
+    import oracle
+
+    nh = S.shape[0]
+    done, step = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        inp = inputs[step % len(inputs)]
+        S, _ = oracle.recur(S, inp["q"][None], inp["k"][None], inp["v"][None], inp["a"][None], inp["b"][None])
+        done += nh
+        step += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    return done, step, time.perf_counter() - t0
+
+
+# (mode, states, inputs, heads per worker, budget, bits) shared with forked workers
 _CPU_JOB = None
 
 
 def _cpu_worker(i: int):
-    S, inputs, per, budget, bits = _CPU_JOB
-    return _oracle_int8_run(S[i * per:(i + 1) * per], _slice_inputs(inputs, i * per, (i + 1) * per), budget,
-                            bits)
+    mode, S, inputs, per, budget, bits = _CPU_JOB
+    sl = _slice_inputs(inputs, i * per, (i + 1) * per)
+    if mode == "int8":
+        return _oracle_int8_run(S[i * per:(i + 1) * per], sl, budget, bits)
+    return _oracle_fp32_run(S[i * per:(i + 1) * per], sl, budget)
+
+
+# One GPU's share of the host on the GPU machines: worker pools stay within
+# 16 processes whatever the affinity mask shows.
+HOST_SHARE = 16
+
+
+def host_cores() -> dict:
+    """Cores the all-core CPU legs use: the affinity mask, limited by a
+    cgroup CPU quota when one is set and by the one-GPU host share."""
+    aff = len(os.sched_getaffinity(0))
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, per = f.read().split()[:2]
+            if q != "max":
+                quota = int(q) / int(per)
+    except (OSError, ValueError):
+        pass
+    n = aff
+    if quota is not None:
+        n = min(n, max(1, int(quota)))
+    n = max(1, min(n, HOST_SHARE))
+    return {"used": n, "affinity": aff, "cgroup_quota": quota, "host_share": HOST_SHARE}
+
+
+def _all_cores(mode, S, inputs, per, budget, bits, cores):
+    global _CPU_JOB
+    import multiprocessing
+
+    _CPU_JOB = (mode, S, inputs, per, budget, bits)
+    with multiprocessing.get_context("fork").Pool(cores) as pool:
+        res = pool.map(_cpu_worker, range(cores))
+    _CPU_JOB = None
+    return sum(r[0] for r in res), max(r[2] for r in res)
 
 
 def cpu_baselines(cfg: dict, S: np.ndarray, inputs: list) -> dict:
     """The fp64 CPU oracle timed on bounded samples of the workload: the
-    per-step INT8 decode on one thread (the reported baseline) and on every
-    host core as independent processes over disjoint heads, and the
-    unquantized (fp32-state mode) recurrence on one thread.  Runs before
-    anything touches the GPU, so the workers are plain forks."""
-    import multiprocessing
+    per-step INT8 decode on one thread (the reported baseline) and on all
+    usable host cores as independent processes over disjoint heads, and the
+    unquantized recurrence (the fp32-state mode) the same two ways.  Runs
+    before anything touches the GPU, so the workers are plain forks."""
+    import oracle  # noqa: F401  (built before forking)
 
-    import oracle
-
-    global _CPU_JOB
     total = cfg["B"] * cfg["H"]
     nh1 = 2048
     bits = cfg.get("bits", 8)
-    done, step, dt = _oracle_int8_run(S[:nh1], _slice_inputs(inputs, 0, nh1), 12.0, bits)
+    done, step, dt = _oracle_int8_run(S[:nh1], _slice_inputs(inputs, 0, nh1), 10.0, bits)
     one = {"value": done / dt, "unit": "token-head updates/s", "cores": 1, "kind": "oracle",
            "sample": f"first {nh1} of the {total} states, {step} consecutive per-step {bits}-bit decode "
                      f"steps ({done} token-head updates) in {dt:.1f} s, one thread"}
 
-    ncores = max(1, min(16, len(os.sched_getaffinity(0))))
-    per = 512
-    _CPU_JOB = (S, inputs, per, 8.0, bits)
-    with multiprocessing.get_context("fork").Pool(ncores) as pool:
-        res = pool.map(_cpu_worker, range(ncores))
-    _CPU_JOB = None
-    done_all = sum(r[0] for r in res)
-    dt_all = max(r[2] for r in res)
-    allc = {"value": done_all / dt_all, "unit": "token-head updates/s", "cores": ncores, "kind": "oracle",
-            "sample": f"{ncores} processes, each on its own {per} states (the first {ncores * per} of "
-                      f"{total}), consecutive per-step INT8 decode steps for ~8 s: {done_all} "
-                      f"token-head updates in {dt_all:.1f} s"}
+    hc = host_cores()
+    n = hc["used"]
+    per = min(512, total // n)
+    done_all, dt_all = _all_cores("int8", S, inputs, per, 6.0, bits, n)
+    allc = {"value": done_all / dt_all, "unit": "token-head updates/s", "cores": n, "kind": "oracle",
+            "host": hc,
+            "sample": f"{n} processes, each on its own {per} states (the first {n * per} of {total}), "
+                      f"consecutive per-step {bits}-bit decode steps for ~6 s: {done_all} token-head updates "
+                      f"in {dt_all:.1f} s"}
 
     nh32 = 512
-    S64 = S[:nh32]
-    done32, step32 = 0, 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < 5.0:
-        inp = inputs[step32 % len(inputs)]
-        S64, _ = oracle.recur(S64, inp["q"][None, :nh32], inp["k"][None, :nh32], inp["v"][None, :nh32],
-                              inp["a"][None, :nh32], inp["b"][None, :nh32])
-        done32 += nh32
-        step32 += 1
-    dt32 = time.perf_counter() - t0
+    done32, step32, dt32 = _oracle_fp32_run(S[:nh32], _slice_inputs(inputs, 0, nh32), 4.0)
     f32 = {"value": done32 / dt32, "unit": "token-head updates/s", "cores": 1, "kind": "oracle",
            "sample": f"first {nh32} states, {step32} consecutive steps of the unquantized recurrence "
                      f"in fp64 ({done32} token-head updates) in {dt32:.1f} s, one thread"}
-    return {"cpu_baseline": one, "cpu_baseline_all_cores": allc, "cpu_baseline_fp32_state": f32}
+    done32a, dt32a = _all_cores("fp32", S, inputs, per, 4.0, bits, n)
+    f32a = {"value": done32a / dt32a, "unit": "token-head updates/s", "cores": n, "kind": "oracle",
+            "host": hc,
+            "sample": f"{n} processes, each on its own {per} states, consecutive steps of the unquantized "
+                      f"recurrence in fp64 for ~4 s: {done32a} token-head updates in {dt32a:.1f} s"}
+    return {"cpu_baseline": one, "cpu_baseline_all_cores": allc, "cpu_baseline_fp32_state": f32,
+            "cpu_baseline_fp32_state_all_cores": f32a}
+
+
+def settle(torch, fn, min_calls: int = 300, min_s: float = 0.3):
+    """Untimed calls until at least `min_calls` have run and `min_s` of wall
+    time has passed (checked every 50 calls): the GPU reaches its steady
+    clocks under sustained load (the first ~200 calls after an idle spell
+    run up to ~40% slower).  Reported in the JSON line; the timed region
+    stays exactly --steps calls.  Returns (calls, seconds)."""
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(50):
+            fn(calls)
+            calls += 1
+        torch.cuda.synchronize()
+        if calls >= min_calls and time.perf_counter() - t0 >= min_s:
+            return calls, time.perf_counter() - t0
 
 
 def time_launches(torch, fn, steps: int, warmup: int):
@@ -262,21 +326,33 @@ def time_launches(torch, fn, steps: int, warmup: int):
     (the library launches on torch's current stream), one before the first
     timed call and one after the last, divided by `steps`.  Events between
     the calls would sit in the stream between the launches and add their
-    own cost to every call.  Returns (wall seconds, mean per-call seconds)
-    of the same `steps` calls."""
+    own cost to every call, so only two more are recorded: after the first
+    timed call and before the last, giving the durations of those two calls
+    (a clock ramp shows as a first call slower than the last).  Returns
+    (wall seconds, mean per-call seconds, first call seconds, last call
+    seconds) of the same `steps` calls."""
     for i in range(warmup):
         fn(i)
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record(stream)
+    ev[0].record(stream)
     for i in range(steps):
+        if i == steps - 1 and steps > 1:
+            ev[2].record(stream)
         fn(warmup + i)
-    e1.record(stream)
+        if i == 0 and steps > 1:
+            ev[1].record(stream)
+    ev[3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, e0.elapsed_time(e1) * 1e-3 / steps
+    per = ev[0].elapsed_time(ev[3]) * 1e-3 / steps
+    if steps > 1:
+        first, last = ev[0].elapsed_time(ev[1]) * 1e-3, ev[2].elapsed_time(ev[3]) * 1e-3
+    else:
+        first = last = per
+    return wall, per, first, last
 
 
 def prefix_cache_data():
@@ -346,10 +422,12 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
     def fp32_step(i):
         g.gdn_fp32_decode_step(dc, S_p, *ptrs[i % n_sets], o_p, sh)
 
+    log(f"settling the GPU clocks on the {bits}-bit per-step decode")
+    settle_calls, settle_s = settle(torch, int8_step)
     log(f"timing {bits}-bit per-step decode")
-    wall, per = time_launches(torch, int8_step, args.steps, args.warmup)
+    wall, per, first, last = time_launches(torch, int8_step, args.steps, args.warmup)
     log("timing fp32-state decode")
-    wall32, per32 = time_launches(torch, fp32_step, args.steps, args.warmup)
+    wall32, per32, first32, last32 = time_launches(torch, fp32_step, args.steps, args.warmup)
     b8 = step_bytes(cfg, True) * nh
     b32 = step_bytes(cfg, False) * nh
     value = nh * args.steps / wall
@@ -380,10 +458,15 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
                                                + ("" if bits == 8 else f"_b{bits}"), "prefix_cache"),
                      "kernel": f"step_fused_kernel<128x128, bf16, scalar gate, {bits}-bit codes"
                                + (", static scales>" if args.static else ">"),
-                     "algorithmic_bytes_per_launch": b8, "mean_launch_s": per},
+                     "algorithmic_bytes_per_launch": b8, "mean_launch_s": per,
+                     "first_call_s": first, "last_call_s": last},
+        "settle": {"calls": settle_calls, "s": settle_s,
+                   "note": "untimed calls of the same decode before the warm-up, until the GPU holds its "
+                           "steady clocks; the timed region is exactly `steps` calls"},
         "fp32_state": {"value": nh * args.steps / wall32, "ms_per_step": wall32 / args.steps * 1e3,
                        "achieved_GBs": b32 / per32 / 1e9, "frac": b32 / per32 / 1e9 / HBM_PEAK_GBS,
                        "algorithmic_bytes_per_launch": b32, "mean_launch_s": per32,
+                       "first_call_s": first32, "last_call_s": last32,
                        "traffic": stored_traffic("step_fp32", "prefix_cache")},
         "speedup_vs_fp32_state": wall32 / wall,
     }
@@ -438,7 +521,8 @@ def bench_prefill(args, torch, g, cfg, x, cpu):
         g.gdn_prefill(dc, *p, T, sh)
 
     log("timing the prefill")
-    wall, per = time_launches(torch, call, args.steps, args.warmup)
+    settle(torch, call, min_calls=20, min_s=0.3)
+    wall, per, _, _ = time_launches(torch, call, args.steps, args.warmup)
     if kda:
         flops = prefill_kda_chunk_flops(D) * nh * ((T + 15) // 16)
         tag, kernel = "prefill_kda", f"prefill_kda_kernel<{D}>"
@@ -507,13 +591,13 @@ def bench_window(args, torch, g, name):
         if t == W - 1:
             g.gdn_quant_window_flush(dc, sc, W, sh)
 
-    wall_eager, _ = time_launches(torch, token, steps, W * max(1, args.warmup // W))
+    wall_eager = time_launches(torch, token, steps, W * max(1, args.warmup // W))[0]
     if args.no_graph:
         wall, per_window = wall_eager, None
     else:
         # the same windows replayed from a HIP graph of one window's launches
         graph = capture_window(torch, g, d, st, dev_in, o, W)
-        wall, per_window = time_launches(torch, lambda i: graph.replay(), steps // W, max(1, args.warmup // W))
+        wall, per_window = time_launches(torch, lambda i: graph.replay(), steps // W, max(1, args.warmup // W))[:2]
     # per-kernel means: window steps and flushes separately
     stream = torch.cuda.current_stream()
     ev_s = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(W)]
@@ -589,7 +673,7 @@ def bench_window_stagger(args, torch, g, name):
         g.gdn_quant_decode_step_pool(d, st, B, slots, tpos[t], *dev_in[t], o)
         g.gdn_quant_window_flush_pool(d, st, B, slots, ntok[t])
 
-    wall_eager, _ = time_launches(torch, step, steps, W * max(1, args.warmup // W))
+    wall_eager = time_launches(torch, step, steps, W * max(1, args.warmup // W))[0]
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -602,7 +686,7 @@ def bench_window_stagger(args, torch, g, name):
         for i in range(W):
             step(i)
     torch.cuda.synchronize()
-    wall, per = time_launches(torch, lambda i: graph.replay(), steps // W, max(1, args.warmup // W))
+    wall, per = time_launches(torch, lambda i: graph.replay(), steps // W, max(1, args.warmup // W))[:2]
     return {
         "metric": f"token-head state updates/s, {'INT8' if args.bits == 8 else f'{args.bits}-bit'} "
                   f"window-mode decode, staggered windows ({name}, 1 GPU)",
@@ -706,7 +790,7 @@ def bench_tiny(args, torch, g):
     def step(i):
         g.gdn_quant_decode_step(dc, sc, *ptrs[i % T], o_p, 0, sh)
 
-    wall, per = time_launches(torch, step, args.steps, args.warmup)
+    wall, per = time_launches(torch, step, args.steps, args.warmup)[:2]
     return {
         "metric": "per-step INT8 decode latency, tiny workload (1 GPU)",
         "value": wall / args.steps * 1e6, "unit": "us per call (host wall clock)", "n_gpus": 1,
