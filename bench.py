@@ -157,18 +157,30 @@ def prefill_bytes(cfg: dict, T: int) -> int:
     return T * per_token + B * H * 2 * D * D * 4
 
 
+def _stored(kernel: str, workload: str):
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        return json.load(f).get(workload, {}).get(kernel, {})
+
+
 def stored_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel sources."""
-    path = os.path.join(PROFILES, "traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        data = json.load(f)
-    ent = data.get(workload, {}).get(kernel)
+    ent = _stored(kernel, workload)
     if not ent or ent.get("src_hash") != src_hash(kernel_family(kernel)):
         return None
     return ent["bytes_per_launch"]
+
+
+def stored_valu_busy(kernel: str, workload: str):
+    """VALU busy (share of SIMD cycles issuing VALU work) from the committed
+    counter summary, if it was taken on the current kernel sources."""
+    ent = _stored(kernel, workload)
+    if not ent or ent.get("valu_src_hash") != src_hash(kernel_family(kernel)):
+        return None
+    return ent["valu_busy"]
 
 
 def _oracle_int8_run(S: np.ndarray, inputs: list, budget_s: float, bits: int = 8):
@@ -430,6 +442,7 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
     wall32, per32, first32, last32 = time_launches(torch, fp32_step, args.steps, args.warmup)
     b8 = step_bytes(cfg, True) * nh
     b32 = step_bytes(cfg, False) * nh
+    step_tag = "step_fused" + ("_static" if args.static else "") + ("" if bits == 8 else f"_b{bits}")
     value = nh * args.steps / wall
     res = {
         "metric": ("token-head state updates/s, INT8 GDN per-step decode (1 GPU)" if bits == 8 else
@@ -454,8 +467,9 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": b8 / per / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": b8 / per / 1e9 / HBM_PEAK_GBS,
-                     "traffic": stored_traffic("step_fused" + ("_static" if args.static else "")
-                                               + ("" if bits == 8 else f"_b{bits}"), "prefix_cache"),
+                     "traffic": stored_traffic(step_tag, "prefix_cache"),
+                     # the other limit: share of SIMD cycles issuing VALU work
+                     "valu_busy": stored_valu_busy(step_tag, "prefix_cache"),
                      "kernel": f"step_fused_kernel<128x128, bf16, scalar gate, {bits}-bit codes"
                                + (", static scales>" if args.static else ">"),
                      "algorithmic_bytes_per_launch": b8, "mean_launch_s": per,
@@ -869,22 +883,14 @@ def summarize_pmc(fetch_db: str, write_db: str, copy_fetch_db: str, copy_write_d
             continue
         b = fetch[k] * 1024 * fscale + write[k] * 1024 * wscale
         lines.append(f"| {k} | {fetch[k]:.1f} | {write[k]:.1f} | {b:.4g} |")
-        for tag in ("step_fused", "step_fp32", "window_step", "flush", "prefill", "prefill_kda"):
-            if f"gdnq::{tag}_kernel" in k:
-                # template arguments after the geometry: the code width is the
-                # last one of the window kernels and the next-to-last of the
-                # fused step, whose last one is the static-scale flag
-                args = [x.strip() for x in k.rstrip(">").split(",")]
-                if tag == "step_fused":
-                    bits, static = args[-2], args[-1] == "true"
-                    tag += "_static" if static else ""
-                else:
-                    bits = args[-1]
-                if tag not in ("step_fp32", "prefill", "prefill_kda") and bits in ("6", "4"):
-                    tag += "_b" + bits
-                data.setdefault(workload, {})[tag] = {
-                    "bytes_per_launch": b, "src_hash": src_hash(kernel_family(tag)), "fetch_kib": fetch[k],
-                    "write_kib": write[k], "fetch_scale": fscale, "write_scale": wscale}
+        # template arguments after the geometry: the code width is the last
+        # one of the window kernels and the next-to-last of the fused step,
+        # whose last one is the static-scale flag (kernel_tag)
+        tag = kernel_tag(k)
+        if tag:
+            data.setdefault(workload, {}).setdefault(tag, {}).update({
+                "bytes_per_launch": b, "src_hash": src_hash(kernel_family(tag)), "fetch_kib": fetch[k],
+                "write_kib": write[k], "fetch_scale": fscale, "write_scale": wscale})
     with open(path, "w") as f:
         json.dump(data, f, indent=1)
     text = "\n".join(lines)
@@ -930,6 +936,7 @@ def summarize_counters(db: str):
     names = sorted({cn for d in agg.values() for cn in d})
     print("| kernel | dispatches | " + " | ".join(names) + " | VALU/wave | VALU busy |")
     print("|---|---|" + "---|" * (len(names) + 2))
+    found = {}
     for k, d in sorted(agg.items()):
         m = {cn: float(np.mean(v)) for cn, v in d.items()}
         per_wave = m["SQ_INSTS_VALU"] / m["SQ_WAVES"] if "SQ_INSTS_VALU" in m and m.get("SQ_WAVES") else None
@@ -940,6 +947,41 @@ def summarize_counters(db: str):
         pw = f"{per_wave:.1f}" if per_wave is not None else ""
         bz = f"{100 * busy:.1f}%" if busy is not None else ""
         print(f"| {k} | {n} | {cells} | {pw} | {bz} |")
+        if per_wave is not None and busy is not None:
+            found[k] = (per_wave, busy)
+    return found
+
+
+def store_valu(db: str, workload: str):
+    """--summarize-counters with --workload: also record VALU per wave and
+    VALU busy of the kernels the benchmark reports in profiles/traffic.json,
+    under the current kernel source hash."""
+    found = summarize_counters(db)
+    path = os.path.join(PROFILES, "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    for k, (pw, busy) in found.items():
+        tag = kernel_tag(k)
+        if tag:
+            data.setdefault(workload, {}).setdefault(tag, {}).update(
+                {"valu_per_wave": pw, "valu_busy": busy, "valu_src_hash": src_hash(kernel_family(tag))})
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+
+
+def kernel_tag(k: str):
+    """The benchmark's tag of a kernel name from a rocprofv3 database."""
+    for tag in ("step_fused", "step_fp32", "window_step", "flush", "prefill_kda", "prefill"):
+        if f"gdnq::{tag}_kernel" in k:
+            args = [x.strip() for x in k.rstrip(">").split(",")]
+            if tag == "step_fused":
+                bits, static = args[-2], args[-1] == "true"
+                tag += "_static" if static else ""
+            else:
+                bits = args[-1]
+            if tag not in ("step_fp32", "prefill", "prefill_kda") and bits in ("6", "4"):
+                tag += "_b" + bits
+            return tag
+    return None
 
 
 def main():
@@ -976,12 +1018,18 @@ def main():
                     help="per-kernel mean durations from a rocprofv3 --kernel-trace database (no GPU needed)")
     ap.add_argument("--summarize-counters", metavar="PMC_DB",
                     help="per-kernel counter means and VALU busy from a rocprofv3 --pmc database (no GPU needed)")
+    ap.add_argument("--store", action="store_true",
+                    help="with --summarize-counters: record VALU per wave and busy in profiles/traffic.json "
+                         "for --workload")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.steps)
         return
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters)
+        if args.store:
+            store_valu(args.summarize_counters, args.workload)
+        else:
+            summarize_counters(args.summarize_counters)
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.workload, args.md)

@@ -30,11 +30,17 @@
 
 namespace gdnq {
 
+// Row stride of the transposed row-maxima table (padded, 16-byte rows).
+template <class G>
+constexpr int row_table_stride() { return G::ROWS_W + 4; }
+
 template <class G>
 struct CodecLds {
     float rho[G::DK];
     float red[2][G::NW][G::DV];
     float iota[G::DV];
+    // per wave: the lanes' row maxima over their 8 columns, [column block][row]
+    alignas(16) float rt[G::NW][G::NCB][row_table_stride<G>()];
     int misc;
     int flag[2][G::NW];  // per-wave flags of block_any, two sets used in turn
 };
@@ -83,6 +89,31 @@ __device__ __forceinline__ RowMap row_map(const Lane &c, const int *hp_lds, int 
 }
 
 
+// m / Qb rounded to nearest even for the code range's Qb (127, 31 or 7):
+// q0 = m r, e = m - q0 Qb (exact, one fma), q1 = q0 + e r, with r = 1/Qb
+// rounded.  Checked exhaustively, for every positive finite fp32 m and
+// each of the three Qb, to equal the correctly rounded quotient (the
+// division sequence it replaces costs about three times the instructions).
+template <int BITS>
+__device__ __forceinline__ float div_by_qmax(float m)
+{
+    constexpr float QB = (float)code_qmax<BITS>();
+    constexpr float R = 1.0f / QB;
+    const float q0 = m * R;
+    return fmaf(fmaf(-q0, QB, m), R, q0);
+}
+
+// 1/s rounded to nearest even for the row scales the codec forms (s is the
+// rounded square root of a positive finite fp32, so 2^-75 <= s < 2^65): the
+// hardware reciprocal r0 (about one ulp) and one correction with the exact
+// residual 1 - s r0.  Compared on gfx950 with the IEEE quotient 1.0f / s for
+// every fp32 s in [2^-75, 2^65): identical for all of them.
+__device__ __forceinline__ float recip_row_scale(float s)
+{
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    return fmaf(fmaf(-s, r0, 1.0f), r0, r0);
+}
+
 // Column scales from the per-wave column maxima in L.red[0]; thread t < DV
 // owns column t.  Writes c to global memory and iota to LDS.  Codes of
 // BITS bits span [-Qb, Qb]: c = m/Qb, iota = Qb/m.
@@ -98,7 +129,7 @@ __device__ __forceinline__ void column_scales(const Lane &c, CodecLds<G> &L, flo
         if (m > 0.0f) {
             io = QB / m;
             if (__builtin_isinf(io)) io = 0.0f;
-            else cj = m / QB;
+            else cj = div_by_qmax<BITS>(m);
         }
         col_scale[c.t] = cj;
         L.iota[c.t] = io;
@@ -132,18 +163,32 @@ __device__ void codec_rowcol(float (&P)[8][8], const Lane &c, CodecLds<G> &L, in
     }
     const int row0 = row0_of<G>(c);
     {
-        // this lane ends up with the full max of row k = row_scatter_k(cb)
-        const float rk = row_reduce_scatter<G, OpMax>(r, c.cb);
-        const int k = row_scatter_k<G>(c.cb);
-        if (G::NCB == 8 || (c.cb & 1) == 0) {
-            const float s = (rk > 0.0f) ? sqrtf(rk) : 0.0f;
-            const float rho = (s > 0.0f) ? 1.0f / s : 0.0f;
-            const int i = row0 + (k >> 2) * (G::RGW * 4) + (k & 3);
+        // Row maxima, transposed through LDS inside the wave (a row group
+        // lives in one wave): each lane stores its 8 partials, two runs of 4
+        // rows of its column block; lane L then takes the NCB/PAIR partials
+        // of the wave's row L/PAIR (PAIR = 64/ROWS_W lanes per row, joined by
+        // one DPP step) and forms that row's scale.
+        constexpr int RS = row_table_stride<G>();
+        constexpr int PAIR = 64 / G::ROWS_W;
+        float *rt = &L.rt[c.w][0][0];
+        *reinterpret_cast<float4 *>(rt + c.cb * RS + 4 * c.rgl) = make_float4(r[0], r[1], r[2], r[3]);
+        *reinterpret_cast<float4 *>(rt + c.cb * RS + G::RGW * 4 + 4 * c.rgl) = make_float4(r[4], r[5], r[6], r[7]);
+        wave_lds_sync();
+        const int lr = c.lane / PAIR, part = c.lane % PAIR;
+        const float *col = rt + part * (G::NCB / PAIR) * RS + lr;
+        float rk = col[0];
+#pragma unroll
+        for (int e = 1; e < G::NCB / PAIR; e++) rk = fmaxf(rk, col[e * RS]);
+        if constexpr (PAIR == 2) rk = fmaxf(rk, dpp<DPP_XOR1>(rk));
+        const float s = (rk > 0.0f) ? sqrtf(rk) : 0.0f;
+        const float rho = (s > 0.0f) ? recip_row_scale(s) : 0.0f;
+        if (part == 0) {
+            const int i = c.w * G::ROWS_W + lr;
             L.rho[i] = rho;
             row_scale[i] = s;
         }
     }
-    wave_lds_sync();  // a row group lives in one wave
+    wave_lds_sync();
     float rho[8];
     load_rows_f32<G>(L.rho + row0, rho);
     float m[8];
@@ -156,11 +201,11 @@ __device__ void codec_rowcol(float (&P)[8][8], const Lane &c, CodecLds<G> &L, in
             P[k][j] = P[k][j] * rho[k];
             m[j] = fmaxf(m[j], fabsf(P[k][j]));
         }
+    float io[8];
     column_max_to_lds<G>(c, L, m);
     __syncthreads();
     column_scales<G, BITS>(c, L, col_scale);
     __syncthreads();
-    float io[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) io[j] = L.iota[c.cb * 8 + j];
     constexpr int RB = code_row_bytes<G, BITS>();

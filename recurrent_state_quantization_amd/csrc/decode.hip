@@ -40,19 +40,30 @@ struct StepArgs {
     size_t plane_r, plane_c;  // static scales: offsets of the rho and iota planes
 };
 
-// Column sums of R (retrieval) and O (output) partials plus k.q, reduced to
-// LDS; consumer threads (t < DV) then hold full sums.
+// Column sums of R (retrieval) and O (output) partials, reduced to LDS, and
+// k.q as one partial per wave of its last DK threads; the column threads
+// then hold full sums.
+//
+// Work done once per row or column is spread so that the waves sharing a
+// SIMD across resident workgroups carry about the same number of
+// instructions: the first DK threads form the per-row factors and the first
+// DV threads the column scales (codec), while the last DK threads reduce
+// k.q and the last DV threads finish u and o.
 template <class G>
 struct StepLds {
     alignas(16) float rv[4][G::DK];  // per key row: a s, a s k, a s q, k (read as float4)
     float red[G::NW][2][G::DV];
-    float red_kq[G::NW];
+    float red_kq[G::DK / 64];
     float u[G::DV];
 };
 
 template <class G>
-__device__ __forceinline__ void reduce_ro(const Lane &c, StepLds<G> &S, const float (&R)[8], const float (&O)[8],
-                                          float kq_part)
+constexpr int kq_first_thread() { return G::NT - G::DK; }
+template <class G>
+constexpr int col_first_thread() { return G::NT - G::DV; }
+
+template <class G>
+__device__ __forceinline__ void reduce_ro(const Lane &c, StepLds<G> &S, const float (&R)[8], const float (&O)[8])
 {
     float x[16], z[4];
 #pragma unroll
@@ -66,8 +77,26 @@ __device__ __forceinline__ void reduce_ro(const Lane &c, StepLds<G> &S, const fl
         const int idx = scatter_index(c, p);
         S.red[c.w][idx >> 3][c.cb * 8 + (idx & 7)] = z[p];
     }
-    kq_part = col_allreduce<G, OpSum>(kq_part);
-    if (c.lane == 0) S.red_kq[c.w] = kq_part;
+}
+
+// k.q over the key rows: thread kq_first_thread + i holds k_i q_i; each of
+// those waves sums its 64 rows (DPP and permlane steps) into red_kq.
+template <class G>
+__device__ __forceinline__ void reduce_kq(const Lane &c, StepLds<G> &S, float ki, float qi)
+{
+    if (c.t >= kq_first_thread<G>()) {  // whole waves (NT - DK is a multiple of 64)
+        const float kq = col_allreduce<G, OpSum>(row_sum<G>(ki * qi));
+        if (c.lane == 0) S.red_kq[c.w - kq_first_thread<G>() / 64] = kq;
+    }
+}
+
+template <class G>
+__device__ __forceinline__ float sum_kq(const StepLds<G> &S)
+{
+    float kq = S.red_kq[0];
+#pragma unroll
+    for (int w = 1; w < G::DK / 64; w++) kq += S.red_kq[w];
+    return kq;
 }
 
 template <class G, bool BF16, bool KDA, int BITS, bool STATIC>
@@ -89,7 +118,7 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     map_inputs(A.map, x);
     const size_t hi = x.in, hk = x.key;
     const int tr = c.t % G::DK;
-    const int tc = c.t % G::DV;
+    const int tc = c.t % G::DV;   // for t >= NT - DV: t - (NT - DV) (NT is a multiple of DV)
     const float ki = load1<BF16>(A.k, hk * G::DK + tr);
     const float qi = load1<BF16>(A.q, hk * G::DK + tr);
     const float ai = KDA ? A.a[hi * G::DK + tr] : A.a[hi];
@@ -100,7 +129,7 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     float *rs = A.row_scale + h * G::DK;
     float *cs = A.col_scale + h * G::DV;
     const float si = rs[tr];
-    const float cj = cs[tc];   // v_j and c_j serve the consumer lanes (t < DV; columns wrap)
+    const float cj = cs[tc];   // v_j and c_j serve the column threads (t >= NT - DV; columns wrap)
     float rho_t = 0.0f, io_t = 0.0f;  // static scales: one reciprocal per row / column, via LDS
     if constexpr (STATIC) {
         rho_t = A.row_scale[A.plane_r + h * G::DK + tr];
@@ -116,21 +145,19 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     float cc[8];
     load_f32x8(cs + c.cb * 8, cc);
     const float bh = A.b[hi];
-    float kq_row = 0.0f;
     if (c.t < G::DK) {
         const float asi = ai * si;
         SL.rv[0][c.t] = asi;
         SL.rv[1][c.t] = asi * ki;
         SL.rv[2][c.t] = asi * qi;
         SL.rv[3][c.t] = ki;
-        kq_row = ki * qi;
     }
     if constexpr (STATIC) {
         if (c.t < G::DK) L.rho[c.t] = rho_t;
         if (c.t < G::DV) L.iota[c.t] = io_t;
     }
+    reduce_kq<G>(c, SL, ki, qi);  // row t % DK in thread t: the last DK threads hold every row once
     __syncthreads();
-    const float kq = row_sum<G>(kq_row);  // this lane's row group's share: reduce_ro adds the rest
     float X[8][8];
 #pragma unroll
     for (int k = 0; k < 8; k++) unpack_code8<BITS>(qraw[k], X[k]);
@@ -150,7 +177,7 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
                 R[j] = fmaf(X[k][j], ask[k], R[j]);
                 O[j] = fmaf(X[k][j], asq[k], O[j]);
             }
-        reduce_ro<G>(c, SL, R, O, kq);
+        reduce_ro<G>(c, SL, R, O);
     }
     // The decayed, dequantized state (Q_ij c_j)(a_i s_i), formed while the
     // other waves finish their sums; only k and u remain for the update.
@@ -165,17 +192,16 @@ __global__ __launch_bounds__(G::NT) void step_fused_kernel(StepArgs A)
     }
     load_rows_f32<G>(&SL.rv[3][row0], kk);
     __syncthreads();
-    if (c.t < G::DV) {
-        float Rj = SL.red[0][0][c.t], Oj = SL.red[0][1][c.t], kqs = SL.red_kq[0];
+    if (c.t >= col_first_thread<G>()) {  // column tc = t - (NT - DV)
+        float Rj = SL.red[0][0][tc], Oj = SL.red[0][1][tc];
 #pragma unroll
         for (int w = 1; w < G::NW; w++) {
-            Rj += SL.red[w][0][c.t];
-            Oj += SL.red[w][1][c.t];
-            kqs += SL.red_kq[w];
+            Rj += SL.red[w][0][tc];
+            Oj += SL.red[w][1][tc];
         }
         const float u = bh * (vj - cj * Rj);
-        store1<BF16>(A.o, hi * G::DV + c.t, fmaf(u, kqs, cj * Oj));
-        SL.u[c.t] = u;
+        store1<BF16>(A.o, hi * G::DV + tc, fmaf(u, sum_kq<G>(SL), cj * Oj));
+        SL.u[tc] = u;
     }
     __syncthreads();
     float u8[8];
@@ -229,12 +255,15 @@ __global__ __launch_bounds__(G::NT) void step_fp32_kernel(StepArgs A)
     float vj = 0.0f;
     if (c.t < G::DV) vj = load1<BF16>(A.v, h * G::DV + c.t);
 
-    float ak[8], aq[8], kq = 0.0f;
+    float ak[8], aq[8];
 #pragma unroll
     for (int k = 0; k < 8; k++) {
         ak[k] = av[k] * kk[k];
         aq[k] = av[k] * qq[k];
-        kq = fmaf(kk[k], qq[k], kq);
+    }
+    {
+        const int tr = c.t % G::DK;
+        reduce_kq<G>(c, SL, load1<BF16>(A.k, hk * G::DK + tr), load1<BF16>(A.q, hk * G::DK + tr));
     }
     float R[8], O[8];
 #pragma unroll
@@ -249,18 +278,17 @@ __global__ __launch_bounds__(G::NT) void step_fp32_kernel(StepArgs A)
             R[j] = fmaf(X[k][j], ak[k], R[j]);
             O[j] = fmaf(X[k][j], aq[k], O[j]);
         }
-    reduce_ro<G>(c, SL, R, O, kq);
+    reduce_ro<G>(c, SL, R, O);
     __syncthreads();
     if (c.t < G::DV) {
-        float Rj = SL.red[0][0][c.t], Oj = SL.red[0][1][c.t], kqs = SL.red_kq[0];
+        float Rj = SL.red[0][0][c.t], Oj = SL.red[0][1][c.t];
 #pragma unroll
         for (int w = 1; w < G::NW; w++) {
             Rj += SL.red[w][0][c.t];
             Oj += SL.red[w][1][c.t];
-            kqs += SL.red_kq[w];
         }
         const float u = bh * (vj - Rj);
-        store1<BF16>(A.o, h * G::DV + c.t, fmaf(u, kqs, Oj));
+        store1<BF16>(A.o, h * G::DV + c.t, fmaf(u, sum_kq<G>(SL), Oj));
         SL.u[c.t] = u;
     }
     __syncthreads();
