@@ -9,11 +9,14 @@ update, output, requantize, write back).  The fp32-state kernel
 
 Printed: one JSON line (metric, value = token-head updates/s, roofline of
 the decode kernel against 8 TB/s HBM, and the plain fp64 CPU oracle timed
-on a bounded sample of the same workload).
+on a bounded sample of the same workload).  The line also carries, under
+"window", the three window-mode workloads run as their configurations
+state them over their whole length (gdn_serving, kda, damp: decode steps
+and flushes, each with its own roofline and oracle baseline).
 
     python bench.py [--steps 100] [--warmup 200] [--gpus 1]
                     [--workload prefix_cache|gdn_serving|kda|damp|tiny|prefill|prefill_kda]
-                    [--no-cpu] [--no-graph] [--no-diag] [--bits 8|6|4] [--copy-calibration]
+                    [--no-cpu] [--no-window] [--bits 8|6|4] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -567,58 +570,135 @@ def bench_prefill(args, torch, g, cfg, x, cpu):
     return res
 
 
-def bench_window(args, torch, g, name):
-    """Window-mode workloads: steps = decode tokens (flushes every W)."""
-    cfg = dict(synth.WORKLOADS[name], bits=args.bits)
-    nh, dk, dv, W, r = cfg["B"] * cfg["H"], cfg["dk"], cfg["dv"], cfg["W"], cfg["r"]
+WINDOW_CHUNK = 256   # decode steps per graph of the full-length window runs
+
+
+def cpu_window_baseline(name: str, budget_s: float = 8.0) -> dict:
+    """The fp64 oracle in window mode on 4 heads of the workload (B=1, H=4,
+    its distributions and seed): the window start as the workload defines
+    it (512 unquantized warm-up steps for gdn_serving, zero otherwise; DAMP
+    rows from the oracle's calibration over the workload's calibration
+    steps), then the workload's T decode steps, window by window (decode
+    and flush: compensators and the codec), until T or budget_s is reached.
+    The window-start work is not timed."""
+    import oracle
+
+    cfg = dict(synth.WORKLOADS[name], B=1, H=4)
+    nh, dk, dv, W, r, T = 4, cfg["dk"], cfg["dv"], cfg["W"], cfg["r"], cfg["T"]
+    S = np.zeros((nh, dk, dv))
+    t_start = 0
+    if cfg.get("s0") == "warmup":
+        w = synth.steps_inputs(cfg, 0, cfg["warmup"])
+        S, _ = oracle.recur(S, w["q"], w["k"], w["v"], w["a"], w["b"])
+        t_start = cfg["warmup"]
+    hp = None
+    if cfg.get("n_hp"):
+        cal = synth.calib_inputs(cfg, cfg["n_cal"])
+        hp, _ = oracle.calibrate(np.zeros((nh, dk, dv), np.float32), cal["k"], cal["v"], cal["a"], cal["b"],
+                                 cfg["n_hp"])
+    enc = oracle.compress(S, r, 20, hp_idx=hp)
+    done, t = 0, 0
+    t0 = time.perf_counter()
+    while t < T and time.perf_counter() - t0 < budget_s:
+        x = synth.steps_inputs(cfg, t_start + t, W)
+        if hp is None:
+            X0 = oracle.state_base(enc["Q"], enc["s"], enc["c"], enc["p"], enc["w"])
+        else:
+            X0 = oracle.state_base(enc["Q"], None, enc["c"], enc["p"], enc["w"], hp_idx=hp, hp_rows=enc["hp_rows"])
+        _, _, SW = oracle.window(X0, x["q"], x["k"], x["v"], x["a"], x["b"])
+        enc = oracle.compress(SW, r, 20, hp_idx=hp)
+        t += W
+        done += W * nh
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "token-head updates/s", "cores": 1, "kind": "oracle",
+            "sample": f"4 heads of the {name} workload (B=1, H=4, same distributions), steps 0-{t - 1} of its "
+                      f"T={T} in windows of {W} with {r} compensators"
+                      + (f" and {cfg['n_hp']} fp16 rows" if hp is not None else "")
+                      + f", decode and flush: {done} token-head updates in {dt:.1f} s, one thread"}
+
+
+def bench_window_full(args, torch, g, name: str, cpu=None) -> dict:
+    """A window workload as its configuration states it, timed over its
+    whole T decode steps: the window start (gdn_serving: 512 warm-up steps
+    of the fp32-state kernel from zero, then the codec with its
+    compensators; kda, damp: the zero state; damp: its fp16 rows chosen by
+    calibrate_scales over 256 calibration steps from zero), then T steps in
+    windows of W, each window W decode steps and one flush.  Inputs are
+    drawn on the GPU in chunks of WINDOW_CHUNK steps (every step distinct);
+    each chunk runs as one HIP graph (its windows' decode steps and
+    flushes), and the timed figure is the sum of the chunks' replays
+    (event pairs on the launch stream), the drawing of inputs left out."""
+    cfg = dict(synth.WORKLOADS[name])
+    B, H, dk, dv, W, r, T = cfg["B"], cfg["H"], cfg["dk"], cfg["dv"], cfg["W"], cfg["r"], cfg["T"]
+    nh = B * H
     n_hp = cfg.get("n_hp", 0)
-    if n_hp and args.bits != 8:
-        print("the DAMP layout keeps 8-bit codes: --bits applies to the other workloads", file=sys.stderr)
-        sys.exit(2)
-    d = g.Desc(B=cfg["B"], H=cfg["H"], dk=dk, dv=dv, W=W, r=r, bits=args.bits,
-               decay=g.DECAY_CHANNEL if cfg["decay"] == "channel" else g.DECAY_SCALAR, io_dtype=g.IO_BF16,
-               layout=g.LAYOUT_DAMP if n_hp else g.LAYOUT_ROWCOL, n_hp=n_hp, power_iters=20)
+    kda = cfg["decay"] == "channel"
+    d = g.Desc(B=B, H=H, dk=dk, dv=dv, W=W, r=r, decay=g.DECAY_CHANNEL if kda else g.DECAY_SCALAR,
+               io_dtype=g.IO_BF16, layout=g.LAYOUT_DAMP if n_hp else g.LAYOUT_ROWCOL, n_hp=n_hp, power_iters=20)
     st = g.alloc_state(d)
+    S = torch.zeros(nh * dk * dv, dtype=torch.float32, device="cuda")
+    t_start = 0
+    if cfg.get("s0") == "warmup":
+        log(f"{name}: {cfg['warmup']} warm-up steps of the fp32-state kernel")
+        for c0 in range(0, cfg["warmup"], WINDOW_CHUNK):
+            n = min(WINDOW_CHUNK, cfg["warmup"] - c0)
+            x = synth.device_steps_inputs(cfg, c0, n, torch)
+            o32 = torch.empty(nh * dv, dtype=torch.bfloat16, device="cuda")
+            for i in range(n):
+                g.gdn_fp32_decode_step(d, S, x["q"][i], x["k"][i], x["v"][i], x["a"][i], x["b"][i], o32)
+        t_start = cfg["warmup"]
     if n_hp:
-        gr = synth.misc_rng(cfg["seed"], 5)
-        hp = np.stack([np.sort(gr.choice(dk, n_hp, replace=False)) for _ in range(nh)]).astype(np.int32)
-        st["hp_idx"].copy_(torch.from_numpy(hp.reshape(-1)))
-    S = synth.random_states(cfg["seed"], nh, dk, dv, scale=0.3)
-    g.gdn_state_quantize(d, torch.from_numpy(S).cuda(), st)
-    steps = max(W, (args.steps // W) * W)
-    log(f"generating {W} input steps for {nh} heads")
-    dev_in = []
-    for t in range(W):
-        inp = synth.step_inputs(cfg, t)
-        bits = lambda n: torch.from_numpy(inp[n + "16"].view(np.int16)).cuda().view(torch.bfloat16)
-        dev_in.append([bits("q"), bits("k"), bits("v"), torch.from_numpy(inp["a"]).cuda(),
-                       torch.from_numpy(inp["b"]).cuda()])
+        log(f"{name}: calibrating the fp16 rows over {cfg['n_cal']} steps")
+        cal = synth.device_steps_inputs(cfg, 0, cfg["n_cal"], torch, purpose=synth.STREAM_CALIB)
+        g.calibrate_scales(d, S, cal["k"], cal["v"], cal["a"], cal["b"], cfg["n_cal"], st["hp_idx"])
+        del cal
+    g.gdn_state_quantize(d, S, st)
+    del S
+    torch.cuda.synchronize()
+
+    chunk = max(W, (WINDOW_CHUNK // W) * W)
+    x = synth.device_steps_inputs(cfg, t_start, chunk, torch)
     o = torch.empty(nh * dv, dtype=torch.bfloat16, device="cuda")
+    dc, sc, sh = d.c(), g.state_struct(st), None
+    ptr = {k: v.data_ptr() for k, v in x.items()}
+    es = {k: v[0].numel() * v.element_size() for k, v in x.items()}   # bytes per step
 
-    dc, sc, sh = d.c(), g.state_struct(st), torch.cuda.current_stream().cuda_stream
-    ptrs = [[x.data_ptr() for x in inp] for inp in dev_in]
-    o_p = o.data_ptr()
+    def launch_chunk(stream):
+        for i in range(chunk):
+            t = i % W
+            g.gdn_quant_decode_step(dc, sc, ptr["q"] + i * es["q"], ptr["k"] + i * es["k"], ptr["v"] + i * es["v"],
+                                    ptr["a"] + i * es["a"], ptr["b"] + i * es["b"], o.data_ptr(), t, stream)
+            if t == W - 1:
+                g.gdn_quant_window_flush(dc, sc, W, stream)
 
-    def token(i):
-        t = i % W
-        g.gdn_quant_decode_step(dc, sc, *ptrs[t], o_p, t, sh)
-        if t == W - 1:
-            g.gdn_quant_window_flush(dc, sc, W, sh)
-
-    wall_eager = time_launches(torch, token, steps, W * max(1, args.warmup // W))[0]
-    if args.no_graph:
-        wall, per_window = wall_eager, None
-    else:
-        # the same windows replayed from a HIP graph of one window's launches
-        graph = capture_window(torch, g, d, st, dev_in, o, W)
-        wall, per_window = time_launches(torch, lambda i: graph.replay(), steps // W, max(1, args.warmup // W))[:2]
-    # per-kernel means: window steps and flushes separately
     stream = torch.cuda.current_stream()
+    if args.eager:   # kernel launches from the host (for counter passes)
+        run = lambda: launch_chunk(stream.cuda_stream)
+    else:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            launch_chunk(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        run = graph.replay
+    log(f"{name}: {T} decode steps in chunks of {chunk}")
+    total = 0.0
+    for c0 in range(0, T, chunk):
+        if c0 > 0:
+            synth.device_steps_inputs(cfg, t_start + c0, chunk, torch, out=x)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1) * 1e-3
+    # per-kernel durations of one more window, eager, on the same state
     ev_s = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(W)]
     ev_f = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    synth.device_steps_inputs(cfg, t_start + T, chunk, torch, out=x)
     for t in range(W):
         ev_s[t][0].record(stream)
-        g.gdn_quant_decode_step(d, st, *dev_in[t], o, t)
+        g.gdn_quant_decode_step(d, st, x["q"][t], x["k"][t], x["v"][t], x["a"][t], x["b"][t], o, t)
         ev_s[t][1].record(stream)
     ev_f[0].record(stream)
     g.gdn_quant_window_flush(d, st, W)
@@ -626,30 +706,42 @@ def bench_window(args, torch, g, name):
     torch.cuda.synchronize()
     t_steps = [a.elapsed_time(b) * 1e-3 for a, b in ev_s]
     t_flush = ev_f[0].elapsed_time(ev_f[1]) * 1e-3
-    bsteps = [window_step_bytes(cfg, t) * nh for t in range(W)]
+    wcfg = dict(cfg, bits=8)
+    win_bytes = (sum(window_step_bytes(wcfg, t) for t in range(W)) + flush_bytes(wcfg, W)) * nh
+    nwin = T // W
     res = {
-        "metric": f"token-head state updates/s, {'INT8' if args.bits == 8 else f'{args.bits}-bit'} "
-                  f"window-mode decode ({name}, 1 GPU)",
-        "value": nh * steps / wall, "unit": "token-head updates/s", "n_gpus": 1, "steps": steps,
-        "warmup": args.warmup, "ms_per_step": wall / steps * 1e3, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": f"int{args.bits} state, fp32 math, bf16 q/k/v/o",
-        "data": "synthetic", "config": {"workload": name, "B": cfg["B"], "H": cfg["H"], "W": W, "r": r, "bits": args.bits,
-                                         "n_hp": n_hp, "decay": cfg["decay"]},
-        "roofline": {"bound": "hbm", "achieved": sum(bsteps) / sum(t_steps) / 1e9, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": sum(bsteps) / sum(t_steps) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": stored_traffic("window_step" + ("" if args.bits == 8 else f"_b{args.bits}"), name),
-                     "kernel": "window_step_kernel (mean over window positions)"},
-        "launch": "eager calls" if args.no_graph else "one HIP graph per window (W decode steps + flush), replayed",
-        "window_us": None if per_window is None else per_window * 1e6,
-        "eager": {"value": nh * steps / wall_eager, "ms_per_step": wall_eager / steps * 1e3},
-        "window_step_us": [round(x * 1e6, 2) for x in t_steps],
+        "metric": f"token-head state updates/s, INT8 window-mode decode ({name}, 1 GPU)",
+        "value": nh * T / total, "unit": "token-head updates/s", "steps": T, "timed_s": total,
+        "config": {"workload": f"{name}: B={B}, H={H}, dk=dv={dk}, T={T}, W={W}, r={r}"
+                               + (f", {n_hp} fp16 rows per head (calibrate_scales, {cfg['n_cal']} steps)" if n_hp else "")
+                               + (", per-key-channel gate" if kda else ", scalar gate")
+                               + (f", window start after {cfg['warmup']} fp32 steps" if t_start else ", zero start"),
+                   "B": B, "H": H, "W": W, "r": r, "T": T, "n_hp": n_hp, "decay": cfg["decay"]},
+        "data": "synthetic, drawn on the GPU (torch generator, seeded per chunk): every decode step distinct",
+        "launch": (f"eager launches, {chunk} decode steps per timed chunk" if args.eager else
+                   f"one HIP graph per {chunk} decode steps ({chunk // W} windows: decode steps and flushes), "
+                   "replayed once per chunk of fresh inputs; timed: the replays"),
+        # the whole mode, flushes included: algorithmic bytes of a window's
+        # W decode steps and its flush, times the windows, over the timed sum
+        "roofline": {"bound": "hbm", "achieved": win_bytes * nwin / total / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": win_bytes * nwin / total / 1e9 / HBM_PEAK_GBS,
+                     "algorithmic_bytes_per_window": win_bytes, "windows": nwin,
+                     "kernel": "window_step_kernel x W + flush_kernel"},
+        "window_step_us": [round(v * 1e6, 2) for v in t_steps],
         "flush_us": t_flush * 1e6,
-        "flush_GBs": flush_bytes(cfg, W) * nh / t_flush / 1e9,
-        "cpu_baseline": None,
+        "flush_share": t_flush / (t_flush + sum(t_steps)),
     }
-    if not args.no_diag:
-        res["outliers"] = window_outliers(torch, g, d, st, dev_in, o, nh, dk, dv, W, n_hp)
+    res["cpu_baseline"] = cpu
     return res
+
+
+def window_line(args, res: dict, name: str) -> dict:
+    """The full JSON line of a window workload run on its own."""
+    out = {"metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": res["steps"],
+           "warmup": 0, "ms_per_step": res["timed_s"] / res["steps"] * 1e3, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "int8 state (fp16 rows for DAMP), fp32 math, bf16 q/k/v/o"}
+    out.update({k: v for k, v in res.items() if k not in out})
+    return out
 
 
 def bench_window_stagger(args, torch, g, name):
@@ -716,30 +808,6 @@ def bench_window_stagger(args, torch, g, name):
     }
 
 
-def capture_window(torch, g, d, st, dev_in, o, W):
-    """One window (W decode steps and the flush) captured as a HIP graph.
-    The library launches on torch's current stream, which is the capturing
-    stream inside torch.cuda.graph; it sets or copies no memory, so the
-    graph holds kernel nodes only.  One eager window on a side stream
-    precedes the capture (it advances the state like any other window)."""
-    def window():
-        for t in range(W):
-            g.gdn_quant_decode_step(d, st, *dev_in[t], o, t)
-        g.gdn_quant_window_flush(d, st, W)
-
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        window()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        window()
-    torch.cuda.synchronize()
-    return graph
-
-
 def _max_over_median(x):
     """Per head max|x| / median|x| (x: [nh, E]); the median over heads."""
     a = x.abs()
@@ -754,30 +822,6 @@ def host_outliers(X: np.ndarray) -> dict:
     r = lambda a: float(np.median(a.max(axis=1) / np.maximum(np.median(a, axis=1), 1e-30)))
     Y = np.abs(X).astype(np.float64) / np.sqrt(np.maximum(np.abs(X).max(axis=2, keepdims=True), 1e-30))
     return {"state": r(A), "after_smoothing": r(Y.reshape(X.shape[0], -1))}
-
-
-def window_outliers(torch, g, d, st, dev_in, o, nh, dk, dv, W, n_hp):
-    """Diagnostic after one more window: the outlier ratio max/median of
-    the rebuilt state, of the residual left after the compensators (the
-    codec's input), and of that residual after key-row smoothing."""
-    import dataclasses
-
-    dbg = dataclasses.replace(d, flags=g.DEBUG_PREQUANT)
-    st = dict(st)
-    st["prequant_out"] = torch.empty(nh * dk * dv, dtype=torch.float32, device="cuda")
-    for t in range(W):
-        g.gdn_quant_decode_step(dbg, st, *dev_in[t], o, t)
-    g.gdn_quant_window_flush(dbg, st, W)
-    S_out = torch.empty(nh * dk * dv, dtype=torch.float32, device="cuda")
-    g.gdn_state_dequantize(d, st, S_out)
-    torch.cuda.synchronize()
-    R = st["prequant_out"].view(nh, dk * dv)
-    out = {"rebuilt_state": _max_over_median(S_out.view(nh, dk * dv)),
-           "after_compensators": _max_over_median(R)}
-    if not n_hp:
-        Y = R.view(nh, dk, dv) / st["row_scale"].view(nh, dk, 1)
-        out["after_smoothing"] = _max_over_median(Y.reshape(nh, dk * dv))
-    return out
 
 
 def bench_tiny(args, torch, g):
@@ -1005,11 +1049,11 @@ def main():
     ap.add_argument("--stagger", action="store_true",
                     help="window workloads: entries at staggered window positions, each step followed "
                          "by a pool flush of the entries whose window ends (pool entry points)")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="window workloads: time eager calls only (for counter passes)")
-    ap.add_argument("--no-diag", action="store_true",
-                    help="window workloads: skip the outlier diagnostic (its extra window writes the "
-                         "fp32 codec input and would count in kernel traces and counters)")
+    ap.add_argument("--eager", action="store_true",
+                    help="window workloads: launch each chunk's kernels from the host instead of a HIP graph "
+                         "(for counter passes)")
+    ap.add_argument("--no-window", action="store_true",
+                    help="prefix_cache: leave out the window workloads' keys (gdn_serving, kda, damp)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
                     help="summarize rocprofv3 --pmc databases into profiles/traffic.json (no GPU needed)")
@@ -1043,12 +1087,20 @@ def main():
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
     data = cpu = None
+    windows = () if args.no_window else ("gdn_serving", "kda", "damp")
+    wcpu = {}
     if args.workload == "prefix_cache" and not args.copy_calibration:
         data = prefix_cache_data()
         data = (dict(data[0], bits=args.bits),) + data[1:]
         if not args.no_cpu and not args.static:
             log("timing the CPU oracle")
             cpu = cpu_baselines(*data)
+            for name in windows:
+                log(f"timing the CPU oracle on {name}")
+                wcpu[name] = cpu_window_baseline(name)
+    if args.workload in ("gdn_serving", "kda", "damp") and not args.stagger and not args.no_cpu:
+        log(f"timing the CPU oracle on {args.workload}")
+        wcpu[args.workload] = cpu_window_baseline(args.workload)
     if args.workload in ("prefill", "prefill_kda") and not args.copy_calibration:
         data = prefill_data(args.workload)
         cpu = None
@@ -1067,6 +1119,8 @@ def main():
         return
     if args.workload == "prefix_cache":
         res = bench_prefix_cache(args, torch, g, *data, cpu)
+        if windows and args.bits == 8 and not args.static and not args.pool:
+            res["window"] = {name: bench_window_full(args, torch, g, name, wcpu.get(name)) for name in windows}
     elif args.workload in ("prefill", "prefill_kda"):
         res = bench_prefill(args, torch, g, *data, cpu)
     elif args.workload == "tiny":
@@ -1074,7 +1128,8 @@ def main():
     elif args.stagger:
         res = bench_window_stagger(args, torch, g, args.workload)
     else:
-        res = bench_window(args, torch, g, args.workload)
+        res = window_line(args, bench_window_full(args, torch, g, args.workload, wcpu.get(args.workload)),
+                          args.workload)
     print(json.dumps(res), flush=True)
 
 

@@ -106,35 +106,40 @@ struct WinLds {
 };
 
 // Key-side vector of slot l (a compensator or a buffered token), entries
-// l16*PER .. l16*PER+PER-1, and for a token its gate exponents (xe[0] for
-// the scalar gate, one per entry for KDA); false (nothing read) for a
-// DAMP-row slot, the k.q slot and l >= NS.
-template <class G, bool KDA>
+// l16*PER .. l16*PER+PER-1; false (nothing read) for a DAMP-row slot, the
+// k.q slot and l >= NS.
+template <class G>
 __device__ __forceinline__ bool slot_kvec(const WinArgs &A, size_t h, int l, int NS, int n_hp, int l16,
-                                          float (&x)[G::DK / 16], int (&xe)[G::DK / 16])
+                                          float (&x)[G::DK / 16])
 {
     constexpr int PER = G::DK / 16;
     const int r = A.r;
     if (l >= NS || (l >= r && l < r + n_hp)) return false;
-    const size_t tok = h * A.W + (l - r - n_hp);
-    const float *vec = (l < r) ? A.comp_k + ((h * r + l) * G::DK) : A.buf_k + tok * G::DK;
+    const float *vec = (l < r) ? A.comp_k + ((h * r + l) * G::DK) : A.buf_k + (h * A.W + (l - r - n_hp)) * G::DK;
 #pragma unroll
     for (int e = 0; e < PER; e += 4) {
         const float4 v = *reinterpret_cast<const float4 *>(vec + l16 * PER + e);
         x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
     }
-    if (l >= r) {
-        if constexpr (KDA) {
-#pragma unroll
-            for (int e = 0; e < PER; e += 4) {
-                const int4 v = *reinterpret_cast<const int4 *>(A.buf_g + tok * G::DK + l16 * PER + e);
-                xe[e] = v.x; xe[e + 1] = v.y; xe[e + 2] = v.z; xe[e + 3] = v.w;
-            }
-        } else {
-            xe[0] = A.buf_g[tok];
-        }
-    }
     return true;
+}
+
+// Gate exponents of buffered token j (slot r + n_hp + j): entries
+// l16*PER .. +PER-1 for KDA, the head's one value for the scalar gate.
+template <class G, bool KDA>
+__device__ __forceinline__ void slot_kexp(const WinArgs &A, size_t h, int j, int l16, int (&xe)[G::DK / 16])
+{
+    constexpr int PER = G::DK / 16;
+    const size_t tok = h * A.W + j;
+    if constexpr (KDA) {
+#pragma unroll
+        for (int e = 0; e < PER; e += 4) {
+            const int4 v = *reinterpret_cast<const int4 *>(A.buf_g + tok * G::DK + l16 * PER + e);
+            xe[e] = v.x; xe[e + 1] = v.y; xe[e + 2] = v.z; xe[e + 3] = v.w;
+        }
+    } else {
+        xe[0] = A.buf_g[tok];
+    }
 }
 
 // Value-side entries col..col+7 of slot l (l < NS), loaded as raw bits so
@@ -192,12 +197,13 @@ __device__ __forceinline__ void load_tile_codes(const int8_t *codes, const Lane 
 // 8 workgroups per CU (64 VGPRs, no spills; the column scales wait in LDS
 // so the prefetched slot vectors fit beside the codes): 2048 heads run as
 // one round over the 256 CUs, 8192 as four.  The 6-bit unpack needs more
-// temporaries: 7 per CU (72 VGPRs) keeps it from spilling.
-template <int BITS>
-constexpr int step_min_blocks() { return BITS == 6 ? 7 : 8; }
+// temporaries, and the per-channel gate its tokens' gate exponents: 7 per
+// CU (72 VGPRs) keeps those from spilling.
+template <int BITS, bool KDA>
+constexpr int step_min_blocks() { return (BITS == 6 || KDA) ? 7 : 8; }
 
 template <class G, bool BF16, bool KDA, bool DAMP, int BITS>
-__global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_kernel(WinArgs A)
+__global__ __launch_bounds__(G::NT, (step_min_blocks<BITS, KDA>())) void window_step_kernel(WinArgs A)
 {
     static_assert(!DAMP || BITS == 8, "the DAMP layout keeps 8-bit codes");
     __shared__ WinLds<G> L;
@@ -238,13 +244,14 @@ __global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_ke
     constexpr int PER = G::DK / 16;
     const int l16 = c.t & 15;
     float xk[PER];
-    int xe[PER];
-    const bool xk0 = slot_kvec<G, KDA>(A, h, c.t >> 4, NS, n_hp, l16, xk, xe);
+    const bool xk0 = slot_kvec<G>(A, h, c.t >> 4, NS, n_hp, l16, xk);
     constexpr int NRG = G::NW * G::RGW;
     const int rg = c.w * G::RGW + c.rgl;
     uint4 uvraw[2];
     bool uv16 = false;
-    if (rg < NS) uv16 = slot_vvec_load<G>(A, h, rg, n_hp, c.cb * 8, uvraw);
+    // (with the per-channel gate this load waits until after the slot dot
+    // products, whose per-channel exponents need the registers)
+    if (!KDA && rg < NS) uv16 = slot_vvec_load<G>(A, h, rg, n_hp, c.cb * 8, uvraw);
     __builtin_amdgcn_sched_barrier(0);
 
     // fixed INT8 tile: the DAMP row map needs the row indices in LDS, so
@@ -279,14 +286,15 @@ __global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_ke
         load_tile_codes<G, true, BITS>(codes, c, rm, qraw);
     }
 
-    // slot dot products: alpha_l = kvec_l . (G.k), beta_l = kvec_l . (G.q)
-    // for the fixed state's slots; for a buffered token
-    // alpha_l = ((G_t/G_l) . k_l) . k_t = sum (k^_l m_t k_t) 2^(e_t - e_l)
-    // (beta with q_t); slot NS is k . q.  16 lanes per slot.
+    // slot dot products.  A buffered token l gives
+    //   alpha_l = ((G_t/G_l) . k_l) . k_t = sum_c k^_l,c m_t,c k_t,c 2^(e_t,c - e_l,c)
+    // (beta_l with q_t), and a compensator p, part of the fixed state, the
+    // same with k^ = p and e_l = 0: (G_t . p) . k_t.  A DAMP row i gives
+    // G_t,i k_t,i; slot NS is k . q.  16 lanes per slot.
     for (int base = 0; base <= NS; base += G::NT / 16) {
         const int l = base + (c.t >> 4);
         if (l > NS) break;  // whole 16-lane groups leave together
-        const bool has = base == 0 ? xk0 : slot_kvec<G, KDA>(A, h, l, NS, n_hp, l16, xk, xe);
+        const bool has = base == 0 ? xk0 : slot_kvec<G>(A, h, l, NS, n_hp, l16, xk);
         float al = 0.0f, be = 0.0f;
         if (l == NS) {
 #pragma unroll
@@ -297,41 +305,44 @@ __global__ __launch_bounds__(G::NT, step_min_blocks<BITS>()) void window_step_ke
                 al = L.gk[i];
                 be = L.gq[i];
             }
-        } else if (l < r) {  // compensator: part of the fixed state
-#pragma unroll
-            for (int e = 0; e < PER; e++) {
-                al = fmaf(xk[e], L.gk[l16 * PER + e], al);
-                be = fmaf(xk[e], L.gq[l16 * PER + e], be);
-            }
-        } else if constexpr (KDA) {
-#pragma unroll
-            for (int e = 0; e < PER; e++) {
-                const int i = l16 * PER + e;
-                const float x = ldexp_f(xk[e], L.ge[i] - xe[e]);
-                al = fmaf(x, L.mk[i], al);
-                be = fmaf(x, L.mq[i], be);
-            }
         } else {
+            // the slot's gate exponents (zero for a compensator; loaded here,
+            // not held across the first barrier with the prefetched vector)
+            int xe[PER];
+            if (l >= r) {
+                slot_kexp<G, KDA>(A, h, l - r - n_hp, l16, xe);
+            } else {
 #pragma unroll
-            for (int e = 0; e < PER; e++) {
-                al = fmaf(xk[e], L.mk[l16 * PER + e], al);
-                be = fmaf(xk[e], L.mq[l16 * PER + e], be);
+                for (int e = 0; e < PER; e++) xe[e] = 0;
             }
-        }
-        al = sum16(al);
-        be = sum16(be);
-        if constexpr (!KDA) {
-            if (has && l >= r) {  // the scalar gate's ratio, once per slot
+            if constexpr (KDA) {
+#pragma unroll
+                for (int e = 0; e < PER; e++) {
+                    const int i = l16 * PER + e;
+                    const float x = ldexp_f(xk[e], L.ge[i] - xe[e]);
+                    al = fmaf(x, L.mk[i], al);
+                    be = fmaf(x, L.mq[i], be);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < PER; e++) {
+                    al = fmaf(xk[e], L.mk[l16 * PER + e], al);
+                    be = fmaf(xk[e], L.mq[l16 * PER + e], be);
+                }
+                // the scalar gate's ratio, once per slot
                 al = ldexp_f(al, L.ge[0] - xe[0]);
                 be = ldexp_f(be, L.ge[0] - xe[0]);
             }
         }
+        al = sum16(al);
+        be = sum16(be);
         if (l16 == 0) {
             L.alpha[l] = al;
             L.beta[l] = be;
         }
     }
 
+    if (KDA && rg < NS) uv16 = slot_vvec_load<G>(A, h, rg, n_hp, c.cb * 8, uvraw);
     // fixed-state mat-vecs straight off the codes
     float gsk[8], gsq[8];
     load_rows_f32<G>(&L.sgk[row0_of<G>(c)], gsk);

@@ -200,3 +200,36 @@ def random_states(seed: int, nh: int, dk: int, dv: int, scale: float = 1.0, tag:
 
 def misc_rng(seed: int, tag: int = 0) -> np.random.Generator:
     return rng_for(seed, STREAM_MISC, tag)
+
+
+def device_steps_inputs(cfg: dict, t0: int, n: int, torch, purpose: int = STREAM_STEP, out: dict | None = None,
+                        hk: int | None = None):
+    """Inputs of steps t0 .. t0+n-1 drawn on the GPU with torch's generator
+    (seeded by the workload seed, the stream purpose and t0), for bulk runs
+    whose inputs no oracle reads: the same distributions as step_inputs
+    (q, k ~ N(0,1) normalised per head, v ~ N(0,1), a ~ U[a_lo, 1), b ~
+    U[0, 1)), but other values.  q, k, v come back in the I/O dtype (bf16 or
+    fp32), a, b in fp32; shapes q, k [n, B*hk, dk], v [n, B*H, dv],
+    a [n, B*H, 1|dk], b [n, B*H].  With `out` (a dict of such tensors, as
+    returned by an earlier call) the values are written into it."""
+    nh = cfg["B"] * cfg["H"]
+    nk = cfg["B"] * (hk or cfg["H"])
+    dk, dv = cfg["dk"], cfg["dv"]
+    na = dk if cfg["decay"] == "channel" else 1
+    io = torch.bfloat16 if cfg["io"] == "bf16" else torch.float32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(int(np.random.SeedSequence(cfg["seed"], spawn_key=(purpose, t0)).generate_state(1)[0]))
+    if out is None:
+        out = dict(q=torch.empty((n, nk, dk), dtype=io, device="cuda"), k=torch.empty((n, nk, dk), dtype=io, device="cuda"),
+                   v=torch.empty((n, nh, dv), dtype=io, device="cuda"),
+                   a=torch.empty((n, nh, na), dtype=torch.float32, device="cuda"),
+                   b=torch.empty((n, nh), dtype=torch.float32, device="cuda"))
+    for name in ("q", "k"):
+        x = torch.randn((n, nk, dk), generator=g, device="cuda")
+        out[name].copy_(x / x.norm(dim=-1, keepdim=True))
+    out["v"].copy_(torch.randn((n, nh, dv), generator=g, device="cuda"))
+    out["a"].copy_(torch.rand((n, nh, na), generator=g, device="cuda") * (1.0 - cfg["a_lo"]) + cfg["a_lo"])
+    out["a"].clamp_(max=1.0)
+    out["b"].copy_(torch.rand((n, nh), generator=g, device="cuda"))
+    return out
+
