@@ -40,7 +40,7 @@ __global__ __launch_bounds__(G::NT, 2) void quantize_kernel(QuantArgs A)
 #pragma unroll
     for (int k = 0; k < 8; k++) load_f32x8(A.S + h * E + (size_t)row_of<G>(c, k) * G::DV + c.cb * 8, P[k]);
     __syncthreads();
-    power_deflate<G>(P, c, L, A.r, A.iters, A.comp_k + h * A.r * G::DK, A.comp_v + h * A.r * G::DV);
+    power_deflate<G, !DAMP>(P, c, L, A.r, A.iters, A.comp_k + h * A.r * G::DK, A.comp_v + h * A.r * G::DV);
     if (A.prequant) {
 #pragma unroll
         for (int k = 0; k < 8; k++) store_f32x8(A.prequant + h * E + (size_t)row_of<G>(c, k) * G::DV + c.cb * 8, P[k]);

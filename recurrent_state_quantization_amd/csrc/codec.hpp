@@ -341,22 +341,68 @@ __device__ __forceinline__ void column_sum_scattered(const Lane &c, float (&red)
     }
 }
 
+// Full row sums x[8] of the lane's 8 rows from its per-row partial sums
+// xp[8] (over its 8 columns), transposed through LDS inside the wave like
+// the codec's row maxima: the partials go to the wave's table L.rt, lane L
+// adds the NCB/PAIR partials of the wave's row L/PAIR (one DPP step joins
+// the pair) and stores the sum in L.rho, and every lane reads back its 8
+// rows.  Uses L.rt[w] and the wave's rows of L.rho; consecutive calls in a
+// wave need no other synchronization.
+template <class G>
+__device__ __forceinline__ void row_sums(CodecLds<G> &L, const Lane &c, const float (&xp)[8], float (&x)[8])
+{
+    constexpr int RS = row_table_stride<G>();
+    constexpr int PAIR = 64 / G::ROWS_W;
+    float *rt = &L.rt[c.w][0][0];
+    *reinterpret_cast<float4 *>(rt + c.cb * RS + 4 * c.rgl) = make_float4(xp[0], xp[1], xp[2], xp[3]);
+    *reinterpret_cast<float4 *>(rt + c.cb * RS + G::RGW * 4 + 4 * c.rgl) = make_float4(xp[4], xp[5], xp[6], xp[7]);
+    wave_lds_sync();
+    const int lr = c.lane / PAIR, part = c.lane % PAIR;
+    const float *col = rt + part * (G::NCB / PAIR) * RS + lr;
+    float s = col[0];
+#pragma unroll
+    for (int e = 1; e < G::NCB / PAIR; e++) s += col[e * RS];
+    if constexpr (PAIR == 2) s += dpp<DPP_XOR1>(s);
+    if (part == 0) L.rho[c.w * G::ROWS_W + lr] = s;
+    wave_lds_sync();
+    load_rows_f32<G>(L.rho + row0_of<G>(c), x);
+}
+
 // One power-iteration step y = P^T (P v); when |y|^2 != 0, v <- y / |y|
 // (v is kept otherwise).  Returns |y|^2, the same value in every lane.
 // The norm and the scaling run on the two columns a lane holds after the
 // reduce-scatter; the scaled values are then gathered back to all lanes.
-template <class G>
-__device__ __forceinline__ float power_step(const float (&P)[8][8], const Lane &c, float (&red)[G::NW][G::DV],
-                                            float (&v)[8])
+// Row sums of P v for the lane's 8 rows: through LDS (LDS_ROWS) or by a DPP
+// all-reduce per row.  The LDS form issues fewer instructions and pays two
+// wave-local LDS round trips, which the other resident workgroups hide at
+// four per CU; at two or three per CU (the DAMP flush) the DPP form is
+// faster.
+template <class G, bool LDS_ROWS>
+__device__ __forceinline__ void row_dots(const float (&P)[8][8], const Lane &c, CodecLds<G> &L, const float (&v)[8],
+                                         float (&x)[8])
 {
-    float x[8];
+    float xp[8];
 #pragma unroll
     for (int k = 0; k < 8; k++) {
         float s = P[k][0] * v[0];
 #pragma unroll
         for (int j = 1; j < 8; j++) s = fmaf(P[k][j], v[j], s);
-        x[k] = row_sum<G>(s);
+        xp[k] = s;
     }
+    if constexpr (LDS_ROWS) {
+        row_sums<G>(L, c, xp, x);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; k++) x[k] = row_sum<G>(xp[k]);
+    }
+}
+
+template <class G, bool LDS_ROWS>
+__device__ __forceinline__ float power_step(const float (&P)[8][8], const Lane &c, CodecLds<G> &L,
+                                            float (&red)[G::NW][G::DV], float (&v)[8])
+{
+    float x[8];
+    row_dots<G, LDS_ROWS>(P, c, L, v, x);
     float yp[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) {
@@ -390,8 +436,8 @@ __device__ __forceinline__ float power_step(const float (&P)[8][8], const Lane &
 //   vector of P's largest column (lowest index on ties) when P != 0,
 //   otherwise keep v; v = y/|y|.
 // p = P v, w = v (fp32), P -= p w^T.  P == 0 gives p = w = 0.
-// comp_k: this head's [r][DK]; comp_v: [r][DV].
-template <class G>
+// comp_k: this head's [r][DK]; comp_v: [r][DV].  LDS_ROWS: see row_dots.
+template <class G, bool LDS_ROWS = true>
 __device__ void power_deflate(float (&P)[8][8], const Lane &c, CodecLds<G> &L, int r, int iters,
                               float *__restrict__ comp_k, float *__restrict__ comp_v)
 {
@@ -412,7 +458,7 @@ __device__ void power_deflate(float (&P)[8][8], const Lane &c, CodecLds<G> &L, i
             for (int j = 0; j < 8; j++) v[j] = v0;
             // first step, with the restart rule; L.red[0] is free here (the
             // barrier of block_any follows every earlier read of it)
-            float n2 = power_step<G>(P, c, L.red[0], v);
+            float n2 = power_step<G, LDS_ROWS>(P, c, L, L.red[0], v);
             if (n2 == 0.0f) {  // uniform: every lane holds the same n2
                 float cn[8], cs[8];
 #pragma unroll
@@ -437,25 +483,19 @@ __device__ void power_deflate(float (&P)[8][8], const Lane &c, CodecLds<G> &L, i
                 const int jb = L.misc;
 #pragma unroll
                 for (int j = 0; j < 8; j++) v[j] = (c.cb * 8 + j == jb) ? 1.0f : 0.0f;
-                n2 = power_step<G>(P, c, L.red[0], v);
+                n2 = power_step<G, LDS_ROWS>(P, c, L, L.red[0], v);
             }
             if (n2 != 0.0f) {
                 // remaining steps two at a time so each LDS buffer is fixed;
                 // consecutive steps alternate buffers, so one barrier per
                 // step orders every read of a buffer before its next write
                 for (int it = 1; it < iters; it += 2) {
-                    if (power_step<G>(P, c, L.red[1], v) == 0.0f) break;
+                    if (power_step<G, LDS_ROWS>(P, c, L, L.red[1], v) == 0.0f) break;
                     if (it + 1 >= iters) break;
-                    if (power_step<G>(P, c, L.red[0], v) == 0.0f) break;
+                    if (power_step<G, LDS_ROWS>(P, c, L, L.red[0], v) == 0.0f) break;
                 }
             }
-#pragma unroll
-            for (int k = 0; k < 8; k++) {
-                float s = P[k][0] * v[0];
-#pragma unroll
-                for (int j = 1; j < 8; j++) s = fmaf(P[k][j], v[j], s);
-                p[k] = row_sum<G>(s);
-            }
+            row_dots<G, LDS_ROWS>(P, c, L, v, p);
         }
         if (c.cb == 0) {
 #pragma unroll

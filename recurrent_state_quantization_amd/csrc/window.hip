@@ -582,7 +582,7 @@ __global__ __launch_bounds__(G::NT, (flush_min_blocks<G, DAMP>())) void flush_ke
         }
     }
 
-    power_deflate<G>(P, c, L, A.r, A.iters, A.comp_k + h * A.r * G::DK, A.comp_v + h * A.r * G::DV);
+    power_deflate<G, !DAMP>(P, c, L, A.r, A.iters, A.comp_k + h * A.r * G::DK, A.comp_v + h * A.r * G::DV);
     if (A.prequant) {
         float *pq = A.prequant + h * (size_t)G::DK * G::DV;
 #pragma unroll
