@@ -30,13 +30,22 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fPIC", "-shared", "-std=c11"]
+# GDNQ_SANITIZE=1: AddressSanitizer and UndefinedBehaviorSanitizer build with
+# the ROCm toolchain's clang (the runtime the instrumented HIP library uses;
+# it must be preloaded into the process)
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+             "-shared-libsan", "-ffp-contract=off", "-fPIC", "-shared", "-std=c11"]
 
 
 def build(force: bool = False) -> str:
-    """Compile oracle.c into liboracle.so next to it (gcc)."""
+    """Compile oracle.c into liboracle.so next to it (gcc; with GDNQ_SANITIZE=1,
+    clang with the address and undefined-behaviour sanitizers)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
-        subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        if os.environ.get("GDNQ_SANITIZE") == "1":
+            subprocess.run(["/opt/rocm/llvm/bin/clang", *SAN_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        else:
+            subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
         os.replace(tmp, _LIB)
     return _LIB
 

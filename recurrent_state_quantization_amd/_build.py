@@ -9,6 +9,12 @@ Each source is compiled to an object in parallel, then linked.  Flags:
     kernels run without IEEE NaN quieting and max() needs no
     canonicalizing moves (max reductions fuse with DPP);
   * packed fp32 instructions are switched off for the device code.
+
+With GDNQ_SANITIZE=1 in the environment the host side of every source
+(argument checks, launchers) is built with AddressSanitizer and
+UndefinedBehaviorSanitizer (-Xarch_host, so device code is unchanged); the
+library then needs clang's ASan runtime preloaded into the process
+(sanitizer_runtime() names it).
 """
 from __future__ import annotations
 
@@ -35,9 +41,24 @@ COMMON = [
 ]
 
 
+SANITIZE = os.environ.get("GDNQ_SANITIZE") == "1"
+# host code only: each sanitizer flag behind -Xarch_host
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the ASan runtime of the toolchain's clang (for LD_PRELOAD)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    return subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                          text=True, check=True).stdout.strip()
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON]
+    cmd = [HIPCC, *COMMON, *(HOST_SANITIZE if SANITIZE else [])]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -54,7 +75,8 @@ def build(jobs: int | None = None) -> str:
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *(HOST_SANITIZE if SANITIZE else []),
+                        "-Xarch_host", "-shared-libsan" if SANITIZE else "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
