@@ -227,13 +227,25 @@ int gdn_quant_window_flush_pool(const gdnq_desc *desc, const gdnq_state *state, 
  * residual through the codec of desc->layout (layout 1 reads
  * state->hp_idx).  Writes codes, scales, compensators; sets g_cur to 1
  * when given.  This is the back half of the flush.
+ * Defining passages: LeapQuant project page, residual-smoothing paragraph
+ * (key rows balanced by their smoothing scales before the low-bit codes)
+ * and Compensator Tokens paragraph (high-precision rank-1 terms taken out
+ * first); STEPQuant page (key-row and value-column scales); DAMP abstract
+ * (layout 1).  The codec's steps are the ones listed at the top of this
+ * header.  Errors: GDNQ_EINVAL for a NULL, misaligned or overlapping
+ * buffer; S is read only.
  */
 int gdn_state_quantize(const gdnq_desc *desc, const float *S, const gdnq_state *state,
                        void *stream);
 
 /*
  * Decode the stored state: S_out [B,H,dk,dv] fp32 (device) =
- * D(Q) + sum_c p_c w_c^T, i.e. the fixed state of the window start.
+ * D(Q) + sum_c p_c w_c^T, i.e. the fixed state of the window start
+ * (LeapQuant project page, per-window quantization paragraph: the
+ * low-bit state the window's outputs are computed from; residual-smoothing
+ * and Compensator Tokens paragraphs for its parts).  D(Q)_ij = (Q_ij c_j)
+ * s_i (layout 0) or Q_ij c_j and the fp16 rows (layout 1).  Only the
+ * state arrays are read; S_out must not overlap them.
  */
 int gdn_state_dequantize(const gdnq_desc *desc, const gdnq_state *state, float *S_out,
                          void *stream);
@@ -282,7 +294,12 @@ int calibrate_static_scales(const gdnq_desc *desc, const float *S0, const void *
 
 /*
  * Baseline: one decode token on fp32 states S [B,H,dk,dv] (device, in
- * place), same inputs and output as gdn_quant_decode_step.
+ * place), same inputs and output as gdn_quant_decode_step.  This is the
+ * comparator the pages measure against (LeapQuant project page,
+ * kernel-speed paragraph: the quantized kernel's speedups are stated over
+ * the FP32 recurrent state; the update is LinQuant's appendix Table 3).
+ * Per head it reads and writes the dk x dv fp32 state once.  Errors:
+ * GDNQ_EINVAL for a NULL, misaligned or overlapping buffer.
  */
 int gdn_fp32_decode_step(const gdnq_desc *desc, float *S, const void *q, const void *k,
                          const void *v, const float *a, const float *b, void *o, void *stream);
