@@ -186,6 +186,15 @@ def stored_valu_busy(kernel: str, workload: str):
     return ent["valu_busy"]
 
 
+def window_traffic(workload: str, W: int):
+    """HBM bytes of one window (W decode steps and the flush) from the
+    committed counters: the window step's mean bytes per dispatch (taken
+    over whole windows, so over every position equally) times W, plus the
+    flush's; None unless both were taken on the current kernel sources."""
+    step, flush = stored_traffic("window_step", workload), stored_traffic("flush", workload)
+    return None if step is None or flush is None else step * W + flush
+
+
 def _oracle_int8_run(S: np.ndarray, inputs: list, budget_s: float, bits: int = 8):
     """Consecutive per-step quantized decodes (b-bit codes) of the states S
     by the fp64 CPU oracle (one thread) until budget_s has passed:
@@ -725,8 +734,11 @@ def bench_window_full(args, torch, g, name: str, cpu=None) -> dict:
         # W decode steps and its flush, times the windows, over the timed sum
         "roofline": {"bound": "hbm", "achieved": win_bytes * nwin / total / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": win_bytes * nwin / total / 1e9 / HBM_PEAK_GBS,
+                     "traffic": window_traffic(name, W),
                      "algorithmic_bytes_per_window": win_bytes, "windows": nwin,
-                     "kernel": "window_step_kernel x W + flush_kernel"},
+                     "kernel": "window_step_kernel x W + flush_kernel",
+                     "valu_busy": {"window_step": stored_valu_busy("window_step", name),
+                                   "flush": stored_valu_busy("flush", name)}},
         "window_step_us": [round(v * 1e6, 2) for v in t_steps],
         "flush_us": t_flush * 1e6,
         "flush_share": t_flush / (t_flush + sum(t_steps)),
