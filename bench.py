@@ -551,7 +551,7 @@ def bench_prefill(args, torch, g, cfg, x, cpu):
     wall, per, _, _ = time_launches(torch, call, args.steps, args.warmup)
     if kda:
         flops = prefill_kda_chunk_flops(D) * nh * ((T + 15) // 16)
-        tag, kernel = "prefill_kda", f"prefill_kda_kernel<{D}>"
+        tag, kernel = "prefill_kda", f"prefill_kda_ws_kernel<{D}>" if D == 128 else f"prefill_kda_kernel<{D}>"
     else:
         flops = prefill_chunk_flops(D) * nh * ((T + 63) // 64)
         tag, kernel = "prefill", f"prefill_kernel<{D}>"
@@ -1026,6 +1026,8 @@ def store_valu(db: str, workload: str):
 
 def kernel_tag(k: str):
     """The benchmark's tag of a kernel name from a rocprofv3 database."""
+    if "gdnq::prefill_kda_ws_kernel" in k:   # the two-group form of the per-channel-gate prefill
+        return "prefill_kda"
     for tag in ("step_fused", "step_fp32", "window_step", "flush", "prefill_kda", "prefill"):
         if f"gdnq::{tag}_kernel" in k:
             args = [x.strip() for x in k.rstrip(">").split(",")]

@@ -34,9 +34,10 @@
 // more than 2^-60, pair by pair on the VALU (one e^{G_ic - G_jc} per pair
 // and channel).  U and W by forward substitution in fp32.
 //
-// Mapping: one workgroup per (batch, head) of D/16 waves (two per SIMD:
-// the chunk-local phases are latency-bound, and a second wave on each SIMD
-// hides part of it); wave w owns value columns 16w..16w+15 of the state,
+// Mapping (prefill_kda_kernel, used for D = 64; D = 128 takes the two-group
+// form at the end of this file): one workgroup per (batch, head) of D/16
+// waves (two per SIMD: the chunk-local phases are latency-bound, and a
+// second wave on each SIMD hides part of it); wave w owns value columns 16w..16w+15 of the state,
 // kept in fp32 MFMA accumulators for the whole sequence (the layout and the
 // permuted contraction of the scalar-gate kernel).  Products over the
 // chunk's 16 tokens use v_mfma_f32_16x16x16_bf16, whose accumulator layout
@@ -622,6 +623,473 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
                 Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + 16 * et + ln] = S[et][dt][r];
 }
 
+// ---------------------------------------------------------------------------
+// Two-group form for D = 128 (twelve waves, one workgroup per head): waves
+// 0-3 (the chunk group) run the chunk-local phases of chunk c + 1 --
+// element-wise operands, the decayed Gram sums, U and W by substitution --
+// while waves 4-11 (the state group, 16 value columns each, two per SIMD)
+// run the state phases of chunk c: U' = U - W S and O = (Q . 2^G) S, the
+// outputs, the state update.  The chunk-local phases do not read S, so the
+// two chains overlap on the SIMDs.  One iteration, four barriers:
+//   1. chunk group: element-wise operands       state group: U', O products
+//   2. chunk group: Gram products (factored)    state group: -
+//   3. chunk group: Gram halves added           state group: P U', outputs
+//   4. chunk group: substitution for U and W    state group: state update,
+//                                               output stores, staging
+// (a chunk that takes the pairwise Gram sums merges phases 2 and 3).  What
+// the chunk group hands to the state group (Q . 2^G, K . 2^(G_C - G),
+// 2^(G_C), P, U, -W) is double-buffered by chunk parity.  The state group
+// loads and stages the raw inputs: those of chunk c + 2 go out at the start
+// of the iteration; K, Q and the gates are staged in phase 4 (chunk c + 1
+// reads them no more), V^T and beta at the start of the next iteration.
+// The arithmetic of every phase is that of prefill_kda_kernel.
+template <int D>
+struct KdaWsLds {
+    static constexpr int SD = D + 8, SG = D + 4, ST = KC + 8, SK = KC + 4;
+    // raw chunk inputs (staging writes, the chunk group reads)
+    alignas(16) __bf16 kr[KC * SD];
+    alignas(16) __bf16 qr[KC * SD];
+    alignas(16) float g[KC * SG];
+    alignas(16) __bf16 vt[D * ST];
+    alignas(16) float beta[KC];
+    // chunk-group scratch
+    alignas(16) float kgf[D * SK];
+    alignas(16) float xf[KC * SG];
+    alignas(16) float yf[KC * SG];
+    alignas(16) float zf[KC * SG];
+    alignas(16) float gp[2][KC * SA];
+    alignas(16) float at[KC * SA];
+    // chunk group -> state group, by chunk parity
+    alignas(16) __bf16 qgh[2][KC * SD];
+    alignas(16) __bf16 qgl[2][KC * SD];
+    alignas(16) __bf16 kch[2][D * ST];
+    alignas(16) __bf16 kcl[2][D * ST];
+    alignas(16) __bf16 wh[2][KC * SD];
+    alignas(16) __bf16 wl[2][KC * SD];
+    alignas(16) float uf[2][KC * SG];
+    alignas(16) __bf16 ph[2][KC * ST];
+    alignas(16) __bf16 pl[2][KC * ST];
+    alignas(16) float egc[2][D];
+    // the state group's outputs, token-major
+    alignas(16) __bf16 ob[KC * SD];
+    uint8_t pij[NPAIR];
+    int pairwise;
+};
+
+template <int D>
+constexpr int kda_ws_threads() { return 768; }
+
+template <int D>
+__global__ __launch_bounds__(768, 1) void prefill_kda_ws_kernel(PrefillKdaArgs A)
+{
+    static_assert(D == 128, "two groups of four waves: D = 128");
+    using Lds = KdaWsLds<D>;
+    constexpr int SD = Lds::SD, SG = Lds::SG, ST = Lds::ST, SK = Lds::SK;
+    constexpr int NT = 768, GT = 256;         // threads, threads of the chunk group
+    constexpr int ST_T = NT - GT;             // threads of the state group (they also stage)
+    constexpr int ET = 1;                     // 16-column tiles of the state per state wave
+    constexpr int KB = D / 32;                // 32-wide blocks along a head dim
+    constexpr int DT = D / 16;                // 16-row tiles along a head dim
+    __shared__ Lds L;
+
+    const int tid0 = (int)__builtin_amdgcn_workitem_id_x();
+    const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+    const bool chunk_group = wave < 4;        // wave-uniform
+    const unsigned bh = __builtin_amdgcn_workgroup_id_x();
+    const unsigned bb = div_by(bh, A.byH), hh = bh - bb * (unsigned)A.H;
+    const unsigned kh = div_by(hh, A.byG);
+    const int T = A.T;
+    const int nch = (T + KC - 1) / KC;
+    const size_t tk = (size_t)A.HK * D, tv = (size_t)A.H * D;
+    const __bf16 *qg = A.q + (size_t)bb * T * tk + (size_t)kh * D;
+    const __bf16 *kg = A.k + (size_t)bb * T * tk + (size_t)kh * D;
+    const __bf16 *vg = A.v + (size_t)bb * T * tv + (size_t)hh * D;
+    __bf16 *og = A.o + (size_t)bb * T * tv + (size_t)hh * D;
+    const float *ag = A.a + (size_t)bb * T * tv + (size_t)hh * D;
+    const float *bg = A.b + (size_t)bb * T * A.H + hh;
+    float *Sg = A.S + (size_t)bh * D * D;
+    const int e0 = 16 * (wave - 4);  // state group: value columns e0 + 16 et + ln
+    int lg = (tid0 & 63) >> 4, ln = tid0 & 15;
+
+    for (int x = tid0; x < 2 * KC * ST; x += NT) {
+        (&L.ph[0][0])[x] = (__bf16)0.0f;
+        (&L.pl[0][0])[x] = (__bf16)0.0f;
+    }
+    for (int x = tid0; x < KC * SA; x += NT) L.at[x] = 0.0f;
+    if (tid0 == 0) L.pairwise = 0;
+    for (int p = tid0; p < NPAIR; p += NT) {
+        const int i = pair_row(p);
+        L.pij[p] = (uint8_t)(i | (p - i * (i + 1) / 2) << 4);
+    }
+    __syncthreads();  // the first chunk's staging may set the flag
+
+    auto load_chunk = [=](int c0, int tid, KdaChunkRegs &r) {
+        const int t = tid / (D / 4), c = 4 * (tid % (D / 4));
+        const size_t u = (size_t)min(c0 + t, T - 1);
+        r.k = *reinterpret_cast<const u32x2 *>(kg + u * tk + c);
+        r.q = *reinterpret_cast<const u32x2 *>(qg + u * tk + c);
+        const int tv_ = tid % KC, cv = 4 * (tid / KC);
+        r.v = *reinterpret_cast<const u32x2 *>(vg + (size_t)min(c0 + tv_, T - 1) * tv + cv);
+        const int cg = tid - (ST_T - D);
+        if (cg >= 0) {
+#pragma unroll
+            for (int t2 = 0; t2 < KC; t2++) r.a[t2] = ag[(size_t)min(c0 + t2, T - 1) * tv + cg];
+            r.b = bg[(size_t)min(c0 + (cg & (KC - 1)), T - 1) * A.H];
+        }
+    };
+    static_assert(KC * D / 4 == ST_T, "one 8-byte piece of K, Q and V per state-group thread");
+    // K, Q (token-major, zero past the end) and the gates: cumulative
+    // log2-gates from the chunk start (padding gate 1), the pairwise flag
+    auto stage_kqg = [&](int cs, int tid, const KdaChunkRegs &r) {
+        const int nv = min(KC, T - cs);
+        const int t = tid / (D / 4), c = 4 * (tid % (D / 4));
+        const u32x2 z = {0u, 0u};
+        *reinterpret_cast<u32x2 *>(&L.kr[t * SD + c]) = t < nv ? r.k : z;
+        *reinterpret_cast<u32x2 *>(&L.qr[t * SD + c]) = t < nv ? r.q : z;
+        if (const int cg = tid - (ST_T - D); cg >= 0) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int t2 = 0; t2 < KC; t2++) {
+                acc += t2 < nv ? __builtin_amdgcn_logf(r.a[t2]) : 0.0f;
+                L.g[t2 * SG + cg] = acc;
+            }
+            if (!(acc >= -kFactorRange)) L.pairwise = cs + 1;
+        }
+    };
+    // V^T (zero past the end) and beta
+    auto stage_vb = [&](int cs, int tid, const KdaChunkRegs &r) {
+        const int nv = min(KC, T - cs);
+        const u32x2 z = {0u, 0u};
+        const int tv_ = tid % KC, cv = 4 * (tid / KC);
+        const bf16x4 vv = __builtin_bit_cast(bf16x4, tv_ < nv ? r.v : z);
+#pragma unroll
+        for (int e = 0; e < 4; e++) L.vt[(cv + e) * ST + tv_] = vv[e];
+        if (const int cg = tid - (ST_T - D); cg >= 0 && cg < KC) L.beta[cg] = cg < nv ? r.b : 0.0f;
+    };
+
+    floatx4 S[ET][DT];  // state group: S[et][dt][r] = S[16 dt + 4 lg + r][e0 + 16 et + ln]
+    if (!chunk_group) {
+#pragma unroll
+        for (int et = 0; et < ET; et++)
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    S[et][dt][r] = Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + 16 * et + ln];
+    }
+    KdaChunkRegs nx;
+    if (!chunk_group) {
+        load_chunk(0, tid0 - GT, nx);
+        stage_kqg(0, tid0 - GT, nx);
+    }
+    __syncthreads();
+
+    for (int c = -1; c < nch; c++) {
+        int tid = tid0;
+        asm volatile("" : "+v"(lg), "+v"(ln), "+v"(tid));
+        const int kb = (c + 1) & 1, sb = c & 1;
+        const bool kwork = chunk_group && c + 1 < nch;  // chunk c + 1 (chunk group)
+        const bool swork = !chunk_group && c >= 0;      // chunk c (state group)
+        const int c1 = (c + 1) * KC;                    // first token of chunk c + 1
+        const bool factored = __builtin_amdgcn_readfirstlane(L.pairwise) != c1 + 1;
+
+        // ================= phase 1
+        if (!chunk_group && c + 1 < nch) stage_vb(c1, tid - GT, nx);
+        if (!chunk_group && c + 2 < nch) load_chunk(c1 + KC, tid - GT, nx);  // in flight until its staging
+        if (kwork) {
+            // element-wise operands of chunk c + 1 (arithmetic as in
+            // prefill_kda_kernel), 8 tokens of one key channel per thread
+            constexpr int TPT = KC * D / GT;
+            static_assert(TPT == 8, "8 tokens per thread");
+            const int ch = tid % D, t0 = TPT * (tid / D);
+            const float gC = L.g[(KC - 1) * SG + ch], gm = L.g[kRefToken * SG + ch];
+            const float egC = __builtin_amdgcn_exp2f(gC);
+            const float egm = __builtin_amdgcn_exp2f(gm), emg = __builtin_amdgcn_exp2f(-gm);
+            if (tid < D) L.egc[kb][ch] = egC;
+            floatx4 kg0, kg1;
+            bf16x8 kh8, kl8;
+#pragma unroll
+            for (int e = 0; e < TPT; e++) {
+                const int t = t0 + e;
+                const float gv = L.g[t * SG + ch];
+                const float kv = (float)L.kr[t * SD + ch], qv = (float)L.qr[t * SD + ch];
+                const float e1 = __builtin_amdgcn_exp2f(gv);
+                const float ei = factored ? __builtin_amdgcn_exp2f(-gv) : 0.0f;
+                const float e2 = factored ? egC * ei : __builtin_amdgcn_exp2f(gC - gv);
+                if (e < 4) kg0[e] = kv * e1;
+                else kg1[e - 4] = kv * e1;
+                split(kv * e2, kh8, kl8, e);
+                const float qe = qv * e1;
+                const __bf16 qh = (__bf16)qe;
+                L.qgh[kb][t * SD + ch] = qh;
+                L.qgl[kb][t * SD + ch] = (__bf16)(qe - (float)qh);
+                if (factored) {
+                    const float fl = e1 * emg, fr = egm * ei;
+                    L.xf[t * SG + ch] = kv * fl;
+                    L.yf[t * SG + ch] = kv * fr;
+                    L.zf[t * SG + ch] = qv * fl;
+                }
+            }
+            *reinterpret_cast<floatx4 *>(&L.kgf[ch * SK + t0]) = kg0;
+            *reinterpret_cast<floatx4 *>(&L.kgf[ch * SK + t0 + 4]) = kg1;
+            *reinterpret_cast<bf16x8 *>(&L.kch[kb][ch * ST + t0]) = kh8;
+            *reinterpret_cast<bf16x8 *>(&L.kcl[kb][ch * ST + t0]) = kl8;
+        }
+        floatx4 U[ET], O[ET];
+        bf16x4 Vh[ET], Vl[ET];
+        if (swork) {
+            // U' = U - W S and O = (Q . 2^G) S for chunk c
+#pragma unroll
+            for (int et = 0; et < ET; et++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) U[et][r] = L.uf[sb][(4 * lg + r) * SG + e0 + 16 * et + ln];
+            bf16x8 Sh[ET][KB], Sl[ET][KB];
+#pragma unroll
+            for (int et = 0; et < ET; et++)
+#pragma unroll
+                for (int k2 = 0; k2 < KB; k2++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        split(S[et][2 * k2][r], Sh[et][k2], Sl[et][k2], r);
+                        split(S[et][2 * k2 + 1][r], Sh[et][k2], Sl[et][k2], 4 + r);
+                    }
+#pragma unroll
+            for (int et = 0; et < ET; et++) O[et] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k2 = 0; k2 < KB; k2++) {
+                const int row = ln * SD + 4 * lg + 32 * k2;
+                const bf16x8 wh = ld_pair(&L.wh[sb][row]), wl = ld_pair(&L.wl[sb][row]);
+                const bf16x8 qh = ld_pair(&L.qgh[sb][row]), ql = ld_pair(&L.qgl[sb][row]);
+#pragma unroll
+                for (int et = 0; et < ET; et++) {
+                    U[et] = mma32(wh, Sh[et][k2], U[et]);
+                    O[et] = mma32(qh, Sh[et][k2], O[et]);
+                }
+#pragma unroll
+                for (int et = 0; et < ET; et++) {
+                    U[et] = mma32(wh, Sl[et][k2], U[et]);
+                    O[et] = mma32(qh, Sl[et][k2], O[et]);
+                }
+#pragma unroll
+                for (int et = 0; et < ET; et++) {
+                    U[et] = mma32(wl, Sh[et][k2], U[et]);
+                    O[et] = mma32(ql, Sh[et][k2], O[et]);
+                }
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                const floatx4 ec = ldf4(&L.egc[sb][16 * dt + 4 * lg]);
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+#pragma unroll
+                    for (int et = 0; et < ET; et++) S[et][dt][r] *= ec[r];
+            }
+#pragma unroll
+            for (int et = 0; et < ET; et++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) split(U[et][r], Vh[et], Vl[et], r);
+        }
+        // O += P U' (own accumulator, added on the VALU), outputs to ob
+        auto outputs = [&]() {
+            const bf16x4 pah = ld4(&L.ph[sb][ln * ST + 4 * lg]), pal = ld4(&L.pl[sb][ln * ST + 4 * lg]);
+#pragma unroll
+            for (int et = 0; et < ET; et++) {
+                floatx4 pu = mma16(pah, Vh[et], floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+                pu = mma16(pah, Vl[et], pu);
+                pu = mma16(pal, Vh[et], pu);
+                O[et] += pu;
+            }
+#pragma unroll
+            for (int et = 0; et < ET; et++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) L.ob[(4 * lg + r) * SD + e0 + 16 * et + ln] = (__bf16)O[et][r];
+        };
+        // S <- diag(2^{G_C}) S + (K . 2^(G_C - G))^T U' (S already decayed)
+        auto state_update = [&]() {
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                const bf16x4 kah = ld4(&L.kch[sb][(16 * dt + ln) * ST + 4 * lg]);
+                const bf16x4 kal = ld4(&L.kcl[sb][(16 * dt + ln) * ST + 4 * lg]);
+#pragma unroll
+                for (int et = 0; et < ET; et++) {
+                    S[et][dt] = mma16(kah, Vh[et], S[et][dt]);
+                    S[et][dt] = mma16(kah, Vl[et], S[et][dt]);
+                    S[et][dt] = mma16(kal, Vh[et], S[et][dt]);
+                }
+            }
+        };
+        __syncthreads();  // B1: operands of chunk c + 1 staged
+
+        // ================= phase 2 (and 3)
+        if (factored) {
+            // decayed Gram sums of chunk c + 1, factored (waves 0-3 as in
+            // prefill_kda_kernel)
+            floatx4 m = {0.0f, 0.0f, 0.0f, 0.0f};
+            const bool isp = wave >= 2, first = (wave & 1) == 0;
+            if (kwork) {
+                constexpr int CPG = D / 8;
+                const int cb = (wave & 1) * (D / 2) + CPG * lg;
+                const float *xa = (isp ? L.yf : L.xf) + ln * SG + cb;
+                const float *yb = (isp ? L.zf : L.yf) + ln * SG + cb;
+                floatx4 m0 = {0.0f, 0.0f, 0.0f, 0.0f}, m1 = m0;
+#pragma unroll
+                for (int s4 = 0; s4 < CPG; s4 += 4) {
+                    const floatx4 xv = ldf4(xa + s4), yv = ldf4(yb + s4);
+                    m0 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[0], yv[0], m0, 0, 0, 0);
+                    m1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[1], yv[1], m1, 0, 0, 0);
+                    m0 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[2], yv[2], m0, 0, 0, 0);
+                    m1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[3], yv[3], m1, 0, 0, 0);
+                }
+                m = m0 + m1;
+                if (!first) *reinterpret_cast<floatx4 *>(&L.gp[isp][ln * SA + 4 * lg]) = m;
+            }
+            __syncthreads();  // B2: second halves staged
+            if (kwork && first) {
+                m += ldf4(&L.gp[isp][ln * SA + 4 * lg]);
+                if (!isp) {
+                    const floatx4 bi = ldf4(&L.beta[4 * lg]);
+                    floatx4 w;
+#pragma unroll
+                    for (int r = 0; r < 4; r++) w[r] = 4 * lg + r > ln ? bi[r] * m[r] : 0.0f;
+                    *reinterpret_cast<floatx4 *>(&L.at[ln * SA + 4 * lg]) = w;
+                } else {
+                    bf16x4 h, l;
+#pragma unroll
+                    for (int r = 0; r < 4; r++) split(ln >= 4 * lg + r ? m[r] : 0.0f, h, l, r);
+                    *reinterpret_cast<bf16x4 *>(&L.ph[kb][ln * ST + 4 * lg]) = h;
+                    *reinterpret_cast<bf16x4 *>(&L.pl[kb][ln * ST + 4 * lg]) = l;
+                }
+            }
+            if (swork) outputs();
+        } else {
+            if (kwork) {
+                // decayed Gram sums of chunk c + 1, pair by pair: D/8 lanes per
+                // pair, 8 key channels each, in batches of three passes (the
+                // reads of a batch go out first)
+                constexpr int LPP = D / 8, PPI = GT / LPP;
+                constexpr int NP = (NPAIR + PPI - 1) / PPI, NB = 3;
+                const int cb = tid % LPP, slot = tid / LPP, c8 = 8 * cb;
+#pragma unroll
+                for (int n0 = 0; n0 < NP; n0 += NB) {
+                    int pi[NB], pj[NB];
+                    bf16x8 kiv[NB], qiv[NB], kjv[NB];
+                    floatx4 gi0[NB], gi1[NB], gj0[NB], gj1[NB];
+#pragma unroll
+                    for (int n = 0; n < NB; n++) {
+                        const int ij = L.pij[min((n0 + n) * PPI + slot, NPAIR - 1)];
+                        pi[n] = ij & 15;
+                        pj[n] = ij >> 4;
+                    }
+#pragma unroll
+                    for (int n = 0; n < NB; n++) {
+                        kiv[n] = ld8(&L.kr[pi[n] * SD + c8]);
+                        qiv[n] = ld8(&L.qr[pi[n] * SD + c8]);
+                        kjv[n] = ld8(&L.kr[pj[n] * SD + c8]);
+                        gi0[n] = ldf4(&L.g[pi[n] * SG + c8]);
+                        gi1[n] = ldf4(&L.g[pi[n] * SG + c8 + 4]);
+                        gj0[n] = ldf4(&L.g[pj[n] * SG + c8]);
+                        gj1[n] = ldf4(&L.g[pj[n] * SG + c8 + 4]);
+                    }
+#pragma unroll
+                    for (int n = 0; n < NB; n++) {
+                        const int i = pi[n], j = pj[n];
+                        float sa = 0.0f, sp = 0.0f;
+#pragma unroll
+                        for (int e = 0; e < 8; e++) {
+                            const float gi = e < 4 ? gi0[n][e] : gi1[n][e - 4];
+                            const float gj = e < 4 ? gj0[n][e] : gj1[n][e - 4];
+                            const float t = (float)kjv[n][e] * __builtin_amdgcn_exp2f(gi - gj);
+                            sa = fmaf((float)kiv[n][e], t, sa);
+                            sp = fmaf((float)qiv[n][e], t, sp);
+                        }
+                        sa = group_sum<LPP>(sa);
+                        sp = group_sum<LPP>(sp);
+                        if (cb == 0 && (n0 + n) * PPI + slot < NPAIR) {
+                            if (j < i) L.at[j * SA + i] = L.beta[i] * sa;
+                            const __bf16 h = (__bf16)sp;
+                            L.ph[kb][i * ST + j] = h;
+                            L.pl[kb][i * ST + j] = (__bf16)(sp - (float)h);
+                        }
+                    }
+                }
+            }
+            if (swork) outputs();
+        }
+        __syncthreads();  // B3: A^T and P of chunk c + 1 complete; ob of chunk c complete
+
+        // ================= phase 4
+        if (kwork) {
+            // U = T1 V and W = T1 (K . 2^G) of chunk c + 1 by forward
+            // substitution (as in prefill_kda_kernel)
+            const bool isw = tid >= D;  // wave-uniform
+            const int ch = isw ? tid - D : tid;
+            float y[KC];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const floatx4 bq = ldf4(&L.beta[4 * q]);
+                if (isw) {
+                    const floatx4 rq = ldf4(&L.kgf[ch * SK + 4 * q]);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) y[4 * q + e] = bq[e] * rq[e];
+                } else {
+                    const bf16x4 rq = ld4(&L.vt[ch * ST + 4 * q]);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) y[4 * q + e] = bq[e] * (float)rq[e];
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                constexpr int HS = KC / 2;
+                floatx4 col[HS][4];
+#pragma unroll
+                for (int s = h * HS; s < min(KC - 1, (h + 1) * HS); s++)
+#pragma unroll
+                    for (int q = (s + 1) / 4; q < 4; q++) col[s - h * HS][q] = ldf4(&L.at[s * SA + 4 * q]);
+#pragma unroll
+                for (int s = h * HS; s < min(KC - 1, (h + 1) * HS); s++)
+#pragma unroll
+                    for (int q = (s + 1) / 4; q < 4; q++)
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            if (4 * q + e > s) y[4 * q + e] = fmaf(-col[s - h * HS][q][e], y[s], y[4 * q + e]);
+            }
+            if (isw) {
+#pragma unroll
+                for (int t = 0; t < KC; t++) {
+                    const float w = -y[t];
+                    const __bf16 h = (__bf16)w;
+                    L.wh[kb][t * SD + ch] = h;
+                    L.wl[kb][t * SD + ch] = (__bf16)(w - (float)h);
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < KC; t++) L.uf[kb][t * SG + ch] = y[t];
+            }
+        }
+        if (swork) state_update();
+        if (swork) {
+            const int c0 = c * KC, nv = min(KC, T - c0);
+            const int x = tid - GT, t = x / (D / 8), c8 = 8 * (x % (D / 8));
+            static_assert(KC * D / 8 <= ST_T, "one 16-byte output piece per state-group thread");
+            if (x < KC * D / 8 && t < nv)
+                *reinterpret_cast<u32x4 *>(og + (size_t)(c0 + t) * tv + c8) =
+                    *reinterpret_cast<const u32x4 *>(&L.ob[t * SD + c8]);
+        }
+        if (!chunk_group && c + 2 < nch) stage_kqg(c1 + KC, tid - GT, nx);  // chunk c + 1 reads K, Q, G no more
+        __syncthreads();  // B4: U, -W of chunk c + 1 complete; chunk c + 2's K, Q, G staged
+    }
+
+    if (!chunk_group) {
+#pragma unroll
+        for (int et = 0; et < ET; et++)
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + 16 * et + ln] = S[et][dt][r];
+    }
+}
+
 hipError_t launch_prefill_kda(const gdnq_desc &d, float *S, const void *q, const void *k, const void *v,
                               const float *a, const float *b, void *o, int T, hipStream_t st)
 {
@@ -640,7 +1108,7 @@ hipError_t launch_prefill_kda(const gdnq_desc &d, float *S, const void *q, const
                      make_divisor((unsigned)(d.H / hk))};
     const unsigned grid = (unsigned)d.B * (unsigned)d.H;
     if (d.dk == 128) {
-        hipLaunchKernelGGL(prefill_kda_kernel<128>, dim3(grid), dim3(kda_threads<128>()), 0, st, A);
+        hipLaunchKernelGGL(prefill_kda_ws_kernel<128>, dim3(grid), dim3(kda_ws_threads<128>()), 0, st, A);
     } else {
         hipLaunchKernelGGL(prefill_kda_kernel<64>, dim3(grid), dim3(kda_threads<64>()), 0, st, A);
     }
