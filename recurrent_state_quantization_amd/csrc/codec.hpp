@@ -63,29 +63,56 @@ __device__ __forceinline__ bool block_any(CodecLds<G> &L, const Lane &c, bool x,
 }
 
 // Which of a thread's 8 rows are DAMP (fp16) rows, their slot in hp_idx and,
-// for the other rows, their index among the compacted INT8 rows.
+// for the other rows, their index among the compacted INT8 rows.  hp lists
+// the n_hp <= 64 DAMP rows strictly ascending (in LDS or global memory, the
+// same list for every thread), so a row's slot and its compacted index both
+// follow from the number of DAMP rows below it.  Lane t of each wave reads
+// hp[t]; the rows go into a DK-bit mask (one word per 32 rows) by an OR
+// across the wave; a thread's rows lie in its wave's words, and each takes
+// a population count of the bits below it.
 struct RowMap {
     int slot[8];   // -1: INT8 row
     int crow[8];   // compacted INT8 row index (valid when slot < 0)
 };
 
-template <class G>
-__device__ __forceinline__ RowMap row_map(const Lane &c, const int *hp_lds, int n_hp)
+__device__ __forceinline__ uint32_t wave_or(uint32_t x)
 {
-    RowMap m;
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, true);  // row_half_mirror
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, true);  // row_mirror
+    return (uint32_t)(__builtin_amdgcn_readlane((int)x, 0) | __builtin_amdgcn_readlane((int)x, 16) |
+                      __builtin_amdgcn_readlane((int)x, 32) | __builtin_amdgcn_readlane((int)x, 48));
+}
+
+template <class G, class P>
+__device__ __forceinline__ RowMap row_map(const Lane &c, P hp, int n_hp)
+{
+    constexpr int NWD = G::DK / 32;
+    const int hv = c.lane < n_hp ? (int)hp[c.lane] : -1;
+    uint32_t m[NWD];
+#pragma unroll
+    for (int w = 0; w < NWD; w++) m[w] = wave_or(hv >= 0 && (hv >> 5) == w ? 1u << (hv & 31) : 0u);
+    RowMap r;
 #pragma unroll
     for (int k = 0; k < 8; k++) {
         const int i = row_of<G>(c, k);
-        int slot = -1, below = 0;
-        for (int t = 0; t < n_hp; t++) {
-            const int h = hp_lds[t];
-            slot = (h == i) ? t : slot;
-            below += (h < i) ? 1 : 0;
+        // the word of row i and the DAMP rows in the words before it
+        // (wave-uniform: the wave's rows span whole words)
+        const int wd = (c.w * G::ROWS_W + (k >> 2) * G::RGW * 4) >> 5;
+        uint32_t word = 0u;
+        int before = 0;
+#pragma unroll
+        for (int w = 0; w < NWD; w++) {
+            word = w == wd ? m[w] : word;
+            before += w < wd ? __builtin_popcount(m[w]) : 0;
         }
-        m.slot[k] = slot;
-        m.crow[k] = i - below;
+        const int b = i & 31;
+        const int below = before + __builtin_popcount(word & ((1u << b) - 1u));
+        r.slot[k] = (word >> b) & 1u ? below : -1;
+        r.crow[k] = i - below;
     }
-    return m;
+    return r;
 }
 
 

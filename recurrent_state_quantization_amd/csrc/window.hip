@@ -254,13 +254,14 @@ __global__ __launch_bounds__(G::NT, (step_min_blocks<BITS, KDA>())) void window_
     if (!KDA && rg < NS) uv16 = slot_vvec_load<G>(A, h, rg, n_hp, c.cb * 8, uvraw);
     __builtin_amdgcn_sched_barrier(0);
 
-    // fixed INT8 tile: the DAMP row map needs the row indices in LDS, so
-    // DAMP loads its codes after the barrier
+    // fixed INT8 tile (DAMP: its row map from the head's row list in global
+    // memory, so that these loads too go out before the first barrier)
     const size_t nrows_c = (size_t)(G::DK - n_hp);
     const int8_t *codes = A.codes + h * nrows_c * code_row_bytes<G, BITS>();
     CodeWord qraw[8];
     RowMap rm;
-    if constexpr (!DAMP) load_tile_codes<G, false, BITS>(codes, c, rm, qraw);
+    if constexpr (DAMP) rm = row_map<G>(c, A.hp_idx + h * n_hp, n_hp);
+    load_tile_codes<G, DAMP, BITS>(codes, c, rm, qraw);
 
     // per-row vectors: gate product, gated k and q (and times the row scale)
     if (c.t < G::DK) {
@@ -281,10 +282,6 @@ __global__ __launch_bounds__(G::NT, (step_min_blocks<BITS, KDA>())) void window_
     if (c.t < G::DV) L.cs[c.t] = cj;
     if (DAMP && c.t < n_hp) L.hp[c.t] = hpi;
     __syncthreads();
-    if constexpr (DAMP) {
-        rm = row_map<G>(c, L.hp, n_hp);
-        load_tile_codes<G, true, BITS>(codes, c, rm, qraw);
-    }
 
     // slot dot products.  A buffered token l gives
     //   alpha_l = ((G_t/G_l) . k_l) . k_t = sum_c k^_l,c m_t,c k_t,c 2^(e_t,c - e_l,c)
