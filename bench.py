@@ -1097,7 +1097,7 @@ def main():
         sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the decode path shards over independent "
-              f"(batch, head) states with no exchange, and this build measures one GPU's share "
+              f"(batch, head) states with no exchange, and this benchmark measures one GPU's share "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
     data = cpu = None

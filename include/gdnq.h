@@ -78,7 +78,7 @@ extern "C" {
 enum {
     GDNQ_OK = 0,
     GDNQ_EINVAL = 1,      /* invalid argument (null, misaligned, overlap, range) */
-    GDNQ_EUNSUPPORTED = 2,/* shape or mode this build does not implement        */
+    GDNQ_EUNSUPPORTED = 2,/* shape or mode the library does not implement       */
     GDNQ_ELAUNCH = 3      /* the HIP runtime reported an error at launch        */
 };
 
