@@ -111,6 +111,41 @@ def test_damp_codec_bit_exact(dk, dv):
     assert np.array_equal(back, oracle.dequantize_damp(Qc, c, rows, hp))
 
 
+@pytest.mark.parametrize("dk,n_hp", [(128, 8), (128, 64), (64, 32), (64, 3)])
+def test_damp_codec_row_lists_at_word_edges(dk, n_hp):
+    """The fp16-row lists the kernels turn into a per-32-row bit mask: rows at
+    the edges of the mask words, whole words listed, the first and last rows,
+    and the largest list a head may carry; codes, scales and rows against
+    the oracle bit for bit."""
+    torch = torch_cuda()
+    g = lib()
+    dv = dk
+    gr = synth.misc_rng(17, n_hp)
+    edges = [0, 31, 32, 63, 64, 95, 96, 127]
+    lists = [
+        [i for i in edges if i < dk],            # word edges (padded below)
+        list(range(n_hp)),                        # the first rows
+        list(range(dk - n_hp, dk)),               # the last rows
+        list(range(0, dk, dk // n_hp))[:n_hp],    # spread evenly
+        list(gr.choice(dk, n_hp, replace=False)), # anywhere
+    ]
+    hp = []
+    for rows in lists:
+        rows = sorted(set(rows))[:n_hp]
+        rest = [i for i in range(dk) if i not in rows]
+        rows = rows + list(gr.choice(rest, n_hp - len(rows), replace=False))
+        hp.append(np.sort(np.array(rows)))
+    hp = np.stack(hp).astype(np.int32)
+    nh = hp.shape[0]
+    X = _uneven(19, nh, dk, dv)
+    d, st, back = _codec_case(torch, g, nh, dk, dv, X, layout=1, hp=hp)
+    Qc, c, rows = oracle.quantize_damp(X, hp)
+    assert np.array_equal(host(st["codes"]).reshape(nh, dk - n_hp, dv), Qc)
+    assert np.array_equal(host(st["col_scale"]).reshape(nh, dv), c)
+    assert np.array_equal(host(st["hp_rows"]).view(np.uint16).reshape(nh, n_hp, dv), rows)
+    assert np.array_equal(back, oracle.dequantize_damp(Qc, c, rows, hp))
+
+
 @pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("r", [1, 2, 4])
 def test_codec_with_compensators(layout, r):
