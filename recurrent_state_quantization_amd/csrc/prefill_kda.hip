@@ -853,8 +853,18 @@ __global__ __launch_bounds__(768, 1) void prefill_kda_ws_kernel(PrefillKdaArgs A
                         split(S[et][2 * k2][r], Sh[et][k2], Sl[et][k2], r);
                         split(S[et][2 * k2 + 1][r], Sh[et][k2], Sl[et][k2], 4 + r);
                     }
+            // the three split-part products of each go to accumulators of
+            // their own (chains of KB instead of 3 KB dependent products),
+            // added on the VALU
+            floatx4 U1[ET], U2[ET], O1[ET], O2[ET];
 #pragma unroll
-            for (int et = 0; et < ET; et++) O[et] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int et = 0; et < ET; et++) {
+                O[et] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                U1[et] = O[et];
+                U2[et] = O[et];
+                O1[et] = O[et];
+                O2[et] = O[et];
+            }
 #pragma unroll
             for (int k2 = 0; k2 < KB; k2++) {
                 const int row = ln * SD + 4 * lg + 32 * k2;
@@ -864,17 +874,16 @@ __global__ __launch_bounds__(768, 1) void prefill_kda_ws_kernel(PrefillKdaArgs A
                 for (int et = 0; et < ET; et++) {
                     U[et] = mma32(wh, Sh[et][k2], U[et]);
                     O[et] = mma32(qh, Sh[et][k2], O[et]);
+                    U1[et] = mma32(wh, Sl[et][k2], U1[et]);
+                    O1[et] = mma32(qh, Sl[et][k2], O1[et]);
+                    U2[et] = mma32(wl, Sh[et][k2], U2[et]);
+                    O2[et] = mma32(ql, Sh[et][k2], O2[et]);
                 }
+            }
 #pragma unroll
-                for (int et = 0; et < ET; et++) {
-                    U[et] = mma32(wh, Sl[et][k2], U[et]);
-                    O[et] = mma32(qh, Sl[et][k2], O[et]);
-                }
-#pragma unroll
-                for (int et = 0; et < ET; et++) {
-                    U[et] = mma32(wl, Sh[et][k2], U[et]);
-                    O[et] = mma32(ql, Sh[et][k2], O[et]);
-                }
+            for (int et = 0; et < ET; et++) {
+                U[et] += U1[et] + U2[et];
+                O[et] += O1[et] + O2[et];
             }
 #pragma unroll
             for (int dt = 0; dt < DT; dt++) {
