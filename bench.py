@@ -125,16 +125,19 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 
 
 def prefill_chunk_flops(D: int, C: int = 64) -> int:
-    """Algorithmic flops of one C-token chunk of one head in the chunk form
-    (each product of the form counted once; the second bf16 parts that keep
-    fp32 accuracy are not counted): K K^T and Q K^T on the 10 lower 16x16
-    tiles, the triangular inverse (forward substitution on four 16x16
-    blocks, then 4 + 12 block products), W and U (C x C x D each),
-    U - W S and Q S (C x D x D each), the causal P U' (6 of 8 32-token
-    blocks) and the state update (D x C x D)."""
-    gram = 2 * 10 * 16 * 16 * D * 2
-    inv = 2 * (4 * 16 * 120 + 16 * 16 * 16 * 16)
-    return gram + inv + 2 * (2 * C * C * D) + 2 * (2 * C * D * D) + (6 * C * C * D * 2) // 8 + 2 * D * C * D
+    """Algorithmic flops of one C-token chunk (C = 64 or 32) of one head in
+    the chunk form (each product of the form counted once; the second bf16
+    parts that keep fp32 accuracy are not counted): K K^T and Q K^T on the
+    lower 16x16 tiles (10 or 3), the triangular inverse (forward
+    substitution on the 16x16 diagonal blocks, then the block merges: 16 or
+    2 block products), the two C x C x D products (W and U, or U and T1 (K S)),
+    the two C x D x D products (W S and Q S, or K S and Q S), the causal
+    P U' (6 of 8 or 3 of 4 blocks) and the state update (D x C x D)."""
+    nb = C // 16
+    gram = 2 * (nb * (nb + 1) // 2) * 16 * 16 * D * 2
+    merges, (pn, pd) = {64: (16, (6, 8)), 32: (2, (3, 4))}[C]
+    inv = 2 * (nb * 16 * 120 + merges * 16 * 16 * 16)
+    return gram + inv + 2 * (2 * C * C * D) + 2 * (2 * C * D * D) + (pn * C * C * D * 2) // pd + 2 * D * C * D
 
 
 def prefill_kda_chunk_flops(D: int, C: int = 16) -> int:
@@ -553,8 +556,9 @@ def bench_prefill(args, torch, g, cfg, x, cpu):
         flops = prefill_kda_chunk_flops(D) * nh * ((T + 15) // 16)
         tag, kernel = "prefill_kda", f"prefill_kda_ws_kernel<{D}>" if D == 128 else f"prefill_kda_kernel<{D}>"
     else:
-        flops = prefill_chunk_flops(D) * nh * ((T + 63) // 64)
-        tag, kernel = "prefill", f"prefill_kernel<{D}>"
+        C = 32 if D == 128 else 64
+        flops = prefill_chunk_flops(D, C) * nh * ((T + C - 1) // C)
+        tag, kernel = "prefill", f"prefill_ws_kernel<{D}>" if D == 128 else f"prefill_kernel<{D}>"
     nbytes = prefill_bytes(cfg, T)
     res = {
         "metric": f"token-head state updates/s, chunkwise {'KDA' if kda else 'GDN'} prefill (1 GPU)",
@@ -1028,6 +1032,8 @@ def kernel_tag(k: str):
     """The benchmark's tag of a kernel name from a rocprofv3 database."""
     if "gdnq::prefill_kda_ws_kernel" in k:   # the two-group form of the per-channel-gate prefill
         return "prefill_kda"
+    if "gdnq::prefill_ws_kernel" in k:       # the two-group form of the scalar-gate prefill
+        return "prefill"
     for tag in ("step_fused", "step_fp32", "window_step", "flush", "prefill_kda", "prefill"):
         if f"gdnq::{tag}_kernel" in k:
             args = [x.strip() for x in k.rstrip(">").split(",")]

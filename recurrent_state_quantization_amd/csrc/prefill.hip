@@ -637,6 +637,509 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kernel(PrefillArgs A)
                 Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + 16 * et + ln] = S[et][dt][r];
 }
 
+// ---------------------------------------------------------------------------
+// Two wave groups, 32-token chunks (D = 128, prefill_ws_kernel).
+//
+// The chunk-local part of a chunk (staging, the A and P tiles, the inverse T
+// and its scaled splits T1, T2) never reads the state, so it runs a chunk
+// ahead of the state part on waves of its own.  Per chunk there are two
+// phases, each closed by a barrier; in iteration c:
+//   phase X  chunk group: the Gram tiles of chunk c+1 (waves 0-2, one 16x16
+//            tile of A and of P each);
+//            state group: chunk c's U' = T2 V - T1 (K S), O = diag(e^g) Q S
+//            + P U' (outputs to LDS) and the state update;
+//   phase Y  chunk group: the inverse of chunk c+1 with T1 and T2 (wave 0:
+//            both 16x16 diagonal blocks by forward substitution, the one
+//            merge and the splits, in-wave through LDS), while waves 1-3
+//            stage chunk c+2 (K, Q, V, the gates) and load chunk c+3;
+//            state group: chunk c's output stores, the split state, and
+//            chunk c+1's K S and Q S.
+// The state group is four waves of 32 value columns; its state stays in MFMA
+// accumulators.  Tiles are double-buffered by chunk parity: a chunk's buffer
+// is written while the chunk is prepared and read until it is finished, and
+// is restaged for chunk c+2 only in phase Y of iteration c.  U' = T2 V -
+// T1 (K S) is the form's U - W S with W S = T1 (K S) taken in the other
+// order: the chunk group then has no D-wide product, and the state group's
+// K S reads its operands in the same pass as Q S.
+constexpr int WC = 32;  // tokens per chunk of the two-group kernel
+
+namespace {
+
+// LDS accesses of one wave complete in issue order: once its own stores have
+// completed, its other lanes read them (and the compiler keeps the order)
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// one staging wave's share of a chunk: 8 pieces of one tensor (16 tokens x
+// 32 channels each, in the A-operand layout), and the gate and beta of
+// token lane
+struct WsRegs {
+    u32x4 x[8];
+    float a, b;
+};
+
+}  // namespace
+
+template <int D>
+struct __attribute__((aligned(16))) WsBuf {
+    static constexpr int SD = D + 8;    // row stride (bf16) of [WC][D] tiles
+    static constexpr int SC = WC + 8;   // row stride (bf16) of [.][WC] tiles
+    __bf16 kr[WC * SD];                 // K, token-major
+    __bf16 qr[WC * SD];                 // Q, token-major
+    __bf16 kt[D * SC];                  // K^T
+    __bf16 vt[D * SC];                  // V^T
+    __bf16 ph[WC * SC], pl[WC * SC];    // P = (Q K^T . Gam . [i >= j]), split
+    __bf16 t1h[WC * SC], t1l[WC * SC];  // T1 = T diag(beta e^g), split
+    __bf16 t2h[WC * SC], t2l[WC * SC];  // T2 = T diag(beta), split
+    float g[WC], eg[WC], gam[WC], beta[WC];
+};
+
+template <int D>
+struct WsLds {
+    static constexpr int SF = WC + 4;   // row stride (fp32) of [WC][WC] tiles
+    WsBuf<D> b[2];                      // by chunk parity
+    float a[WC * SF];                   // A^T of the chunk being inverted
+    float t[WC * SF];                   // its T (lower)
+    __bf16 out[WC * (D + 8)];           // outputs of the chunk being finished
+};
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
+{
+    using Buf = WsBuf<D>;
+    constexpr int SD = Buf::SD, SC = Buf::SC, SF = WsLds<D>::SF;
+    constexpr int NT = 512, GT = 256;  // threads; chunk-group threads
+    constexpr int KB = D / 32, DT = D / 16;
+    static_assert(D == 128, "four state waves of 32 value columns");
+    __shared__ WsLds<D> L;
+
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const unsigned bh = __builtin_amdgcn_workgroup_id_x();
+    const unsigned bb = div_by(bh, A.byH), hh = bh - bb * (unsigned)A.H;
+    const unsigned kh = div_by(hh, A.byG);
+    const int T = A.T;
+    const size_t tk = (size_t)A.HK * D, tv = (size_t)A.H * D;
+    const __bf16 *qg = A.q + (size_t)bb * T * tk + (size_t)kh * D;
+    const __bf16 *kg = A.k + (size_t)bb * T * tk + (size_t)kh * D;
+    const __bf16 *vg = A.v + (size_t)bb * T * tv + (size_t)hh * D;
+    __bf16 *og = A.o + (size_t)bb * T * tv + (size_t)hh * D;
+    const float *ag = A.a + (size_t)bb * T * A.H + hh;
+    const float *bg = A.b + (size_t)bb * T * A.H + hh;
+    float *Sg = A.S + (size_t)bh * D * D;
+    const bool cgroup = wave < 4;
+    const int e0 = 32 * (wave - 4);  // state waves: value columns e0 + 16 et + ln, et = 0, 1
+    int lg = (tid & 63) >> 4, ln = tid & 15;
+    const int nch = (T + WC - 1) / WC;
+
+    // P's upper tile is never written: clear it once in both buffers
+    for (int x = tid; x < WC * SC; x += NT) {
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+            L.b[p].ph[x] = (__bf16)0.0f;
+            L.b[p].pl[x] = (__bf16)0.0f;
+        }
+    }
+
+    // S[et][dt][r] = S[16 dt + 4 lg + r][e0 + 16 et + ln] (state waves)
+    floatx4 S[2][DT];
+
+    // identity operands of the transposes: eye[h] holds B[k][n] = (k == n + 16 h)
+    bf16x8 eye[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) eye[h][i] = (__bf16)(8 * lg + i == ln + 16 * h ? 1.0f : 0.0f);
+
+    // Staging waves 1, 2, 3 load K, Q, V: piece p = token group p / KB (16
+    // tokens), channel block p % KB (32 channels); lane (lg, ln) takes token
+    // 16 tg + ln, channels 32 db + 8 lg .. +7.  Wave 2 also loads the gate
+    // and beta of token lane.  Rows past the end are clamped here and zeroed
+    // when staged.
+    const __bf16 *src = wave == 1 ? kg : (wave == 2 ? qg : vg);
+    const size_t sstr = wave == 3 ? tv : tk;
+    auto load = [=](int c0) {
+        WsRegs r;
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            const int tg = p / KB, db = p % KB;
+            const size_t u = (size_t)min(c0 + 16 * tg + ln, T - 1);
+            r.x[p] = *reinterpret_cast<const u32x4 *>(src + u * sstr + 32 * db + 8 * lg);
+        }
+        r.a = 1.0f;
+        r.b = 0.0f;
+        if (wave == 2) {
+            const size_t ua = (size_t)min(c0 + (tid & 63), T - 1);
+            r.a = ag[ua * A.H];
+            r.b = bg[ua * A.H];
+        }
+        return r;
+    };
+
+    // stage chunk c0 into B: K, Q token-major; K^T, V^T through the matrix
+    // cores (exact: one product by 1 per output); the cumulative log2-gates
+    // (padding: gate 1, beta 0)
+    auto stage = [&](Buf &B, int c0, const WsRegs &r) {
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            const int tg = p / KB, db = p % KB;
+            const u32x4 x = keep(r.x[p], c0 + 16 * tg + ln < T);
+            const int row = (16 * tg + ln) * SD + 32 * db + 8 * lg;
+            if (wave == 1) *reinterpret_cast<u32x4 *>(&B.kr[row]) = x;
+            if (wave == 2) *reinterpret_cast<u32x4 *>(&B.qr[row]) = x;
+            if (wave != 2) {
+                __bf16 *dst = wave == 1 ? B.kt : B.vt;
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const floatx4 tx = mma(__builtin_bit_cast(bf16x8, x), eye[h], floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+                    *reinterpret_cast<bf16x4 *>(&dst[(32 * db + 16 * h + ln) * SC + 16 * tg + 4 * lg]) =
+                        bf16x4{(__bf16)tx[0], (__bf16)tx[1], (__bf16)tx[2], (__bf16)tx[3]};
+                }
+            }
+        }
+        if (wave == 2) {
+            const int lane = tid & 63;
+            const bool ok = lane < WC && c0 + lane < T;
+            const float x = scan64(__builtin_amdgcn_logf(ok ? r.a : 1.0f));
+            const float glast =
+                __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), WC - 1));
+            if (lane < WC) {
+                B.g[lane] = x;
+                B.eg[lane] = __builtin_amdgcn_exp2f(x);
+                B.gam[lane] = __builtin_amdgcn_exp2f(glast - x);
+                B.beta[lane] = ok ? r.b : 0.0f;
+            }
+        }
+    };
+
+    // A = strictly lower diag(beta)(K K^T . Gam), stored transposed (fp32),
+    // and P = (Q K^T . Gam . [i >= j]) (split): tile (I, J) = (0,0), (1,0),
+    // (1,1) on waves 0, 1, 2; lane (lg, ln) holds 4 consecutive i of one j
+    // for A^T and 4 consecutive j of one i for P
+    auto gram = [&](Buf &B) {
+        const int I = wave == 0 ? 0 : 1, J = wave == 2 ? 1 : 0;
+        floatx4 gk = {0.0f, 0.0f, 0.0f, 0.0f}, gq = gk;
+#pragma unroll
+        for (int kb = 0; kb < KB; kb++) {
+            const bf16x8 kj = ld8(&B.kr[(16 * J + ln) * SD + 32 * kb + 8 * lg]);
+            gk = mma(ld8(&B.kr[(16 * I + ln) * SD + 32 * kb + 8 * lg]), kj, gk);
+            gq = mma(kj, ld8(&B.qr[(16 * I + ln) * SD + 32 * kb + 8 * lg]), gq);
+        }
+        {
+            const int i0 = 16 * I + 4 * lg, j = 16 * J + ln;
+            const floatx4 gi = *reinterpret_cast<const floatx4 *>(&B.g[i0]);
+            const floatx4 bi = *reinterpret_cast<const floatx4 *>(&B.beta[i0]);
+            const float gj = B.g[j];
+            floatx4 out;
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                out[r] = i0 + r > j ? (bi[r] * gk[r]) * __builtin_amdgcn_exp2f(gi[r] - gj) : 0.0f;
+            *reinterpret_cast<floatx4 *>(&L.a[j * SF + i0]) = out;
+        }
+        {
+            const int i = 16 * I + ln, j0 = 16 * J + 4 * lg;
+            const float gi = B.g[i];
+            const floatx4 gj = *reinterpret_cast<const floatx4 *>(&B.g[j0]);
+            bf16x4 h, l;
+#pragma unroll
+            for (int r = 0; r < 4; r++) split(i >= j0 + r ? gq[r] * __builtin_amdgcn_exp2f(gi - gj[r]) : 0.0f, h, l, r);
+            *reinterpret_cast<bf16x4 *>(&B.ph[i * SC + j0]) = h;
+            *reinterpret_cast<bf16x4 *>(&B.pl[i * SC + j0]) = l;
+        }
+    };
+
+    // T = (I + A)^{-1} and its scaled splits, on wave 0.  The two diagonal
+    // blocks by forward substitution (lane = block lg < 2, column ln; y = T e_c
+    // - e_c solves y_r = -A_rc - sum_{s<r} A_rs y_s, updated right-looking),
+    // then T[16:32, 0:16] = -T11 A10 T00 on v_mfma_f32_16x16x4f32, then
+    // T1 = T diag(beta e^g), T2 = T diag(beta) split (T's upper part is 0).
+    auto invert = [&](Buf &B) {
+        if (lg < 2) {
+            const float *At = &L.a[16 * lg * SF + 16 * lg];  // At[s * SF + r] = A_rs
+            floatx4 yv[4], col[15][4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) yv[q] = *reinterpret_cast<const floatx4 *>(&At[ln * SF + 4 * q]);
+#pragma unroll
+            for (int s = 0; s < 15; s++)
+#pragma unroll
+                for (int q = (s + 1) / 4; q < 4; q++) col[s][q] = *reinterpret_cast<const floatx4 *>(&At[s * SF + 4 * q]);
+            __builtin_amdgcn_sched_barrier(0);
+            float y[16];
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) y[4 * q + e] = -yv[q][e];
+#pragma unroll
+            for (int s = 0; s < 15; s++)
+#pragma unroll
+                for (int q = (s + 1) / 4; q < 4; q++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        if (4 * q + e > s) y[4 * q + e] = fmaf(-col[s][q][e], y[s], y[4 * q + e]);
+            float *Tb = &L.t[16 * lg * SF + 16 * lg];
+#pragma unroll
+            for (int r = 0; r < 16; r++) Tb[r * SF + ln] = y[r];
+            Tb[ln * SF + ln] = 1.0f;
+        }
+        wave_lds_sync();
+        {
+            floatx4 X = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 4; s++) X = mma4(L.a[(4 * s + lg) * SF + 16 + ln], L.t[(4 * s + lg) * SF + ln], X);
+            floatx4 Y = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 4; s++) Y = mma4(L.t[(16 + ln) * SF + 16 + 4 * lg + s], X[s], Y);
+#pragma unroll
+            for (int r = 0; r < 4; r++) L.t[(16 + 4 * lg + r) * SF + ln] = -Y[r];
+        }
+        wave_lds_sync();
+        const int lane = tid & 63, i = lane >> 1, j0 = 16 * (lane & 1);
+        bf16x8 h1[2], l1[2], h2[2], l2[2];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const floatx4 tq = *reinterpret_cast<const floatx4 *>(&L.t[i * SF + j0 + 4 * q]);
+            const floatx4 bq = *reinterpret_cast<const floatx4 *>(&B.beta[j0 + 4 * q]);
+            const floatx4 eq = *reinterpret_cast<const floatx4 *>(&B.eg[j0 + 4 * q]);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float t = j0 + 4 * q + e <= i ? tq[e] : 0.0f;
+                const float t2 = t * bq[e];
+                const float t1 = t2 * eq[e];
+                split(t1, h1[q / 2], l1[q / 2], 4 * (q % 2) + e);
+                split(t2, h2[q / 2], l2[q / 2], 4 * (q % 2) + e);
+            }
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++) {
+            *reinterpret_cast<bf16x8 *>(&B.t1h[i * SC + j0 + 8 * hf]) = h1[hf];
+            *reinterpret_cast<bf16x8 *>(&B.t1l[i * SC + j0 + 8 * hf]) = l1[hf];
+            *reinterpret_cast<bf16x8 *>(&B.t2h[i * SC + j0 + 8 * hf]) = h2[hf];
+            *reinterpret_cast<bf16x8 *>(&B.t2l[i * SC + j0 + 8 * hf]) = l2[hf];
+        }
+    };
+
+    // K S and Q S of the next chunk: [et][it], lane (lg, ln) holds rows
+    // (tokens) 16 it + 4 lg + r of value column e0 + 16 et + ln
+    floatx4 KS[2][2], QS[2][2];
+    auto state_products = [&](Buf &B) {
+        bf16x8 Sh[2][KB], Sl[2][KB];  // contraction over key rows, permuted slots
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    split(S[et][2 * kb][r], Sh[et][kb], Sl[et][kb], r);
+                    split(S[et][2 * kb + 1][r], Sh[et][kb], Sl[et][kb], 4 + r);
+                }
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int it = 0; it < 2; it++) {
+                KS[et][it] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                QS[et][it] = KS[et][it];
+            }
+#pragma unroll
+        for (int kb = 0; kb < KB; kb++) {
+            bf16x8 ka[2], qa[2];
+#pragma unroll
+            for (int it = 0; it < 2; it++) {
+                const int row = (16 * it + ln) * SD + 32 * kb + 4 * lg;
+                ka[it] = ld_pair(&B.kr[row]);
+                qa[it] = ld_pair(&B.qr[row]);
+            }
+#pragma unroll
+            for (int it = 0; it < 2; it++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) {
+                    KS[et][it] = mma(ka[it], Sh[et][kb], KS[et][it]);
+                    QS[et][it] = mma(qa[it], Sh[et][kb], QS[et][it]);
+                }
+#pragma unroll
+            for (int it = 0; it < 2; it++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) {
+                    KS[et][it] = mma(ka[it], Sl[et][kb], KS[et][it]);
+                    QS[et][it] = mma(qa[it], Sl[et][kb], QS[et][it]);
+                }
+        }
+    };
+
+    // chunk finish on the state group: U' = T2 V - T1 (K S), the outputs
+    // diag(e^g) Q S + P U' (to LDS), S <- e^{g_C} S + K^T diag(e^{g_C - g}) U'
+    auto finish = [&](Buf &B) {
+        bf16x8 Xh[2], Xl[2];  // -(K S) over the chunk's tokens, permuted slots
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                split(-KS[et][0][r], Xh[et], Xl[et], r);
+                split(-KS[et][1][r], Xh[et], Xl[et], 4 + r);
+            }
+        bf16x8 t1h[2], t1l[2], t2h[2], t2l[2], vb[2];
+#pragma unroll
+        for (int it = 0; it < 2; it++) {
+            const int row = (16 * it + ln) * SC + 4 * lg;
+            t1h[it] = ld_pair(&B.t1h[row]);
+            t1l[it] = ld_pair(&B.t1l[row]);
+            t2h[it] = ld_pair(&B.t2h[row]);
+            t2l[it] = ld_pair(&B.t2l[row]);
+        }
+#pragma unroll
+        for (int et = 0; et < 2; et++) vb[et] = ld_pair(&B.vt[(e0 + 16 * et + ln) * SC + 4 * lg]);
+        floatx4 U[2][2];
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int it = 0; it < 2; it++) U[et][it] = mma(t2h[it], vb[et], floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int it = 0; it < 2; it++) U[et][it] = mma(t1h[it], Xh[et], U[et][it]);
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int it = 0; it < 2; it++) U[et][it] = mma(t2l[it], vb[et], U[et][it]);
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int it = 0; it < 2; it++) U[et][it] = mma(t1h[it], Xl[et], U[et][it]);
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int it = 0; it < 2; it++) U[et][it] = mma(t1l[it], Xh[et], U[et][it]);
+        floatx4 O[2][2];
+#pragma unroll
+        for (int it = 0; it < 2; it++) {
+            const floatx4 eg = *reinterpret_cast<const floatx4 *>(&B.eg[16 * it + 4 * lg]);
+#pragma unroll
+            for (int et = 0; et < 2; et++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) O[et][it][r] = QS[et][it][r] * eg[r];
+        }
+        // U' as operands over the chunk's tokens, plain and scaled by e^{g_C - g_j}
+        bf16x8 Vh[2], Vl[2], Gh[2], Gl[2];
+        {
+            const floatx4 ga = *reinterpret_cast<const floatx4 *>(&B.gam[4 * lg]);
+            const floatx4 gc = *reinterpret_cast<const floatx4 *>(&B.gam[16 + 4 * lg]);
+#pragma unroll
+            for (int et = 0; et < 2; et++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    split(U[et][0][r], Vh[et], Vl[et], r);
+                    split(U[et][1][r], Vh[et], Vl[et], 4 + r);
+                    split(U[et][0][r] * ga[r], Gh[et], Gl[et], r);
+                    split(U[et][1][r] * gc[r], Gh[et], Gl[et], 4 + r);
+                }
+        }
+        // O += P U' (P's upper tile is zero)
+        {
+            bf16x8 phv[2], plv[2];
+#pragma unroll
+            for (int it = 0; it < 2; it++) {
+                const int row = (16 * it + ln) * SC + 4 * lg;
+                phv[it] = ld_pair(&B.ph[row]);
+                plv[it] = ld_pair(&B.pl[row]);
+            }
+#pragma unroll
+            for (int it = 0; it < 2; it++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) O[et][it] = mma(phv[it], Vh[et], O[et][it]);
+#pragma unroll
+            for (int it = 0; it < 2; it++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) O[et][it] = mma(phv[it], Vl[et], O[et][it]);
+#pragma unroll
+            for (int it = 0; it < 2; it++)
+#pragma unroll
+                for (int et = 0; et < 2; et++) O[et][it] = mma(plv[it], Vh[et], O[et][it]);
+        }
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int it = 0; it < 2; it++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) L.out[(16 * it + 4 * lg + r) * SD + e0 + 16 * et + ln] = (__bf16)O[et][it][r];
+        const float egc = B.eg[WC - 1];
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) S[et][dt] *= egc;
+        bf16x8 ka[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) ka[dt] = ld_pair(&B.kt[(16 * dt + ln) * SC + 4 * lg]);
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int et = 0; et < 2; et++) S[et][dt] = mma(ka[dt], Gh[et], S[et][dt]);
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int et = 0; et < 2; et++) S[et][dt] = mma(ka[dt], Gl[et], S[et][dt]);
+    };
+
+    // Each group runs its own loop (same trip count, the same two barriers per
+    // iteration), so neither group's registers are held across the other's
+    // code.  Iteration c: chunk c+1 is prepared while chunk c is finished;
+    // chunk c+2 is staged into chunk c's buffer once chunk c no longer reads
+    // it, from registers loaded an iteration earlier.
+    if (cgroup) {
+        WsRegs nx;
+        if (wave >= 1 && nch > 0) nx = load(0);
+        for (int c = -2; c < nch; c++) {
+            asm volatile("" : "+v"(lg), "+v"(ln));
+            Buf &Bk = L.b[(c + 1) & 1];
+            Buf &Bs = L.b[c & 1];
+            const bool prep = c + 1 >= 0 && c + 1 < nch;
+            // ---- phase X
+            if (wave < 3 && prep) gram(Bk);
+            __syncthreads();
+            // ---- phase Y
+            if (wave == 0) {
+                if (prep) invert(Bk);
+            } else if (c + 2 < nch) {
+                stage(Bs, (c + 2) * WC, nx);
+                if (c + 3 < nch) nx = load((c + 3) * WC);
+            }
+            __syncthreads();
+        }
+    } else {
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    S[et][dt][r] = Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + 16 * et + ln];
+        for (int c = -2; c < nch; c++) {
+            asm volatile("" : "+v"(lg), "+v"(ln));
+            Buf &Bk = L.b[(c + 1) & 1];
+            Buf &Bs = L.b[c & 1];
+            // ---- phase X
+            if (c >= 0) finish(Bs);
+            __syncthreads();
+            // ---- phase Y
+            if (c >= 0) {
+                const int c0 = c * WC;
+                for (int x = tid - GT; x < WC * D / 8; x += NT - GT) {
+                    const int t = x / (D / 8), col = 8 * (x % (D / 8));
+                    if (c0 + t < T)
+                        *reinterpret_cast<u32x4 *>(og + (size_t)(c0 + t) * tv + col) =
+                            *reinterpret_cast<const u32x4 *>(&L.out[t * SD + col]);
+                }
+            }
+            if (c + 1 >= 0 && c + 1 < nch) state_products(Bk);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int et = 0; et < 2; et++)
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + 16 * et + ln] = S[et][dt][r];
+    }
+}
+
 hipError_t launch_prefill(const gdnq_desc &d, float *S, const void *q, const void *k, const void *v,
                           const float *a, const float *b, void *o, int T, hipStream_t st)
 {
@@ -655,7 +1158,7 @@ hipError_t launch_prefill(const gdnq_desc &d, float *S, const void *q, const voi
                   make_divisor((unsigned)(d.H / hk))};
     const unsigned grid = (unsigned)d.B * (unsigned)d.H;
     if (d.dk == 128) {
-        hipLaunchKernelGGL(prefill_kernel<128>, dim3(grid), dim3(256), 0, st, A);
+        hipLaunchKernelGGL(prefill_ws_kernel<128>, dim3(grid), dim3(512), 0, st, A);
     } else {
         hipLaunchKernelGGL(prefill_kernel<64>, dim3(grid), dim3(128), 0, st, A);
     }

@@ -2,8 +2,8 @@
 sequential recurrence (oracle.recur: the Gated DeltaNet and KDA rows of
 LinQuant's Table 3 run token by token in fp64).
 
-The kernels compute the same recurrence 64 tokens (scalar gate) or 16
-tokens (per-channel gate) at a time with bf16 matrix products whose fp32
+The kernels compute the same recurrence 32 tokens (scalar gate, D = 128),
+64 tokens (scalar gate, D = 64) or 16 tokens (per-channel gate) at a time with bf16 matrix products whose fp32
 operands are split in two bf16 parts (operand error near 2^-17), so the
 bars are those of fp32 arithmetic on bf16 inputs:
   * state after the last token: l2-relative error per head <= 1e-4;
@@ -103,7 +103,7 @@ DECAYS = ["scalar", "channel"]
 
 
 @pytest.mark.parametrize("decay", DECAYS)
-@pytest.mark.parametrize("D,T", [(128, 150), (128, 64), (128, 37), (128, 16), (128, 1), (64, 200), (64, 128),
+@pytest.mark.parametrize("D,T", [(128, 150), (128, 64), (128, 37), (128, 32), (128, 16), (128, 1), (64, 200), (64, 128),
                                  (64, 9)])
 def test_prefill_parity(D, T, decay):
     cfg = _cfg(2, 3, D, seed=21 + T, decay=decay)
