@@ -654,14 +654,16 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kernel(PrefillArgs A)
 //            stage chunk c+2 (K, Q, V, the gates) and load chunk c+3;
 //            state group: chunk c's output stores, the split state, and
 //            chunk c+1's K S and Q S.
-// The state group is four waves of 32 value columns; its state stays in MFMA
-// accumulators.  Tiles are double-buffered by chunk parity: a chunk's buffer
+// The state group is WS_SW waves of D / WS_SW value columns; its state stays
+// in MFMA accumulators.  Four waves of 32 columns measured faster than eight
+// of 16 (each LDS operand read then feeds two accumulators).  Tiles are double-buffered by chunk parity: a chunk's buffer
 // is written while the chunk is prepared and read until it is finished, and
 // is restaged for chunk c+2 only in phase Y of iteration c.  U' = T2 V -
 // T1 (K S) is the form's U - W S with W S = T1 (K S) taken in the other
 // order: the chunk group then has no D-wide product, and the state group's
 // K S reads its operands in the same pass as Q S.
-constexpr int WC = 32;  // tokens per chunk of the two-group kernel
+constexpr int WC = 32;     // tokens per chunk of the two-group kernel
+constexpr int WS_SW = 4;   // its state waves (D / WS_SW value columns each)
 
 namespace {
 
@@ -703,13 +705,14 @@ struct WsLds {
 };
 
 template <int D>
-__global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
+__global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(PrefillArgs A)
 {
     using Buf = WsBuf<D>;
     constexpr int SD = Buf::SD, SC = Buf::SC, SF = WsLds<D>::SF;
-    constexpr int NT = 512, GT = 256;  // threads; chunk-group threads
+    constexpr int NT = 64 * (4 + WS_SW), GT = 256;  // threads; chunk-group threads
+    constexpr int ET = D / 16 / WS_SW;               // 16-column tiles per state wave
     constexpr int KB = D / 32, DT = D / 16;
-    static_assert(D == 128, "four state waves of 32 value columns");
+    static_assert(D == 128 && ET >= 1 && ET * 16 * WS_SW == D, "state waves split the value columns");
     __shared__ WsLds<D> L;
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
@@ -727,7 +730,7 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
     const float *bg = A.b + (size_t)bb * T * A.H + hh;
     float *Sg = A.S + (size_t)bh * D * D;
     const bool cgroup = wave < 4;
-    const int e0 = 32 * (wave - 4);  // state waves: value columns e0 + 16 et + ln, et = 0, 1
+    const int e0 = 16 * ET * (wave - 4);  // state waves: value columns e0 + 16 et + ln, et < ET
     int lg = (tid & 63) >> 4, ln = tid & 15;
     const int nch = (T + WC - 1) / WC;
 
@@ -741,7 +744,7 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
     }
 
     // S[et][dt][r] = S[16 dt + 4 lg + r][e0 + 16 et + ln] (state waves)
-    floatx4 S[2][DT];
+    floatx4 S[ET][DT];
 
     // identity operands of the transposes: eye[h] holds B[k][n] = (k == n + 16 h)
     bf16x8 eye[2];
@@ -855,26 +858,38 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
     auto invert = [&](Buf &B) {
         if (lg < 2) {
             const float *At = &L.a[16 * lg * SF + 16 * lg];  // At[s * SF + r] = A_rs
+            // the columns of steps 0-6 are loaded up front, those of steps
+            // 7-14 once steps 0-2 have freed their registers
             floatx4 yv[4], col[15][4];
+            auto load_cols = [&](int s0, int s1) {
+#pragma unroll
+                for (int s = s0; s < s1; s++)
+#pragma unroll
+                    for (int q = (s + 1) / 4; q < 4; q++) col[s][q] = *reinterpret_cast<const floatx4 *>(&At[s * SF + 4 * q]);
+            };
+            float y[16];
+            auto steps = [&](int s0, int s1) {
+#pragma unroll
+                for (int s = s0; s < s1; s++)
+#pragma unroll
+                    for (int q = (s + 1) / 4; q < 4; q++)
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            if (4 * q + e > s) y[4 * q + e] = fmaf(-col[s][q][e], y[s], y[4 * q + e]);
+            };
 #pragma unroll
             for (int q = 0; q < 4; q++) yv[q] = *reinterpret_cast<const floatx4 *>(&At[ln * SF + 4 * q]);
-#pragma unroll
-            for (int s = 0; s < 15; s++)
-#pragma unroll
-                for (int q = (s + 1) / 4; q < 4; q++) col[s][q] = *reinterpret_cast<const floatx4 *>(&At[s * SF + 4 * q]);
+            load_cols(0, 7);
             __builtin_amdgcn_sched_barrier(0);
-            float y[16];
 #pragma unroll
             for (int q = 0; q < 4; q++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) y[4 * q + e] = -yv[q][e];
-#pragma unroll
-            for (int s = 0; s < 15; s++)
-#pragma unroll
-                for (int q = (s + 1) / 4; q < 4; q++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        if (4 * q + e > s) y[4 * q + e] = fmaf(-col[s][q][e], y[s], y[4 * q + e]);
+            steps(0, 3);
+            __builtin_amdgcn_sched_barrier(0);
+            load_cols(7, 15);
+            __builtin_amdgcn_sched_barrier(0);
+            steps(3, 15);
             float *Tb = &L.t[16 * lg * SF + 16 * lg];
 #pragma unroll
             for (int r = 0; r < 16; r++) Tb[r * SF + ln] = y[r];
@@ -919,11 +934,11 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
 
     // K S and Q S of the next chunk: [et][it], lane (lg, ln) holds rows
     // (tokens) 16 it + 4 lg + r of value column e0 + 16 et + ln
-    floatx4 KS[2][2], QS[2][2];
+    floatx4 KS[ET][2], QS[ET][2];
     auto state_products = [&](Buf &B) {
-        bf16x8 Sh[2][KB], Sl[2][KB];  // contraction over key rows, permuted slots
+        bf16x8 Sh[ET][KB], Sl[ET][KB];  // contraction over key rows, permuted slots
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int kb = 0; kb < KB; kb++)
 #pragma unroll
@@ -932,7 +947,7 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
                     split(S[et][2 * kb + 1][r], Sh[et][kb], Sl[et][kb], 4 + r);
                 }
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int it = 0; it < 2; it++) {
                 KS[et][it] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -950,14 +965,14 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
 #pragma unroll
             for (int it = 0; it < 2; it++)
 #pragma unroll
-                for (int et = 0; et < 2; et++) {
+                for (int et = 0; et < ET; et++) {
                     KS[et][it] = mma(ka[it], Sh[et][kb], KS[et][it]);
                     QS[et][it] = mma(qa[it], Sh[et][kb], QS[et][it]);
                 }
 #pragma unroll
             for (int it = 0; it < 2; it++)
 #pragma unroll
-                for (int et = 0; et < 2; et++) {
+                for (int et = 0; et < ET; et++) {
                     KS[et][it] = mma(ka[it], Sl[et][kb], KS[et][it]);
                     QS[et][it] = mma(qa[it], Sl[et][kb], QS[et][it]);
                 }
@@ -967,15 +982,15 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
     // chunk finish on the state group: U' = T2 V - T1 (K S), the outputs
     // diag(e^g) Q S + P U' (to LDS), S <- e^{g_C} S + K^T diag(e^{g_C - g}) U'
     auto finish = [&](Buf &B) {
-        bf16x8 Xh[2], Xl[2];  // -(K S) over the chunk's tokens, permuted slots
+        bf16x8 Xh[ET], Xl[ET];  // -(K S) over the chunk's tokens, permuted slots
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 split(-KS[et][0][r], Xh[et], Xl[et], r);
                 split(-KS[et][1][r], Xh[et], Xl[et], 4 + r);
             }
-        bf16x8 t1h[2], t1l[2], t2h[2], t2l[2], vb[2];
+        bf16x8 t1h[2], t1l[2], t2h[2], t2l[2], vb[ET];
 #pragma unroll
         for (int it = 0; it < 2; it++) {
             const int row = (16 * it + ln) * SC + 4 * lg;
@@ -985,44 +1000,44 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
             t2l[it] = ld_pair(&B.t2l[row]);
         }
 #pragma unroll
-        for (int et = 0; et < 2; et++) vb[et] = ld_pair(&B.vt[(e0 + 16 * et + ln) * SC + 4 * lg]);
-        floatx4 U[2][2];
+        for (int et = 0; et < ET; et++) vb[et] = ld_pair(&B.vt[(e0 + 16 * et + ln) * SC + 4 * lg]);
+        floatx4 U[ET][2];
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int it = 0; it < 2; it++) U[et][it] = mma(t2h[it], vb[et], floatx4{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int it = 0; it < 2; it++) U[et][it] = mma(t1h[it], Xh[et], U[et][it]);
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int it = 0; it < 2; it++) U[et][it] = mma(t2l[it], vb[et], U[et][it]);
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int it = 0; it < 2; it++) U[et][it] = mma(t1h[it], Xl[et], U[et][it]);
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int it = 0; it < 2; it++) U[et][it] = mma(t1l[it], Xh[et], U[et][it]);
-        floatx4 O[2][2];
+        floatx4 O[ET][2];
 #pragma unroll
         for (int it = 0; it < 2; it++) {
             const floatx4 eg = *reinterpret_cast<const floatx4 *>(&B.eg[16 * it + 4 * lg]);
 #pragma unroll
-            for (int et = 0; et < 2; et++)
+            for (int et = 0; et < ET; et++)
 #pragma unroll
                 for (int r = 0; r < 4; r++) O[et][it][r] = QS[et][it][r] * eg[r];
         }
         // U' as operands over the chunk's tokens, plain and scaled by e^{g_C - g_j}
-        bf16x8 Vh[2], Vl[2], Gh[2], Gl[2];
+        bf16x8 Vh[ET], Vl[ET], Gh[ET], Gl[ET];
         {
             const floatx4 ga = *reinterpret_cast<const floatx4 *>(&B.gam[4 * lg]);
             const floatx4 gc = *reinterpret_cast<const floatx4 *>(&B.gam[16 + 4 * lg]);
 #pragma unroll
-            for (int et = 0; et < 2; et++)
+            for (int et = 0; et < ET; et++)
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     split(U[et][0][r], Vh[et], Vl[et], r);
@@ -1043,25 +1058,25 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
 #pragma unroll
             for (int it = 0; it < 2; it++)
 #pragma unroll
-                for (int et = 0; et < 2; et++) O[et][it] = mma(phv[it], Vh[et], O[et][it]);
+                for (int et = 0; et < ET; et++) O[et][it] = mma(phv[it], Vh[et], O[et][it]);
 #pragma unroll
             for (int it = 0; it < 2; it++)
 #pragma unroll
-                for (int et = 0; et < 2; et++) O[et][it] = mma(phv[it], Vl[et], O[et][it]);
+                for (int et = 0; et < ET; et++) O[et][it] = mma(phv[it], Vl[et], O[et][it]);
 #pragma unroll
             for (int it = 0; it < 2; it++)
 #pragma unroll
-                for (int et = 0; et < 2; et++) O[et][it] = mma(plv[it], Vh[et], O[et][it]);
+                for (int et = 0; et < ET; et++) O[et][it] = mma(plv[it], Vh[et], O[et][it]);
         }
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int it = 0; it < 2; it++)
 #pragma unroll
                 for (int r = 0; r < 4; r++) L.out[(16 * it + 4 * lg + r) * SD + e0 + 16 * et + ln] = (__bf16)O[et][it][r];
         const float egc = B.eg[WC - 1];
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int dt = 0; dt < DT; dt++) S[et][dt] *= egc;
         bf16x8 ka[DT];
@@ -1070,21 +1085,33 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
 #pragma unroll
         for (int dt = 0; dt < DT; dt++)
 #pragma unroll
-            for (int et = 0; et < 2; et++) S[et][dt] = mma(ka[dt], Gh[et], S[et][dt]);
+            for (int et = 0; et < ET; et++) S[et][dt] = mma(ka[dt], Gh[et], S[et][dt]);
 #pragma unroll
         for (int dt = 0; dt < DT; dt++)
 #pragma unroll
-            for (int et = 0; et < 2; et++) S[et][dt] = mma(ka[dt], Gl[et], S[et][dt]);
+            for (int et = 0; et < ET; et++) S[et][dt] = mma(ka[dt], Gl[et], S[et][dt]);
     };
 
-    // Each group runs its own loop (same trip count, the same two barriers per
-    // iteration), so neither group's registers are held across the other's
-    // code.  Iteration c: chunk c+1 is prepared while chunk c is finished;
+    // Wave 0, the staging waves and the state group each run a loop of their
+    // own (same trip count, the same two barriers per iteration), so no
+    // role's registers are held across another role's code.  Iteration c: chunk c+1 is prepared while chunk c is finished;
     // chunk c+2 is staged into chunk c's buffer once chunk c no longer reads
     // it, from registers loaded an iteration earlier.
-    if (cgroup) {
+    if (wave == 0) {
+        for (int c = -2; c < nch; c++) {
+            asm volatile("" : "+v"(lg), "+v"(ln));
+            Buf &Bk = L.b[(c + 1) & 1];
+            const bool prep = c + 1 >= 0 && c + 1 < nch;
+            // ---- phase X
+            if (prep) gram(Bk);
+            __syncthreads();
+            // ---- phase Y
+            if (prep) invert(Bk);
+            __syncthreads();
+        }
+    } else if (cgroup) {
         WsRegs nx;
-        if (wave >= 1 && nch > 0) nx = load(0);
+        if (nch > 0) nx = load(0);
         for (int c = -2; c < nch; c++) {
             asm volatile("" : "+v"(lg), "+v"(ln));
             Buf &Bk = L.b[(c + 1) & 1];
@@ -1094,9 +1121,7 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
             if (wave < 3 && prep) gram(Bk);
             __syncthreads();
             // ---- phase Y
-            if (wave == 0) {
-                if (prep) invert(Bk);
-            } else if (c + 2 < nch) {
+            if (c + 2 < nch) {
                 stage(Bs, (c + 2) * WC, nx);
                 if (c + 3 < nch) nx = load((c + 3) * WC);
             }
@@ -1104,7 +1129,7 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
         }
     } else {
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int dt = 0; dt < DT; dt++)
 #pragma unroll
@@ -1131,7 +1156,7 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs A)
             __syncthreads();
         }
 #pragma unroll
-        for (int et = 0; et < 2; et++)
+        for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int dt = 0; dt < DT; dt++)
 #pragma unroll
@@ -1158,7 +1183,7 @@ hipError_t launch_prefill(const gdnq_desc &d, float *S, const void *q, const voi
                   make_divisor((unsigned)(d.H / hk))};
     const unsigned grid = (unsigned)d.B * (unsigned)d.H;
     if (d.dk == 128) {
-        hipLaunchKernelGGL(prefill_ws_kernel<128>, dim3(grid), dim3(512), 0, st, A);
+        hipLaunchKernelGGL(prefill_ws_kernel<128>, dim3(grid), dim3(64 * (4 + WS_SW)), 0, st, A);
     } else {
         hipLaunchKernelGGL(prefill_kernel<64>, dim3(grid), dim3(128), 0, st, A);
     }
