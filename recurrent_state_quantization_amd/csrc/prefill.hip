@@ -647,13 +647,13 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kernel(PrefillArgs A)
 //   phase X  chunk group: the Gram tiles of chunk c+1 (waves 0-2, one 16x16
 //            tile of A and of P each);
 //            state group: chunk c's U' = T2 V - T1 (K S), O = diag(e^g) Q S
-//            + P U' (outputs to LDS) and the state update;
+//            + P U' and its stores (each wave its own columns, through
+//            LDS), and the state update;
 //   phase Y  chunk group: the inverse of chunk c+1 with T1 and T2 (wave 0:
 //            both 16x16 diagonal blocks by forward substitution, the one
 //            merge and the splits, in-wave through LDS), while waves 1-3
 //            stage chunk c+2 (K, Q, V, the gates) and load chunk c+3;
-//            state group: chunk c's output stores, the split state, and
-//            chunk c+1's K S and Q S.
+//            state group: the split state and chunk c+1's K S and Q S.
 // The state group is WS_SW waves of D / WS_SW value columns; its state stays
 // in MFMA accumulators.  Four waves of 32 columns measured faster than eight
 // of 16 (each LDS operand read then feeds two accumulators).  Tiles are double-buffered by chunk parity: a chunk's buffer
@@ -701,7 +701,7 @@ struct WsLds {
     WsBuf<D> b[2];                      // by chunk parity
     float a[WC * SF];                   // A^T of the chunk being inverted
     float t[WC * SF];                   // its T (lower)
-    __bf16 out[WC * (D + 8)];           // outputs of the chunk being finished
+    __bf16 out[WC * (D + 8)];           // outputs of the chunk being finished (per wave, its columns)
 };
 
 template <int D>
@@ -709,7 +709,7 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
 {
     using Buf = WsBuf<D>;
     constexpr int SD = Buf::SD, SC = Buf::SC, SF = WsLds<D>::SF;
-    constexpr int NT = 64 * (4 + WS_SW), GT = 256;  // threads; chunk-group threads
+    constexpr int NT = 64 * (4 + WS_SW);             // threads (waves 0-3: chunk group)
     constexpr int ET = D / 16 / WS_SW;               // 16-column tiles per state wave
     constexpr int KB = D / 32, DT = D / 16;
     static_assert(D == 128 && ET >= 1 && ET * 16 * WS_SW == D, "state waves split the value columns");
@@ -981,7 +981,7 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
 
     // chunk finish on the state group: U' = T2 V - T1 (K S), the outputs
     // diag(e^g) Q S + P U' (to LDS), S <- e^{g_C} S + K^T diag(e^{g_C - g}) U'
-    auto finish = [&](Buf &B) {
+    auto finish = [&](Buf &B, int c0) {
         bf16x8 Xh[ET], Xl[ET];  // -(K S) over the chunk's tokens, permuted slots
 #pragma unroll
         for (int et = 0; et < ET; et++)
@@ -1068,12 +1068,26 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
 #pragma unroll
                 for (int et = 0; et < ET; et++) O[et][it] = mma(plv[it], Vh[et], O[et][it]);
         }
+        // outputs: each wave writes its own columns to LDS and reads them back
+        // as 16-byte rows (no other wave touches them, so no barrier)
 #pragma unroll
         for (int et = 0; et < ET; et++)
 #pragma unroll
             for (int it = 0; it < 2; it++)
 #pragma unroll
                 for (int r = 0; r < 4; r++) L.out[(16 * it + 4 * lg + r) * SD + e0 + 16 * et + ln] = (__bf16)O[et][it][r];
+        wave_lds_sync();
+        {
+            constexpr int VPT = 2 * ET;  // 16-byte pieces per token row of the wave's columns
+            const int lane = tid & 63;
+#pragma unroll
+            for (int x = lane; x < WC * VPT; x += 64) {
+                const int t = x / VPT, col = e0 + 8 * (x % VPT);
+                if (c0 + t < T)
+                    *reinterpret_cast<u32x4 *>(og + (size_t)(c0 + t) * tv + col) =
+                        *reinterpret_cast<const u32x4 *>(&L.out[t * SD + col]);
+            }
+        }
         const float egc = B.eg[WC - 1];
 #pragma unroll
         for (int et = 0; et < ET; et++)
@@ -1140,18 +1154,9 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
             Buf &Bk = L.b[(c + 1) & 1];
             Buf &Bs = L.b[c & 1];
             // ---- phase X
-            if (c >= 0) finish(Bs);
+            if (c >= 0) finish(Bs, c * WC);
             __syncthreads();
             // ---- phase Y
-            if (c >= 0) {
-                const int c0 = c * WC;
-                for (int x = tid - GT; x < WC * D / 8; x += NT - GT) {
-                    const int t = x / (D / 8), col = 8 * (x % (D / 8));
-                    if (c0 + t < T)
-                        *reinterpret_cast<u32x4 *>(og + (size_t)(c0 + t) * tv + col) =
-                            *reinterpret_cast<const u32x4 *>(&L.out[t * SD + col]);
-                }
-            }
             if (c + 1 >= 0 && c + 1 < nch) state_products(Bk);
             __syncthreads();
         }
