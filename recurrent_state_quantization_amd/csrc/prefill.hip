@@ -644,14 +644,14 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kernel(PrefillArgs A)
 // and its scaled splits T1, T2) never reads the state, so it runs a chunk
 // ahead of the state part on waves of its own.  Per chunk there are two
 // phases, each closed by a barrier; in iteration c:
-//   phase X  chunk group: the Gram tiles of chunk c+1 (waves 0-2, one 16x16
-//            tile of A and of P each);
+//   phase X  chunk group: the Gram tiles of chunk c+1 (waves 0-2), wave 0
+//            taking A's three tiles and from them T's diagonal blocks
+//            (forward substitution) and its one block merge, in-wave
+//            through LDS;
 //            state group: chunk c's U' = T2 V - T1 (K S), O = diag(e^g) Q S
 //            + P U' and its stores (each wave its own columns, through
 //            LDS), and the state update;
-//   phase Y  chunk group: the inverse of chunk c+1 with T1 and T2 (wave 0:
-//            both 16x16 diagonal blocks by forward substitution, the one
-//            merge and the splits, in-wave through LDS), while waves 1-3
+//   phase Y  chunk group: T1 and T2 of chunk c+1 (wave 0), while waves 1-3
 //            stage chunk c+2 (K, Q, V, the gates) and load chunk c+3;
 //            state group: the split state and chunk c+1's K S and Q S.
 // The state group is WS_SW waves of D / WS_SW value columns; its state stays
@@ -815,47 +815,46 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
     };
 
     // A = strictly lower diag(beta)(K K^T . Gam), stored transposed (fp32),
-    // and P = (Q K^T . Gam . [i >= j]) (split): tile (I, J) = (0,0), (1,0),
-    // (1,1) on waves 0, 1, 2; lane (lg, ln) holds 4 consecutive i of one j
-    // for A^T and 4 consecutive j of one i for P
-    auto gram = [&](Buf &B) {
-        const int I = wave == 0 ? 0 : 1, J = wave == 2 ? 1 : 0;
-        floatx4 gk = {0.0f, 0.0f, 0.0f, 0.0f}, gq = gk;
+    // and P = (Q K^T . Gam . [i >= j]) (split), one lower 16x16 tile (I, J)
+    // each: wave 0 takes A's three tiles, wave 1 P(0,0) and P(1,0), wave 2
+    // P(1,1).  Lane (lg, ln) holds 4 consecutive i of one j
+    // for A^T and 4 consecutive j of one i for P.
+    auto gram_a = [&](Buf &B, int I, int J) {
+        floatx4 gk = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kb = 0; kb < KB; kb++) {
-            const bf16x8 kj = ld8(&B.kr[(16 * J + ln) * SD + 32 * kb + 8 * lg]);
-            gk = mma(ld8(&B.kr[(16 * I + ln) * SD + 32 * kb + 8 * lg]), kj, gk);
-            gq = mma(kj, ld8(&B.qr[(16 * I + ln) * SD + 32 * kb + 8 * lg]), gq);
-        }
-        {
-            const int i0 = 16 * I + 4 * lg, j = 16 * J + ln;
-            const floatx4 gi = *reinterpret_cast<const floatx4 *>(&B.g[i0]);
-            const floatx4 bi = *reinterpret_cast<const floatx4 *>(&B.beta[i0]);
-            const float gj = B.g[j];
-            floatx4 out;
+        for (int kb = 0; kb < KB; kb++)
+            gk = mma(ld8(&B.kr[(16 * I + ln) * SD + 32 * kb + 8 * lg]), ld8(&B.kr[(16 * J + ln) * SD + 32 * kb + 8 * lg]), gk);
+        const int i0 = 16 * I + 4 * lg, j = 16 * J + ln;
+        const floatx4 gi = *reinterpret_cast<const floatx4 *>(&B.g[i0]);
+        const floatx4 bi = *reinterpret_cast<const floatx4 *>(&B.beta[i0]);
+        const float gj = B.g[j];
+        floatx4 out;
 #pragma unroll
-            for (int r = 0; r < 4; r++)
-                out[r] = i0 + r > j ? (bi[r] * gk[r]) * __builtin_amdgcn_exp2f(gi[r] - gj) : 0.0f;
-            *reinterpret_cast<floatx4 *>(&L.a[j * SF + i0]) = out;
-        }
-        {
-            const int i = 16 * I + ln, j0 = 16 * J + 4 * lg;
-            const float gi = B.g[i];
-            const floatx4 gj = *reinterpret_cast<const floatx4 *>(&B.g[j0]);
-            bf16x4 h, l;
+        for (int r = 0; r < 4; r++) out[r] = i0 + r > j ? (bi[r] * gk[r]) * __builtin_amdgcn_exp2f(gi[r] - gj) : 0.0f;
+        *reinterpret_cast<floatx4 *>(&L.a[j * SF + i0]) = out;
+    };
+    auto gram_p = [&](Buf &B, int I, int J) {
+        floatx4 gq = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int r = 0; r < 4; r++) split(i >= j0 + r ? gq[r] * __builtin_amdgcn_exp2f(gi - gj[r]) : 0.0f, h, l, r);
-            *reinterpret_cast<bf16x4 *>(&B.ph[i * SC + j0]) = h;
-            *reinterpret_cast<bf16x4 *>(&B.pl[i * SC + j0]) = l;
-        }
+        for (int kb = 0; kb < KB; kb++)
+            gq = mma(ld8(&B.kr[(16 * J + ln) * SD + 32 * kb + 8 * lg]), ld8(&B.qr[(16 * I + ln) * SD + 32 * kb + 8 * lg]), gq);
+        const int i = 16 * I + ln, j0 = 16 * J + 4 * lg;
+        const float gi = B.g[i];
+        const floatx4 gj = *reinterpret_cast<const floatx4 *>(&B.g[j0]);
+        bf16x4 h, l;
+#pragma unroll
+        for (int r = 0; r < 4; r++) split(i >= j0 + r ? gq[r] * __builtin_amdgcn_exp2f(gi - gj[r]) : 0.0f, h, l, r);
+        *reinterpret_cast<bf16x4 *>(&B.ph[i * SC + j0]) = h;
+        *reinterpret_cast<bf16x4 *>(&B.pl[i * SC + j0]) = l;
     };
 
-    // T = (I + A)^{-1} and its scaled splits, on wave 0.  The two diagonal
-    // blocks by forward substitution (lane = block lg < 2, column ln; y = T e_c
-    // - e_c solves y_r = -A_rc - sum_{s<r} A_rs y_s, updated right-looking),
-    // then T[16:32, 0:16] = -T11 A10 T00 on v_mfma_f32_16x16x4f32, then
-    // T1 = T diag(beta e^g), T2 = T diag(beta) split (T's upper part is 0).
-    auto invert = [&](Buf &B) {
+    // T = (I + A)^{-1} and its scaled splits, on wave 0.  invert_diag: the two
+    // diagonal blocks by forward substitution (lane = block lg < 2, column ln;
+    // y = T e_c - e_c solves y_r = -A_rc - sum_{s<r} A_rs y_s, updated
+    // right-looking); invert_merge: T[16:32, 0:16] = -T11 A10 T00 on
+    // v_mfma_f32_16x16x4f32; invert_split: T1 = T diag(beta e^g),
+    // T2 = T diag(beta) split (T's upper part is 0).
+    auto invert_diag = [&]() {
         if (lg < 2) {
             const float *At = &L.a[16 * lg * SF + 16 * lg];  // At[s * SF + r] = A_rs
             // the columns of steps 0-6 are loaded up front, those of steps
@@ -895,7 +894,8 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
             for (int r = 0; r < 16; r++) Tb[r * SF + ln] = y[r];
             Tb[ln * SF + ln] = 1.0f;
         }
-        wave_lds_sync();
+    };
+    auto invert_merge = [&]() {
         {
             floatx4 X = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -906,7 +906,8 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
 #pragma unroll
             for (int r = 0; r < 4; r++) L.t[(16 + 4 * lg + r) * SF + ln] = -Y[r];
         }
-        wave_lds_sync();
+    };
+    auto invert_split = [&](Buf &B) {
         const int lane = tid & 63, i = lane >> 1, j0 = 16 * (lane & 1);
         bf16x8 h1[2], l1[2], h2[2], l2[2];
 #pragma unroll
@@ -1116,11 +1117,19 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
             asm volatile("" : "+v"(lg), "+v"(ln));
             Buf &Bk = L.b[(c + 1) & 1];
             const bool prep = c + 1 >= 0 && c + 1 < nch;
-            // ---- phase X
-            if (prep) gram(Bk);
+            // ---- phase X: A, T's diagonal blocks and the merge (in-wave)
+            if (prep) {
+                gram_a(Bk, 0, 0);
+                gram_a(Bk, 1, 1);
+                gram_a(Bk, 1, 0);
+                wave_lds_sync();
+                invert_diag();
+                wave_lds_sync();
+                invert_merge();
+            }
             __syncthreads();
-            // ---- phase Y
-            if (prep) invert(Bk);
+            // ---- phase Y: T1, T2
+            if (prep) invert_split(Bk);
             __syncthreads();
         }
     } else if (cgroup) {
@@ -1132,7 +1141,14 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
             Buf &Bs = L.b[c & 1];
             const bool prep = c + 1 >= 0 && c + 1 < nch;
             // ---- phase X
-            if (wave < 3 && prep) gram(Bk);
+            if (prep) {
+                if (wave == 1) {
+                    gram_p(Bk, 0, 0);
+                    gram_p(Bk, 1, 0);
+                } else if (wave == 2) {
+                    gram_p(Bk, 1, 1);
+                }
+            }
             __syncthreads();
             // ---- phase Y
             if (c + 2 < nch) {
