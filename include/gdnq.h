@@ -309,8 +309,9 @@ int gdn_fp32_decode_step(const gdnq_desc *desc, float *S, const void *q, const v
  * Recurrences", abstract: chunkwise-parallel prefill casts most of the
  * recurrence as dense matrix products; appendix Table 3, Gated DeltaNet and
  * KDA rows).  Runs T tokens of the recurrence for all B*H heads at once,
- * chunk by chunk on the matrix cores (64 tokens per chunk for the scalar
- * gate, 16 for the per-channel gate), and writes every token's output:
+ * chunk by chunk on the matrix cores (32 tokens per chunk for the scalar
+ * gate at dk = 128, 64 at dk = 64, 16 for the per-channel gate), and writes
+ * every token's output:
  *   S      device fp32 [B,H,dk,dv], in place: the state before token 0 on
  *          entry (zeros for a new sequence, gdn_state_dequantize's output to
  *          continue a cached prefix), the state after token T-1 on return.

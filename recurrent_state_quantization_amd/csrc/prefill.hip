@@ -30,18 +30,20 @@
 // lo = bf16(x - hi) (x - hi is exact in fp32), and a product takes hi*y +
 // lo*y, or hi*hi' + hi*lo' + lo*hi' when both operands are split, leaving
 // a relative operand error near 2^-17.  The unit lower-triangular inverse
-// runs in fp32: forward substitution on the 16x16 diagonal blocks, then two
-// block-merge levels on v_mfma_f32_16x16x4f32.
+// runs in fp32: forward substitution on the 16x16 diagonal blocks, then
+// block merges on v_mfma_f32_16x16x4f32.
 //
-// Mapping: one workgroup per (batch, head) walks the chunks in order.  Wave
-// w owns value columns 16w..16w+15 of the state, which stays in fp32 MFMA
-// accumulators for the whole sequence: every state-dependent product
-// (U' = U - W S, Q S, the state update) needs only the wave's own columns,
-// and the accumulators feed the next product's operand directly by
-// permuting the contraction index (slots 0..3 of lane group g take
-// k = 4g..4g+3 of one 16-row tile, slots 4..7 those of the next tile; the
-// LDS operand on the other side is read in the same order).  The chunk-local
-// part (K K^T, Q K^T, the inverse, W) is shared through LDS.
+// Two kernels: prefill_kernel (below, 64-token chunks, one group of waves,
+// used for D = 64) and prefill_ws_kernel (further down, 32-token chunks, a
+// chunk group and a state group of waves, used for D = 128).  In both, one
+// workgroup per (batch, head) walks the chunks in order and each state wave
+// owns 32 value columns of the state, which stay in fp32 MFMA accumulators
+// for the whole sequence: every state-dependent product needs only the
+// wave's own columns, and the accumulators feed the next product's operand
+// directly by permuting the contraction index (slots 0..3 of lane group g
+// take k = 4g..4g+3 of one 16-row tile, slots 4..7 those of the next tile;
+// the LDS operand on the other side is read in the same order).  The
+// chunk-local part (K K^T, Q K^T, the inverse) is shared through LDS.
 #include <hip/hip_runtime.h>
 
 #include "launch.hpp"
@@ -1109,9 +1111,10 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
 
     // Wave 0, the staging waves and the state group each run a loop of their
     // own (same trip count, the same two barriers per iteration), so no
-    // role's registers are held across another role's code.  Iteration c: chunk c+1 is prepared while chunk c is finished;
-    // chunk c+2 is staged into chunk c's buffer once chunk c no longer reads
-    // it, from registers loaded an iteration earlier.
+    // role's registers are held across another role's code.  Iteration c:
+    // chunk c+1 is prepared while chunk c is finished; chunk c+2 is staged
+    // into chunk c's buffer once chunk c no longer reads it, from registers
+    // loaded an iteration earlier.
     if (wave == 0) {
         for (int c = -2; c < nch; c++) {
             asm volatile("" : "+v"(lg), "+v"(ln));
