@@ -16,7 +16,7 @@ the identity gates (a = 1, b = 0 keep the state bit for bit), sampled heads
 of the full-size workloads; and T = 0, prefill followed by
 gdn_state_quantize, a per-channel gate whose channels are all equal (the
 scalar-gate kernel's result within the bars), and gates small enough that
-a chunk's decay underflows.
+a chunk's decay underflows (either gate).
 """
 import numpy as np
 import pytest
@@ -169,6 +169,37 @@ def test_prefill_kda_underflowing_gates():
     S = dev(S0.copy())
     o = torch.empty((1, T, 2, 128), dtype=torch.bfloat16, device="cuda")
     say("prefill kda small gates")
+    g.gdn_prefill(desc_for(cfg), S, _bf16_dev(inp["q16"]), _bf16_dev(inp["k16"]), _bf16_dev(inp["v16"]),
+                  dev(inp["a_dev"]), dev(inp["b_dev"]), o, T)
+    torch.cuda.synchronize()
+    o_host = synth.bf16_to_f32(o.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert np.isfinite(host(S)).all()
+    _check(cfg, T, inp, host(S), o_host, S0)
+
+
+def test_prefill_underflowing_scalar_gates():
+    """Scalar gates small enough that a 32-token chunk's decay leaves fp32's
+    range: head 0 has eight gates of 1e-6 in a row inside its second chunk
+    (a decay near 2^-160, so 2^g of the chunk's later tokens and
+    2^(g_C - g) of its earlier ones flush to zero), head 1 a gate drawn from
+    U[1e-4, 1] at one token in ten; T = 100 leaves a ragged last chunk."""
+    cfg = _cfg(1, 2, 128, seed=49)
+    T = 100
+    S0 = synth.random_states(21, 2, 128, 128, scale=0.5)
+    inp = _inputs(cfg, T)
+    a = inp["a"].copy()                                   # [T, B*H, 1]
+    a[40:48, 0, 0] = 1e-6
+    rng = synth.misc_rng(49, 1)
+    small = rng.uniform(1e-4, 1.0, T).astype(np.float32)
+    pick = rng.uniform(size=T) < 0.1
+    a[pick, 1, 0] = small[pick]
+    inp["a"] = a
+    inp["a_dev"] = np.ascontiguousarray(np.swapaxes(a[..., 0].reshape(T, 1, 2), 0, 1))
+    torch = torch_cuda()
+    g = lib()
+    S = dev(S0.copy())
+    o = torch.empty((1, T, 2, 128), dtype=torch.bfloat16, device="cuda")
+    say("prefill scalar small gates")
     g.gdn_prefill(desc_for(cfg), S, _bf16_dev(inp["q16"]), _bf16_dev(inp["k16"]), _bf16_dev(inp["v16"]),
                   dev(inp["a_dev"]), dev(inp["b_dev"]), o, T)
     torch.cuda.synchronize()
