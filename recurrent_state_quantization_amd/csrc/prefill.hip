@@ -658,9 +658,10 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kernel(PrefillArgs A)
 //            state group: the split state and chunk c+1's K S and Q S.
 // The state group is WS_SW waves of D / WS_SW value columns; its state stays
 // in MFMA accumulators.  Four waves of 32 columns measured faster than eight
-// of 16 (each LDS operand read then feeds two accumulators).  Tiles are double-buffered by chunk parity: a chunk's buffer
-// is written while the chunk is prepared and read until it is finished, and
-// is restaged for chunk c+2 only in phase Y of iteration c.  U' = T2 V -
+// of 16 (each LDS operand read then feeds two accumulators).  Tiles are
+// double-buffered by chunk parity: a chunk's buffer is written while the
+// chunk is prepared and read until it is finished, and is restaged for
+// chunk c+2 only in phase Y of iteration c.  U' = T2 V -
 // T1 (K S) is the form's U - W S with W S = T1 (K S) taken in the other
 // order: the chunk group then has no D-wide product, and the state group's
 // K S reads its operands in the same pass as Q S.
@@ -819,8 +820,8 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
     // A = strictly lower diag(beta)(K K^T . Gam), stored transposed (fp32),
     // and P = (Q K^T . Gam . [i >= j]) (split), one lower 16x16 tile (I, J)
     // each: wave 0 takes A's three tiles, wave 1 P(0,0) and P(1,0), wave 2
-    // P(1,1).  Lane (lg, ln) holds 4 consecutive i of one j
-    // for A^T and 4 consecutive j of one i for P.
+    // P(1,1).  Lane (lg, ln) holds 4 consecutive i of one j for A^T and 4
+    // consecutive j of one i for P.
     auto gram_a = [&](Buf &B, int I, int J) {
         floatx4 gk = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -983,7 +984,8 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
     };
 
     // chunk finish on the state group: U' = T2 V - T1 (K S), the outputs
-    // diag(e^g) Q S + P U' (to LDS), S <- e^{g_C} S + K^T diag(e^{g_C - g}) U'
+    // diag(e^g) Q S + P U' (stored by each wave for its columns), and
+    // S <- e^{g_C} S + K^T diag(e^{g_C - g}) U'
     auto finish = [&](Buf &B, int c0) {
         bf16x8 Xh[ET], Xl[ET];  // -(K S) over the chunk's tokens, permuted slots
 #pragma unroll
