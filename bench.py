@@ -994,19 +994,26 @@ def summarize_counters(db: str):
     for k, cn, v in rows:
         agg[k.split("(")[0]][cn].append(v)
     names = sorted({cn for d in agg.values() for cn in d})
-    print("| kernel | dispatches | " + " | ".join(names) + " | VALU/wave | VALU busy |")
-    print("|---|---|" + "---|" * (len(names) + 2))
+    mcol = "SQ_VALU_MFMA_BUSY_CYCLES" in names
+    print("| kernel | dispatches | " + " | ".join(names) + " | VALU/wave | VALU busy |"
+          + (" matrix busy |" if mcol else ""))
+    print("|---|---|" + "---|" * (len(names) + 2 + mcol))
     found = {}
     for k, d in sorted(agg.items()):
         m = {cn: float(np.mean(v)) for cn, v in d.items()}
         per_wave = m["SQ_INSTS_VALU"] / m["SQ_WAVES"] if "SQ_INSTS_VALU" in m and m.get("SQ_WAVES") else None
+        # GRBM_GUI_ACTIVE sums the 8 XCDs; SQ_ACTIVE_INST_VALU sums the 256 CUs
+        # and SQ_VALU_MFMA_BUSY_CYCLES the 1024 SIMDs (matrix pipes)
         busy = (m["SQ_ACTIVE_INST_VALU"] / 256 / (m["GRBM_GUI_ACTIVE"] / 8)
                 if "SQ_ACTIVE_INST_VALU" in m and m.get("GRBM_GUI_ACTIVE") else None)
+        mbusy = (m["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / (m["GRBM_GUI_ACTIVE"] / 8)
+                 if "SQ_VALU_MFMA_BUSY_CYCLES" in m and m.get("GRBM_GUI_ACTIVE") else None)
         n = len(next(iter(d.values())))
         cells = " | ".join(f"{m[cn]:.4g}" if cn in m else "" for cn in names)
         pw = f"{per_wave:.1f}" if per_wave is not None else ""
         bz = f"{100 * busy:.1f}%" if busy is not None else ""
-        print(f"| {k} | {n} | {cells} | {pw} | {bz} |")
+        mb = (f" {100 * mbusy:.1f}% |" if mbusy is not None else " |") if mcol else ""
+        print(f"| {k} | {n} | {cells} | {pw} | {bz} |{mb}")
         if per_wave is not None and busy is not None:
             found[k] = (per_wave, busy)
     return found
