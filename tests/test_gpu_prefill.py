@@ -103,7 +103,7 @@ DECAYS = ["scalar", "channel"]
 
 
 @pytest.mark.parametrize("decay", DECAYS)
-@pytest.mark.parametrize("D,T", [(128, 150), (128, 64), (128, 37), (128, 32), (128, 16), (128, 1), (64, 200), (64, 128),
+@pytest.mark.parametrize("D,T", [(128, 150), (128, 65), (128, 64), (128, 37), (128, 32), (128, 16), (128, 1), (64, 200), (64, 128),
                                  (64, 9)])
 def test_prefill_parity(D, T, decay):
     cfg = _cfg(2, 3, D, seed=21 + T, decay=decay)
