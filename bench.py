@@ -506,8 +506,8 @@ def bench_prefix_cache(args, torch, g, cfg, S, inputs, cpu):
     return res
 
 
-def prefill_data(name: str = "prefill"):
-    cfg = synth.WORKLOADS[name]
+def prefill_data(name: str = "prefill", batch: int = 0):
+    cfg = dict(synth.WORKLOADS[name], **({"B": batch} if batch else {}))
     log(f"generating {cfg['T']} tokens x {cfg['B'] * cfg['H']} heads of prefill input")
     return cfg, synth.token_major_inputs(cfg, cfg["T"])
 
@@ -558,7 +558,11 @@ def bench_prefill(args, torch, g, cfg, x, cpu):
     else:
         C = 32 if D == 128 else 64
         flops = prefill_chunk_flops(D, C) * nh * ((T + C - 1) // C)
-        tag, kernel = "prefill", f"prefill_ws_kernel<{D}>" if D == 128 else f"prefill_kernel<{D}>"
+        # dk = 128: workgroups per head as the library picks them (the most of
+        # 4, 2, 1 with one workgroup per CU); their chunk-local work repeats
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+        ns = 4 if nh * 4 <= ncu else 2 if nh * 2 <= ncu else 1
+        tag, kernel = "prefill", f"prefill_ws_kernel<{D}, {ns}>" if D == 128 else f"prefill_kernel<{D}>"
     nbytes = prefill_bytes(cfg, T)
     res = {
         "metric": f"token-head state updates/s, chunkwise {'KDA' if kda else 'GDN'} prefill (1 GPU)",
@@ -573,7 +577,7 @@ def bench_prefill(args, torch, g, cfg, x, cpu):
                    "B": B, "H": H, "T": T, "dk": D},
         "roofline": {"bound": "mfma", "achieved": flops / per / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / per / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": stored_traffic(tag, tag),
+                     "traffic": stored_traffic(tag, tag) if B == synth.WORKLOADS[tag]["B"] else None,
                      "kernel": kernel, "algorithmic_flops_per_launch": flops,
                      "mean_launch_s": per},
         "hbm": {"algorithmic_bytes_per_launch": nbytes, "achieved_GBs": nbytes / per / 1e9,
@@ -1065,6 +1069,8 @@ def main():
     ap.add_argument("--workload", default="prefix_cache",
                     choices=["prefix_cache", "gdn_serving", "kda", "damp", "tiny", "prefill", "prefill_kda"])
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="prefill workloads: sequences per call in place of the workload's B")
     ap.add_argument("--bits", type=int, default=8, choices=[8, 6, 4],
                     help="code width of the quantized state (default 8)")
     ap.add_argument("--pool", type=int, default=0,
@@ -1129,7 +1135,7 @@ def main():
         log(f"timing the CPU oracle on {args.workload}")
         wcpu[args.workload] = cpu_window_baseline(args.workload)
     if args.workload in ("prefill", "prefill_kda") and not args.copy_calibration:
-        data = prefill_data(args.workload)
+        data = prefill_data(args.workload, args.batch)
         cpu = None
         if not args.no_cpu:
             log("timing the CPU oracle")

@@ -707,20 +707,26 @@ struct WsLds {
     __bf16 out[WC * (D + 8)];           // outputs of the chunk being finished (per wave, its columns)
 };
 
-template <int D>
-__global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(PrefillArgs A)
+// NS workgroups share a head (NS = 1, 2, 4): each prepares every chunk in
+// full (the chunk-local work is small) and finishes D / NS of the head's value
+// columns, so a batch of fewer heads than CUs still fills the chip.
+template <int D, int NS>
+__global__ __launch_bounds__(64 * (4 + WS_SW / NS), 1) void prefill_ws_kernel(PrefillArgs A)
 {
     using Buf = WsBuf<D>;
     constexpr int SD = Buf::SD, SC = Buf::SC, SF = WsLds<D>::SF;
-    constexpr int NT = 64 * (4 + WS_SW);             // threads (waves 0-3: chunk group)
+    constexpr int NT = 64 * (4 + WS_SW / NS);        // threads (waves 0-3: chunk group)
     constexpr int ET = D / 16 / WS_SW;               // 16-column tiles per state wave
     constexpr int KB = D / 32, DT = D / 16;
     static_assert(D == 128 && ET >= 1 && ET * 16 * WS_SW == D, "state waves split the value columns");
+    static_assert(NS >= 1 && WS_SW % NS == 0, "each workgroup keeps whole state waves");
     __shared__ WsLds<D> L;
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const unsigned bh = __builtin_amdgcn_workgroup_id_x();
+    const unsigned gid = __builtin_amdgcn_workgroup_id_x();
+    const unsigned bh = gid / NS;                    // the head
+    const int part = (int)(gid % NS);                // its share of the value columns
     const unsigned bb = div_by(bh, A.byH), hh = bh - bb * (unsigned)A.H;
     const unsigned kh = div_by(hh, A.byG);
     const int T = A.T;
@@ -733,7 +739,11 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
     const float *bg = A.b + (size_t)bb * T * A.H + hh;
     float *Sg = A.S + (size_t)bh * D * D;
     const bool cgroup = wave < 4;
-    const int e0 = 16 * ET * (wave - 4);  // state waves: value columns e0 + 16 et + ln, et < ET
+    // chunk-group role: 0 Gram tiles of A and the inverse, 1 K, 2 Q and the
+    // gates, 3 V.  With fewer than four state waves, role 0 goes to the
+    // SIMD of wave 3, which then hosts no state wave.
+    const int role = NS > 1 ? (wave + 1) & 3 : wave;
+    const int e0 = part * (D / NS) + 16 * ET * (wave - 4);  // state waves: value columns e0 + 16 et + ln
     int lg = (tid & 63) >> 4, ln = tid & 15;
     const int nch = (T + WC - 1) / WC;
 
@@ -761,8 +771,8 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
     // 16 tg + ln, channels 32 db + 8 lg .. +7.  Wave 2 also loads the gate
     // and beta of token lane.  Rows past the end are clamped here and zeroed
     // when staged.
-    const __bf16 *src = wave == 1 ? kg : (wave == 2 ? qg : vg);
-    const size_t sstr = wave == 3 ? tv : tk;
+    const __bf16 *src = role == 1 ? kg : (role == 2 ? qg : vg);
+    const size_t sstr = role == 3 ? tv : tk;
     auto load = [=](int c0) {
         WsRegs r;
 #pragma unroll
@@ -773,7 +783,7 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
         }
         r.a = 1.0f;
         r.b = 0.0f;
-        if (wave == 2) {
+        if (role == 2) {
             const size_t ua = (size_t)min(c0 + (tid & 63), T - 1);
             r.a = ag[ua * A.H];
             r.b = bg[ua * A.H];
@@ -790,10 +800,10 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
             const int tg = p / KB, db = p % KB;
             const u32x4 x = keep(r.x[p], c0 + 16 * tg + ln < T);
             const int row = (16 * tg + ln) * SD + 32 * db + 8 * lg;
-            if (wave == 1) *reinterpret_cast<u32x4 *>(&B.kr[row]) = x;
-            if (wave == 2) *reinterpret_cast<u32x4 *>(&B.qr[row]) = x;
-            if (wave != 2) {
-                __bf16 *dst = wave == 1 ? B.kt : B.vt;
+            if (role == 1) *reinterpret_cast<u32x4 *>(&B.kr[row]) = x;
+            if (role == 2) *reinterpret_cast<u32x4 *>(&B.qr[row]) = x;
+            if (role != 2) {
+                __bf16 *dst = role == 1 ? B.kt : B.vt;
 #pragma unroll
                 for (int h = 0; h < 2; h++) {
                     const floatx4 tx = mma(__builtin_bit_cast(bf16x8, x), eye[h], floatx4{0.0f, 0.0f, 0.0f, 0.0f});
@@ -802,7 +812,7 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
                 }
             }
         }
-        if (wave == 2) {
+        if (role == 2) {
             const int lane = tid & 63;
             const bool ok = lane < WC && c0 + lane < T;
             const float x = scan64(__builtin_amdgcn_logf(ok ? r.a : 1.0f));
@@ -1117,7 +1127,7 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
     // chunk c+1 is prepared while chunk c is finished; chunk c+2 is staged
     // into chunk c's buffer once chunk c no longer reads it, from registers
     // loaded an iteration earlier.
-    if (wave == 0) {
+    if (cgroup && role == 0) {
         for (int c = -2; c < nch; c++) {
             asm volatile("" : "+v"(lg), "+v"(ln));
             Buf &Bk = L.b[(c + 1) & 1];
@@ -1147,10 +1157,10 @@ __global__ __launch_bounds__(64 * (4 + WS_SW), 1) void prefill_ws_kernel(Prefill
             const bool prep = c + 1 >= 0 && c + 1 < nch;
             // ---- phase X
             if (prep) {
-                if (wave == 1) {
+                if (role == 1) {
                     gram_p(Bk, 0, 0);
                     gram_p(Bk, 1, 0);
-                } else if (wave == 2) {
+                } else if (role == 2) {
                     gram_p(Bk, 1, 1);
                 }
             }
@@ -1209,7 +1219,18 @@ hipError_t launch_prefill(const gdnq_desc &d, float *S, const void *q, const voi
                   make_divisor((unsigned)(d.H / hk))};
     const unsigned grid = (unsigned)d.B * (unsigned)d.H;
     if (d.dk == 128) {
-        hipLaunchKernelGGL(prefill_ws_kernel<128>, dim3(grid), dim3(64 * (4 + WS_SW)), 0, st, A);
+        // workgroups per head: the most of 1, 2, 4 that keeps one workgroup per CU
+        int dev = 0, ncu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        const unsigned ns = grid * 4u <= (unsigned)ncu ? 4u : grid * 2u <= (unsigned)ncu ? 2u : 1u;
+        if (ns == 4)
+            hipLaunchKernelGGL((prefill_ws_kernel<128, 4>), dim3(grid * 4), dim3(64 * (4 + WS_SW / 4)), 0, st, A);
+        else if (ns == 2)
+            hipLaunchKernelGGL((prefill_ws_kernel<128, 2>), dim3(grid * 2), dim3(64 * (4 + WS_SW / 2)), 0, st, A);
+        else
+            hipLaunchKernelGGL((prefill_ws_kernel<128, 1>), dim3(grid), dim3(64 * (4 + WS_SW)), 0, st, A);
     } else {
         hipLaunchKernelGGL(prefill_kernel<64>, dim3(grid), dim3(128), 0, st, A);
     }

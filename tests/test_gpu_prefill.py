@@ -241,6 +241,22 @@ def test_prefill_kda_chunk_paths():
     _check(cfg, T, inp, host(S), o_host, S0)
 
 
+@pytest.mark.parametrize("part", ["quarter", "half", "half+1"])
+def test_prefill_heads_per_cu_splits(part):
+    """With fewer heads than CUs, dk = 128 splits each head's value columns
+    over 4 (heads <= CUs/4) or 2 (heads <= CUs/2) workgroups, each redoing
+    the chunk-local work: head counts on both sides of those lines, against
+    the oracle."""
+    torch = torch_cuda()
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    H = {"quarter": ncu // 4, "half": ncu // 2, "half+1": ncu // 2 + 1}[part]
+    cfg = _cfg(1, H, 128, seed=57)
+    T = 40
+    S0 = synth.random_states(27, H, 128, 128, scale=0.5)
+    inp, S, o = _run(cfg, T, S0)
+    _check(cfg, T, inp, S, o, S0)
+
+
 def test_prefill_empty_is_noop():
     torch = torch_cuda()
     g = lib()
