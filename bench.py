@@ -552,16 +552,16 @@ def bench_prefill(args, torch, g, cfg, x, cpu):
     log("timing the prefill")
     settle(torch, call, min_calls=20, min_s=0.3)
     wall, per, _, _ = time_launches(torch, call, args.steps, args.warmup)
+    # dk = 128: workgroups per head as the library picks them (the most of 4,
+    # 2, 1 with one workgroup per CU); their chunk-local work repeats
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    ns = 4 if nh * 4 <= ncu else 2 if nh * 2 <= ncu else 1
     if kda:
         flops = prefill_kda_chunk_flops(D) * nh * ((T + 15) // 16)
-        tag, kernel = "prefill_kda", f"prefill_kda_ws_kernel<{D}>" if D == 128 else f"prefill_kda_kernel<{D}>"
+        tag, kernel = "prefill_kda", f"prefill_kda_ws_kernel<{D}, {ns}>" if D == 128 else f"prefill_kda_kernel<{D}>"
     else:
         C = 32 if D == 128 else 64
         flops = prefill_chunk_flops(D, C) * nh * ((T + C - 1) // C)
-        # dk = 128: workgroups per head as the library picks them (the most of
-        # 4, 2, 1 with one workgroup per CU); their chunk-local work repeats
-        ncu = torch.cuda.get_device_properties(0).multi_processor_count
-        ns = 4 if nh * 4 <= ncu else 2 if nh * 2 <= ncu else 1
         tag, kernel = "prefill", f"prefill_ws_kernel<{D}, {ns}>" if D == 128 else f"prefill_kernel<{D}>"
     nbytes = prefill_bytes(cfg, T)
     res = {

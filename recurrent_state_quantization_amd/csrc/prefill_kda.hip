@@ -676,17 +676,33 @@ struct KdaWsLds {
     int pairwise;
 };
 
-template <int D>
-constexpr int kda_ws_threads() { return 768; }
+// One staging thread's share of a chunk: PPT 8-byte pieces of each of K, Q
+// and V, and for the last D threads the gates of one key channel and, for
+// channel c < KC, b of token c.
+template <int PPT>
+struct KdaWsRegs {
+    u32x2 k[PPT], q[PPT], v[PPT];
+    float a[KC];
+    float b;
+};
 
-template <int D>
-__global__ __launch_bounds__(768, 1) void prefill_kda_ws_kernel(PrefillKdaArgs A)
+// threads per workgroup: the chunk group's 4 waves and 8 / NS state waves
+template <int NS>
+constexpr int kda_ws_threads() { return 64 * (4 + 8 / NS); }
+
+// NS workgroups share a head (NS = 1, 2, 4) when a call has fewer heads than
+// CUs: each prepares every chunk in full and finishes D / NS of the head's
+// value columns.
+template <int D, int NS>
+__global__ __launch_bounds__(kda_ws_threads<NS>(), 1) void prefill_kda_ws_kernel(PrefillKdaArgs A)
 {
     static_assert(D == 128, "two groups of four waves: D = 128");
     using Lds = KdaWsLds<D>;
     constexpr int SD = Lds::SD, SG = Lds::SG, ST = Lds::ST, SK = Lds::SK;
-    constexpr int NT = 768, GT = 256;         // threads, threads of the chunk group
+    constexpr int NT = kda_ws_threads<NS>(), GT = 256;  // threads, threads of the chunk group
     constexpr int ST_T = NT - GT;             // threads of the state group (they also stage)
+    constexpr int PPT = KC * D / 4 / ST_T;    // 8-byte pieces of each of K, Q, V per staging thread
+    static_assert(PPT * ST_T == KC * D / 4 && ST_T >= D, "the state group stages whole chunks");
     constexpr int ET = 1;                     // 16-column tiles of the state per state wave
     constexpr int KB = D / 32;                // 32-wide blocks along a head dim
     constexpr int DT = D / 16;                // 16-row tiles along a head dim
@@ -695,7 +711,9 @@ __global__ __launch_bounds__(768, 1) void prefill_kda_ws_kernel(PrefillKdaArgs A
     const int tid0 = (int)__builtin_amdgcn_workitem_id_x();
     const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const bool chunk_group = wave < 4;        // wave-uniform
-    const unsigned bh = __builtin_amdgcn_workgroup_id_x();
+    const unsigned gid = __builtin_amdgcn_workgroup_id_x();
+    const unsigned bh = gid / NS;             // the head
+    const int part = (int)(gid % NS);         // its share of the value columns
     const unsigned bb = div_by(bh, A.byH), hh = bh - bb * (unsigned)A.H;
     const unsigned kh = div_by(hh, A.byG);
     const int T = A.T;
@@ -708,7 +726,7 @@ __global__ __launch_bounds__(768, 1) void prefill_kda_ws_kernel(PrefillKdaArgs A
     const float *ag = A.a + (size_t)bb * T * tv + (size_t)hh * D;
     const float *bg = A.b + (size_t)bb * T * A.H + hh;
     float *Sg = A.S + (size_t)bh * D * D;
-    const int e0 = 16 * (wave - 4);  // state group: value columns e0 + 16 et + ln
+    const int e0 = part * (D / NS) + 16 * (wave - 4);  // state group: value columns e0 + 16 et + ln
     int lg = (tid0 & 63) >> 4, ln = tid0 & 15;
 
     for (int x = tid0; x < 2 * KC * ST; x += NT) {
@@ -723,13 +741,17 @@ __global__ __launch_bounds__(768, 1) void prefill_kda_ws_kernel(PrefillKdaArgs A
     }
     __syncthreads();  // the first chunk's staging may set the flag
 
-    auto load_chunk = [=](int c0, int tid, KdaChunkRegs &r) {
-        const int t = tid / (D / 4), c = 4 * (tid % (D / 4));
-        const size_t u = (size_t)min(c0 + t, T - 1);
-        r.k = *reinterpret_cast<const u32x2 *>(kg + u * tk + c);
-        r.q = *reinterpret_cast<const u32x2 *>(qg + u * tk + c);
-        const int tv_ = tid % KC, cv = 4 * (tid / KC);
-        r.v = *reinterpret_cast<const u32x2 *>(vg + (size_t)min(c0 + tv_, T - 1) * tv + cv);
+    auto load_chunk = [=](int c0, int tid, KdaWsRegs<PPT> &r) {
+#pragma unroll
+        for (int p = 0; p < PPT; p++) {
+            const int x = tid + p * ST_T;
+            const int t = x / (D / 4), c = 4 * (x % (D / 4));
+            const size_t u = (size_t)min(c0 + t, T - 1);
+            r.k[p] = *reinterpret_cast<const u32x2 *>(kg + u * tk + c);
+            r.q[p] = *reinterpret_cast<const u32x2 *>(qg + u * tk + c);
+            const int tv_ = x % KC, cv = 4 * (x / KC);
+            r.v[p] = *reinterpret_cast<const u32x2 *>(vg + (size_t)min(c0 + tv_, T - 1) * tv + cv);
+        }
         const int cg = tid - (ST_T - D);
         if (cg >= 0) {
 #pragma unroll
@@ -737,15 +759,18 @@ __global__ __launch_bounds__(768, 1) void prefill_kda_ws_kernel(PrefillKdaArgs A
             r.b = bg[(size_t)min(c0 + (cg & (KC - 1)), T - 1) * A.H];
         }
     };
-    static_assert(KC * D / 4 == ST_T, "one 8-byte piece of K, Q and V per state-group thread");
     // K, Q (token-major, zero past the end) and the gates: cumulative
     // log2-gates from the chunk start (padding gate 1), the pairwise flag
-    auto stage_kqg = [&](int cs, int tid, const KdaChunkRegs &r) {
+    auto stage_kqg = [&](int cs, int tid, const KdaWsRegs<PPT> &r) {
         const int nv = min(KC, T - cs);
-        const int t = tid / (D / 4), c = 4 * (tid % (D / 4));
         const u32x2 z = {0u, 0u};
-        *reinterpret_cast<u32x2 *>(&L.kr[t * SD + c]) = t < nv ? r.k : z;
-        *reinterpret_cast<u32x2 *>(&L.qr[t * SD + c]) = t < nv ? r.q : z;
+#pragma unroll
+        for (int p = 0; p < PPT; p++) {
+            const int x = tid + p * ST_T;
+            const int t = x / (D / 4), c = 4 * (x % (D / 4));
+            *reinterpret_cast<u32x2 *>(&L.kr[t * SD + c]) = t < nv ? r.k[p] : z;
+            *reinterpret_cast<u32x2 *>(&L.qr[t * SD + c]) = t < nv ? r.q[p] : z;
+        }
         if (const int cg = tid - (ST_T - D); cg >= 0) {
             float acc = 0.0f;
 #pragma unroll
@@ -757,13 +782,17 @@ __global__ __launch_bounds__(768, 1) void prefill_kda_ws_kernel(PrefillKdaArgs A
         }
     };
     // V^T (zero past the end) and beta
-    auto stage_vb = [&](int cs, int tid, const KdaChunkRegs &r) {
+    auto stage_vb = [&](int cs, int tid, const KdaWsRegs<PPT> &r) {
         const int nv = min(KC, T - cs);
         const u32x2 z = {0u, 0u};
-        const int tv_ = tid % KC, cv = 4 * (tid / KC);
-        const bf16x4 vv = __builtin_bit_cast(bf16x4, tv_ < nv ? r.v : z);
 #pragma unroll
-        for (int e = 0; e < 4; e++) L.vt[(cv + e) * ST + tv_] = vv[e];
+        for (int p = 0; p < PPT; p++) {
+            const int x = tid + p * ST_T;
+            const int tv_ = x % KC, cv = 4 * (x / KC);
+            const bf16x4 vv = __builtin_bit_cast(bf16x4, tv_ < nv ? r.v[p] : z);
+#pragma unroll
+            for (int e = 0; e < 4; e++) L.vt[(cv + e) * ST + tv_] = vv[e];
+        }
         if (const int cg = tid - (ST_T - D); cg >= 0 && cg < KC) L.beta[cg] = cg < nv ? r.b : 0.0f;
     };
 
@@ -777,7 +806,7 @@ __global__ __launch_bounds__(768, 1) void prefill_kda_ws_kernel(PrefillKdaArgs A
                 for (int r = 0; r < 4; r++)
                     S[et][dt][r] = Sg[(size_t)(16 * dt + 4 * lg + r) * D + e0 + 16 * et + ln];
     }
-    KdaChunkRegs nx;
+    KdaWsRegs<PPT> nx;
     if (!chunk_group) {
         load_chunk(0, tid0 - GT, nx);
         stage_kqg(0, tid0 - GT, nx);
@@ -1077,10 +1106,12 @@ __global__ __launch_bounds__(768, 1) void prefill_kda_ws_kernel(PrefillKdaArgs A
         }
         if (swork) state_update();
         if (swork) {
+            // the workgroup's columns: PW 16-byte pieces per token row
+            constexpr int PW = D / NS / 8;
             const int c0 = c * KC, nv = min(KC, T - c0);
-            const int x = tid - GT, t = x / (D / 8), c8 = 8 * (x % (D / 8));
-            static_assert(KC * D / 8 <= ST_T, "one 16-byte output piece per state-group thread");
-            if (x < KC * D / 8 && t < nv)
+            const int x = tid - GT, t = x / PW, c8 = part * (D / NS) + 8 * (x % PW);
+            static_assert(KC * PW <= ST_T, "one 16-byte output piece per state-group thread");
+            if (x < KC * PW && t < nv)
                 *reinterpret_cast<u32x4 *>(og + (size_t)(c0 + t) * tv + c8) =
                     *reinterpret_cast<const u32x4 *>(&L.ob[t * SD + c8]);
         }
@@ -1117,7 +1148,17 @@ hipError_t launch_prefill_kda(const gdnq_desc &d, float *S, const void *q, const
                      make_divisor((unsigned)(d.H / hk))};
     const unsigned grid = (unsigned)d.B * (unsigned)d.H;
     if (d.dk == 128) {
-        hipLaunchKernelGGL(prefill_kda_ws_kernel<128>, dim3(grid), dim3(kda_ws_threads<128>()), 0, st, A);
+        // workgroups per head: the most of 1, 2, 4 that keeps one workgroup per CU
+        int dev = 0, ncu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (grid * 4u <= (unsigned)ncu)
+            hipLaunchKernelGGL((prefill_kda_ws_kernel<128, 4>), dim3(grid * 4), dim3(kda_ws_threads<4>()), 0, st, A);
+        else if (grid * 2u <= (unsigned)ncu)
+            hipLaunchKernelGGL((prefill_kda_ws_kernel<128, 2>), dim3(grid * 2), dim3(kda_ws_threads<2>()), 0, st, A);
+        else
+            hipLaunchKernelGGL((prefill_kda_ws_kernel<128, 1>), dim3(grid), dim3(kda_ws_threads<1>()), 0, st, A);
     } else {
         hipLaunchKernelGGL(prefill_kda_kernel<64>, dim3(grid), dim3(kda_threads<64>()), 0, st, A);
     }

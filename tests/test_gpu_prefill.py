@@ -241,16 +241,17 @@ def test_prefill_kda_chunk_paths():
     _check(cfg, T, inp, host(S), o_host, S0)
 
 
+@pytest.mark.parametrize("decay", DECAYS)
 @pytest.mark.parametrize("part", ["quarter", "half", "half+1"])
-def test_prefill_heads_per_cu_splits(part):
+def test_prefill_heads_per_cu_splits(part, decay):
     """With fewer heads than CUs, dk = 128 splits each head's value columns
     over 4 (heads <= CUs/4) or 2 (heads <= CUs/2) workgroups, each redoing
     the chunk-local work: head counts on both sides of those lines, against
-    the oracle."""
+    the oracle, for both gates."""
     torch = torch_cuda()
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     H = {"quarter": ncu // 4, "half": ncu // 2, "half+1": ncu // 2 + 1}[part]
-    cfg = _cfg(1, H, 128, seed=57)
+    cfg = _cfg(1, H, 128, seed=57, decay=decay)
     T = 40
     S0 = synth.random_states(27, H, 128, 128, scale=0.5)
     inp, S, o = _run(cfg, T, S0)
