@@ -624,12 +624,13 @@ __global__ __launch_bounds__(kda_threads<D>(), 1) void prefill_kda_kernel(Prefil
 }
 
 // ---------------------------------------------------------------------------
-// Two-group form for D = 128 (twelve waves, one workgroup per head): waves
-// 0-3 (the chunk group) run the chunk-local phases of chunk c + 1 --
+// Two-group form for D = 128 (twelve waves, one workgroup per head; with
+// fewer heads than CUs, NS = 2 or 4 workgroups per head, see the kernel):
+// waves 0-3 (the chunk group) run the chunk-local phases of chunk c + 1 --
 // element-wise operands, the decayed Gram sums, U and W by substitution --
-// while waves 4-11 (the state group, 16 value columns each, two per SIMD)
-// run the state phases of chunk c: U' = U - W S and O = (Q . 2^G) S, the
-// outputs, the state update.  The chunk-local phases do not read S, so the
+// while waves 4 and up (the state group, 16 value columns each, two per
+// SIMD at NS = 1) run the state phases of chunk c: U' = U - W S and
+// O = (Q . 2^G) S, the outputs, the state update.  The chunk-local phases do not read S, so the
 // two chains overlap on the SIMDs.  One iteration, four barriers:
 //   1. chunk group: element-wise operands       state group: U', O products
 //   2. chunk group: Gram products (factored)    state group: -
