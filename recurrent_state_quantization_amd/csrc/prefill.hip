@@ -649,13 +649,17 @@ __global__ __launch_bounds__(D * 2, 1) void prefill_kernel(PrefillArgs A)
 //   phase X  chunk group: the Gram tiles of chunk c+1 (waves 0-2), wave 0
 //            taking A's three tiles and from them T's diagonal blocks
 //            (forward substitution) and its one block merge, in-wave
-//            through LDS;
+//            through LDS; K^T of chunk c+1 from its staged K tile;
 //            state group: chunk c's U' = T2 V - T1 (K S), O = diag(e^g) Q S
 //            + P U' and its stores (each wave its own columns, through
-//            LDS), and the state update;
+//            LDS);
 //   phase Y  chunk group: T1 and T2 of chunk c+1 (wave 0), while waves 1-3
 //            stage chunk c+2 (K, Q, V, the gates) and load chunk c+3;
-//            state group: the split state and chunk c+1's K S and Q S.
+//            state group: chunk c's state update, the split state and chunk
+//            c+1's K S and Q S.
+// (Roles as for NS = 1; a split head rotates the chunk roles, see the
+// kernel.)  The state update sits in phase Y, beside the lighter chunk work:
+// K^T is the one staged tile that phase Y does not rewrite.
 // The state group is WS_SW waves of D / WS_SW value columns; its state stays
 // in MFMA accumulators.  Four waves of 32 columns measured faster than eight
 // of 16 (each LDS operand read then feeds two accumulators).  Tiles are
@@ -791,9 +795,9 @@ __global__ __launch_bounds__(64 * (4 + WS_SW / NS), 1) void prefill_ws_kernel(Pr
         return r;
     };
 
-    // stage chunk c0 into B: K, Q token-major; K^T, V^T through the matrix
-    // cores (exact: one product by 1 per output); the cumulative log2-gates
-    // (padding: gate 1, beta 0)
+    // stage chunk c0 into B: K, Q token-major; V^T through the matrix cores
+    // (exact: one product by 1 per output; K^T follows in the next phase);
+    // the cumulative log2-gates (padding: gate 1, beta 0)
     auto stage = [&](Buf &B, int c0, const WsRegs &r) {
 #pragma unroll
         for (int p = 0; p < 8; p++) {
@@ -802,8 +806,8 @@ __global__ __launch_bounds__(64 * (4 + WS_SW / NS), 1) void prefill_ws_kernel(Pr
             const int row = (16 * tg + ln) * SD + 32 * db + 8 * lg;
             if (role == 1) *reinterpret_cast<u32x4 *>(&B.kr[row]) = x;
             if (role == 2) *reinterpret_cast<u32x4 *>(&B.qr[row]) = x;
-            if (role != 2) {
-                __bf16 *dst = role == 1 ? B.kt : B.vt;
+            if (role == 3) {
+                __bf16 *dst = B.vt;
 #pragma unroll
                 for (int h = 0; h < 2; h++) {
                     const floatx4 tx = mma(__builtin_bit_cast(bf16x8, x), eye[h], floatx4{0.0f, 0.0f, 0.0f, 0.0f});
@@ -994,8 +998,10 @@ __global__ __launch_bounds__(64 * (4 + WS_SW / NS), 1) void prefill_ws_kernel(Pr
     };
 
     // chunk finish on the state group: U' = T2 V - T1 (K S), the outputs
-    // diag(e^g) Q S + P U' (stored by each wave for its columns), and
-    // S <- e^{g_C} S + K^T diag(e^{g_C - g}) U'
+    // diag(e^g) Q S + P U' (stored by each wave for its columns), and the
+    // operands of S <- e^{g_C} S + K^T diag(e^{g_C - g}) U' for phase Y
+    bf16x8 Ghk[ET], Glk[ET];  // U' scaled by e^{g_C - g_j}, split, held from phase X to Y
+    float egck = 0.0f;
     auto finish = [&](Buf &B, int c0) {
         bf16x8 Xh[ET], Xl[ET];  // -(K S) over the chunk's tokens, permuted slots
 #pragma unroll
@@ -1103,22 +1109,46 @@ __global__ __launch_bounds__(64 * (4 + WS_SW / NS), 1) void prefill_ws_kernel(Pr
                         *reinterpret_cast<const u32x4 *>(&L.out[t * SD + col]);
             }
         }
-        const float egc = B.eg[WC - 1];
+#pragma unroll
+        for (int et = 0; et < ET; et++) {
+            Ghk[et] = Gh[et];
+            Glk[et] = Gl[et];
+        }
+        egck = B.eg[WC - 1];
+    };
+    // the state update of chunk c, in phase Y: its K^T is staged a phase late
+    // (from the K tile) and no wave restages it meanwhile; 2^{g_C} was read
+    // in phase X, before the gates were restaged
+    auto state_update = [&](Buf &B) {
 #pragma unroll
         for (int et = 0; et < ET; et++)
 #pragma unroll
-            for (int dt = 0; dt < DT; dt++) S[et][dt] *= egc;
+            for (int dt = 0; dt < DT; dt++) S[et][dt] *= egck;
         bf16x8 ka[DT];
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) ka[dt] = ld_pair(&B.kt[(16 * dt + ln) * SC + 4 * lg]);
 #pragma unroll
         for (int dt = 0; dt < DT; dt++)
 #pragma unroll
-            for (int et = 0; et < ET; et++) S[et][dt] = mma(ka[dt], Gh[et], S[et][dt]);
+            for (int et = 0; et < ET; et++) S[et][dt] = mma(ka[dt], Ghk[et], S[et][dt]);
 #pragma unroll
         for (int dt = 0; dt < DT; dt++)
 #pragma unroll
-            for (int et = 0; et < ET; et++) S[et][dt] = mma(ka[dt], Gl[et], S[et][dt]);
+            for (int et = 0; et < ET; et++) S[et][dt] = mma(ka[dt], Glk[et], S[et][dt]);
+    };
+    // K^T of a staged chunk from its token-major K tile (role 1, phase X)
+    auto stage_kt = [&](Buf &B) {
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            const int tg = p / KB, db = p % KB;
+            const bf16x8 x = ld8(&B.kr[(16 * tg + ln) * SD + 32 * db + 8 * lg]);
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const floatx4 tx = mma(x, eye[h], floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+                *reinterpret_cast<bf16x4 *>(&B.kt[(32 * db + 16 * h + ln) * SC + 16 * tg + 4 * lg]) =
+                    bf16x4{(__bf16)tx[0], (__bf16)tx[1], (__bf16)tx[2], (__bf16)tx[3]};
+            }
+        }
     };
 
     // Wave 0, the staging waves and the state group each run a loop of their
@@ -1160,6 +1190,7 @@ __global__ __launch_bounds__(64 * (4 + WS_SW / NS), 1) void prefill_ws_kernel(Pr
                 if (role == 1) {
                     gram_p(Bk, 0, 0);
                     gram_p(Bk, 1, 0);
+                    stage_kt(Bk);
                 } else if (role == 2) {
                     gram_p(Bk, 1, 1);
                 }
@@ -1188,6 +1219,7 @@ __global__ __launch_bounds__(64 * (4 + WS_SW / NS), 1) void prefill_ws_kernel(Pr
             if (c >= 0) finish(Bs, c * WC);
             __syncthreads();
             // ---- phase Y
+            if (c >= 0) state_update(Bs);
             if (c + 1 >= 0 && c + 1 < nch) state_products(Bk);
             __syncthreads();
         }
